@@ -1,0 +1,163 @@
+/*
+ * libqlora -- a linear layer with a frozen quantized weight and a trainable
+ * low-rank (LoRA) adapter, forward and backward, on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * What is computed (sources are cited by page title and section):
+ *
+ *   y  = x . deq(W) + s . (x A) B,          s = alpha / r
+ *
+ *   - "Parameter-efficient fine-tuning of GPT-2 with LoRA" (keras-io),
+ *     "LoRA equation" and "Create LoRA layer": the adapter output (x A) B is
+ *     added to the frozen layer's output, scaled by alpha / rank; the original
+ *     layer is frozen.
+ *   - "Introduce QLoRA-like technique" (keras PR), "Highlights": the frozen
+ *     kernel is stored as int8 while the adapter is trained in float.
+ *   - keras-llm-light README, "Weights quantization": the adapter weights are
+ *     kept in fp32; "Simplified Int4Variable quantization": two 4-bit values
+ *     per byte.
+ *   - "How to fine-tune the 4-bit model?" (GPTQ-for-LLaMa issue): a 4-bit
+ *     frozen matrix under an fp32 rank-4 adapter; gradients need the product
+ *     with the transposed quantized matrix.
+ *
+ * Readings where the pages give no formula (int8 format QLORA_W8):
+ *   weight scale sw[n] = absmax_k |W[k,n]| / 127 (one per output channel);
+ *   codes q[n,k] = round-half-even(W[k,n] * (127 / absmax)) in [-127, 127];
+ *   activations are quantized the same way with one scale per row of x
+ *   (sx[m]), and the base product is the exact int32 sum of code products,
+ *   rescaled by sx[m] * sw[n].
+ * 4-bit format QLORA_W4G128: one fp16 scale per 128 consecutive inputs of an
+ *   output channel, sc = f16(absmax / 7), codes round-half-even(W * (1/sc)) in
+ *   [-7, 7]; the forward multiplies x (not quantized) by the dequantized weight.
+ * Backward: the activation quantizer is passed straight through,
+ *   dx = dy . deq(W)^T + s (dy B^T) A^T,  dA = s x^T (dy B^T),  dB = s (x A)^T dy,
+ *   and the frozen weight receives no gradient (there is no dW argument).
+ *
+ * Layouts (all row-major, all pointers are DEVICE memory owned by the caller):
+ *   W      float32 [K, N]                 (input to qlora_quantize only)
+ *   codes  QLORA_W8:     int8  [N, K]     (output channel major, K contiguous)
+ *          QLORA_W4G128: uint8 [N, K/2]   (byte j holds k = 2j in the low
+ *                                          nibble, 2j+1 in the high nibble,
+ *                                          two's complement)
+ *   scales QLORA_W8:     float32 [N]
+ *          QLORA_W4G128: float16 [N, K/128]
+ *   x, dx  [M, K] in the compute dtype;  y, dy  [M, N] in the compute dtype
+ *   A, dA  float32 [K, r];               B, dB  float32 [r, N]
+ *   t      float32 [M, r]  (t = x A, unscaled; saved by the forward)
+ *
+ * Conventions shared by every entry point:
+ *   - The library never allocates, frees or synchronizes. Work is enqueued on
+ *     `stream` (a hipStream_t; NULL = the default stream) and the call returns
+ *     immediately. Scratch memory is passed in as `ws` of `ws_bytes`, sized by
+ *     the matching *_workspace query; it may be reused between calls that are
+ *     ordered on one stream.
+ *   - Arguments are validated before anything is launched; a non-OK status
+ *     means nothing was enqueued. Device faults surface at the caller's next
+ *     synchronization.
+ *   - Constraints: 1 <= M, 16 <= K, 16 <= N, K % 16 == 0, N % 16 == 0,
+ *     1 <= r <= 32, all pointers 16-byte aligned; QLORA_W4G128 needs
+ *     K % 128 == 0 and the bf16 compute dtype.
+ *   - Outputs (y, t, dx, dA, dB) are overwritten, never accumulated into.
+ *     codes, scales, A and B are only read by qlora_fwd / qlora_bwd.
+ *   - Non-finite x or dy propagate into the outputs; nothing is checked on
+ *     the hot path.
+ *   - Results do not depend on how the work is split across the GPU: every
+ *     reduction has a fixed order, so repeated calls give identical bytes.
+ *   - The library holds no mutable global state; calls on different streams
+ *     may run concurrently as long as their buffers do not overlap.
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_EINVAL = 1,       /* bad pointer, size, alignment or enum */
+  QLORA_EUNSUPPORTED = 2, /* valid but not implemented (e.g. W4 with f32) */
+  QLORA_EWORKSPACE = 3,   /* ws smaller than the *_workspace query */
+  QLORA_ERANGE = 4,       /* size products overflow the index range */
+  QLORA_EHIP = 5          /* a kernel launch was rejected by the runtime */
+} qlora_status;
+
+typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
+typedef enum { QLORA_W8 = 0, QLORA_W4G128 = 1 } qlora_wfmt;
+
+/* One frozen layer with its adapter. All pointers are device memory owned by
+ * the caller and only read by the library. */
+typedef struct {
+  int32_t K, N, r;        /* in-features, out-features, adapter rank */
+  float alpha;            /* s = alpha / r, computed as one float32 divide */
+  int32_t fmt;            /* qlora_wfmt */
+  const void* codes;      /* see "Layouts" */
+  const void* scales;     /* see "Layouts" */
+  const float* A;         /* [K, r] */
+  const float* B;         /* [r, N] */
+} qlora_linear;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* qlora_status_str(int status);
+
+/* Bytes needed for the codes and scales of a K x N weight in format fmt.
+ * Host-only arithmetic; usable without a GPU. */
+int qlora_weight_bytes(int K, int N, int fmt, size_t* codes_bytes,
+                       size_t* scale_bytes);
+
+/* Quantize a float32 weight W [K, N] into codes and scales (format above).
+ * One-time preparation of the frozen weight ("Introduce QLoRA-like
+ * technique", benchmark.py: model.quantize("int8")). Channels (W8) or groups
+ * (W4G128) whose abs-max is 0 -- or so small that the inverse scale
+ * overflows (W8) -- get scale 0 and zero codes; a non-finite abs-max, or an
+ * fp16 scale overflow (W4G128), stores a NaN scale and zero codes so that
+ * the NaN reaches every output that uses it. W is only read. */
+int qlora_quantize(const float* W, int K, int N, int fmt, void* codes,
+                   void* scales, void* stream);
+
+/* Workspace needed by qlora_fwd / qlora_fwd_acc for M rows. */
+int qlora_fwd_workspace(const qlora_linear* L, int M, int dtype,
+                        size_t* bytes);
+
+/* Forward ("LoRA equation"): y [M, N] = x . deq(W) + s (x A) B, rounded once
+ * to the compute dtype. For QLORA_W8, x is quantized per row and the base
+ * product is an int8 x int8 -> int32 sum rescaled by sx[m] * sw[n]. If t_save
+ * is not NULL, t = x A (float32 [M, r]) is written there for the backward. */
+int qlora_fwd(const qlora_linear* L, int M, int dtype, const void* x, void* y,
+              float* t_save, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace needed by qlora_bwd for M rows. */
+int qlora_bwd_workspace(const qlora_linear* L, int M, int dtype,
+                        size_t* bytes);
+
+/* Backward of qlora_fwd for the output gradient dy [M, N]:
+ *   u  = dy B^T                                   (float32, internal)
+ *   dB = s t^T dy          float32 [r, N]
+ *   dA = s x^T u           float32 [K, r]
+ *   dx = dy deq(W)^T + s u A^T   [M, K] in the compute dtype (skipped if NULL)
+ * t_saved is the t written by qlora_fwd; pass NULL to recompute it from x.
+ * The frozen weight gets no gradient ("Why does LoRA reduce memory
+ * footprint?": only the adapter is trained). */
+int qlora_bwd(const qlora_linear* L, int M, int dtype, const void* x,
+              const void* dy, const float* t_saved, void* dx, float* dA,
+              float* dB, void* ws, size_t ws_bytes, void* stream);
+
+/* Test hook: the forward's per-row activation quantizer alone. x [M, K] in
+ * the compute dtype -> xq int8 [M, K], sx float32 [M]. Same kernel as
+ * qlora_fwd. */
+int qlora_quantize_rows(const void* x, int M, int K, int dtype, int8_t* xq,
+                        float* sx, void* stream);
+
+/* Test hook: the forward's exact int32 product acc [M, N] = xq . codes^T for
+ * QLORA_W8 (same quantizer and main loop as qlora_fwd, integer output). */
+int qlora_fwd_acc(const qlora_linear* L, int M, int dtype, const void* x,
+                  int32_t* acc, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H */

@@ -1,0 +1,241 @@
+"""Thin ctypes binding of libqlora (include/qlora.h), same names as the C ABI.
+
+Argument marshalling only: every step of the computation runs in the HIP
+library. PyTorch provides device memory (outputs and workspaces are
+allocated here with torch) and the stream (torch's current stream).
+If libqlora.so is missing, every call raises: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqlora.so")
+
+QLORA_OK, QLORA_EINVAL, QLORA_EUNSUPPORTED, QLORA_EWORKSPACE, QLORA_ERANGE, QLORA_EHIP = range(6)
+QLORA_F32, QLORA_BF16 = 0, 1
+QLORA_W8, QLORA_W4G128 = 0, 1
+
+_FMT = {"w8": QLORA_W8, "w4g128": QLORA_W4G128}
+
+
+class QloraError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {qlora_status_str(status)} ({status})")
+
+
+class qlora_linear(ctypes.Structure):
+    _fields_ = [
+        ("K", ctypes.c_int32),
+        ("N", ctypes.c_int32),
+        ("r", ctypes.c_int32),
+        ("alpha", ctypes.c_float),
+        ("fmt", ctypes.c_int32),
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("A", ctypes.c_void_p),
+        ("B", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+EXPORTS = (
+    "qlora_status_str", "qlora_weight_bytes", "qlora_quantize",
+    "qlora_fwd_workspace", "qlora_fwd", "qlora_bwd_workspace", "qlora_bwd",
+    "qlora_quantize_rows", "qlora_fwd_acc",
+)
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqlora.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m quantized_frozen_weight_amd.build_lib`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    psz = ctypes.POINTER(ctypes.c_size_t)
+    plin = ctypes.POINTER(qlora_linear)
+    L.qlora_status_str.argtypes = [i]
+    L.qlora_status_str.restype = ctypes.c_char_p
+    L.qlora_weight_bytes.argtypes = [i, i, i, psz, psz]
+    L.qlora_quantize.argtypes = [vp, i, i, i, vp, vp, vp]
+    L.qlora_fwd_workspace.argtypes = [plin, i, i, psz]
+    L.qlora_fwd.argtypes = [plin, i, i, vp, vp, vp, vp, sz, vp]
+    L.qlora_bwd_workspace.argtypes = [plin, i, i, psz]
+    L.qlora_bwd.argtypes = [plin, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.qlora_quantize_rows.argtypes = [vp, i, i, i, vp, vp, vp]
+    L.qlora_fwd_acc.argtypes = [plin, i, i, vp, vp, vp, sz, vp]
+    for name in EXPORTS[1:]:
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str) -> None:
+    if status != QLORA_OK:
+        raise QloraError(status, what)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return QLORA_F32
+    if t.dtype == torch.bfloat16:
+        return QLORA_BF16
+    raise TypeError(f"unsupported activation dtype {t.dtype}")
+
+
+def qlora_status_str(status: int) -> str:
+    return lib().qlora_status_str(int(status)).decode()
+
+
+def qlora_weight_bytes(K: int, N: int, fmt: str = "w8") -> Tuple[int, int]:
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().qlora_weight_bytes(K, N, _FMT[fmt], ctypes.byref(cb), ctypes.byref(sb)),
+           "qlora_weight_bytes")
+    return cb.value, sb.value
+
+
+@dataclass
+class QLinear:
+    """A frozen quantized weight plus its adapter (device tensors)."""
+    K: int
+    N: int
+    r: int
+    alpha: float
+    fmt: str
+    codes: object     # int8 [N, K]  or uint8 [N, K/2]
+    scales: object    # float32 [N] or float16 [N, K/128]
+    A: object         # float32 [K, r]
+    B: object         # float32 [r, N]
+
+    def cstruct(self) -> qlora_linear:
+        return qlora_linear(self.K, self.N, self.r, float(self.alpha), _FMT[self.fmt],
+                            _ptr(self.codes), _ptr(self.scales), _ptr(self.A),
+                            _ptr(self.B))
+
+
+def qlora_quantize(W, fmt: str = "w8"):
+    """W float32 [K, N] on the GPU -> (codes, scales) in the library's layout."""
+    import torch
+    K, N = W.shape
+    cb, sb = qlora_weight_bytes(K, N, fmt)
+    if fmt == "w8":
+        codes = torch.empty((N, K), dtype=torch.int8, device=W.device)
+        scales = torch.empty((N,), dtype=torch.float32, device=W.device)
+    else:
+        codes = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+        scales = torch.empty((N, K // 128), dtype=torch.float16, device=W.device)
+    assert codes.numel() * codes.element_size() == cb
+    assert scales.numel() * scales.element_size() == sb
+    W = W.contiguous()
+    _check(lib().qlora_quantize(_ptr(W), K, N, _FMT[fmt], _ptr(codes), _ptr(scales),
+                                _stream()), "qlora_quantize")
+    return codes, scales
+
+
+def qlora_fwd_workspace(layer: QLinear, M: int, dtype: int) -> int:
+    n = ctypes.c_size_t()
+    s = layer.cstruct()
+    _check(lib().qlora_fwd_workspace(ctypes.byref(s), M, dtype, ctypes.byref(n)),
+           "qlora_fwd_workspace")
+    return n.value
+
+
+def qlora_bwd_workspace(layer: QLinear, M: int, dtype: int) -> int:
+    n = ctypes.c_size_t()
+    s = layer.cstruct()
+    _check(lib().qlora_bwd_workspace(ctypes.byref(s), M, dtype, ctypes.byref(n)),
+           "qlora_bwd_workspace")
+    return n.value
+
+
+def _workspace(nbytes: int, device, ws=None):
+    import torch
+    if ws is not None:
+        return ws
+    return torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=device)
+
+
+def qlora_fwd(layer: QLinear, x, save_t: bool = True, y=None, t=None, ws=None):
+    """y = x deq(W) + s (x A) B. Returns (y, t) (t is None if not saved)."""
+    import torch
+    M = x.shape[0]
+    dt = _dtype_code(x)
+    if y is None:
+        y = torch.empty((M, layer.N), dtype=x.dtype, device=x.device)
+    if save_t and t is None:
+        t = torch.empty((M, layer.r), dtype=torch.float32, device=x.device)
+    nbytes = qlora_fwd_workspace(layer, M, dt)
+    ws = _workspace(nbytes, x.device, ws)
+    s = layer.cstruct()
+    _check(lib().qlora_fwd(ctypes.byref(s), M, dt, _ptr(x), _ptr(y),
+                           _ptr(t) if save_t else None, _ptr(ws),
+                           ws.numel() * ws.element_size(), _stream()), "qlora_fwd")
+    return y, (t if save_t else None)
+
+
+def qlora_bwd(layer: QLinear, x, dy, t=None, need_dx: bool = True, dx=None,
+              dA=None, dB=None, ws=None):
+    """Returns (dx or None, dA [K, r], dB [r, N])."""
+    import torch
+    M = x.shape[0]
+    dt = _dtype_code(x)
+    if need_dx and dx is None:
+        dx = torch.empty((M, layer.K), dtype=x.dtype, device=x.device)
+    if dA is None:
+        dA = torch.empty((layer.K, layer.r), dtype=torch.float32, device=x.device)
+    if dB is None:
+        dB = torch.empty((layer.r, layer.N), dtype=torch.float32, device=x.device)
+    nbytes = qlora_bwd_workspace(layer, M, dt)
+    ws = _workspace(nbytes, x.device, ws)
+    s = layer.cstruct()
+    _check(lib().qlora_bwd(ctypes.byref(s), M, dt, _ptr(x), _ptr(dy), _ptr(t),
+                           _ptr(dx) if need_dx else None, _ptr(dA), _ptr(dB),
+                           _ptr(ws), ws.numel() * ws.element_size(), _stream()),
+           "qlora_bwd")
+    return (dx if need_dx else None), dA, dB
+
+
+def qlora_quantize_rows(x):
+    """Test hook: (xq int8 [M, K], sx float32 [M]) from the forward's quantizer."""
+    import torch
+    M, K = x.shape
+    xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    sx = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(lib().qlora_quantize_rows(_ptr(x), M, K, _dtype_code(x), _ptr(xq), _ptr(sx),
+                                     _stream()), "qlora_quantize_rows")
+    return xq, sx
+
+
+def qlora_fwd_acc(layer: QLinear, x):
+    """Test hook: exact int32 product of the quantized rows and codes [M, N]."""
+    import torch
+    M = x.shape[0]
+    dt = _dtype_code(x)
+    acc = torch.empty((M, layer.N), dtype=torch.int32, device=x.device)
+    ws = _workspace(qlora_fwd_workspace(layer, M, dt), x.device)
+    s = layer.cstruct()
+    _check(lib().qlora_fwd_acc(ctypes.byref(s), M, dt, _ptr(x), _ptr(acc), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream()),
+           "qlora_fwd_acc")
+    return acc

@@ -1,0 +1,274 @@
+// C ABI of libqlora: argument validation, workspace layout, and the kernel
+// sequence of each call. Contract and citations: include/qlora.h.
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+#include "qlora.h"
+
+namespace {
+
+using namespace qlora;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+inline bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+inline bool fits_int(long long a, long long b) {
+  return a > 0 && b > 0 && a * b < (1LL << 31);
+}
+
+int check_dtype(int dtype) {
+  return (dtype == QLORA_F32 || dtype == QLORA_BF16) ? QLORA_OK : QLORA_EINVAL;
+}
+
+int check_shape(int M, int K, int N, int r) {
+  if (M < 1 || K < 16 || N < 16 || r < 1 || r > 32) return QLORA_EINVAL;
+  if (K % 16 || N % 16) return QLORA_EINVAL;
+  if (!fits_int(M, K) || !fits_int(M, N) || !fits_int(K, N)) return QLORA_ERANGE;
+  return QLORA_OK;
+}
+
+// Validate a layer description (weights only; data pointers are checked by
+// the individual calls).
+int check_linear(const qlora_linear* L, int M, int dtype) {
+  if (L == nullptr) return QLORA_EINVAL;
+  int st = check_dtype(dtype);
+  if (st) return st;
+  st = check_shape(M, L->K, L->N, L->r);
+  if (st) return st;
+  if (L->fmt != QLORA_W8 && L->fmt != QLORA_W4G128) return QLORA_EINVAL;
+  if (L->fmt == QLORA_W4G128) {
+    if (L->K % 128) return QLORA_EINVAL;
+    if (dtype != QLORA_BF16) return QLORA_EUNSUPPORTED;
+  }
+  const void* ptrs[4] = {L->codes, L->scales, L->A, L->B};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return QLORA_EINVAL;
+  return QLORA_OK;
+}
+
+inline float lora_s(const qlora_linear* L) {
+  return L->alpha / (float)L->r;   // one float32 divide
+}
+
+struct FwdLayout {
+  size_t xq, sx, t, total;
+};
+FwdLayout fwd_layout(const qlora_linear* L, int M) {
+  FwdLayout w{};
+  size_t off = 0;
+  if (L->fmt == QLORA_W8) {
+    w.xq = off; off = align_up(off + (size_t)M * L->K);
+    w.sx = off; off = align_up(off + (size_t)M * 4);
+  }
+  w.t = off; off = align_up(off + (size_t)M * L->r * 4);
+  w.total = off;
+  return w;
+}
+
+struct BwdLayout {
+  size_t t, u, dys, pB, pA, total;
+};
+BwdLayout bwd_layout(const qlora_linear* L, int M, int dtype) {
+  BwdLayout w{};
+  size_t off = 0;
+  w.t = off; off = align_up(off + (size_t)M * L->r * 4);
+  w.u = off; off = align_up(off + (size_t)M * L->r * 4);
+  w.dys = off;
+  if (L->fmt == QLORA_W8 && dtype == QLORA_BF16) off = align_up(off + (size_t)M * L->N * 2);
+  w.pB = off; off = align_up(off + skinny_partial_floats(M, L->r, L->N) * 4);
+  w.pA = off; off = align_up(off + skinny_partial_floats(M, L->r, L->K) * 4);
+  w.total = off;
+  return w;
+}
+
+inline char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? QLORA_OK : QLORA_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qlora_status_str(int status) {
+  switch (status) {
+    case QLORA_OK: return "ok";
+    case QLORA_EINVAL: return "invalid argument";
+    case QLORA_EUNSUPPORTED: return "unsupported combination";
+    case QLORA_EWORKSPACE: return "workspace too small";
+    case QLORA_ERANGE: return "size out of range";
+    case QLORA_EHIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+int qlora_weight_bytes(int K, int N, int fmt, size_t* codes_bytes,
+                       size_t* scale_bytes) {
+  if (codes_bytes == nullptr || scale_bytes == nullptr) return QLORA_EINVAL;
+  if (K < 16 || N < 16 || K % 16 || N % 16) return QLORA_EINVAL;
+  if (!fits_int(K, N)) return QLORA_ERANGE;
+  if (fmt == QLORA_W8) {
+    *codes_bytes = (size_t)K * N;
+    *scale_bytes = (size_t)N * 4;
+    return QLORA_OK;
+  }
+  if (fmt == QLORA_W4G128) {
+    if (K % 128) return QLORA_EINVAL;
+    *codes_bytes = (size_t)K * N / 2;
+    *scale_bytes = (size_t)N * (K / 128) * 2;
+    return QLORA_OK;
+  }
+  return QLORA_EINVAL;
+}
+
+int qlora_quantize(const float* W, int K, int N, int fmt, void* codes,
+                   void* scales, void* stream) {
+  size_t cb, sb;
+  int st = qlora_weight_bytes(K, N, fmt, &cb, &sb);
+  if (st) return st;
+  if (!W || !codes || !scales || !aligned16(W) || !aligned16(codes) || !aligned16(scales))
+    return QLORA_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (fmt == QLORA_W8)
+    launch_quantize_w8(W, K, N, static_cast<int8_t*>(codes),
+                       static_cast<float*>(scales), s);
+  else
+    launch_quantize_w4(W, K, N, static_cast<uint8_t*>(codes),
+                       static_cast<_Float16*>(scales), s);
+  return launch_status();
+}
+
+int qlora_fwd_workspace(const qlora_linear* L, int M, int dtype, size_t* bytes) {
+  if (bytes == nullptr) return QLORA_EINVAL;
+  int st = check_linear(L, M, dtype);
+  if (st) return st;
+  *bytes = fwd_layout(L, M).total;
+  return QLORA_OK;
+}
+
+int qlora_fwd(const qlora_linear* L, int M, int dtype, const void* x, void* y,
+              float* t_save, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_linear(L, M, dtype);
+  if (st) return st;
+  if (!x || !y || !aligned16(x) || !aligned16(y)) return QLORA_EINVAL;
+  if (t_save && !aligned16(t_save)) return QLORA_EINVAL;
+  const FwdLayout w = fwd_layout(L, M);
+  if (ws_bytes < w.total || (w.total && (!ws || !aligned16(ws)))) return QLORA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* t = t_save ? t_save : reinterpret_cast<float*>(at(ws, w.t));
+  (void)hipGetLastError();
+  if (L->fmt == QLORA_W8) {
+    int8_t* xq = reinterpret_cast<int8_t*>(at(ws, w.xq));
+    float* sx = reinterpret_cast<float*>(at(ws, w.sx));
+    launch_rowquant(dtype, x, M, L->K, L->A, L->r, xq, sx, t, s);
+    launch_gemm_fwd_w8(dtype, M, L->N, L->K, xq,
+                       static_cast<const int8_t*>(L->codes), sx,
+                       static_cast<const float*>(L->scales), t, L->B, L->r,
+                       lora_s(L), y, nullptr, s);
+  } else {
+    launch_lora_down(dtype, x, M, L->K, L->A, L->r, t, s);
+    launch_gemm_fwd_w4(M, L->N, L->K, static_cast<const uint16_t*>(x),
+                       static_cast<const uint8_t*>(L->codes),
+                       static_cast<const _Float16*>(L->scales), t, L->B, L->r,
+                       lora_s(L), static_cast<uint16_t*>(y), s);
+  }
+  return launch_status();
+}
+
+int qlora_bwd_workspace(const qlora_linear* L, int M, int dtype, size_t* bytes) {
+  if (bytes == nullptr) return QLORA_EINVAL;
+  int st = check_linear(L, M, dtype);
+  if (st) return st;
+  *bytes = bwd_layout(L, M, dtype).total;
+  return QLORA_OK;
+}
+
+int qlora_bwd(const qlora_linear* L, int M, int dtype, const void* x,
+              const void* dy, const float* t_saved, void* dx, float* dA,
+              float* dB, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_linear(L, M, dtype);
+  if (st) return st;
+  if (!x || !dy || !dA || !dB) return QLORA_EINVAL;
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(dA) || !aligned16(dB)) return QLORA_EINVAL;
+  if ((t_saved && !aligned16(t_saved)) || (dx && !aligned16(dx))) return QLORA_EINVAL;
+  const BwdLayout w = bwd_layout(L, M, dtype);
+  if (ws_bytes < w.total || !ws || !aligned16(ws)) return QLORA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float sc = lora_s(L);
+  float* u = reinterpret_cast<float*>(at(ws, w.u));
+  (void)hipGetLastError();
+  const float* t = t_saved;
+  if (t == nullptr) {
+    float* tw = reinterpret_cast<float*>(at(ws, w.t));
+    launch_lora_down(dtype, x, M, L->K, L->A, L->r, tw, s);
+    t = tw;
+  }
+  const bool w8 = L->fmt == QLORA_W8;
+  uint16_t* dys = (w8 && dtype == QLORA_BF16)
+                      ? reinterpret_cast<uint16_t*>(at(ws, w.dys)) : nullptr;
+  launch_bwd_rows(dtype, dy, M, L->N, L->B, L->r,
+                  w8 ? static_cast<const float*>(L->scales) : nullptr, dys, u, s);
+  launch_skinny(dtype, M, L->r, L->N, t, dy, sc, dB, false,
+                reinterpret_cast<float*>(at(ws, w.pB)), s);
+  launch_skinny(dtype, M, L->r, L->K, u, x, sc, dA, true,
+                reinterpret_cast<float*>(at(ws, w.pA)), s);
+  if (dx != nullptr) {
+    if (w8 && dtype == QLORA_BF16)
+      launch_gemm_dx_w8(M, L->K, L->N, dys, static_cast<const int8_t*>(L->codes),
+                        u, L->A, L->r, sc, static_cast<uint16_t*>(dx), s);
+    else if (w8)
+      launch_gemm_dx_f32(M, L->K, L->N, static_cast<const float*>(dy),
+                         static_cast<const int8_t*>(L->codes),
+                         static_cast<const float*>(L->scales), u, L->A, L->r,
+                         sc, static_cast<float*>(dx), s);
+    else
+      launch_gemm_dx_w4(M, L->K, L->N, static_cast<const uint16_t*>(dy),
+                        static_cast<const uint8_t*>(L->codes),
+                        static_cast<const _Float16*>(L->scales), u, L->A,
+                        L->r, sc, static_cast<uint16_t*>(dx), s);
+  }
+  return launch_status();
+}
+
+int qlora_quantize_rows(const void* x, int M, int K, int dtype, int8_t* xq,
+                        float* sx, void* stream) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if (M < 1 || K < 16 || K % 16) return QLORA_EINVAL;
+  if (!fits_int(M, K)) return QLORA_ERANGE;
+  if (!x || !xq || !sx || !aligned16(x) || !aligned16(xq) || !aligned16(sx))
+    return QLORA_EINVAL;
+  (void)hipGetLastError();
+  launch_rowquant(dtype, x, M, K, nullptr, 1, xq, sx, nullptr,
+                  static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int qlora_fwd_acc(const qlora_linear* L, int M, int dtype, const void* x,
+                  int32_t* acc, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_linear(L, M, dtype);
+  if (st) return st;
+  if (L->fmt != QLORA_W8) return QLORA_EUNSUPPORTED;
+  if (!x || !acc || !aligned16(x) || !aligned16(acc)) return QLORA_EINVAL;
+  const FwdLayout w = fwd_layout(L, M);
+  if (ws_bytes < w.total || !ws || !aligned16(ws)) return QLORA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int8_t* xq = reinterpret_cast<int8_t*>(at(ws, w.xq));
+  float* sx = reinterpret_cast<float*>(at(ws, w.sx));
+  (void)hipGetLastError();
+  launch_rowquant(dtype, x, M, L->K, nullptr, 1, xq, sx, nullptr, s);
+  launch_gemm_fwd_w8(dtype, M, L->N, L->K, xq,
+                     static_cast<const int8_t*>(L->codes), sx,
+                     static_cast<const float*>(L->scales), nullptr, L->B,
+                     L->r, 0.f, nullptr, acc, s);
+  return launch_status();
+}
+
+}  // extern "C"

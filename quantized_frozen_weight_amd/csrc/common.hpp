@@ -1,0 +1,124 @@
+// Shared device helpers for libqlora (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+namespace qlora {
+
+constexpr int kWave = 64;
+
+// ---- dtype tags -----------------------------------------------------------
+struct F32 {};   // float32 activations / gradients
+struct BF16 {};  // bfloat16 activations / gradients (stored as uint16_t)
+
+template <typename T> struct Elem;
+template <> struct Elem<F32> { typedef float type; static constexpr int bytes = 4; };
+template <> struct Elem<BF16> { typedef uint16_t type; static constexpr int bytes = 2; };
+
+// ---- bfloat16 ---------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+
+// float32 -> bfloat16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Small integers (|v| < 256) are exact in bfloat16: take the upper half of
+// the float32 pattern, no rounding needed.
+__device__ __forceinline__ uint32_t pack_int_bf16x2(int lo, int hi) {
+  return (__float_as_uint((float)lo) >> 16) |
+         (__float_as_uint((float)hi) & 0xffff0000u);
+}
+
+// ---- 8-element loads/stores of a row in either dtype -----------------------
+__device__ __forceinline__ void load8(const float* p, float v[8]) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void load8(const uint16_t* p, float v[8]) {
+  u32x4 a = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(a[i] << 16);
+    v[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_out(uint16_t* p, float v) {
+  *p = (uint16_t)f32_to_bf16(v);
+}
+
+// ---- wave reductions ---------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t w = __shfl_xor(v, o, kWave);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// ---- abs-max quantizer shared by weights and activations ----------------------
+// |v| as an ordered integer: for non-negative floats the bit patterns sort like
+// the values, and every NaN pattern sorts above +inf, so an integer max over
+// |v| yields NaN when any element is NaN.
+__device__ __forceinline__ uint32_t abs_bits(float v) {
+  return __float_as_uint(v) & 0x7fffffffu;
+}
+
+struct QuantParams {
+  float inv;    // 127 / absmax (meaningful only when live)
+  float scale;  // stored scale: absmax / 127, 0, or NaN
+  bool live;    // false -> every code is 0
+};
+
+// One float32 divide each for the inverse and the scale; see the header for
+// the zero / overflow / non-finite rules.
+__device__ __forceinline__ QuantParams absmax_params(uint32_t amax_bits,
+                                                     float qmax) {
+  QuantParams p;
+  float a = __uint_as_float(amax_bits);
+  if (amax_bits >= 0x7f800000u) {  // inf or NaN
+    p.inv = 0.f; p.scale = __uint_as_float(0x7fc00000u); p.live = false;
+    return p;
+  }
+  float inv = qmax / a;
+  if (amax_bits == 0u || __float_as_uint(inv) >= 0x7f800000u) {
+    p.inv = 0.f; p.scale = 0.f; p.live = false;
+    return p;
+  }
+  p.inv = inv; p.scale = a / qmax; p.live = true;
+  return p;
+}
+
+__device__ __forceinline__ int quant_code(float v, float inv, float qmax) {
+  float q = __builtin_rintf(v * inv);   // v_rndne_f32: ties to even
+  q = fminf(fmaxf(q, -qmax), qmax);
+  return (int)q;
+}
+
+}  // namespace qlora

@@ -1,0 +1,61 @@
+// Internal launchers (one per kernel family). Shapes are validated by the
+// C-ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlora {
+
+// dtype: 0 = float32, 1 = bfloat16 (matches qlora_dtype)
+
+void launch_quantize_w8(const float* W, int K, int N, int8_t* codes,
+                        float* scales, hipStream_t st);
+void launch_quantize_w4(const float* W, int K, int N, uint8_t* packed,
+                        _Float16* scales, hipStream_t st);
+
+void launch_rowquant(int dtype, const void* x, int M, int K, const float* A,
+                     int r, int8_t* xq, float* sx, float* t, hipStream_t st);
+void launch_lora_down(int dtype, const void* x, int M, int K, const float* A,
+                      int r, float* t, hipStream_t st);
+
+// y = acc * sx[m] * sw[n] + s * t B   (acc_out != nullptr: write int32 acc)
+void launch_gemm_fwd_w8(int dtype, int M, int N, int K, const int8_t* xq,
+                        const int8_t* codes, const float* sx, const float* sw,
+                        const float* t, const float* B, int r, float s,
+                        void* y, int32_t* acc_out, hipStream_t st);
+// y = x deq4(W) + s * t B   (bf16 x and y)
+void launch_gemm_fwd_w4(int M, int N, int K, const uint16_t* x,
+                        const uint8_t* packed, const _Float16* scales,
+                        const float* t, const float* B, int r, float s,
+                        uint16_t* y, hipStream_t st);
+
+// u = dy B^T (float32 [M, r]); if dys != nullptr also dys = bf16(dy * sw[n])
+void launch_bwd_rows(int dtype, const void* dy, int M, int N, const float* B,
+                     int r, const float* sw, uint16_t* dys, float* u,
+                     hipStream_t st);
+
+// out = s * P^T Q over the M rows, P float32 [M, r], Q [M, C] in dtype.
+// transpose_out = false: out[j * C + c] (dB [r, N]); true: out[c * r + j]
+// (dA [K, r]). partial: workspace of skinny_partial_floats(M, r, C) floats.
+size_t skinny_partial_floats(int M, int r, int C);
+void launch_skinny(int dtype, int M, int r, int C, const float* P,
+                   const void* Q, float s, float* out, bool transpose_out,
+                   float* partial, hipStream_t st);
+
+// dx = dys codes + s u A^T   (bf16; dys = dy * sw already folded)
+void launch_gemm_dx_w8(int M, int K, int N, const uint16_t* dys,
+                       const int8_t* codes, const float* u, const float* A,
+                       int r, float s, uint16_t* dx, hipStream_t st);
+// dx = dy (codes * sw)^T + s u A^T in float32
+void launch_gemm_dx_f32(int M, int K, int N, const float* dy,
+                        const int8_t* codes, const float* sw, const float* u,
+                        const float* A, int r, float s, float* dx,
+                        hipStream_t st);
+// dx = dy deq4(W)^T + s u A^T   (bf16)
+void launch_gemm_dx_w4(int M, int K, int N, const uint16_t* dy,
+                       const uint8_t* packed, const _Float16* scales,
+                       const float* u, const float* A, int r, float s,
+                       uint16_t* dx, hipStream_t st);
+
+}  // namespace qlora

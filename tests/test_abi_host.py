@@ -1,0 +1,156 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+* libqlora.so loads and exports every function include/qlora.h declares;
+* size arithmetic against sizes printed on the pages (tests/golden);
+* argument validation returns the documented status before any launch.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_frozen_weight_amd import binding as Q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "page_sizes.txt")
+
+FAKE = 0x100000   # aligned, never dereferenced: every call below fails validation
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return Q.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(qlora_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    for n in ("qlora_quantize", "qlora_fwd", "qlora_bwd", "qlora_fwd_workspace",
+              "qlora_bwd_workspace", "qlora_weight_bytes", "qlora_status_str",
+              "qlora_quantize_rows", "qlora_fwd_acc"):
+        assert n in names
+    assert set(names) == set(Q.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert Q.qlora_status_str(code)
+    assert Q.qlora_status_str(99) == "unknown status"
+
+
+def _golden():
+    rows = []
+    for line in open(GOLDEN):
+        line = line.split("#")[0].strip()
+        if line:
+            name, K, N, r, val = line.split()
+            rows.append((name, int(K), int(N), int(r), float(val)))
+    return rows
+
+
+def test_sizes_match_the_pages(lib):
+    for name, K, N, r, val in _golden():
+        if name == "fp32_kernel_mib":
+            # the frozen kernel the pages list in float32 ...
+            assert round(K * N * 4 / 2 ** 20, 3) == val
+            # ... is a quarter of that as int8 codes, an eighth as 4-bit
+            cb, sb = Q.qlora_weight_bytes(K, N, "w8")
+            assert cb * 4 == K * N * 4 and sb == N * 4
+            cb4, sb4 = Q.qlora_weight_bytes(K, N, "w4g128")
+            assert cb4 * 8 == K * N * 4 and sb4 == N * (K // 128) * 2
+        elif name == "fp32_lora_A_mib":
+            assert round(K * r * 4 / 2 ** 20, 3) == val
+        elif name == "dense_params":
+            assert K * N == val
+        elif name == "lora_params":
+            assert r * (K + N) == val
+
+
+def test_weight_bytes_rejects_bad_shapes(lib):
+    for K, N, fmt in ((8, 16, "w8"), (16, 20, "w8"), (144, 16, "w4g128")):
+        with pytest.raises(Q.QloraError) as e:
+            Q.qlora_weight_bytes(K, N, fmt)
+        assert e.value.status == Q.QLORA_EINVAL
+
+
+def _lin(K=256, N=256, r=4, fmt=Q.QLORA_W8, ptr=FAKE):
+    return Q.qlora_linear(K, N, r, 8.0, fmt, ptr, ptr, ptr, ptr)
+
+
+def _fwd_ws(lib, lin, M=64, dtype=Q.QLORA_BF16):
+    n = ctypes.c_size_t()
+    st = lib.qlora_fwd_workspace(ctypes.byref(lin), M, dtype, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_queries(lib):
+    st, n = _fwd_ws(lib, _lin())
+    assert st == Q.QLORA_OK and n >= 64 * 256 + 64 * 4 + 64 * 4 * 4
+    n2 = ctypes.c_size_t()
+    assert lib.qlora_bwd_workspace(ctypes.byref(_lin()), 64, Q.QLORA_BF16,
+                                   ctypes.byref(n2)) == Q.QLORA_OK
+    assert n2.value >= 64 * 256 * 2
+
+
+@pytest.mark.parametrize("kw,M,dtype,want", [
+    (dict(r=0), 64, Q.QLORA_BF16, Q.QLORA_EINVAL),
+    (dict(r=33), 64, Q.QLORA_BF16, Q.QLORA_EINVAL),
+    (dict(K=200), 64, Q.QLORA_BF16, Q.QLORA_EINVAL),
+    (dict(N=8), 64, Q.QLORA_BF16, Q.QLORA_EINVAL),
+    (dict(), 0, Q.QLORA_BF16, Q.QLORA_EINVAL),
+    (dict(), 64, 7, Q.QLORA_EINVAL),
+    (dict(fmt=5), 64, Q.QLORA_BF16, Q.QLORA_EINVAL),
+    (dict(fmt=Q.QLORA_W4G128, K=192), 64, Q.QLORA_BF16, Q.QLORA_EINVAL),
+    (dict(fmt=Q.QLORA_W4G128), 64, Q.QLORA_F32, Q.QLORA_EUNSUPPORTED),
+    (dict(ptr=FAKE + 4), 64, Q.QLORA_BF16, Q.QLORA_EINVAL),
+    (dict(ptr=None), 64, Q.QLORA_BF16, Q.QLORA_EINVAL),
+    (dict(K=65536, N=65536), 64, Q.QLORA_BF16, Q.QLORA_ERANGE),
+])
+def test_layer_validation(lib, kw, M, dtype, want):
+    st, _ = _fwd_ws(lib, _lin(**kw), M, dtype)
+    assert st == want
+
+
+def test_calls_fail_before_launch(lib):
+    lin = _lin()
+    st, need = _fwd_ws(lib, lin)
+    # workspace too small
+    assert lib.qlora_fwd(ctypes.byref(lin), 64, Q.QLORA_BF16, FAKE, FAKE, FAKE, FAKE,
+                         need - 1, None) == Q.QLORA_EWORKSPACE
+    # null / misaligned data pointers
+    assert lib.qlora_fwd(ctypes.byref(lin), 64, Q.QLORA_BF16, None, FAKE, None, FAKE,
+                         need, None) == Q.QLORA_EINVAL
+    assert lib.qlora_fwd(ctypes.byref(lin), 64, Q.QLORA_BF16, FAKE + 2, FAKE, None, FAKE,
+                         need, None) == Q.QLORA_EINVAL
+    assert lib.qlora_bwd(ctypes.byref(lin), 64, Q.QLORA_BF16, FAKE, FAKE, None, None,
+                         None, FAKE, FAKE, 1 << 30, None) == Q.QLORA_EINVAL
+    n = ctypes.c_size_t()
+    lib.qlora_bwd_workspace(ctypes.byref(lin), 64, Q.QLORA_BF16, ctypes.byref(n))
+    assert lib.qlora_bwd(ctypes.byref(lin), 64, Q.QLORA_BF16, FAKE, FAKE, None, FAKE,
+                         FAKE, FAKE, FAKE, n.value - 1, None) == Q.QLORA_EWORKSPACE
+    assert lib.qlora_quantize(FAKE, 100, 64, Q.QLORA_W8, FAKE, FAKE, None) == Q.QLORA_EINVAL
+    assert lib.qlora_quantize(None, 128, 64, Q.QLORA_W8, FAKE, FAKE, None) == Q.QLORA_EINVAL
+    assert lib.qlora_quantize_rows(FAKE, 4, 24, Q.QLORA_BF16, FAKE, FAKE, None) == Q.QLORA_EINVAL
+    assert lib.qlora_fwd_acc(ctypes.byref(_lin(fmt=Q.QLORA_W4G128)), 64, Q.QLORA_BF16,
+                             FAKE, FAKE, FAKE, 1 << 30, None) == Q.QLORA_EUNSUPPORTED
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(Q, "_lib", None)
+    monkeypatch.setattr(Q, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        Q.lib()
