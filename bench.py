@@ -1,0 +1,313 @@
+"""Benchmark: fwd+bwd throughput of the frozen-int8 + LoRA linear on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+
+A step is one training pass of the workload's layer stack through libqlora:
+the forward of every layer (per-row activation quantization + x A, int8
+MFMA product with the fused dequant + LoRA epilogue), then the backward of
+every layer in reverse (dy B^T, dB, dA, and the bf16 MFMA input gradient).
+The one-time weight quantization is timed separately (``quantize_ms``).
+Inputs are seeded synthetic tensors already resident in HBM. Steps are
+captured once in a HIP graph and replayed; ``value`` is the workload's
+algorithmic operations divided by the measured time per step.
+
+Prints ONE JSON line (see the keys below), including the roofline of the
+dominant kernel, timed live with HIP events recorded by the library around
+each of its launches, and the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd TFLOP/s of int8-weight+LoRA linear; % of MFMA/HBM roofline"
+# MI355X published dense peaks
+PEAK = {"bf16": 2.5e15, "int8": 5.0e15, "f32": 157.3e12, "hbm": 8.0e12}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", type=int, default=2, help="1..5 (default: the 32-layer MLP)")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="approximate CPU time budget of the oracle baseline (0: skip)")
+    p.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    return p.parse_args()
+
+
+class Layer:
+    """Device buffers and ready-made C arguments for one layer."""
+
+    def __init__(self, w, idx, dev):
+        import torch
+        from quantized_frozen_weight_amd import binding as Q
+        from quantized_frozen_weight_amd import workloads as WL
+        self.K, self.N = w.layers[idx]
+        M = w.M
+        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        self.W = torch.from_numpy(WL.weight(w, idx)).to(dev)
+        x, _ = WL.as_compute_dtype(WL.activations(w, idx), w.dtype)
+        dy, _ = WL.as_compute_dtype(WL.out_grad(w, idx), w.dtype)
+        self.x, self.dy = x.to(dev), dy.to(dev)
+        self.A = torch.from_numpy(WL.lora_A(w, idx)).to(dev)
+        self.B = torch.from_numpy(WL.lora_B(w, idx)).to(dev)
+        cb, sb = Q.qlora_weight_bytes(self.K, self.N, w.wfmt)
+        if w.wfmt == "w8":
+            self.codes = torch.empty((self.N, self.K), dtype=torch.int8, device=dev)
+            self.scales = torch.empty((self.N,), dtype=torch.float32, device=dev)
+        else:
+            self.codes = torch.empty((self.N, self.K // 2), dtype=torch.uint8, device=dev)
+            self.scales = torch.empty((self.N, self.K // 128), dtype=torch.float16, device=dev)
+        self.y = torch.empty((M, self.N), dtype=tdt, device=dev)
+        self.t = torch.empty((M, w.r), dtype=torch.float32, device=dev)
+        self.dx = torch.empty((M, self.K), dtype=tdt, device=dev)
+        self.dA = torch.empty((self.K, w.r), dtype=torch.float32, device=dev)
+        self.dB = torch.empty((w.r, self.N), dtype=torch.float32, device=dev)
+        self.lin = Q.QLinear(self.K, self.N, w.r, w.alpha, w.wfmt, self.codes,
+                             self.scales, self.A, self.B)
+        self.cs = self.lin.cstruct()
+        self.fmt = Q.QLORA_W8 if w.wfmt == "w8" else Q.QLORA_W4G128
+        self.dt = Q.QLORA_BF16 if w.dtype == "bf16" else Q.QLORA_F32
+        self.fwd_ws = Q.qlora_fwd_workspace(self.lin, M, self.dt)
+        self.bwd_ws = Q.qlora_bwd_workspace(self.lin, M, self.dt)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(each GPU would run the same step on its own rows; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from quantized_frozen_weight_amd import binding as Q
+    from quantized_frozen_weight_amd import workloads as WL
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = Q.lib()
+    w = WL.WORKLOADS[args.workload]
+    M = w.M
+    layers = [Layer(w, i, dev) for i in range(len(w.layers))]
+    ws_bytes = max(max(l.fwd_ws, l.bwd_ws) for l in layers)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    wsp = ws.data_ptr()
+
+    def check(st, what):
+        if st != 0:
+            raise Q.QloraError(st, what)
+
+    # one-time weight quantization (not part of the step)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream().cuda_stream
+    e0.record()
+    for l in layers:
+        check(lib.qlora_quantize(l.W.data_ptr(), l.K, l.N, l.fmt, l.codes.data_ptr(),
+                                 l.scales.data_ptr(), stream), "quantize")
+    e1.record()
+    torch.cuda.synchronize()
+    quantize_ms = e0.elapsed_time(e1)
+
+    def step(ev_f=None, ev_b=None):
+        st = torch.cuda.current_stream().cuda_stream
+        for i, l in enumerate(layers):
+            a, b = (ev_f[i] if ev_f else (None, None))
+            check(lib.qlora_fwd_timed(ctypes.byref(l.cs), M, l.dt, l.x.data_ptr(),
+                                      l.y.data_ptr(), l.t.data_ptr(), wsp, ws_bytes, st,
+                                      a, b), "fwd")
+        for i in reversed(range(len(layers))):
+            l = layers[i]
+            a, b = (ev_b[i] if ev_b else (None, None))
+            check(lib.qlora_bwd_timed(ctypes.byref(l.cs), M, l.dt, l.x.data_ptr(),
+                                      l.dy.data_ptr(), l.t.data_ptr(), l.dx.data_ptr(),
+                                      l.dA.data_ptr(), l.dB.data_ptr(), wsp, ws_bytes, st,
+                                      a, b), "bwd")
+
+    # eager warm-up (also loads every kernel)
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+
+    use_graph = not args.no_graph
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        run = g.replay
+    else:
+        run = step
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = e0.elapsed_time(e1) / args.steps
+    ops = w.total_ops()
+    value = ops / (ms * 1e-3) / 1e12
+
+    # eager time per step, for reference (host launch cost included)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / 10
+
+    roof = dominant_kernel_roofline(w, layers, step, torch)
+    cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+bf16" if w.dtype == "bf16" else "int8+f32",
+        "data": "synthetic",
+        "config": {
+            "workload": describe(w),
+            "rows": M,
+            "layers": len(w.layers),
+            "rank": w.r,
+            "alpha": w.alpha,
+            "weights": w.wfmt,
+            "ops_per_step": ops,
+            "hip_graph": use_graph,
+        },
+        "wall_ms_per_step": round(wall_ms, 5),
+        "eager_ms_per_step": round(eager_ms, 5),
+        "quantize_ms": round(quantize_ms, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def describe(w):
+    shapes = {}
+    for K, N in w.layers:
+        shapes[(K, N)] = shapes.get((K, N), 0) + 1
+    s = ", ".join(f"{c}x{K}->{N}" if c > 1 else f"{K}->{N}" for (K, N), c in shapes.items())
+    return f"{w.name}: {len(w.layers)} linears, {w.M} rows, {s}, {w.wfmt} weights, " \
+           f"LoRA r={w.r} alpha={w.alpha:g}, {w.dtype} activations"
+
+
+def dominant_kernel_roofline(w, layers, step, torch):
+    """Time the input-gradient launch (the step's largest kernel) live.
+
+    Each launch is bracketed by HIP events that the library records on the
+    stream it launches on. Algorithmic work per launch: 2 M K (N + r) flops
+    for dx (the product over N plus the rank-r term) and 2 M r (N + K) for
+    the first stage of dB and dA that rides in the same launch; peak: dense
+    bf16 MFMA.
+    """
+    n = len(layers)
+    reps = 5
+    pairs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)] for _ in range(reps)]
+    for rep in pairs:          # materialize the events
+        for a, b in rep:
+            a.record(); b.record()
+    torch.cuda.synchronize()
+    for rep in pairs:
+        step(ev_b=[(a.cuda_event, b.cuda_event) for a, b in rep])
+    torch.cuda.synchronize()
+    tot_ms = sum(a.elapsed_time(b) for rep in pairs for a, b in rep)
+    launches = n * reps
+    avg_ms = tot_ms / launches
+    flops = sum(2.0 * w.M * l.K * (l.N + w.r) + 2.0 * w.M * w.r * (l.N + l.K)
+                for l in layers) / n
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    peak = PEAK["bf16" if w.dtype == "bf16" else "f32"] / 1e12
+    return {
+        "kernel": "bf16_kernel (input gradient on bf16 MFMA + adapter-gradient stage 1)",
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": None,
+        "avg_launch_us": round(avg_ms * 1e3, 3),
+        "launches_timed": launches,
+        "flops_per_launch": flops,
+    }
+
+
+def cpu_baseline(w, budget_s):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    whole layers (all rows), forward + backward, until the budget is used."""
+    from oracle import qlora_oracle as O
+    from quantized_frozen_weight_amd import workloads as WL
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    done_ops, spent, n = 0, 0.0, 0
+    for i in range(len(w.layers)):
+        W, A, B = WL.weight(w, i), WL.lora_A(w, i), WL.lora_B(w, i)
+        _, x = WL.as_compute_dtype(WL.activations(w, i), w.dtype)
+        _, dy = WL.as_compute_dtype(WL.out_grad(w, i), w.dtype)
+        if w.wfmt == "w8":
+            c, s = O.quantize_w8(W)
+        else:
+            c, s = O.quantize_w4(W)
+        t0 = time.perf_counter()
+        if w.wfmt == "w8":
+            O.fwd_w8(x, c, s, A, B, w.alpha, w.dtype)
+            O.bwd(x, dy, O.dequant_w8(c, s), A, B, w.alpha, w.dtype)
+        else:
+            O.fwd_w4(x, c, s, A, B, w.alpha, w.dtype)
+            O.bwd(x, dy, O.dequant_w4(c, s), A, B, w.alpha, w.dtype)
+        spent += time.perf_counter() - t0
+        done_ops += w.ops_per_layer(*w.layers[i])
+        n += 1
+        if spent >= budget_s:
+            break
+    return {
+        "value": round(done_ops / spent / 1e12, 5),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{n} of {len(w.layers)} layers, all {w.M} rows, fwd+bwd "
+                  f"(numpy float64 oracle), {spent:.1f} s",
+    }
+
+
+if __name__ == "__main__":
+    main()

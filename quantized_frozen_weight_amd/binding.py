@@ -14,7 +14,9 @@ from dataclasses import dataclass
 from typing import Optional, Tuple
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libqlora.so")
+# QLORA_LIB may point at another build of the same library (e.g. a tuning
+# variant); by default the in-tree build next to this file is loaded.
+LIB_PATH = os.environ.get("QLORA_LIB") or os.path.join(HERE, "libqlora.so")
 
 QLORA_OK, QLORA_EINVAL, QLORA_EUNSUPPORTED, QLORA_EWORKSPACE, QLORA_ERANGE, QLORA_EHIP = range(6)
 QLORA_F32, QLORA_BF16 = 0, 1
@@ -48,7 +50,7 @@ _lib = None
 EXPORTS = (
     "qlora_status_str", "qlora_weight_bytes", "qlora_quantize",
     "qlora_fwd_workspace", "qlora_fwd", "qlora_bwd_workspace", "qlora_bwd",
-    "qlora_quantize_rows", "qlora_fwd_acc",
+    "qlora_quantize_rows", "qlora_fwd_acc", "qlora_fwd_timed", "qlora_bwd_timed",
 )
 
 
@@ -75,6 +77,8 @@ def lib() -> ctypes.CDLL:
     L.qlora_bwd.argtypes = [plin, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.qlora_quantize_rows.argtypes = [vp, i, i, i, vp, vp, vp]
     L.qlora_fwd_acc.argtypes = [plin, i, i, vp, vp, vp, sz, vp]
+    L.qlora_fwd_timed.argtypes = [plin, i, i, vp, vp, vp, vp, sz, vp, vp, vp]
+    L.qlora_bwd_timed.argtypes = [plin, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
     for name in EXPORTS[1:]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L

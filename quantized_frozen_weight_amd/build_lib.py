@@ -47,18 +47,27 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *sources(), "-o", tmp]
+def build(verbose: bool = False, out: str = LIB_PATH, defines=()) -> str:
+    """Compile every csrc/*.hip into one shared library at ``out``.
+
+    ``defines`` are extra -D flags (tuning knobs such as QLORA_D_SMALL)."""
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-I", INCLUDE,
+           "-I", CSRC, *sources(), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         sys.stderr.write(proc.stdout + proc.stderr)
         raise RuntimeError(f"hipcc failed ({proc.returncode})")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=LIB_PATH)
+    ap.add_argument("-D", dest="defines", action="append", default=[])
+    a = ap.parse_args()
+    print(build(verbose=True, out=a.out, defines=a.defines))

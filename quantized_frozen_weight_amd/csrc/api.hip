@@ -87,6 +87,11 @@ BwdLayout bwd_layout(const qlora_linear* L, int M, int dtype) {
 
 inline char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
+// Optional timing marks around a call's main product kernel.
+void mark(void* ev, hipStream_t s) {
+  if (ev != nullptr) (void)hipEventRecord(static_cast<hipEvent_t>(ev), s);
+}
+
 int launch_status() {
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? QLORA_OK : QLORA_EHIP;
@@ -153,8 +158,9 @@ int qlora_fwd_workspace(const qlora_linear* L, int M, int dtype, size_t* bytes) 
   return QLORA_OK;
 }
 
-int qlora_fwd(const qlora_linear* L, int M, int dtype, const void* x, void* y,
-              float* t_save, void* ws, size_t ws_bytes, void* stream) {
+int qlora_fwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
+                    void* y, float* t_save, void* ws, size_t ws_bytes,
+                    void* stream, void* ev_start, void* ev_stop) {
   int st = check_linear(L, M, dtype);
   if (st) return st;
   if (!x || !y || !aligned16(x) || !aligned16(y)) return QLORA_EINVAL;
@@ -168,18 +174,28 @@ int qlora_fwd(const qlora_linear* L, int M, int dtype, const void* x, void* y,
     int8_t* xq = reinterpret_cast<int8_t*>(at(ws, w.xq));
     float* sx = reinterpret_cast<float*>(at(ws, w.sx));
     launch_rowquant(dtype, x, M, L->K, L->A, L->r, xq, sx, t, s);
+    mark(ev_start, s);
     launch_gemm_fwd_w8(dtype, M, L->N, L->K, xq,
                        static_cast<const int8_t*>(L->codes), sx,
                        static_cast<const float*>(L->scales), t, L->B, L->r,
                        lora_s(L), y, nullptr, s);
+    mark(ev_stop, s);
   } else {
     launch_lora_down(dtype, x, M, L->K, L->A, L->r, t, s);
+    mark(ev_start, s);
     launch_gemm_fwd_w4(M, L->N, L->K, static_cast<const uint16_t*>(x),
                        static_cast<const uint8_t*>(L->codes),
                        static_cast<const _Float16*>(L->scales), t, L->B, L->r,
                        lora_s(L), static_cast<uint16_t*>(y), s);
+    mark(ev_stop, s);
   }
   return launch_status();
+}
+
+int qlora_fwd(const qlora_linear* L, int M, int dtype, const void* x, void* y,
+              float* t_save, void* ws, size_t ws_bytes, void* stream) {
+  return qlora_fwd_timed(L, M, dtype, x, y, t_save, ws, ws_bytes, stream,
+                         nullptr, nullptr);
 }
 
 int qlora_bwd_workspace(const qlora_linear* L, int M, int dtype, size_t* bytes) {
@@ -190,9 +206,10 @@ int qlora_bwd_workspace(const qlora_linear* L, int M, int dtype, size_t* bytes) 
   return QLORA_OK;
 }
 
-int qlora_bwd(const qlora_linear* L, int M, int dtype, const void* x,
-              const void* dy, const float* t_saved, void* dx, float* dA,
-              float* dB, void* ws, size_t ws_bytes, void* stream) {
+int qlora_bwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
+                    const void* dy, const float* t_saved, void* dx, float* dA,
+                    float* dB, void* ws, size_t ws_bytes, void* stream,
+                    void* ev_start, void* ev_stop) {
   int st = check_linear(L, M, dtype);
   if (st) return st;
   if (!x || !dy || !dA || !dB) return QLORA_EINVAL;
@@ -215,26 +232,44 @@ int qlora_bwd(const qlora_linear* L, int M, int dtype, const void* x,
                       ? reinterpret_cast<uint16_t*>(at(ws, w.dys)) : nullptr;
   launch_bwd_rows(dtype, dy, M, L->N, L->B, L->r,
                   w8 ? static_cast<const float*>(L->scales) : nullptr, dys, u, s);
-  launch_skinny(dtype, M, L->r, L->N, t, dy, sc, dB, false,
-                reinterpret_cast<float*>(at(ws, w.pB)), s);
-  launch_skinny(dtype, M, L->r, L->K, u, x, sc, dA, true,
-                reinterpret_cast<float*>(at(ws, w.pA)), s);
-  if (dx != nullptr) {
-    if (w8 && dtype == QLORA_BF16)
+  const SkinnyJobs sk = make_adapter_grad_jobs(
+      M, L->r, sc, t, dy, L->N, dB, reinterpret_cast<float*>(at(ws, w.pB)), u, x,
+      L->K, dA, reinterpret_cast<float*>(at(ws, w.pA)));
+  mark(ev_start, s);
+#ifndef QLORA_FUSE_STAGE1
+#define QLORA_FUSE_STAGE1 1
+#endif
+  if (dx != nullptr && dtype == QLORA_BF16 && !QLORA_FUSE_STAGE1) launch_skinny_stage1(dtype, sk, s);
+  if (dx != nullptr && dtype == QLORA_BF16) {
+    // input gradient with the adapter-gradient stage 1 riding along
+    if (w8)
       launch_gemm_dx_w8(M, L->K, L->N, dys, static_cast<const int8_t*>(L->codes),
-                        u, L->A, L->r, sc, static_cast<uint16_t*>(dx), s);
-    else if (w8)
+                        u, L->A, L->r, sc, static_cast<uint16_t*>(dx),
+                        QLORA_FUSE_STAGE1 ? &sk : nullptr, s);
+    else
+      launch_gemm_dx_w4(M, L->K, L->N, static_cast<const uint16_t*>(dy),
+                        static_cast<const uint8_t*>(L->codes),
+                        static_cast<const _Float16*>(L->scales), u, L->A, L->r,
+                        sc, static_cast<uint16_t*>(dx),
+                        QLORA_FUSE_STAGE1 ? &sk : nullptr, s);
+  } else {
+    launch_skinny_stage1(dtype, sk, s);
+    if (dx != nullptr)
       launch_gemm_dx_f32(M, L->K, L->N, static_cast<const float*>(dy),
                          static_cast<const int8_t*>(L->codes),
                          static_cast<const float*>(L->scales), u, L->A, L->r,
                          sc, static_cast<float*>(dx), s);
-    else
-      launch_gemm_dx_w4(M, L->K, L->N, static_cast<const uint16_t*>(dy),
-                        static_cast<const uint8_t*>(L->codes),
-                        static_cast<const _Float16*>(L->scales), u, L->A,
-                        L->r, sc, static_cast<uint16_t*>(dx), s);
   }
+  mark(ev_stop, s);
+  launch_skinny_stage2(sk, s);
   return launch_status();
+}
+
+int qlora_bwd(const qlora_linear* L, int M, int dtype, const void* x,
+              const void* dy, const float* t_saved, void* dx, float* dA,
+              float* dB, void* ws, size_t ws_bytes, void* stream) {
+  return qlora_bwd_timed(L, M, dtype, x, dy, t_saved, dx, dA, dB, ws, ws_bytes,
+                         stream, nullptr, nullptr);
 }
 
 int qlora_quantize_rows(const void* x, int M, int K, int dtype, int8_t* xq,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "skinny.hpp"
+
 namespace qlora {
 
 // dtype: 0 = float32, 1 = bfloat16 (matches qlora_dtype)
@@ -30,23 +32,29 @@ void launch_gemm_fwd_w4(int M, int N, int K, const uint16_t* x,
                         const float* t, const float* B, int r, float s,
                         uint16_t* y, hipStream_t st);
 
-// u = dy B^T (float32 [M, r]); if dys != nullptr also dys = bf16(dy * sw[n])
+// u = dy B^T (float32 [M, r]); if dys != nullptr also dys = bf16(dy * sw[n]).
 void launch_bwd_rows(int dtype, const void* dy, int M, int N, const float* B,
                      int r, const float* sw, uint16_t* dys, float* u,
                      hipStream_t st);
 
-// out = s * P^T Q over the M rows, P float32 [M, r], Q [M, C] in dtype.
-// transpose_out = false: out[j * C + c] (dB [r, N]); true: out[c * r + j]
-// (dA [K, r]). partial: workspace of skinny_partial_floats(M, r, C) floats.
+// Adapter gradients dB = s t^T dy ([r, N]) and dA = s x^T u (stored [K, r]):
+// stage 1 writes per-split partial sums (partB / partA hold
+// skinny_partial_floats(M, r, N / K) floats), stage 2 adds them in order.
+// Stage 1 normally rides along with the input-gradient launch.
 size_t skinny_partial_floats(int M, int r, int C);
-void launch_skinny(int dtype, int M, int r, int C, const float* P,
-                   const void* Q, float s, float* out, bool transpose_out,
-                   float* partial, hipStream_t st);
+SkinnyJobs make_adapter_grad_jobs(int M, int r, float s, const float* t,
+                                  const void* dy, int N, float* dB, float* partB,
+                                  const float* u, const void* x, int K, float* dA,
+                                  float* partA);
+void launch_skinny_stage1(int dtype, const SkinnyJobs& p, hipStream_t st);
+void launch_skinny_stage2(const SkinnyJobs& p, hipStream_t st);
 
 // dx = dys codes + s u A^T   (bf16; dys = dy * sw already folded)
+// sk (optional): adapter-gradient stage 1 run as extra blocks of this launch.
 void launch_gemm_dx_w8(int M, int K, int N, const uint16_t* dys,
                        const int8_t* codes, const float* u, const float* A,
-                       int r, float s, uint16_t* dx, hipStream_t st);
+                       int r, float s, uint16_t* dx, const SkinnyJobs* sk,
+                       hipStream_t st);
 // dx = dy (codes * sw)^T + s u A^T in float32
 void launch_gemm_dx_f32(int M, int K, int N, const float* dy,
                         const int8_t* codes, const float* sw, const float* u,
@@ -56,6 +64,6 @@ void launch_gemm_dx_f32(int M, int K, int N, const float* dy,
 void launch_gemm_dx_w4(int M, int K, int N, const uint16_t* dy,
                        const uint8_t* packed, const _Float16* scales,
                        const float* u, const float* A, int r, float s,
-                       uint16_t* dx, hipStream_t st);
+                       uint16_t* dx, const SkinnyJobs* sk, hipStream_t st);
 
 }  // namespace qlora

@@ -1,6 +1,4 @@
-// Weight quantizers (one-time preparation of the frozen weight) and the
-// forward prologue: per-row activation quantization fused with the LoRA down
-// projection t = x A.
+// Weight quantizers: one-time preparation of the frozen weight.
 //
 // Formats ("Introduce QLoRA-like technique", "Highlights": int8 frozen
 // kernels; keras-llm-light README, "Simplified Int4Variable quantization":
@@ -146,105 +144,6 @@ void launch_quantize_w4(const float* W, int K, int N, uint8_t* packed,
                         _Float16* scales, hipStream_t st) {
   w4_quant_kernel<<<dim3((N + 63) / 64, K / 128), 256, 0, st>>>(W, K, N, packed,
                                                                scales);
-}
-
-// ---------------------------------------------------------------------------
-// Forward prologue, one wave per row:
-//   pass 1: row abs-max (integer max of |x| bits, NaN-propagating)
-//   pass 2: codes xq = rint(x * 127/absmax), scale sx = absmax/127, and the
-//           adapter down projection t[m, :] = x[m, :] A in float32.
-// With QUANT = false only t is produced (4-bit forward; backward recompute).
-// ---------------------------------------------------------------------------
-template <typename T, int RMAX, bool QUANT>
-__global__ __launch_bounds__(256) void rowquant_kernel(
-    const typename Elem<T>::type* __restrict__ x, int M, int K,
-    const float* __restrict__ A, int r, int8_t* __restrict__ xq,
-    float* __restrict__ sx, float* __restrict__ t) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= M) return;
-  const auto* xr = x + (long)row * K;
-  const int nchunk = K / 8;
-  QuantParams p{0.f, 0.f, false};
-  if (QUANT) {
-    uint32_t m = 0;
-    for (int c = lane; c < nchunk; c += 64) {
-      float v[8];
-      load8(xr + 8 * c, v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint32_t b = abs_bits(v[i]);
-        m = b > m ? b : m;
-      }
-    }
-    m = wave_max_u32(m);
-    p = absmax_params(m, 127.f);
-  }
-  float acc[RMAX];
-#pragma unroll
-  for (int j = 0; j < RMAX; ++j) acc[j] = 0.f;
-  for (int c = lane; c < nchunk; c += 64) {
-    float v[8];
-    load8(xr + 8 * c, v);
-    if (QUANT) {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t q0 = p.live ? (uint32_t)(quant_code(v[i], p.inv, 127.f) & 0xff) : 0u;
-        uint32_t q1 = p.live ? (uint32_t)(quant_code(v[i + 4], p.inv, 127.f) & 0xff) : 0u;
-        lo |= q0 << (8 * i);
-        hi |= q1 << (8 * i);
-      }
-      u32x2 pk = {lo, hi};
-      *reinterpret_cast<u32x2*>(xq + (long)row * K + 8 * c) = pk;
-    }
-    if (t != nullptr) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float* a = A + (long)(8 * c + i) * r;
-#pragma unroll
-        for (int j = 0; j < RMAX; ++j)
-          if (j < r) acc[j] = __builtin_fmaf(v[i], a[j], acc[j]);
-      }
-    }
-  }
-  if (t != nullptr) {
-#pragma unroll
-    for (int j = 0; j < RMAX; ++j) {
-      if (j < r) {
-        float s = wave_sum(acc[j]);
-        if (lane == 0) t[(long)row * r + j] = s;
-      }
-    }
-  }
-  if (QUANT && lane == 0) sx[row] = p.scale;
-}
-
-template <typename T, bool QUANT>
-static void rowquant_dispatch(const void* x, int M, int K, const float* A, int r,
-                              int8_t* xq, float* sx, float* t, hipStream_t st) {
-  dim3 grid((M + 3) / 4);
-  const auto* xp = reinterpret_cast<const typename Elem<T>::type*>(x);
-  if (t == nullptr || r <= 4)
-    rowquant_kernel<T, 4, QUANT><<<grid, 256, 0, st>>>(xp, M, K, A, r, xq, sx, t);
-  else if (r <= 8)
-    rowquant_kernel<T, 8, QUANT><<<grid, 256, 0, st>>>(xp, M, K, A, r, xq, sx, t);
-  else if (r <= 16)
-    rowquant_kernel<T, 16, QUANT><<<grid, 256, 0, st>>>(xp, M, K, A, r, xq, sx, t);
-  else
-    rowquant_kernel<T, 32, QUANT><<<grid, 256, 0, st>>>(xp, M, K, A, r, xq, sx, t);
-}
-
-void launch_rowquant(int dtype, const void* x, int M, int K, const float* A,
-                     int r, int8_t* xq, float* sx, float* t, hipStream_t st) {
-  if (dtype == 0) rowquant_dispatch<F32, true>(x, M, K, A, r, xq, sx, t, st);
-  else rowquant_dispatch<BF16, true>(x, M, K, A, r, xq, sx, t, st);
-}
-
-void launch_lora_down(int dtype, const void* x, int M, int K, const float* A,
-                      int r, float* t, hipStream_t st) {
-  if (dtype == 0) rowquant_dispatch<F32, false>(x, M, K, A, r, nullptr, nullptr, t, st);
-  else rowquant_dispatch<BF16, false>(x, M, K, A, r, nullptr, nullptr, t, st);
 }
 
 }  // namespace qlora

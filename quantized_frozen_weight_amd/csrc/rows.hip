@@ -1,0 +1,335 @@
+// Row passes (one wave per row, four rows per block), shared by the forward
+// prologue and the first backward pass:
+//
+//   forward:  t[m, :] = x[m, :] A            (adapter down projection, float32)
+//             xq, sx  = abs-max int8 codes and scale of row m (int8 weights)
+//   backward: u[m, :] = dy[m, :] B^T         (gradient reaching the adapter)
+//             dys     = bf16(dy[m, n] * sw[n])   (int8 weights, bf16 compute:
+//                       the channel scale folded into the gradient rows that
+//                       the input-gradient product consumes)
+//
+// Sources: "Parameter-efficient fine-tuning of GPT-2 with LoRA", "LoRA
+// equation" / "Create LoRA layer" (the adapter branch B(A x) scaled by
+// alpha/r); "Introduce QLoRA-like technique", "Highlights" (int8 frozen
+// kernels); the row quantizer and the straight-through backward are the
+// readings stated in include/qlora.h.
+//
+// Latency, not bandwidth, decides these small passes, so every global load a
+// block needs is issued before anything waits: the row itself (rows of up
+// to 4096 entries stay in registers between the abs-max and the quantize
+// pass; longer rows are streamed twice) and the slice of the rank-r matrix
+// that the block's four rows share, copied to LDS with 16-byte loads. In LDS
+// a lane that holds 8 consecutive row entries k finds the 8 x R adapter
+// values it needs contiguous: A keeps its [k][j] order in groups of 8 rows
+// padded by 4 floats (so the 16 lanes of one LDS read land in distinct
+// banks); B is kept as [j][k].
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace qlora {
+
+namespace {
+
+constexpr int kRowsPerBlock = 4;
+constexpr int kLdsFloats = 17408;          // 68 KB adapter slice budget
+constexpr int kHoldChunks = 8;             // 8 chunks x 8 entries x 64 lanes
+
+enum RowMode { kFwdQuant = 0, kFwdT = 1, kBwd = 2 };
+
+// Slice length (row entries per LDS fill): a multiple of 512 whose grouped
+// layout (8 R + 4 floats per 8 entries) fits the budget.
+template <int R> struct Slice {
+  static constexpr int len = (kLdsFloats / (8 * R + 4)) * 8 / 512 * 512;
+  static_assert(len >= 512, "slice too short");
+};
+
+template <typename T> struct Raw;
+template <> struct Raw<BF16> { u32x4 v; };
+template <> struct Raw<F32> { f32x4 a, b; };
+
+__device__ __forceinline__ void raw_load(const uint16_t* p, Raw<BF16>& r) {
+  r.v = *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void raw_load(const float* p, Raw<F32>& r) {
+  r.a = *reinterpret_cast<const f32x4*>(p);
+  r.b = *reinterpret_cast<const f32x4*>(p + 4);
+}
+__device__ __forceinline__ void raw_zero(Raw<BF16>& r) { r.v = u32x4{0u, 0u, 0u, 0u}; }
+__device__ __forceinline__ void raw_zero(Raw<F32>& r) {
+  r.a = f32x4{0.f, 0.f, 0.f, 0.f};
+  r.b = r.a;
+}
+__device__ __forceinline__ void raw_unpack(const Raw<BF16>& r, float v[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(r.v[i] << 16);
+    v[2 * i + 1] = __uint_as_float(r.v[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void raw_unpack(const Raw<F32>& r, float v[8]) {
+  v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
+  v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
+}
+
+// LDS position of adapter entry (k, j) of the current slice.
+template <int R, int MODE>
+__device__ __forceinline__ int ws_index(int k, int j, int sld) {
+  if constexpr (MODE == kBwd) return j * sld + k;
+  else return (k >> 3) * (8 * R + 4) + (k & 7) * R + j;
+}
+
+// Copy the slice [s0, s0 + len) of the adapter matrix into LDS.
+// MODE < kBwd: A [L, r] row-major; kBwd: B [r, L] row-major.
+template <int R, int MODE>
+__device__ __forceinline__ void stage_slice(float* Ws, const float* __restrict__ W,
+                                            int L, int r, int s0, int len, int sld) {
+  constexpr int SL = Slice<R>::len;
+  constexpr int PER = (R * SL / 4 + 255) / 256;     // 16-byte units per thread
+  if constexpr (MODE == kBwd) {
+    // r rows of len floats
+    const int upr = len / 4;                         // units per row
+    const int n = r * upr;
+    f32x4 v[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int u = threadIdx.x + 256 * q;
+      const int uc = u < n ? u : n - 1;
+      v[q] = *reinterpret_cast<const f32x4*>(W + (long)(uc / upr) * L + s0 + 4 * (uc % upr));
+    }
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int u = threadIdx.x + 256 * q;
+      if (u < n) *reinterpret_cast<f32x4*>(&Ws[(u / upr) * sld + 4 * (u % upr)]) = v[q];
+    }
+  } else {
+    if (R >= 4 && r == R) {
+      // the slice of A is contiguous: len * R floats
+      const int n = len * R / 4;
+      const float* src = W + (long)s0 * R;
+      f32x4 v[PER];
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const int u = threadIdx.x + 256 * q;
+        v[q] = *reinterpret_cast<const f32x4*>(src + 4 * (u < n ? u : n - 1));
+      }
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const int u = threadIdx.x + 256 * q;
+        if (u < n) {
+          const int k = (4 * u) / R, j = (4 * u) % R;
+          *reinterpret_cast<f32x4*>(&Ws[ws_index<R, MODE>(k, j, sld)]) = v[q];
+        }
+      }
+    } else {
+      // rank below the padded width (or tiny ranks): element by element
+      for (int e = threadIdx.x; e < len * R; e += 256) {
+        const int k = e / R, j = e % R;
+        Ws[ws_index<R, MODE>(k, j, sld)] = j < r ? W[(long)(s0 + k) * r + j] : 0.f;
+      }
+    }
+  }
+}
+
+template <typename T, int R, int MODE, bool HOLD>
+__global__ __launch_bounds__(256) void row_kernel(
+    const typename Elem<T>::type* __restrict__ rows, int M, int L,
+    const float* __restrict__ W, int r, float* __restrict__ out_r,
+    int8_t* __restrict__ xq, float* __restrict__ sx,
+    const float* __restrict__ sw, uint16_t* __restrict__ dys) {
+  constexpr int SL = Slice<R>::len;
+  extern __shared__ __attribute__((aligned(16))) float Ws[];
+  const int sld = min(SL, (L + 511) / 512 * 512);
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const bool live = row < M;
+  const auto* xr = rows + (long)row * L;
+  const int nchunk = L / 8;
+  const bool lowrank = out_r != nullptr;
+
+  // Loads are issued unconditionally from clamped addresses and masked
+  // afterwards: predicated loads become branches that make the compiler wait
+  // for every outstanding load at each join.
+  Raw<T> hold[HOLD ? kHoldChunks : 1];
+  if constexpr (HOLD) {
+    const auto* xr0 = rows + (long)(live ? row : M - 1) * L;
+#pragma unroll
+    for (int i = 0; i < kHoldChunks; ++i) {
+      const int c = lane + 64 * i;
+      raw_load(xr0 + 8 * (c < nchunk ? c : nchunk - 1), hold[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kHoldChunks; ++i) {
+      const int c = lane + 64 * i;
+      if (!(live && c < nchunk)) raw_zero(hold[i]);
+    }
+  }
+
+  QuantParams qp{0.f, 0.f, false};
+  float acc[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) acc[j] = 0.f;
+
+  for (int s0 = 0; s0 < L; s0 += SL) {
+    const int len = min(SL, L - s0);
+    if (s0 > 0) __syncthreads();
+    if (lowrank) stage_slice<R, MODE>(Ws, W, L, r, s0, len, sld);
+    if (MODE == kFwdQuant && s0 == 0 && live) {
+      uint32_t m = 0;
+      if constexpr (HOLD) {
+#pragma unroll
+        for (int i = 0; i < kHoldChunks; ++i) {
+          float v[8];
+          raw_unpack(hold[i], v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { uint32_t b = abs_bits(v[e]); m = b > m ? b : m; }
+        }
+      } else {
+        for (int c = lane; c < nchunk; c += 64) {
+          float v[8];
+          load8(xr + 8 * c, v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { uint32_t b = abs_bits(v[e]); m = b > m ? b : m; }
+        }
+      }
+      qp = absmax_params(wave_max_u32(m), 127.f);
+    }
+    __syncthreads();
+    if (!live) continue;
+    // one 8-entry chunk: quantize / scale-fold, then accumulate against the
+    // LDS slice (cl = chunk index within the slice, c = within the row)
+    auto chunk = [&](const float (&v)[8], int c, int cl) {
+      if (MODE == kFwdQuant) {
+        uint32_t lo = 0, hi = 0;
+        if (qp.live) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lo |= (uint32_t)(quant_code(v[e], qp.inv, 127.f) & 0xff) << (8 * e);
+            hi |= (uint32_t)(quant_code(v[e + 4], qp.inv, 127.f) & 0xff) << (8 * e);
+          }
+        }
+        *reinterpret_cast<u32x2*>(xq + (long)row * L + 8 * c) = u32x2{lo, hi};
+      }
+      if (MODE == kBwd && dys != nullptr) {
+        float w[8];
+        load8(sw + 8 * c, w);
+        u32x4 o = {pack_bf16x2(v[0] * w[0], v[1] * w[1]),
+                   pack_bf16x2(v[2] * w[2], v[3] * w[3]),
+                   pack_bf16x2(v[4] * w[4], v[5] * w[5]),
+                   pack_bf16x2(v[6] * w[6], v[7] * w[7])};
+        *reinterpret_cast<u32x4*>(dys + (long)row * L + 8 * c) = o;
+      }
+      if (!lowrank) return;
+      if constexpr (MODE == kBwd) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          if (j >= r) break;
+          const f32x4 a = *reinterpret_cast<const f32x4*>(&Ws[j * sld + 8 * cl]);
+          const f32x4 b = *reinterpret_cast<const f32x4*>(&Ws[j * sld + 8 * cl + 4]);
+          float s = acc[j];
+          s = __builtin_fmaf(v[0], a.x, s); s = __builtin_fmaf(v[1], a.y, s);
+          s = __builtin_fmaf(v[2], a.z, s); s = __builtin_fmaf(v[3], a.w, s);
+          s = __builtin_fmaf(v[4], b.x, s); s = __builtin_fmaf(v[5], b.y, s);
+          s = __builtin_fmaf(v[6], b.z, s); s = __builtin_fmaf(v[7], b.w, s);
+          acc[j] = s;
+        }
+      } else {
+        const float* g = &Ws[cl * (8 * R + 4)];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+          for (int j = 0; j < R; ++j) acc[j] = __builtin_fmaf(v[i], g[i * R + j], acc[j]);
+        }
+      }
+    };
+    if constexpr (HOLD) {
+      // chunk row i covers entries [512 i, 512 i + 512); SL is a multiple of 512
+#pragma unroll
+      for (int i = 0; i < kHoldChunks; ++i) {
+        const int c = lane + 64 * i;
+        if (512 * i < s0 || 512 * i >= s0 + SL || c >= nchunk) continue;
+        float v[8];
+        raw_unpack(hold[i], v);
+        chunk(v, c, c - s0 / 8);
+      }
+    } else {
+      for (int cl = lane; 8 * cl < len; cl += 64) {
+        const int c = s0 / 8 + cl;
+        float v[8];
+        load8(xr + 8 * c, v);
+        chunk(v, c, cl);
+      }
+    }
+  }
+  if (!live) return;
+  if (lowrank) {
+    float mine = 0.f;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const float tot = wave_sum(acc[j]);
+      if (lane == j) mine = tot;
+    }
+    if (lane < r) out_r[(long)row * r + lane] = mine;
+  }
+  if (MODE == kFwdQuant && lane == 0) sx[row] = qp.scale;
+}
+
+template <typename T, int R, int MODE>
+void row_launch(const void* rows, int M, int L, const float* W, int r,
+                float* out_r, int8_t* xq, float* sx, const float* sw,
+                uint16_t* dys, hipStream_t st) {
+  dim3 grid((M + kRowsPerBlock - 1) / kRowsPerBlock);
+  const auto* p = reinterpret_cast<const typename Elem<T>::type*>(rows);
+  constexpr int SL = Slice<R>::len;
+  const int sld = SL < (L + 511) / 512 * 512 ? SL : (L + 511) / 512 * 512;
+  size_t lds = 0;
+  if (out_r != nullptr)
+    lds = (MODE == kBwd ? (size_t)R * sld : (size_t)(sld / 8) * (8 * R + 4)) * sizeof(float);
+  if (L <= kHoldChunks * 512)
+    row_kernel<T, R, MODE, true><<<grid, 256, lds, st>>>(p, M, L, W, r, out_r, xq, sx,
+                                                         sw, dys);
+  else
+    row_kernel<T, R, MODE, false><<<grid, 256, lds, st>>>(p, M, L, W, r, out_r, xq, sx,
+                                                          sw, dys);
+}
+
+template <typename T, int MODE>
+void row_dispatch_r(int r, const void* rows, int M, int L, const float* W,
+                    float* out_r, int8_t* xq, float* sx, const float* sw,
+                    uint16_t* dys, hipStream_t st) {
+  if (r <= 1) row_launch<T, 1, MODE>(rows, M, L, W, r, out_r, xq, sx, sw, dys, st);
+  else if (r <= 2) row_launch<T, 2, MODE>(rows, M, L, W, r, out_r, xq, sx, sw, dys, st);
+  else if (r <= 4) row_launch<T, 4, MODE>(rows, M, L, W, r, out_r, xq, sx, sw, dys, st);
+  else if (r <= 8) row_launch<T, 8, MODE>(rows, M, L, W, r, out_r, xq, sx, sw, dys, st);
+  else if (r <= 16) row_launch<T, 16, MODE>(rows, M, L, W, r, out_r, xq, sx, sw, dys, st);
+  else row_launch<T, 32, MODE>(rows, M, L, W, r, out_r, xq, sx, sw, dys, st);
+}
+
+}  // namespace
+
+void launch_rowquant(int dtype, const void* x, int M, int K, const float* A,
+                     int r, int8_t* xq, float* sx, float* t, hipStream_t st) {
+  const int rr = t == nullptr ? 1 : r;
+  if (dtype == 0)
+    row_dispatch_r<F32, kFwdQuant>(rr, x, M, K, A, t, xq, sx, nullptr, nullptr, st);
+  else
+    row_dispatch_r<BF16, kFwdQuant>(rr, x, M, K, A, t, xq, sx, nullptr, nullptr, st);
+}
+
+void launch_lora_down(int dtype, const void* x, int M, int K, const float* A,
+                      int r, float* t, hipStream_t st) {
+  if (dtype == 0)
+    row_dispatch_r<F32, kFwdT>(r, x, M, K, A, t, nullptr, nullptr, nullptr, nullptr, st);
+  else
+    row_dispatch_r<BF16, kFwdT>(r, x, M, K, A, t, nullptr, nullptr, nullptr, nullptr, st);
+}
+
+void launch_bwd_rows(int dtype, const void* dy, int M, int N, const float* B,
+                     int r, const float* sw, uint16_t* dys, float* u,
+                     hipStream_t st) {
+  if (dtype == 0)
+    row_dispatch_r<F32, kBwd>(r, dy, M, N, B, u, nullptr, nullptr, sw, nullptr, st);
+  else
+    row_dispatch_r<BF16, kBwd>(r, dy, M, N, B, u, nullptr, nullptr, sw, dys, st);
+}
+
+}  // namespace qlora
