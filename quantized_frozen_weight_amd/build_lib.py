@@ -26,12 +26,14 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # no hand-written or compiler-formed packed fp32 ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # IEEE float32 on the device: keep denormals, correctly rounded divide
     "-fno-gpu-flush-denormals-to-zero",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # MFMA accumulators in ordinary VGPRs: no copies between the
+    # accumulation registers and VGPRs inside the main loops
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-Wno-unused-command-line-argument",
 ]
 
@@ -48,19 +50,37 @@ def sources():
 
 
 def build(verbose: bool = False, out: str = LIB_PATH, defines=()) -> str:
-    """Compile every csrc/*.hip into one shared library at ``out``.
+    """Compile every csrc/*.hip (one hipcc per source, in parallel) and link
+    them into one shared library at ``out``.
 
-    ``defines`` are extra -D flags (tuning knobs such as QLORA_D_SMALL)."""
+    ``defines`` are extra -D flags (tuning knobs)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = out + ".objs"
+    os.makedirs(objdir, exist_ok=True)
+    flags = [*HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-I", INCLUDE, "-I", CSRC]
+
+    def run(cmd):
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        proc = subprocess.run(cmd, capture_output=True, text=True)
+        if proc.returncode != 0:
+            sys.stderr.write(proc.stdout + proc.stderr)
+            raise RuntimeError(f"hipcc failed ({proc.returncode}): {cmd[-1]}")
+
+    objs = []
+    cmds = []
+    for src in sources():
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        objs.append(obj)
+        cmds.append([hipcc(), *flags, "-c", src, "-o", obj])
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        list(ex.map(run, cmds))
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-I", INCLUDE,
-           "-I", CSRC, *sources(), "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    proc = subprocess.run(cmd, capture_output=True, text=True)
-    if proc.returncode != 0:
-        sys.stderr.write(proc.stdout + proc.stderr)
-        raise RuntimeError(f"hipcc failed ({proc.returncode})")
+    run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, out)
+    shutil.rmtree(objdir, ignore_errors=True)
     return out
 
 

@@ -157,122 +157,6 @@ __device__ __forceinline__ void epilogue(const AccT (&acc)[FM][FN], const float*
 }
 
 // ---------------------------------------------------------------------------
-// int8 forward
-// ---------------------------------------------------------------------------
-template <int BM, int BN, int D, typename OutT, bool ACC_OUT>
-__global__ __launch_bounds__(256) void fwd_i8_kernel(
-    int M, int N, int K, const int8_t* __restrict__ xq,
-    const int8_t* __restrict__ codes, const float* __restrict__ sx,
-    const float* __restrict__ sw, const float* __restrict__ t,
-    const float* __restrict__ B, int r, float s, OutT* __restrict__ y,
-    int32_t* __restrict__ acc_out) {
-  constexpr int BK = 128, P = BK + 16;               // bytes
-  constexpr int FM = BM / 32, FN = BN / 32;
-  constexpr int CA = BM / 32, CB = BN / 32;          // 16-byte chunks per thread
-  __shared__ __attribute__((aligned(16))) int8_t As[2][BM * P];
-  __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * P];
-  __shared__ __attribute__((aligned(16))) float E[ACC_OUT ? 1 : Epi<BM, BN>::kFloats];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  const int lrow = tid >> 3, lcol = (tid & 7) * 16;
-  const int nk = (K + BK - 1) / BK;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-
-  // The loop runs over nkp = nk rounded up to D slices with no data-dependent
-  // branches (the compiler then keeps D slices of loads in flight): slices
-  // past the end (kt >= nk) re-read the block's own last slice and are
-  // masked to zero; the last D slices issue nothing.
-  const int nkp = (nk + D - 1) / D * D;
-  u32x4 ra[D][CA], rb[D][CB];
-  auto issue = [&](u32x4 (&a)[CA], u32x4 (&b)[CB], int kt) {
-    const bool kok = kt < nk;
-    const int gk = (kok ? kt : nk - 1) * BK + lcol;
-    const int gkc = gk < K ? gk : K - 16;
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int gm = m0 + lrow + 32 * i;
-      const bool ok = kok && gm < M && gk < K;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(xq + (long)(gm < M ? gm : M - 1) * K + gkc);
-      a[i] = ok ? v : zero;
-    }
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int gn = n0 + lrow + 32 * i;
-      const bool ok = kok && gn < N && gk < K;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(codes + (long)(gn < N ? gn : N - 1) * K + gkc);
-      b[i] = ok ? v : zero;
-    }
-  };
-
-#pragma unroll
-  for (int st = 0; st < D; ++st) issue(ra[st], rb[st], st);
-  if constexpr (!ACC_OUT) {
-    Epi<BM, BN> ep;
-    ep.load(M, N, m0, n0, r, t, B, N, 1, sx, sw);
-    ep.store(E, r);
-  }
-
-  i32x4 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
-
-  auto slice = [&](int st, bool refill, int kt) {
-    const int buf = st & 1;
-#pragma unroll
-    for (int i = 0; i < CA; ++i)
-      *reinterpret_cast<u32x4*>(&As[buf][(lrow + 32 * i) * P + lcol]) = ra[st][i];
-#pragma unroll
-    for (int i = 0; i < CB; ++i)
-      *reinterpret_cast<u32x4*>(&Bs[buf][(lrow + 32 * i) * P + lcol]) = rb[st][i];
-    __syncthreads();
-    if (refill) issue(ra[st], rb[st], kt + D);
-#pragma unroll
-    for (int kk = 0; kk < BK / 64; ++kk) {
-      const int koff = kk * 64 + (lane >> 4) * 16;
-      i32x4 af[FM], bf[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const i32x4*>(
-            &As[buf][(wm * (BM / 2) + i * 16 + (lane & 15)) * P + koff]);
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bf[j] = *reinterpret_cast<const i32x4*>(
-            &Bs[buf][(wn * (BN / 2) + j * 16 + (lane & 15)) * P + koff]);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-  };
-  int kt0 = 0;
-  for (; kt0 + D < nkp; kt0 += D) {
-#pragma unroll
-    for (int st = 0; st < D; ++st) slice(st, true, kt0 + st);
-  }
-#pragma unroll
-  for (int st = 0; st < D; ++st) slice(st, false, kt0 + st);
-
-  if constexpr (ACC_OUT) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int m = m0 + wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + ii;
-          const int n = n0 + wn * (BN / 2) + j * 16 + (lane & 15);
-          if (m < M && n < N) acc_out[(long)m * N + n] = acc[i][j][ii];
-        }
-  } else {
-    epilogue<BM, BN, OutT>(acc, E, M, N, m0, n0, wm, wn, r, s, true, y);
-  }
-}
-
-// ---------------------------------------------------------------------------
 // bf16 products (4-bit forward, input gradients). A operand: bf16 rows
 // [M, Kc] with the contraction Kc contiguous, staged directly. B operand
 // (per kind):
@@ -325,47 +209,6 @@ template <int BN> struct BStage<BN, kW4Fwd> {
       }
       *reinterpret_cast<u32x4*>(&Bs[row * PITCH + part * NIB + d * 8]) =
           u32x4{o[0], o[1], o[2], o[3]};
-    }
-  }
-};
-
-// int8 codes, transposed: tile [64 n][BN k] bytes. Thread: k quad kq
-// (4 columns), NPT consecutive n rows.
-template <int BN> struct BStage<BN, kW8T> {
-  static constexpr int KQ = BN / 4;                  // k quads per row
-  static constexpr int NPT = 64 / (256 / KQ);        // n rows per thread (4 or 8)
-  uint32_t w[NPT];
-  __device__ __forceinline__ void load(const void* codes, const _Float16*, int Kw, int Nw,
-                       int c0, int n0, bool kok) {
-    const int8_t* q = reinterpret_cast<const int8_t*>(codes);
-    const int kq = threadIdx.x % KQ, ng = threadIdx.x / KQ;
-    const int gk = c0 + 4 * kq;
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      const int gn = n0 + ng * NPT + i;
-      const bool ok = kok && gn < Nw && gk < Kw;
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(
-          q + (long)(gn < Nw ? gn : Nw - 1) * Kw + (gk < Kw ? gk : Kw - 4));
-      w[i] = ok ? v : 0u;
-    }
-  }
-  template <int PITCH>
-  __device__ __forceinline__ void store(uint16_t* Bs) const {
-    const int kq = threadIdx.x % KQ, ng = threadIdx.x / KQ;
-#pragma unroll
-    for (int jk = 0; jk < 4; ++jk) {
-      uint32_t o[NPT / 2];
-#pragma unroll
-      for (int p = 0; p < NPT / 2; ++p) {
-        const int q0 = ((int)(w[2 * p] << (24 - 8 * jk))) >> 24;
-        const int q1 = ((int)(w[2 * p + 1] << (24 - 8 * jk))) >> 24;
-        o[p] = pack_int_bf16x2(q0, q1);
-      }
-      uint16_t* dst = &Bs[(4 * kq + jk) * PITCH + ng * NPT];
-      if constexpr (NPT == 8)
-        *reinterpret_cast<u32x4*>(dst) = u32x4{o[0], o[1], o[2], o[3]};
-      else
-        *reinterpret_cast<u32x2*>(dst) = u32x2{o[0], o[1]};
     }
   }
 };
@@ -545,36 +388,7 @@ void bf16_launch(const Bf16Args& a, const SkinnyJobs& sk, hipStream_t st) {
   else bf16_launch_r<64, 64, QLORA_D_SMALL, KIND>(a, sk, st);
 }
 
-template <typename OutT, bool ACC>
-void fwd_i8_launch(int M, int N, int K, const int8_t* xq, const int8_t* codes,
-                   const float* sx, const float* sw, const float* t, const float* B,
-                   int r, float s, OutT* y, int32_t* acc_out, hipStream_t st) {
-  if (big_tiles(M, N)) {
-    dim3 grid((N + 127) / 128, (M + 127) / 128);
-    fwd_i8_kernel<128, 128, QLORA_D_BIG, OutT, ACC><<<grid, 256, 0, st>>>(
-        M, N, K, xq, codes, sx, sw, t, B, r, s, y, acc_out);
-  } else {
-    dim3 grid((N + 63) / 64, (M + 63) / 64);
-    fwd_i8_kernel<64, 64, QLORA_D_SMALL, OutT, ACC><<<grid, 256, 0, st>>>(
-        M, N, K, xq, codes, sx, sw, t, B, r, s, y, acc_out);
-  }
-}
-
 }  // namespace
-
-void launch_gemm_fwd_w8(int dtype, int M, int N, int K, const int8_t* xq,
-                        const int8_t* codes, const float* sx, const float* sw,
-                        const float* t, const float* B, int r, float s,
-                        void* y, int32_t* acc_out, hipStream_t st) {
-  if (acc_out != nullptr)
-    fwd_i8_launch<float, true>(M, N, K, xq, codes, sx, sw, t, B, r, s, nullptr, acc_out, st);
-  else if (dtype == 0)
-    fwd_i8_launch<float, false>(M, N, K, xq, codes, sx, sw, t, B, r, s,
-                                reinterpret_cast<float*>(y), nullptr, st);
-  else
-    fwd_i8_launch<uint16_t, false>(M, N, K, xq, codes, sx, sw, t, B, r, s,
-                                   reinterpret_cast<uint16_t*>(y), nullptr, st);
-}
 
 void launch_gemm_fwd_w4(int M, int N, int K, const uint16_t* x,
                         const uint8_t* packed, const _Float16* scales,
@@ -586,18 +400,6 @@ void launch_gemm_fwd_w4(int M, int N, int K, const uint16_t* x,
   a.P = t; a.Q = B; a.ldj = N; a.ldn = 1; a.r = r; a.s = s; a.out = y;
   SkinnyJobs none{};
   bf16_launch<kW4Fwd>(a, none, st);
-}
-
-void launch_gemm_dx_w8(int M, int K, int N, const uint16_t* dys,
-                       const int8_t* codes, const float* u, const float* A,
-                       int r, float s, uint16_t* dx, const SkinnyJobs* sk,
-                       hipStream_t st) {
-  Bf16Args a{};
-  a.M = M; a.Cout = K; a.Kc = N; a.Kw = K; a.Nw = N;
-  a.g = dys; a.codes = codes; a.scales = nullptr;
-  a.P = u; a.Q = A; a.ldj = 1; a.ldn = r; a.r = r; a.s = s; a.out = dx;
-  SkinnyJobs none{};
-  bf16_launch<kW8T>(a, sk != nullptr ? *sk : none, st);
 }
 
 void launch_gemm_dx_w4(int M, int K, int N, const uint16_t* dy,

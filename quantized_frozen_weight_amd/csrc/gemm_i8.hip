@@ -1,0 +1,171 @@
+// Forward product of the frozen int8 layer on v_mfma_i32_16x16x64_i8.
+//
+//   acc[m, n] = sum_k xq[m, k] q[n, k]                       (exact int32)
+//   y[m, n]   = fma(s, sum_j t[m, j] B[j, n], float(acc) * (sx[m] * sw[n]))
+//
+// ("Parameter-efficient fine-tuning of GPT-2 with LoRA", "LoRA equation": the
+// adapter branch is added to the frozen layer's output; "Create LoRA layer":
+// scaled by alpha / rank; "Introduce QLoRA-like technique", "Highlights": the
+// frozen kernel is int8 with one scale per output channel.)
+//
+// Both operands are K-contiguous int8 rows, so every tile moves straight from
+// global memory into the LDS stage ring (ring.hpp) with no conversion. A block
+// of 4 waves (2 x 2) owns a BM x BN output tile; a wave owns (BM/2) x (BN/2)
+// as 16 x 16 MFMA blocks and reads its operands from the swizzled 128-byte
+// rows of the current stage. Tile and depth are picked per shape: 64 x 64 with
+// three stages when the grid is about one wave of blocks (latency-bound, so
+// depth pays), 128 x 128 or 128 x 64 with two stages for large grids (LDS per
+// block then allows several blocks per compute unit).
+#include "launch.hpp"
+#include "ring.hpp"
+
+namespace qlora {
+
+namespace {
+
+constexpr int kCUs = 256;
+
+struct I8Args {
+  int M, N, K;
+  const int8_t* xq;      // [M, K]
+  const int8_t* codes;   // [N, K]
+  const float* sx;       // [M]
+  const float* sw;       // [N]
+  const float* t;        // [M, r]
+  const float* B;        // [r, N]
+  int r;
+  float s;
+  void* y;               // [M, N] float32 or bfloat16
+  int32_t* acc_out;      // [M, N] (test hook) or nullptr
+  int tiles_x;
+};
+
+template <int BM, int BN, int S, int R, typename OutT, bool ACC_OUT>
+__global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
+  constexpr int BK = 128, ASZ = BM * BK, STG = (BM + BN) * BK;
+  constexpr int AI = BM / 32, BI = BN / 32, LPS = AI + BI;   // loads per wave per stage
+  constexpr int FM = BM / 32, FN = BN / 32;
+  static_assert(EpiOps<BM, BN, R, true>::kFloats * 4 <= S * STG, "epilogue fits in the ring");
+  __shared__ __attribute__((aligned(1024))) int8_t ring[S * STG];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  const int m0 = ((int)blockIdx.x / a.tiles_x) * BM, n0 = ((int)blockIdx.x % a.tiles_x) * BN;
+  const int M = a.M, N = a.N, K = a.K;
+  const int nk = (K + BK - 1) / BK;
+
+  EpiOps<BM, BN, R, true> ep;
+  if constexpr (!ACC_OUT) ep.load(M, N, m0, n0, a.r, a.t, a.B, N, 1, a.sx, a.sw);
+
+  // Wave wid fills rows [wid * BM/4, (wid + 1) * BM/4) of A and the same
+  // share of B; one instruction covers 8 rows (8 lanes of 16 bytes per row).
+  auto issue = [&](int kt, int slot) {
+    int8_t* base = ring + slot * STG;
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+      const int rb = wid * (BM / 4) + i * 8, row = rb + (lane >> 3);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
+      const int gk = kt * BK + c * 16, gm = m0 + row;
+      const int8_t* src = gk < K ? a.xq + (long)(gm < M ? gm : M - 1) * K + gk : zero_chunk(lane);
+      lds_dma16(src, base + rb * BK);
+    }
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const int rb = wid * (BN / 4) + i * 8, row = rb + (lane >> 3);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
+      const int gk = kt * BK + c * 16, gn = n0 + row;
+      const int8_t* src = gk < K ? a.codes + (long)(gn < N ? gn : N - 1) * K + gk : zero_chunk(lane);
+      lds_dma16(src, base + ASZ + rb * BK);
+    }
+  };
+
+  i32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st)
+    if (st < nk) issue(st, st);
+  int slot = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_stages<LPS, 0, S - 2>(nk - 1 - kt);   // stage kt has landed (this wave)
+    __builtin_amdgcn_s_barrier();               // ... for every wave; slot kt-1 is free
+    if (kt + S - 1 < nk) issue(kt + S - 1, slot == 0 ? S - 1 : slot - 1);
+    const int8_t* As = ring + slot * STG;
+    const int8_t* Bs = As + ASZ;
+#pragma unroll
+    for (int kk = 0; kk < BK / 64; ++kk) {
+      const int c = kk * 4 + (lane >> 4);
+      i32x4 af[FM], bf[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = *reinterpret_cast<const i32x4*>(As + swz128(wm * (BM / 2) + i * 16 + (lane & 15), c));
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bf[j] = *reinterpret_cast<const i32x4*>(Bs + swz128(wn * (BN / 2) + j * 16 + (lane & 15), c));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    slot = slot == S - 1 ? 0 : slot + 1;
+  }
+
+  if constexpr (ACC_OUT) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int m = m0 + wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + ii;
+          const int n = n0 + wn * (BN / 2) + j * 16 + (lane & 15);
+          if (m < M && n < N) a.acc_out[(long)m * N + n] = acc[i][j][ii];
+        }
+  } else {
+    float* E = reinterpret_cast<float*>(ring);
+    __syncthreads();                 // every wave is done with the ring
+    ep.store(E, M, N, m0, n0, a.r);
+    __syncthreads();
+    epilogue_lowrank<BM, BN, R, true>(acc, E, M, N, m0, n0, wm * (BM / 2), wn * (BN / 2),
+                                      a.s, reinterpret_cast<OutT*>(a.y));
+  }
+}
+
+template <int BM, int BN, int S, typename OutT, bool ACC>
+void launch_tiles(I8Args a, hipStream_t st) {
+  a.tiles_x = (a.N + BN - 1) / BN;
+  const dim3 grid((unsigned)(a.tiles_x * ((a.M + BM - 1) / BM)));
+  if (a.r <= 4) fwd_i8_kernel<BM, BN, S, 4, OutT, ACC><<<grid, 256, 0, st>>>(a);
+  else if (a.r <= 8) fwd_i8_kernel<BM, BN, S, 8, OutT, ACC><<<grid, 256, 0, st>>>(a);
+  else if (a.r <= 16) fwd_i8_kernel<BM, BN, S, 16, OutT, ACC><<<grid, 256, 0, st>>>(a);
+  else fwd_i8_kernel<BM, BN, S, 32, OutT, ACC><<<grid, 256, 0, st>>>(a);
+}
+
+template <typename OutT, bool ACC>
+void launch_shape(const I8Args& a, hipStream_t st) {
+  const long t64 = (long)((a.M + 63) / 64) * ((a.N + 63) / 64);
+  const long t128 = (long)((a.M + 127) / 128) * ((a.N + 127) / 128);
+  if (t64 <= 2 * kCUs) launch_tiles<64, 64, 3, OutT, ACC>(a, st);
+  else if (t128 >= 2 * kCUs) launch_tiles<128, 128, 2, OutT, ACC>(a, st);
+  else launch_tiles<128, 64, 2, OutT, ACC>(a, st);
+}
+
+}  // namespace
+
+void launch_gemm_fwd_w8(int dtype, int M, int N, int K, const int8_t* xq,
+                        const int8_t* codes, const float* sx, const float* sw,
+                        const float* t, const float* B, int r, float s,
+                        void* y, int32_t* acc_out, hipStream_t st) {
+  I8Args a{};
+  a.M = M; a.N = N; a.K = K; a.xq = xq; a.codes = codes; a.sx = sx; a.sw = sw;
+  a.t = t; a.B = B; a.r = r; a.s = s; a.y = y; a.acc_out = acc_out;
+  if (acc_out != nullptr) launch_shape<float, true>(a, st);
+  else if (dtype == 0) launch_shape<float, false>(a, st);
+  else launch_shape<uint16_t, false>(a, st);
+}
+
+}  // namespace qlora
