@@ -255,7 +255,7 @@ def dominant_kernel_roofline(w, layers, step, torch):
     achieved = flops / (avg_ms * 1e-3) / 1e12
     peak = PEAK["bf16" if w.dtype == "bf16" else "f32"] / 1e12
     return {
-        "kernel": "bf16_kernel (input gradient on bf16 MFMA + adapter-gradient stage 1)",
+        "kernel": "dx8_kernel (input gradient on bf16 MFMA + adapter-gradient stage 1)",
         "bound": "mfma",
         "achieved": round(achieved, 2),
         "peak": peak,
