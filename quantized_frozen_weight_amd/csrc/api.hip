@@ -70,17 +70,22 @@ FwdLayout fwd_layout(const qlora_linear* L, int M) {
 }
 
 struct BwdLayout {
-  size_t t, u, dys, pB, pA, total;
+  size_t t, u, pB, pA, total;
 };
+// Partial sums of dA and dB: one per split of the rows. The fused int8
+// backward splits by row block (at least 64 rows), the other paths into at
+// most as many splits, so ceil(M / 64) covers both.
+inline size_t partial_floats(int M, int r, int C) {
+  return (size_t)((M + 63) / 64) * (size_t)r * (size_t)C;
+}
 BwdLayout bwd_layout(const qlora_linear* L, int M, int dtype) {
+  (void)dtype;
   BwdLayout w{};
   size_t off = 0;
   w.t = off; off = align_up(off + (size_t)M * L->r * 4);
   w.u = off; off = align_up(off + (size_t)M * L->r * 4);
-  w.dys = off;
-  if (L->fmt == QLORA_W8 && dtype == QLORA_BF16) off = align_up(off + (size_t)M * L->N * 2);
-  w.pB = off; off = align_up(off + skinny_partial_floats(M, L->r, L->N) * 4);
-  w.pA = off; off = align_up(off + skinny_partial_floats(M, L->r, L->K) * 4);
+  w.pB = off; off = align_up(off + partial_floats(M, L->r, L->N) * 4);
+  w.pA = off; off = align_up(off + partial_floats(M, L->r, L->K) * 4);
   w.total = off;
   return w;
 }
@@ -228,30 +233,35 @@ int qlora_bwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
     t = tw;
   }
   const bool w8 = L->fmt == QLORA_W8;
-  uint16_t* dys = (w8 && dtype == QLORA_BF16)
-                      ? reinterpret_cast<uint16_t*>(at(ws, w.dys)) : nullptr;
-  launch_bwd_rows(dtype, dy, M, L->N, L->B, L->r,
-                  w8 ? static_cast<const float*>(L->scales) : nullptr, dys, u, s);
-  const SkinnyJobs sk = make_adapter_grad_jobs(
-      M, L->r, sc, t, dy, L->N, dB, reinterpret_cast<float*>(at(ws, w.pB)), u, x,
-      L->K, dA, reinterpret_cast<float*>(at(ws, w.pA)));
+  float* partB = reinterpret_cast<float*>(at(ws, w.pB));
+  float* partA = reinterpret_cast<float*>(at(ws, w.pA));
+  if (w8 && dtype == QLORA_BF16 && dx != nullptr) {
+    // one launch: dx, u, and the per-row-block partial sums of dA and dB
+    mark(ev_start, s);
+    launch_bwd_w8_fused(M, L->K, L->N, static_cast<const uint16_t*>(dy),
+                        static_cast<const int8_t*>(L->codes),
+                        static_cast<const float*>(L->scales), L->B, L->A, t,
+                        static_cast<const uint16_t*>(x), L->r, sc,
+                        static_cast<uint16_t*>(dx), partA, partB, s);
+    mark(ev_stop, s);
+    SkinnyJobs sk{};
+    sk.njobs = 2; sk.M = M; sk.r = L->r; sk.s = sc;
+    sk.nsplit = (M + bwd8_row_block(M, L->K) - 1) / bwd8_row_block(M, L->K);
+    sk.partial[0] = partB; sk.C[0] = L->N; sk.out[0] = dB; sk.transpose[0] = 0;
+    sk.partial[1] = partA; sk.C[1] = L->K; sk.out[1] = dA; sk.transpose[1] = 1;
+    launch_skinny_stage2(sk, s);
+    return launch_status();
+  }
+  launch_bwd_rows(dtype, dy, M, L->N, L->B, L->r, nullptr, nullptr, u, s);
+  const SkinnyJobs sk = make_adapter_grad_jobs(M, L->r, sc, t, dy, L->N, dB, partB,
+                                               u, x, L->K, dA, partA);
   mark(ev_start, s);
-#ifndef QLORA_FUSE_STAGE1
-#define QLORA_FUSE_STAGE1 1
-#endif
-  if (dx != nullptr && dtype == QLORA_BF16 && !QLORA_FUSE_STAGE1) launch_skinny_stage1(dtype, sk, s);
   if (dx != nullptr && dtype == QLORA_BF16) {
-    // input gradient with the adapter-gradient stage 1 riding along
-    if (w8)
-      launch_gemm_dx_w8(M, L->K, L->N, dys, static_cast<const int8_t*>(L->codes),
-                        u, L->A, L->r, sc, static_cast<uint16_t*>(dx),
-                        QLORA_FUSE_STAGE1 ? &sk : nullptr, s);
-    else
-      launch_gemm_dx_w4(M, L->K, L->N, static_cast<const uint16_t*>(dy),
-                        static_cast<const uint8_t*>(L->codes),
-                        static_cast<const _Float16*>(L->scales), u, L->A, L->r,
-                        sc, static_cast<uint16_t*>(dx),
-                        QLORA_FUSE_STAGE1 ? &sk : nullptr, s);
+    // 4-bit input gradient with the adapter-gradient stage 1 riding along
+    launch_gemm_dx_w4(M, L->K, L->N, static_cast<const uint16_t*>(dy),
+                      static_cast<const uint8_t*>(L->codes),
+                      static_cast<const _Float16*>(L->scales), u, L->A, L->r,
+                      sc, static_cast<uint16_t*>(dx), &sk, s);
   } else {
     launch_skinny_stage1(dtype, sk, s);
     if (dx != nullptr)

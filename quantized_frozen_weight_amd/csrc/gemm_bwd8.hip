@@ -1,0 +1,489 @@
+// Backward of the frozen int8 layer with its adapter, in one launch (plus the
+// fixed-order combine of the adapter-gradient partial sums):
+//
+//   u  = dy B^T                                  [M, r]
+//   dx = dy deq(W)^T + s u A^T,  deq(W)[k, n] = q[n, k] sw[n]
+//   dB = s t^T dy                                [r, N]
+//   dA = s x^T u                                 [K, r]
+//
+// ("Parameter-efficient fine-tuning of GPT-2 with LoRA", "LoRA equation" and
+// "Why does LoRA reduce memory footprint?": gradients only for the adapter;
+// the quantizer of x is passed straight through; "How to fine-tune the 4-bit
+// model?": the transposed quantized product.)
+//
+// A block owns BM rows x BN columns of dx and walks the whole contraction
+// over n in stages of 64, so on the way it sees every dy value of its rows.
+// The stage ring (ring.hpp) carries three tiles per stage, all moved
+// global -> LDS without registers: the dy rows (swizzled 128-byte rows), the
+// codes [64 n][BN k] in their stored layout (chunk-swizzled), and an aux tile
+// with sw[n] and the adapter's B columns for those n. Once a stage has
+// landed, the whole block converts it in one cooperative pass (every code
+// read and widened once, not once per wave that uses it):
+//   * CB [BN k][64 n] = bf16(q[n, k] sw[n]), the transposed dequantized
+//     weight, as swizzled 128-byte rows;
+//   * BU [16 j][64 n] = bf16(B[j, n]).
+// Then per 32 n, on v_mfma_f32_16x16x32_bf16:
+//   * dx += dy CB^T;
+//   * u  += dy BU^T, one MFMA per row block (the two column waves of a row
+//     split the row blocks);
+//   * dB: the block whose column index equals the stage index modulo the
+//     column-tile count adds t^T dy over its rows for the stage's 64 n on the
+//     vector ALUs in float32 (t exact), giving one partial per row block.
+// After the loop u goes to LDS; the dA partial over the block's rows is a
+// float32 vector-ALU sum of x (a tile loaded into LDS) times u; the dx
+// epilogue adds s u A^T on v_mfma_f32_16x16x4_f32. The partials of dA and dB
+// are added in row-block order by a small second launch. No atomics:
+// results are bitwise reproducible.
+#include "launch.hpp"
+#include "ring.hpp"
+
+namespace qlora {
+
+namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+struct Bwd8Args {
+  int M, K, N;
+  const uint16_t* dy;      // [M, N] bf16
+  const int8_t* codes;     // [N, K]
+  const float* sw;         // [N]
+  const float* B;          // [r, N]
+  const float* A;          // [K, r]
+  const float* t;          // [M, r]
+  const uint16_t* x;       // [M, K] bf16
+  int r;
+  float s;
+  uint16_t* dx;            // [M, K] bf16
+  float* partA;            // [row blocks, r, K]
+  float* partB;            // [row blocks, r, N]
+  int tiles_x;
+};
+
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// NR transposing LDS reads (ds_read_b64_tr_b16) issued together and completed
+// in the same asm block. Written as asm because the builtin form makes the
+// compiler wait for every direct-to-LDS load in flight (the ring's later
+// stages included) before each read.
+template <int NR>
+__device__ __forceinline__ void tr16_reads(const uint32_t (&addr)[NR], uint64_t (&out)[NR]) {
+  static_assert(NR == 4 || NR == 8, "4 or 8 reads");
+  if constexpr (NR == 4) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %5\n\t"
+        "ds_read_b64_tr_b16 %2, %6\n\t"
+        "ds_read_b64_tr_b16 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3])
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3])
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %10\n\t"
+        "ds_read_b64_tr_b16 %3, %11\n\t"
+        "ds_read_b64_tr_b16 %4, %12\n\t"
+        "ds_read_b64_tr_b16 %5, %13\n\t"
+        "ds_read_b64_tr_b16 %6, %14\n\t"
+        "ds_read_b64_tr_b16 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]),
+          "=&v"(out[4]), "=&v"(out[5]), "=&v"(out[6]), "=&v"(out[7])
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]),
+          "v"(addr[4]), "v"(addr[5]), "v"(addr[6]), "v"(addr[7])
+        : "memory");
+  }
+}
+
+// 32-bit LDS address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Chunk swizzle of a code tile with RB-byte rows (RB = 64 or 128).
+template <int RB>
+__device__ __forceinline__ int code_swz(int row) {
+  return (row >> (RB == 64 ? 2 : 1)) & (RB / 16 - 1);
+}
+
+// bfloat16 element e of a swizzled 128-byte-row bf16 tile (64 per row).
+__device__ __forceinline__ float tile_bf16(const int8_t* tile, int row, int e) {
+  const uint16_t v = *reinterpret_cast<const uint16_t*>(tile + swz128(row, e >> 3) + 2 * (e & 7));
+  return __uint_as_float((uint32_t)v << 16);
+}
+
+template <int BM, int BN, int S, int R>
+__global__ __launch_bounds__(256) void bwd8_kernel(Bwd8Args a) {
+  constexpr int KC = 64;                              // n per stage
+  constexpr int AUXI = ((1 + R) * 256 + 4095) / 4096;  // aux DMA instructions per wave
+  constexpr int ASZ = BM * 128, BSZ = KC * BN, XSZ = 4 * AUXI * 1024;
+  constexpr int STG = ASZ + BSZ + XSZ;
+  constexpr int AI = BM / 32, BI = BN / 64, LPS = AI + BI + AUXI;
+  constexpr int FM = BM / 32, FN = BN / 32;
+  constexpr int RPI = 1024 / BN, CPR = BN / 16;
+  constexpr int UCB = (R + 15) / 16;                  // u column blocks of 16
+  constexpr bool XPRE = BM * BN * 2 <= 8192;          // x tile kept outside the ring
+  constexpr int CBSZ = BN * 128;                      // converted codes [BN][64] bf16
+  constexpr int BUSZ = UCB * 16 * 128;                // converted B [16 UCB][64] bf16
+  constexpr int TSZ = BM * R * 4;                     // t tile (pitch r)
+  constexpr int XTSZ = BM * BN * 2;
+  constexpr int EFL = (BM + BN) * R;                  // epilogue floats: U [BM][R], A^T [R][BN]
+  static_assert(EFL * 4 + (XPRE ? 0 : XTSZ) <= S * STG, "epilogue and x tile fit in the ring");
+  static_assert(BN == 64 || BN == 128, "code rows of 64 or 128 bytes");
+  // One LDS array for everything: with a second __shared__ object the
+  // compiler can no longer tell that the ring's reads do not wait on the
+  // direct-to-LDS loads still in flight, and waits for all of them.
+  __shared__ __attribute__((aligned(1024))) int8_t ring[S * STG + CBSZ + BUSZ + TSZ + (XPRE ? XTSZ : 0)];
+  int8_t* CB = ring + S * STG;
+  int8_t* BU = CB + CBSZ;
+  float* Ts = reinterpret_cast<float*>(BU + BUSZ);                             // [BM][r]
+  int8_t* Xs = XPRE ? BU + BUSZ + TSZ : ring + EFL * 4;                        // [BM][BN] bf16
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = wave_id();
+  const int wm = wid >> 1, wn = wid & 1;
+  const int mt = (int)blockIdx.x / a.tiles_x, kt_blk = (int)blockIdx.x % a.tiles_x;
+  const int m0 = mt * BM, k0 = kt_blk * BN;
+  const int M = a.M, K = a.K, N = a.N, r = a.r;
+  const int nk = (N + KC - 1) / KC;
+
+  // t rows of the block (for dB), then A^T of the block's columns (for the
+  // epilogue); masks are applied when stored
+  constexpr int NT = (BM * R + 255) / 256, NQ = (BN * R + 255) / 256;
+  float tv[NT], qv[NQ];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int e = tid + 256 * i, row = e / R, j = e % R, gm = m0 + row;
+    tv[i] = a.t[(long)(gm < M ? gm : M - 1) * r + (j < r ? j : r - 1)];
+  }
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int e = tid + 256 * i, j = e / BN, col = e % BN, gk = k0 + col;
+    qv[i] = a.A[(long)(gk < K ? gk : K - 1) * r + (j < r ? j : r - 1)];
+  }
+
+  // x tile [BM][BN] bf16 as swizzled 128-byte rows (64 columns per row half)
+  auto issue_x = [&]() {
+    constexpr int RH = BN / 64;                        // 128-byte halves per row
+#pragma unroll
+    for (int i = 0; i < BM * RH / 32; ++i) {
+      const int rb = (wid * (BM * RH / 32) + i) * 8, hrow = rb + (lane >> 3);
+      const int row = hrow / RH, half = hrow % RH;
+      const int c = (lane & 7) ^ ((hrow >> 1) & 7);
+      const int gm = m0 + row, gk = k0 + half * 64 + c * 8;
+      const void* src = gk < K ? (const void*)(a.x + (long)(gm < M ? gm : M - 1) * K + gk)
+                               : (const void*)zero_chunk(lane);
+      lds_dma16(src, Xs + rb * 128);
+    }
+  };
+  if constexpr (XPRE) issue_x();
+
+  // Per-lane sources of the stage loads at stage 0; stage kt adds kt * 64 n.
+  // Lanes whose chunk is outside the operand point at the zero page and do
+  // not move. Only a ragged last stage needs the n bound checked.
+  const int8_t* srcA[AI];
+  int nA[AI];                                          // first n of the lane's chunk
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int row = wid * (BM / 4) + i * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7), gm = m0 + row;
+    nA[i] = c * 8;
+    srcA[i] = reinterpret_cast<const int8_t*>(a.dy + (long)(gm < M ? gm : M - 1) * N + c * 8);
+  }
+  const int8_t* srcB[BI];
+  int nB[BI];
+  bool okB[BI];
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int row = (wid * BI + i) * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ code_swz<BN>(row), gk = k0 + c * 16;
+    nB[i] = row;
+    okB[i] = gk < K;
+    srcB[i] = okB[i] ? a.codes + (long)row * K + gk : zero_chunk(lane);
+  }
+  const int8_t* srcX[AUXI];
+  int nX[AUXI];
+  bool okX[AUXI];
+#pragma unroll
+  for (int i = 0; i < AUXI; ++i) {
+    const int e = ((wid * AUXI + i) * 64 + lane) * 4;   // aux float index
+    const int j = e / 64 - 1, nn = e % 64;
+    nX[i] = nn;
+    okX[i] = j < r;
+    srcX[i] = j < 0 ? reinterpret_cast<const int8_t*>(a.sw + nn)
+                    : (j < r ? reinterpret_cast<const int8_t*>(a.B + (long)j * N + nn) : zero_chunk(lane));
+  }
+  auto issue = [&](int kt, int slot) {
+    int8_t* base = ring + slot * STG;
+    const int nb = kt * KC;
+    const bool tail = nb + KC > N;
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+      const int8_t* src = srcA[i] + 2L * nb;
+      if (tail && nb + nA[i] >= N) src = zero_chunk(lane);
+      lds_dma16(src, base + (wid * (BM / 4) + i * 8) * 128);
+    }
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const int8_t* src = okB[i] ? srcB[i] + (long)nb * K : srcB[i];
+      if (tail && nb + nB[i] >= N) src = zero_chunk(lane);
+      lds_dma16(src, base + ASZ + (wid * BI + i) * RPI * BN);
+    }
+#pragma unroll
+    for (int i = 0; i < AUXI; ++i) {
+      const int8_t* src = okX[i] ? srcX[i] + 4L * nb : srcX[i];
+      if (tail && nb + nX[i] >= N) src = zero_chunk(lane);
+      lds_dma16(src, base + ASZ + BSZ + (wid * AUXI + i) * 1024);
+    }
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 uacc[(FM + 1) / 2][UCB];
+#pragma unroll
+  for (int i = 0; i < (FM + 1) / 2; ++i)
+#pragma unroll
+    for (int j = 0; j < UCB; ++j) uacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st)
+    if (st < nk) issue(st, st);
+
+  // t tile into LDS (pitch r); BU rows past the rank stay zero for good
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int e = tid + 256 * i, row = e / R, j = e % R;
+    if (e < BM * R && j < r) Ts[row * r + j] = m0 + row < M ? tv[i] : 0.f;
+  }
+  for (int e = R * 32 + tid; e < UCB * 16 * 32; e += 256)      // 4-byte pairs
+    *reinterpret_cast<uint32_t*>(BU + swz128(e / 32, (e % 32) >> 2) + (e & 3) * 4) = 0u;
+  __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());    // stores land before the first barrier
+
+  const int rows_here = M - m0 < BM ? M - m0 : BM;
+  // dB operand: t as bf16, lane -> rank (lane % 16), rows 32 c + 8 (lane / 16) + e
+  // (read back from LDS after the first barrier of the loop)
+  bf16x8 tfr[UCB][BM / 32];
+  bool tfr_ready = false;
+  // cooperative conversion: thread -> n quad nq, k quads kq0 + 16 h
+  const int nq = tid & 15, kq0 = tid >> 4;
+
+  int slot = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_stages<LPS, 0, S - 2>(nk - 1 - kt);
+    __builtin_amdgcn_s_barrier();                    // stage kt landed; CB, BU free
+    if (kt + S - 1 < nk) issue(kt + S - 1, slot == 0 ? S - 1 : slot - 1);
+    const int8_t* As = ring + slot * STG;
+    const int8_t* Bs = As + ASZ;
+    const float* Xa = reinterpret_cast<const float*>(Bs + BSZ);
+
+    // CB[k][n] = bf16(q[n][k] sw[n]) for the 4 n of nq and 4 k per quad
+    {
+      const f32x4 swv = *reinterpret_cast<const f32x4*>(Xa + 4 * nq);
+#pragma unroll
+      for (int h = 0; h < BN / 64; ++h) {
+        const int kcol = 4 * (kq0 + 16 * h);
+        int raw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = 4 * nq + i;
+          raw[i] = *reinterpret_cast<const int*>(Bs + n * BN + ((((kcol >> 4) ^ code_swz<BN>(n))) << 4) + (kcol & 15));
+        }
+#pragma unroll
+        for (int kk2 = 0; kk2 < 4; ++kk2) {
+          const float v0 = (float)(int8_t)(raw[0] >> (8 * kk2)) * swv.x;
+          const float v1 = (float)(int8_t)(raw[1] >> (8 * kk2)) * swv.y;
+          const float v2 = (float)(int8_t)(raw[2] >> (8 * kk2)) * swv.z;
+          const float v3 = (float)(int8_t)(raw[3] >> (8 * kk2)) * swv.w;
+          *reinterpret_cast<u32x2*>(CB + swz128(kcol + kk2, nq >> 1) + (nq & 1) * 8) =
+              u32x2{pk_bf16(v0, v1), pk_bf16(v2, v3)};
+        }
+      }
+      // BU[j][n] = bf16(B[j][n]), 2 n per entry
+#pragma unroll
+      for (int e = tid; e < R * 32; e += 256) {
+        const int j = e >> 5, p = e & 31;
+        const f32x2 b = *reinterpret_cast<const f32x2*>(Xa + 64 * (1 + j) + 2 * p);
+        *reinterpret_cast<uint32_t*>(BU + swz128(j, p >> 2) + (p & 3) * 4) = pk_bf16(b.x, b.y);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+    __builtin_amdgcn_s_barrier();                    // CB, BU visible
+
+#pragma unroll
+    for (int kk = 0; kk < KC / 32; ++kk) {
+      const int c = kk * 4 + (lane >> 4);
+      bf16x8 af[FM], bf[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(As + swz128(wm * (BM / 2) + i * 16 + (lane & 15), c));
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bf[j] = *reinterpret_cast<const bf16x8*>(CB + swz128(wn * (BN / 2) + j * 16 + (lane & 15), c));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int cb = 0; cb < UCB; ++cb) {
+        const bf16x8 bu = *reinterpret_cast<const bf16x8*>(BU + swz128(cb * 16 + (lane & 15), c));
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          if ((i & 1) == wn)
+            uacc[i >> 1][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bu, uacc[i >> 1][cb], 0, 0, 0);
+      }
+    }
+    // dB partial for this stage's 64 n over the block's rows (one block per
+    // row block and stage), on the matrix cores: wave w takes n in
+    // [16 w, 16 w + 16); dB^T[n][j] = sum_m dy[m][n] t[m][j]. The dy^T operand
+    // comes from the dy tile through transposing reads: in each 16-lane group,
+    // lanes 4 i + p fetch the 4 n at 16 w + 4 p of row i, and lane q receives
+    // n = 16 w + q of rows 0..3.
+    if (kt % a.tiles_x == kt_blk) {
+      if (!tfr_ready) {
+        tfr_ready = true;
+#pragma unroll
+        for (int cb = 0; cb < UCB; ++cb) {
+          const int j = cb * 16 + (lane & 15);
+#pragma unroll
+          for (int c = 0; c < BM / 32; ++c) {
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int m = 32 * c + 8 * (lane >> 4) + e;
+              v[e] = j < r ? Ts[m * r + (j < r ? j : 0)] : 0.f;
+            }
+            tfr[cb][c] = __builtin_bit_cast(bf16x8, u32x4{pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]),
+                                                           pk_bf16(v[4], v[5]), pk_bf16(v[6], v[7])});
+          }
+        }
+      }
+      constexpr int NRD = 2 * (BM / 32);
+      uint32_t tra[NRD];
+      uint64_t trv[NRD];
+      const int q = lane & 15, i4 = q >> 2, p4 = q & 3;
+#pragma unroll
+      for (int c = 0; c < BM / 32; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int m = 32 * c + 8 * (lane >> 4) + 4 * h + i4;
+          const int n = 16 * wid + 4 * p4;
+          tra[2 * c + h] = lds_addr(As + swz128(m, n >> 3) + (n & 7) * 2);
+        }
+      tr16_reads<NRD>(tra, trv);
+      f32x4 dbacc[UCB];
+#pragma unroll
+      for (int cb = 0; cb < UCB; ++cb) dbacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < BM / 32; ++c) {
+        const bf16x8 dyT = __builtin_bit_cast(bf16x8, u32x4{(uint32_t)trv[2 * c], (uint32_t)(trv[2 * c] >> 32),
+                                                            (uint32_t)trv[2 * c + 1], (uint32_t)(trv[2 * c + 1] >> 32)});
+#pragma unroll
+        for (int cb = 0; cb < UCB; ++cb)
+          dbacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dyT, tfr[cb][c], dbacc[cb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int cb = 0; cb < UCB; ++cb) {
+        const int j = cb * 16 + (lane & 15);
+        if (j < r) {
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int gn = kt * KC + 16 * wid + 4 * (lane >> 4) + ii;
+            if (gn < N) a.partB[((long)mt * r + j) * N + gn] = dbacc[cb][ii];
+          }
+        }
+      }
+    }
+    slot = slot == S - 1 ? 0 : slot + 1;
+  }
+
+  // ---- after the contraction: u to LDS, x tile, dA partial, dx epilogue ----
+  float* E = reinterpret_cast<float*>(ring);             // U [BM][R] | A^T [R][BN]
+  __syncthreads();                                        // ring released
+  if constexpr (!XPRE) issue_x();
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    if ((i & 1) != wn) continue;
+#pragma unroll
+    for (int cb = 0; cb < UCB; ++cb) {
+      const int j = cb * 16 + (lane & 15);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int ml = wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + ii;
+        if (j < R) E[ml * R + j] = j < r ? uacc[i >> 1][cb][ii] : 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int e = tid + 256 * i, j = e / BN, col = e % BN;
+    if (e < BN * R) E[BM * R + e] = (j < r && k0 + col < K) ? qv[i] : 0.f;
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+
+  // dA partial: thread -> column k = tid % BN, ranks jb + (256 / BN) jj
+  {
+    constexpr int TPK = 256 / BN, JPT = R / TPK;
+    const int kl = tid % BN, jb = tid / BN;
+    float da[JPT];
+#pragma unroll
+    for (int jj = 0; jj < JPT; ++jj) da[jj] = 0.f;
+#pragma unroll 8
+    for (int m = 0; m < rows_here; ++m) {
+      const int hrow = m * (BN / 64) + kl / 64;
+      const float xv = tile_bf16(Xs, hrow, kl % 64);
+#pragma unroll
+      for (int jj = 0; jj < JPT; ++jj) da[jj] = __builtin_fmaf(xv, E[m * R + jb + TPK * jj], da[jj]);
+    }
+    if (k0 + kl < K) {
+#pragma unroll
+      for (int jj = 0; jj < JPT; ++jj) {
+        const int j = jb + TPK * jj;
+        if (j < r) a.partA[((long)mt * r + j) * K + k0 + kl] = da[jj];
+      }
+    }
+  }
+
+  epilogue_lowrank<BM, BN, R, false>(acc, E, M, K, m0, k0, wm * (BM / 2), wn * (BN / 2), a.s, a.dx);
+}
+
+template <int BM, int BN, int S>
+void launch_tiles(Bwd8Args a, hipStream_t st) {
+  a.tiles_x = (a.K + BN - 1) / BN;
+  const dim3 grid((unsigned)(a.tiles_x * ((a.M + BM - 1) / BM)));
+  if (a.r <= 4) bwd8_kernel<BM, BN, S, 4><<<grid, 256, 0, st>>>(a);
+  else if (a.r <= 8) bwd8_kernel<BM, BN, S, 8><<<grid, 256, 0, st>>>(a);
+  else if (a.r <= 16) bwd8_kernel<BM, BN, S, 16><<<grid, 256, 0, st>>>(a);
+  else bwd8_kernel<BM, BN, S, 32><<<grid, 256, 0, st>>>(a);
+}
+
+}  // namespace
+
+int bwd8_row_block(int M, int K) {
+  const long t64 = (long)((M + 63) / 64) * ((K + 63) / 64);
+  return t64 <= 512 ? 64 : 128;
+}
+
+void launch_bwd_w8_fused(int M, int K, int N, const uint16_t* dy,
+                         const int8_t* codes, const float* sw, const float* B,
+                         const float* A, const float* t, const uint16_t* x,
+                         int r, float s, uint16_t* dx, float* partA, float* partB,
+                         hipStream_t st) {
+  Bwd8Args a{};
+  a.M = M; a.K = K; a.N = N; a.dy = dy; a.codes = codes; a.sw = sw; a.B = B;
+  a.A = A; a.t = t; a.x = x; a.r = r; a.s = s; a.dx = dx; a.partA = partA;
+  a.partB = partB;
+  if (bwd8_row_block(M, K) == 64) launch_tiles<64, 64, 3>(a, st);
+  else launch_tiles<128, 128, 2>(a, st);
+}
+
+}  // namespace qlora

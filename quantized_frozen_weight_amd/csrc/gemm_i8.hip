@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
   static_assert(EpiOps<BM, BN, R, true>::kFloats * 4 <= S * STG, "epilogue fits in the ring");
   __shared__ __attribute__((aligned(1024))) int8_t ring[S * STG];
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wid = wave_id();
   const int wm = wid >> 1, wn = wid & 1;
   const int m0 = ((int)blockIdx.x / a.tiles_x) * BM, n0 = ((int)blockIdx.x % a.tiles_x) * BN;
   const int M = a.M, N = a.N, K = a.K;

@@ -39,9 +39,8 @@ void launch_bwd_rows(int dtype, const void* dy, int M, int N, const float* B,
 
 // Adapter gradients dB = s t^T dy ([r, N]) and dA = s x^T u (stored [K, r]):
 // stage 1 writes per-split partial sums (partB / partA hold
-// skinny_partial_floats(M, r, N / K) floats), stage 2 adds them in order.
+// skinny_nsplit_host(M) * r * N / K floats), stage 2 adds them in order.
 // Stage 1 normally rides along with the input-gradient launch.
-size_t skinny_partial_floats(int M, int r, int C);
 SkinnyJobs make_adapter_grad_jobs(int M, int r, float s, const float* t,
                                   const void* dy, int N, float* dB, float* partB,
                                   const float* u, const void* x, int K, float* dA,
@@ -49,12 +48,15 @@ SkinnyJobs make_adapter_grad_jobs(int M, int r, float s, const float* t,
 void launch_skinny_stage1(int dtype, const SkinnyJobs& p, hipStream_t st);
 void launch_skinny_stage2(const SkinnyJobs& p, hipStream_t st);
 
-// dx = dys codes + s u A^T   (bf16; dys = dy * sw already folded)
-// sk (optional): adapter-gradient stage 1 run as extra blocks of this launch.
-void launch_gemm_dx_w8(int M, int K, int N, const uint16_t* dys,
-                       const int8_t* codes, const float* u, const float* A,
-                       int r, float s, uint16_t* dx, const SkinnyJobs* sk,
-                       hipStream_t st);
+// int8 weights, bf16: dx = dy deq(W)^T + s u A^T with u = dy B^T computed in
+// the same launch, plus per-row-block partial sums of dA (partA [blocks, r, K])
+// and dB (partB [blocks, r, N]); blocks = ceil(M / bwd8_row_block(M, K)).
+int bwd8_row_block(int M, int K);
+void launch_bwd_w8_fused(int M, int K, int N, const uint16_t* dy,
+                         const int8_t* codes, const float* sw, const float* B,
+                         const float* A, const float* t, const uint16_t* x,
+                         int r, float s, uint16_t* dx, float* partA, float* partB,
+                         hipStream_t st);
 // dx = dy (codes * sw)^T + s u A^T in float32
 void launch_gemm_dx_f32(int M, int K, int N, const float* dy,
                         const int8_t* codes, const float* sw, const float* u,

@@ -14,8 +14,8 @@ __global__ __launch_bounds__(256) void skinny_stage1_kernel(SkinnyJobs p) {
   skinny_partial_block<T, R>(p, blockIdx.x, red);
 }
 
-// out = s * sum over splits (split order fixed); one thread per (job, j, c)
-// with all of its split loads in flight together.
+// out = s * sum over splits (split order fixed); one thread per (job, j, c),
+// kSkMaxSplit loads in flight at a time.
 __global__ __launch_bounds__(256) void skinny_stage2_kernel(SkinnyJobs p) {
   const long e0 = (long)blockIdx.x * 256 + threadIdx.x;
   const long n0 = (long)p.r * p.C[0];
@@ -24,16 +24,18 @@ __global__ __launch_bounds__(256) void skinny_stage2_kernel(SkinnyJobs p) {
   if (job == 1 && (p.njobs < 2 || e >= (long)p.r * p.C[1])) return;
   const int C = p.C[job];
   const int j = (int)(e / C), c = (int)(e % C);
-  const float* __restrict__ base = p.partial[job];
+  const float* __restrict__ base = p.partial[job] + (long)j * C + c;
   const long stride = (long)p.r * C;
-  float v[kSkMaxSplit];
-#pragma unroll
-  for (int k = 0; k < kSkMaxSplit; ++k)
-    v[k] = base[(k < p.nsplit ? k : 0) * stride + (long)j * C + c];
   float sum = 0.f;
+  for (int k0 = 0; k0 < p.nsplit; k0 += kSkMaxSplit) {
+    float v[kSkMaxSplit];
 #pragma unroll
-  for (int k = 0; k < kSkMaxSplit; ++k)
-    if (k < p.nsplit) sum += v[k];
+    for (int k = 0; k < kSkMaxSplit; ++k)
+      v[k] = base[(k0 + k < p.nsplit ? k0 + k : k0) * stride];
+#pragma unroll
+    for (int k = 0; k < kSkMaxSplit; ++k)
+      if (k0 + k < p.nsplit) sum += v[k];
+  }
   const float out = p.s * sum;
   if (p.transpose[job]) p.out[job][(long)c * p.r + j] = out;
   else p.out[job][(long)j * C + c] = out;
@@ -51,10 +53,6 @@ void stage1_dispatch(const SkinnyJobs& p, hipStream_t st) {
 }
 
 }  // namespace
-
-size_t skinny_partial_floats(int M, int r, int C) {
-  return (size_t)skinny_nsplit_host(M) * (size_t)r * (size_t)C;
-}
 
 SkinnyJobs make_adapter_grad_jobs(int M, int r, float s, const float* t,
                                   const void* dy, int N, float* dB, float* partB,

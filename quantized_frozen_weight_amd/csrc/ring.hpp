@@ -25,6 +25,18 @@ constexpr int vmcnt_imm(int n) {
   return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14);
 }
 
+// s_waitcnt immediate that waits for every LDS operation of this wave
+// (lgkmcnt 0) and leaves the other counters unconstrained.
+constexpr int lgkmcnt0_imm() { return 15 | (7 << 4) | (0 << 8) | (3 << 14); }
+
+// Index of the calling wave in its block, as a wave-uniform (scalar) value.
+// Plain threadIdx.x / 64 is not known to be uniform to the compiler, which
+// then guards code that depends on it with an exec mask; MFMA instructions
+// ignore the exec mask, so such a guard would not hold.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+}
+
 // Wait until at most min(n, MAXI) stages of LPS loads each are outstanding.
 template <int LPS, int I, int MAXI>
 __device__ __forceinline__ void wait_stages(int n) {

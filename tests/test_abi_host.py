@@ -103,7 +103,13 @@ def test_workspace_queries(lib):
     n2 = ctypes.c_size_t()
     assert lib.qlora_bwd_workspace(ctypes.byref(_lin()), 64, Q.QLORA_BF16,
                                    ctypes.byref(n2)) == Q.QLORA_OK
-    assert n2.value >= 64 * 256 * 2
+    # t and u [M, r] float32, and one partial sum of dA and of dB per block
+    # of 64 rows: [1, r, K + N] float32
+    assert n2.value >= 2 * 64 * 4 * 4 + 4 * (256 + 256) * 4
+    n3 = ctypes.c_size_t()
+    assert lib.qlora_bwd_workspace(ctypes.byref(_lin()), 1000, Q.QLORA_BF16,
+                                   ctypes.byref(n3)) == Q.QLORA_OK
+    assert n3.value >= 2 * 1000 * 4 * 4 + 16 * 4 * (256 + 256) * 4
 
 
 @pytest.mark.parametrize("kw,M,dtype,want", [

@@ -148,6 +148,8 @@ SMALL = [
     (2, 17, 784, 272, 1),
     (2, 130, 128, 144, 16),
     (2, 257, 512, 1040, 32),
+    (2, 64, 3072, 128, 8),      # more dx column tiles than 64-n stages
+    (2, 1000, 64, 2048, 4),     # one column tile walking 32 stages, 16 row blocks
     (3, 200, 3072, 400, 4),
     (5, 1, 128, 16, 4),
     (5, 77, 256, 272, 8),
