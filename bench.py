@@ -45,6 +45,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline (0: skip)")
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 256 MiB device copy (for scaling HBM counters)")
     return p.parse_args()
 
 
@@ -124,20 +126,19 @@ def main():
     torch.cuda.synchronize()
     quantize_ms = e0.elapsed_time(e1)
 
-    def step(ev_f=None, ev_b=None):
+    def step(ev_b=None, repeats=1):
         st = torch.cuda.current_stream().cuda_stream
         for i, l in enumerate(layers):
-            a, b = (ev_f[i] if ev_f else (None, None))
             check(lib.qlora_fwd_timed(ctypes.byref(l.cs), M, l.dt, l.x.data_ptr(),
                                       l.y.data_ptr(), l.t.data_ptr(), wsp, ws_bytes, st,
-                                      a, b), "fwd")
+                                      1, None, None), "fwd")
         for i in reversed(range(len(layers))):
             l = layers[i]
             a, b = (ev_b[i] if ev_b else (None, None))
             check(lib.qlora_bwd_timed(ctypes.byref(l.cs), M, l.dt, l.x.data_ptr(),
                                       l.dy.data_ptr(), l.t.data_ptr(), l.dx.data_ptr(),
                                       l.dA.data_ptr(), l.dB.data_ptr(), wsp, ws_bytes, st,
-                                      a, b), "bwd")
+                                      repeats if ev_b else 1, a, b), "bwd")
 
     # eager warm-up (also loads every kernel)
     for _ in range(3):
@@ -183,6 +184,8 @@ def main():
     torch.cuda.synchronize()
     eager_ms = e0.elapsed_time(e1) / 10
 
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
     roof = dominant_kernel_roofline(w, layers, step, torch)
     cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
 
@@ -227,41 +230,77 @@ def describe(w):
            f"LoRA r={w.r} alpha={w.alpha:g}, {w.dtype} activations"
 
 
-def dominant_kernel_roofline(w, layers, step, torch):
-    """Time the input-gradient launch (the step's largest kernel) live.
+# HBM traffic of the dominant kernel per launch on the benchmarked workload,
+# from two rocprofv3 counter passes (FETCH_SIZE, then WRITE_SIZE, KiB per
+# dispatch), each divided by what the same counter reads per KiB of a plain
+# 256 MiB device copy in the same run. Valid only for the kernel sources it
+# was taken on (their SHA-256); otherwise reported as null.
+TRAFFIC = {
+    "workload": 2,
+    "sources": ["gemm_bwd8.hip", "ring.hpp", "common.hpp", "launch.hpp"],
+    "sha256": "aec4628696117355716e5139c02c3e84230f5efc323812ba0a01631f3bd514e1",
+    "bytes_per_launch": 25014439,
+}
 
-    Each launch is bracketed by HIP events that the library records on the
-    stream it launches on. Algorithmic work per launch: 2 M K (N + r) flops
-    for dx (the product over N plus the rank-r term) and 2 M r (N + K) for
-    the first stage of dB and dA that rides in the same launch; peak: dense
+
+def kernel_sources_sha256(names):
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "quantized_frozen_weight_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def copy_calibration(torch, dev):
+    """A plain device-to-device copy of 256 MiB, three times (its counters
+    calibrate the HBM byte counters of the kernels in the same run)."""
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def dominant_kernel_roofline(w, layers, step, torch):
+    """Time the backward launch (the step's largest kernel) live.
+
+    In one eager step the library launches each layer's backward kernel 20
+    times back to back (same inputs, same outputs) between two HIP events
+    that it records on the stream it launches on; the average duration is
+    the summed intervals over all launches. Algorithmic work per launch of the fused int8
+    backward: 2 M K N for dx, 2 M N r each for u and dB, 2 M K r each for dA
+    and the rank-r term of dx, i.e. 2 M K N + 4 M r (N + K) flops; peak: dense
     bf16 MFMA.
     """
     n = len(layers)
-    reps = 5
-    pairs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(n)] for _ in range(reps)]
-    for rep in pairs:          # materialize the events
-        for a, b in rep:
-            a.record(); b.record()
+    repeats = 20
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n)]
+    for a, b in pairs:         # materialize the events
+        a.record(); b.record()
     torch.cuda.synchronize()
-    for rep in pairs:
-        step(ev_b=[(a.cuda_event, b.cuda_event) for a, b in rep])
+    step(ev_b=[(a.cuda_event, b.cuda_event) for a, b in pairs], repeats=repeats)
     torch.cuda.synchronize()
-    tot_ms = sum(a.elapsed_time(b) for rep in pairs for a, b in rep)
-    launches = n * reps
+    tot_ms = sum(a.elapsed_time(b) for a, b in pairs)
+    launches = n * repeats
     avg_ms = tot_ms / launches
-    flops = sum(2.0 * w.M * l.K * (l.N + w.r) + 2.0 * w.M * w.r * (l.N + l.K)
-                for l in layers) / n
+    flops = sum(2.0 * w.M * l.K * l.N + 4.0 * w.M * w.r * (l.N + l.K) for l in layers) / n
     achieved = flops / (avg_ms * 1e-3) / 1e12
     peak = PEAK["bf16" if w.dtype == "bf16" else "f32"] / 1e12
+    traffic = None
+    if (TRAFFIC["sha256"] is not None and w.cid == TRAFFIC["workload"]
+            and kernel_sources_sha256(TRAFFIC["sources"]) == TRAFFIC["sha256"]):
+        traffic = TRAFFIC["bytes_per_launch"]
     return {
-        "kernel": "dx8_kernel (input gradient on bf16 MFMA + adapter-gradient stage 1)",
+        "kernel": "bwd8_kernel (fused int8 backward: dx, u, dA and dB partial sums, bf16 MFMA)",
         "bound": "mfma",
         "achieved": round(achieved, 2),
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
-        "traffic": None,
+        "traffic": traffic,
         "avg_launch_us": round(avg_ms * 1e3, 3),
         "launches_timed": launches,
         "flops_per_launch": flops,

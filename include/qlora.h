@@ -145,18 +145,23 @@ int qlora_bwd(const qlora_linear* L, int M, int dtype, const void* x,
               const void* dy, const float* t_saved, void* dx, float* dA,
               float* dB, void* ws, size_t ws_bytes, void* stream);
 
-/* qlora_fwd / qlora_bwd with timing marks: if not NULL, ev_start and ev_stop
- * (hipEvent_t) are recorded on `stream` immediately before and after the
- * call's main product kernel (the int8 or 4-bit forward product; the input
- * gradient product, only when dx is not NULL). Results are identical to the
- * unmarked calls; used to time that kernel live. */
+/* qlora_fwd / qlora_bwd with timing marks, for timing the call's main
+ * product kernel live: the int8 or 4-bit forward product; the fused int8
+ * backward (dx, u and the adapter-gradient partial sums) or, on the other
+ * paths, the input-gradient product. That kernel is launched `repeats` times
+ * (>= 1) back to back; every launch rewrites the same outputs from the same
+ * inputs, so results are identical to the unmarked call. If not NULL,
+ * ev_start and ev_stop (hipEvent_t) are recorded on `stream` immediately
+ * before the first and after the last of these launches, so the elapsed
+ * time over `repeats` is the kernel's average duration with the cost of the
+ * two event records spread over the launches. repeats < 1 -> QLORA_EINVAL. */
 int qlora_fwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
                     void* y, float* t_save, void* ws, size_t ws_bytes,
-                    void* stream, void* ev_start, void* ev_stop);
+                    void* stream, int repeats, void* ev_start, void* ev_stop);
 int qlora_bwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
                     const void* dy, const float* t_saved, void* dx, float* dA,
                     float* dB, void* ws, size_t ws_bytes, void* stream,
-                    void* ev_start, void* ev_stop);
+                    int repeats, void* ev_start, void* ev_stop);
 
 /* Test hook: the forward's per-row activation quantizer alone. x [M, K] in
  * the compute dtype -> xq int8 [M, K], sx float32 [M]. Same kernel as

@@ -77,8 +77,8 @@ def lib() -> ctypes.CDLL:
     L.qlora_bwd.argtypes = [plin, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.qlora_quantize_rows.argtypes = [vp, i, i, i, vp, vp, vp]
     L.qlora_fwd_acc.argtypes = [plin, i, i, vp, vp, vp, sz, vp]
-    L.qlora_fwd_timed.argtypes = [plin, i, i, vp, vp, vp, vp, sz, vp, vp, vp]
-    L.qlora_bwd_timed.argtypes = [plin, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+    L.qlora_fwd_timed.argtypes = [plin, i, i, vp, vp, vp, vp, sz, vp, i, vp, vp]
+    L.qlora_bwd_timed.argtypes = [plin, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp, i, vp, vp]
     for name in EXPORTS[1:]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L

@@ -165,9 +165,10 @@ int qlora_fwd_workspace(const qlora_linear* L, int M, int dtype, size_t* bytes) 
 
 int qlora_fwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
                     void* y, float* t_save, void* ws, size_t ws_bytes,
-                    void* stream, void* ev_start, void* ev_stop) {
+                    void* stream, int repeats, void* ev_start, void* ev_stop) {
   int st = check_linear(L, M, dtype);
   if (st) return st;
+  if (repeats < 1) return QLORA_EINVAL;
   if (!x || !y || !aligned16(x) || !aligned16(y)) return QLORA_EINVAL;
   if (t_save && !aligned16(t_save)) return QLORA_EINVAL;
   const FwdLayout w = fwd_layout(L, M);
@@ -180,18 +181,20 @@ int qlora_fwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
     float* sx = reinterpret_cast<float*>(at(ws, w.sx));
     launch_rowquant(dtype, x, M, L->K, L->A, L->r, xq, sx, t, s);
     mark(ev_start, s);
-    launch_gemm_fwd_w8(dtype, M, L->N, L->K, xq,
-                       static_cast<const int8_t*>(L->codes), sx,
-                       static_cast<const float*>(L->scales), t, L->B, L->r,
-                       lora_s(L), y, nullptr, s);
+    for (int rep = 0; rep < repeats; ++rep)
+      launch_gemm_fwd_w8(dtype, M, L->N, L->K, xq,
+                         static_cast<const int8_t*>(L->codes), sx,
+                         static_cast<const float*>(L->scales), t, L->B, L->r,
+                         lora_s(L), y, nullptr, s);
     mark(ev_stop, s);
   } else {
     launch_lora_down(dtype, x, M, L->K, L->A, L->r, t, s);
     mark(ev_start, s);
-    launch_gemm_fwd_w4(M, L->N, L->K, static_cast<const uint16_t*>(x),
-                       static_cast<const uint8_t*>(L->codes),
-                       static_cast<const _Float16*>(L->scales), t, L->B, L->r,
-                       lora_s(L), static_cast<uint16_t*>(y), s);
+    for (int rep = 0; rep < repeats; ++rep)
+      launch_gemm_fwd_w4(M, L->N, L->K, static_cast<const uint16_t*>(x),
+                         static_cast<const uint8_t*>(L->codes),
+                         static_cast<const _Float16*>(L->scales), t, L->B, L->r,
+                         lora_s(L), static_cast<uint16_t*>(y), s);
     mark(ev_stop, s);
   }
   return launch_status();
@@ -199,7 +202,7 @@ int qlora_fwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
 
 int qlora_fwd(const qlora_linear* L, int M, int dtype, const void* x, void* y,
               float* t_save, void* ws, size_t ws_bytes, void* stream) {
-  return qlora_fwd_timed(L, M, dtype, x, y, t_save, ws, ws_bytes, stream,
+  return qlora_fwd_timed(L, M, dtype, x, y, t_save, ws, ws_bytes, stream, 1,
                          nullptr, nullptr);
 }
 
@@ -214,9 +217,10 @@ int qlora_bwd_workspace(const qlora_linear* L, int M, int dtype, size_t* bytes) 
 int qlora_bwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
                     const void* dy, const float* t_saved, void* dx, float* dA,
                     float* dB, void* ws, size_t ws_bytes, void* stream,
-                    void* ev_start, void* ev_stop) {
+                    int repeats, void* ev_start, void* ev_stop) {
   int st = check_linear(L, M, dtype);
   if (st) return st;
+  if (repeats < 1) return QLORA_EINVAL;
   if (!x || !dy || !dA || !dB) return QLORA_EINVAL;
   if (!aligned16(x) || !aligned16(dy) || !aligned16(dA) || !aligned16(dB)) return QLORA_EINVAL;
   if ((t_saved && !aligned16(t_saved)) || (dx && !aligned16(dx))) return QLORA_EINVAL;
@@ -238,11 +242,12 @@ int qlora_bwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
   if (w8 && dtype == QLORA_BF16 && dx != nullptr) {
     // one launch: dx, u, and the per-row-block partial sums of dA and dB
     mark(ev_start, s);
-    launch_bwd_w8_fused(M, L->K, L->N, static_cast<const uint16_t*>(dy),
-                        static_cast<const int8_t*>(L->codes),
-                        static_cast<const float*>(L->scales), L->B, L->A, t,
-                        static_cast<const uint16_t*>(x), L->r, sc,
-                        static_cast<uint16_t*>(dx), partA, partB, s);
+    for (int rep = 0; rep < repeats; ++rep)
+      launch_bwd_w8_fused(M, L->K, L->N, static_cast<const uint16_t*>(dy),
+                          static_cast<const int8_t*>(L->codes),
+                          static_cast<const float*>(L->scales), L->B, L->A, t,
+                          static_cast<const uint16_t*>(x), L->r, sc,
+                          static_cast<uint16_t*>(dx), partA, partB, s);
     mark(ev_stop, s);
     SkinnyJobs sk{};
     sk.njobs = 2; sk.M = M; sk.r = L->r; sk.s = sc;
@@ -255,22 +260,26 @@ int qlora_bwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
   launch_bwd_rows(dtype, dy, M, L->N, L->B, L->r, nullptr, nullptr, u, s);
   const SkinnyJobs sk = make_adapter_grad_jobs(M, L->r, sc, t, dy, L->N, dB, partB,
                                                u, x, L->K, dA, partA);
-  mark(ev_start, s);
   if (dx != nullptr && dtype == QLORA_BF16) {
     // 4-bit input gradient with the adapter-gradient stage 1 riding along
-    launch_gemm_dx_w4(M, L->K, L->N, static_cast<const uint16_t*>(dy),
-                      static_cast<const uint8_t*>(L->codes),
-                      static_cast<const _Float16*>(L->scales), u, L->A, L->r,
-                      sc, static_cast<uint16_t*>(dx), &sk, s);
+    mark(ev_start, s);
+    for (int rep = 0; rep < repeats; ++rep)
+      launch_gemm_dx_w4(M, L->K, L->N, static_cast<const uint16_t*>(dy),
+                        static_cast<const uint8_t*>(L->codes),
+                        static_cast<const _Float16*>(L->scales), u, L->A, L->r,
+                        sc, static_cast<uint16_t*>(dx), &sk, s);
+    mark(ev_stop, s);
   } else {
     launch_skinny_stage1(dtype, sk, s);
+    mark(ev_start, s);
     if (dx != nullptr)
-      launch_gemm_dx_f32(M, L->K, L->N, static_cast<const float*>(dy),
-                         static_cast<const int8_t*>(L->codes),
-                         static_cast<const float*>(L->scales), u, L->A, L->r,
-                         sc, static_cast<float*>(dx), s);
+      for (int rep = 0; rep < repeats; ++rep)
+        launch_gemm_dx_f32(M, L->K, L->N, static_cast<const float*>(dy),
+                           static_cast<const int8_t*>(L->codes),
+                           static_cast<const float*>(L->scales), u, L->A, L->r,
+                           sc, static_cast<float*>(dx), s);
+    mark(ev_stop, s);
   }
-  mark(ev_stop, s);
   launch_skinny_stage2(sk, s);
   return launch_status();
 }
@@ -279,7 +288,7 @@ int qlora_bwd(const qlora_linear* L, int M, int dtype, const void* x,
               const void* dy, const float* t_saved, void* dx, float* dA,
               float* dB, void* ws, size_t ws_bytes, void* stream) {
   return qlora_bwd_timed(L, M, dtype, x, dy, t_saved, dx, dA, dB, ws, ws_bytes,
-                         stream, nullptr, nullptr);
+                         stream, 1, nullptr, nullptr);
 }
 
 int qlora_quantize_rows(const void* x, int M, int K, int dtype, int8_t* xq,

@@ -153,6 +153,11 @@ def test_calls_fail_before_launch(lib):
     assert lib.qlora_quantize_rows(FAKE, 4, 24, Q.QLORA_BF16, FAKE, FAKE, None) == Q.QLORA_EINVAL
     assert lib.qlora_fwd_acc(ctypes.byref(_lin(fmt=Q.QLORA_W4G128)), 64, Q.QLORA_BF16,
                              FAKE, FAKE, FAKE, 1 << 30, None) == Q.QLORA_EUNSUPPORTED
+    # the timed variants need at least one launch of the product kernel
+    assert lib.qlora_fwd_timed(ctypes.byref(lin), 64, Q.QLORA_BF16, FAKE, FAKE, None, FAKE,
+                               need, None, 0, None, None) == Q.QLORA_EINVAL
+    assert lib.qlora_bwd_timed(ctypes.byref(lin), 64, Q.QLORA_BF16, FAKE, FAKE, None, FAKE,
+                               FAKE, FAKE, FAKE, n.value, None, 0, None, None) == Q.QLORA_EINVAL
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

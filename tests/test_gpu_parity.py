@@ -11,6 +11,7 @@ degenerate shapes that span several 128-wide tiles with partial tails.
 
 from __future__ import annotations
 
+import ctypes
 import sys
 
 import numpy as np
@@ -230,6 +231,41 @@ def test_deterministic_and_frozen():
     assert outs[0] == outs[1], "repeated calls must give identical bytes"
     assert torch.equal(codes0, case.lin.codes) and torch.equal(scales0, case.lin.scales)
     assert torch.equal(A0, case.lin.A) and torch.equal(B0, case.lin.B)
+
+
+def test_timed_repeats_are_identical():
+    """The timed entry points launch the product kernel several times; every
+    launch rewrites the same outputs, so results match the plain call bit for
+    bit."""
+    say("timed repeats: mlp layer 1 at 256 rows")
+    w = WL.small(2, 256, 1024, 1024, 8)
+    case = Case(w, 0)
+    y1, t1 = Q.qlora_fwd(case.lin, case.x_t)
+    dx1, dA1, dB1 = Q.qlora_bwd(case.lin, case.x_t, case.dy_t, t=t1)
+    lib = Q.lib()
+    M, K, N = case.M, case.K, case.N
+    cs = case.lin.cstruct()
+    dt = Q.QLORA_BF16
+    ws = torch.empty(max(Q.qlora_fwd_workspace(case.lin, M, dt),
+                         Q.qlora_bwd_workspace(case.lin, M, dt)), dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(y1)
+    t = torch.empty_like(t1)
+    dx, dA, dB = torch.empty_like(dx1), torch.empty_like(dA1), torch.empty_like(dB1)
+    st = torch.cuda.current_stream().cuda_stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(); e1.record()       # torch only reports times of events it has recorded once
+    torch.cuda.synchronize()
+    assert lib.qlora_fwd_timed(ctypes.byref(cs), M, dt, case.x_t.data_ptr(), y.data_ptr(),
+                               t.data_ptr(), ws.data_ptr(), ws.numel(), st, 3,
+                               e0.cuda_event, e1.cuda_event) == 0
+    assert lib.qlora_bwd_timed(ctypes.byref(cs), M, dt, case.x_t.data_ptr(), case.dy_t.data_ptr(),
+                               t.data_ptr(), dx.data_ptr(), dA.data_ptr(), dB.data_ptr(),
+                               ws.data_ptr(), ws.numel(), st, 3, e0.cuda_event, e1.cuda_event) == 0
+    torch.cuda.synchronize()
+    assert e0.elapsed_time(e1) > 0
+    for a, b in [(y, y1), (t, t1), (dx, dx1), (dA, dA1), (dB, dB1)]:
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
 
 
 def test_mlp_stack_all_layers():
