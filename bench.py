@@ -237,7 +237,7 @@ def describe(w):
 # was taken on (their SHA-256); otherwise reported as null.
 TRAFFIC = {
     "workload": 2,
-    "sources": ["gemm_bwd8.hip", "ring.hpp", "common.hpp", "launch.hpp"],
+    "sources": ["gemm_bwd.hip", "ring.hpp", "common.hpp", "launch.hpp"],
     "sha256": "aec4628696117355716e5139c02c3e84230f5efc323812ba0a01631f3bd514e1",
     "bytes_per_launch": 25014439,
 }

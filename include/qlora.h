@@ -56,7 +56,9 @@
  *     synchronization.
  *   - Constraints: 1 <= M, 16 <= K, 16 <= N, K % 16 == 0, N % 16 == 0,
  *     1 <= r <= 32, all pointers 16-byte aligned; QLORA_W4G128 needs
- *     K % 128 == 0 and the bf16 compute dtype.
+ *     K % 128 == 0 and the bf16 compute dtype (EINVAL / EUNSUPPORTED
+ *     otherwise), and qlora_fwd / qlora_bwd take K <= 16384 for it (the
+ *     products keep one block's fp16 scales in LDS; EUNSUPPORTED above).
  *   - Outputs (y, t, dx, dA, dB) are overwritten, never accumulated into.
  *     codes, scales, A and B are only read by qlora_fwd / qlora_bwd.
  *   - Non-finite x or dy propagate into the outputs; nothing is checked on

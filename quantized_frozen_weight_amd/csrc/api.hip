@@ -43,6 +43,7 @@ int check_linear(const qlora_linear* L, int M, int dtype) {
   if (L->fmt == QLORA_W4G128) {
     if (L->K % 128) return QLORA_EINVAL;
     if (dtype != QLORA_BF16) return QLORA_EUNSUPPORTED;
+    if (L->K > 128 * kW4MaxGroups) return QLORA_EUNSUPPORTED;
   }
   const void* ptrs[4] = {L->codes, L->scales, L->A, L->B};
   for (const void* p : ptrs)
@@ -239,19 +240,19 @@ int qlora_bwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
   const bool w8 = L->fmt == QLORA_W8;
   float* partB = reinterpret_cast<float*>(at(ws, w.pB));
   float* partA = reinterpret_cast<float*>(at(ws, w.pA));
-  if (w8 && dtype == QLORA_BF16 && dx != nullptr) {
+  if (dtype == QLORA_BF16 && dx != nullptr) {
     // one launch: dx, u, and the per-row-block partial sums of dA and dB
     mark(ev_start, s);
     for (int rep = 0; rep < repeats; ++rep)
-      launch_bwd_w8_fused(M, L->K, L->N, static_cast<const uint16_t*>(dy),
-                          static_cast<const int8_t*>(L->codes),
-                          static_cast<const float*>(L->scales), L->B, L->A, t,
-                          static_cast<const uint16_t*>(x), L->r, sc,
-                          static_cast<uint16_t*>(dx), partA, partB, s);
+      launch_bwd_fused(w8 ? 0 : 1, M, L->K, L->N, static_cast<const uint16_t*>(dy),
+                       L->codes, L->scales, L->B, L->A, t,
+                       static_cast<const uint16_t*>(x), L->r, sc,
+                       static_cast<uint16_t*>(dx), partA, partB, s);
     mark(ev_stop, s);
     SkinnyJobs sk{};
+    const int bm = bwd_row_block(w8 ? 0 : 1, M, L->K);
     sk.njobs = 2; sk.M = M; sk.r = L->r; sk.s = sc;
-    sk.nsplit = (M + bwd8_row_block(M, L->K) - 1) / bwd8_row_block(M, L->K);
+    sk.nsplit = (M + bm - 1) / bm;
     sk.partial[0] = partB; sk.C[0] = L->N; sk.out[0] = dB; sk.transpose[0] = 0;
     sk.partial[1] = partA; sk.C[1] = L->K; sk.out[1] = dA; sk.transpose[1] = 1;
     launch_skinny_stage2(sk, s);
@@ -260,26 +261,17 @@ int qlora_bwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
   launch_bwd_rows(dtype, dy, M, L->N, L->B, L->r, nullptr, nullptr, u, s);
   const SkinnyJobs sk = make_adapter_grad_jobs(M, L->r, sc, t, dy, L->N, dB, partB,
                                                u, x, L->K, dA, partA);
-  if (dx != nullptr && dtype == QLORA_BF16) {
-    // 4-bit input gradient with the adapter-gradient stage 1 riding along
-    mark(ev_start, s);
+  // float32 compute (int8 weights): the adapter-gradient stage 1, then the
+  // float32 input gradient; or no input gradient at all
+  launch_skinny_stage1(dtype, sk, s);
+  mark(ev_start, s);
+  if (dx != nullptr)
     for (int rep = 0; rep < repeats; ++rep)
-      launch_gemm_dx_w4(M, L->K, L->N, static_cast<const uint16_t*>(dy),
-                        static_cast<const uint8_t*>(L->codes),
-                        static_cast<const _Float16*>(L->scales), u, L->A, L->r,
-                        sc, static_cast<uint16_t*>(dx), &sk, s);
-    mark(ev_stop, s);
-  } else {
-    launch_skinny_stage1(dtype, sk, s);
-    mark(ev_start, s);
-    if (dx != nullptr)
-      for (int rep = 0; rep < repeats; ++rep)
-        launch_gemm_dx_f32(M, L->K, L->N, static_cast<const float*>(dy),
-                           static_cast<const int8_t*>(L->codes),
-                           static_cast<const float*>(L->scales), u, L->A, L->r,
-                           sc, static_cast<float*>(dx), s);
-    mark(ev_stop, s);
-  }
+      launch_gemm_dx_f32(M, L->K, L->N, static_cast<const float*>(dy),
+                         static_cast<const int8_t*>(L->codes),
+                         static_cast<const float*>(L->scales), u, L->A, L->r,
+                         sc, static_cast<float*>(dx), s);
+  mark(ev_stop, s);
   launch_skinny_stage2(sk, s);
   return launch_status();
 }

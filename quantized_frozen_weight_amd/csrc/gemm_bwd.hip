@@ -1,8 +1,10 @@
-// Backward of the frozen int8 layer with its adapter, in one launch (plus the
-// fixed-order combine of the adapter-gradient partial sums):
+// Backward of the frozen-weight layer (int8, or 4-bit with fp16 group
+// scales) with its adapter, in one launch (plus the fixed-order combine of
+// the adapter-gradient partial sums):
 //
 //   u  = dy B^T                                  [M, r]
 //   dx = dy deq(W)^T + s u A^T,  deq(W)[k, n] = q[n, k] sw[n]
+//                                 (4-bit: q[n, k] sc[n, k / 128])
 //   dB = s t^T dy                                [r, N]
 //   dA = s x^T u                                 [K, r]
 //
@@ -19,8 +21,9 @@
 // with sw[n] and the adapter's B columns for those n. Once a stage has
 // landed, the whole block converts it in one cooperative pass (every code
 // read and widened once, not once per wave that uses it):
-//   * CB [BN k][64 n] = bf16(q[n, k] sw[n]), the transposed dequantized
-//     weight, as swizzled 128-byte rows;
+//   * CB [BN k][64 n] = bf16(deq(W)[k, n]), the transposed dequantized
+//     weight, as swizzled 128-byte rows (4-bit: the nibbles unpacked and
+//     scaled by their group's fp16 scale, one 128-wide group per block);
 //   * BU [16 j][64 n] = bf16(B[j, n]).
 // Then per 32 n, on v_mfma_f32_16x16x32_bf16:
 //   * dx += dy CB^T;
@@ -44,11 +47,12 @@ namespace {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-struct Bwd8Args {
+struct BwdArgs {
   int M, K, N;
   const uint16_t* dy;      // [M, N] bf16
-  const int8_t* codes;     // [N, K]
-  const float* sw;         // [N]
+  const int8_t* codes;     // int8 [N, K], or packed 4-bit [N, K / 2]
+  const float* sw;         // int8: channel scales [N]
+  const uint16_t* sc4;     // 4-bit: fp16 group scales [N, K / 128] (bit patterns)
   const float* B;          // [r, N]
   const float* A;          // [K, r]
   const float* t;          // [M, r]
@@ -118,15 +122,21 @@ __device__ __forceinline__ float tile_bf16(const int8_t* tile, int row, int e) {
   return __uint_as_float((uint32_t)v << 16);
 }
 
-template <int BM, int BN, int S, int R>
-__global__ __launch_bounds__(256) void bwd8_kernel(Bwd8Args a) {
+// W4: 4-bit weights (two codes per byte, fp16 scale per 128 k); else int8.
+template <bool W4, int BM, int BN, int S, int R>
+__global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
   constexpr int KC = 64;                              // n per stage
+  constexpr int RB = W4 ? BN / 2 : BN;                // code bytes per row of n
   constexpr int AUXI = ((1 + R) * 256 + 4095) / 4096;  // aux DMA instructions per wave
-  constexpr int ASZ = BM * 128, BSZ = KC * BN, XSZ = 4 * AUXI * 1024;
+  constexpr int ASZ = BM * 128, BSZ = KC * RB, XSZ = 4 * AUXI * 1024;
   constexpr int STG = ASZ + BSZ + XSZ;
-  constexpr int AI = BM / 32, BI = BN / 64, LPS = AI + BI + AUXI;
+  // per wave and stage: dy rows, code rows, aux, and (4-bit) one scale load
+  constexpr int AI = BM / 32, BI = RB / 64, LPS = AI + BI + AUXI + (W4 ? 1 : 0);
   constexpr int FM = BM / 32, FN = BN / 32;
-  constexpr int RPI = 1024 / BN, CPR = BN / 16;
+  constexpr int RPI = 1024 / RB, CPR = RB / 16;
+  static_assert(RB == 64 || RB == 128, "code rows of 64 or 128 bytes");
+  static_assert(!W4 || (BN == 128 && S == 2),
+                "4-bit: one 128-wide k group per block; the scales ride one stage ahead in a register");
   constexpr int UCB = (R + 15) / 16;                  // u column blocks of 16
   constexpr bool XPRE = BM * BN * 2 <= 8192;          // x tile kept outside the ring
   constexpr int CBSZ = BN * 128;                      // converted codes [BN][64] bf16
@@ -135,15 +145,16 @@ __global__ __launch_bounds__(256) void bwd8_kernel(Bwd8Args a) {
   constexpr int XTSZ = BM * BN * 2;
   constexpr int EFL = (BM + BN) * R;                  // epilogue floats: U [BM][R], A^T [R][BN]
   static_assert(EFL * 4 + (XPRE ? 0 : XTSZ) <= S * STG, "epilogue and x tile fit in the ring");
-  static_assert(BN == 64 || BN == 128, "code rows of 64 or 128 bytes");
   // One LDS array for everything: with a second __shared__ object the
   // compiler can no longer tell that the ring's reads do not wait on the
   // direct-to-LDS loads still in flight, and waits for all of them.
-  __shared__ __attribute__((aligned(1024))) int8_t ring[S * STG + CBSZ + BUSZ + TSZ + (XPRE ? XTSZ : 0)];
+  constexpr int SCSZ = W4 ? KC * 4 : 0;               // 4-bit: the stage's scales, float
+  __shared__ __attribute__((aligned(1024))) int8_t ring[S * STG + CBSZ + BUSZ + TSZ + SCSZ + (XPRE ? XTSZ : 0)];
   int8_t* CB = ring + S * STG;
   int8_t* BU = CB + CBSZ;
   float* Ts = reinterpret_cast<float*>(BU + BUSZ);                             // [BM][r]
-  int8_t* Xs = XPRE ? BU + BUSZ + TSZ : ring + EFL * 4;                        // [BM][BN] bf16
+  float* SCs = reinterpret_cast<float*>(BU + BUSZ + TSZ);                      // [64] (4-bit)
+  int8_t* Xs = XPRE ? BU + BUSZ + TSZ + SCSZ : ring + EFL * 4;                 // [BM][BN] bf16
 
   const int tid = threadIdx.x, lane = tid & 63, wid = wave_id();
   const int wm = wid >> 1, wn = wid & 1;
@@ -195,16 +206,17 @@ __global__ __launch_bounds__(256) void bwd8_kernel(Bwd8Args a) {
     nA[i] = c * 8;
     srcA[i] = reinterpret_cast<const int8_t*>(a.dy + (long)(gm < M ? gm : M - 1) * N + c * 8);
   }
+  const long crs = W4 ? K / 2 : K;                    // code bytes per row in memory
   const int8_t* srcB[BI];
   int nB[BI];
   bool okB[BI];
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
     const int row = (wid * BI + i) * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ code_swz<BN>(row), gk = k0 + c * 16;
+    const int c = (lane % CPR) ^ code_swz<RB>(row), gk = (W4 ? k0 / 2 : k0) + c * 16;
     nB[i] = row;
-    okB[i] = gk < K;
-    srcB[i] = okB[i] ? a.codes + (long)row * K + gk : zero_chunk(lane);
+    okB[i] = gk < crs;
+    srcB[i] = okB[i] ? a.codes + (long)row * crs + gk : zero_chunk(lane);
   }
   const int8_t* srcX[AUXI];
   int nX[AUXI];
@@ -215,9 +227,14 @@ __global__ __launch_bounds__(256) void bwd8_kernel(Bwd8Args a) {
     const int j = e / 64 - 1, nn = e % 64;
     nX[i] = nn;
     okX[i] = j < r;
-    srcX[i] = j < 0 ? reinterpret_cast<const int8_t*>(a.sw + nn)
+    okX[i] = okX[i] && !(W4 && j < 0);                 // 4-bit: no channel scales
+    srcX[i] = j < 0 ? (W4 ? zero_chunk(lane) : reinterpret_cast<const int8_t*>(a.sw + nn))
                     : (j < r ? reinterpret_cast<const int8_t*>(a.B + (long)j * N + nn) : zero_chunk(lane));
   }
+  // 4-bit: lane l of wave w loads the scale of n = 16 w + l % 16 of the
+  // stage (k group k0 / 128); kept as raw bits until the stage has landed
+  uint16_t scr = 0;
+  const int scn = 16 * wid + (lane & 15);
   auto issue = [&](int kt, int slot) {
     int8_t* base = ring + slot * STG;
     const int nb = kt * KC;
@@ -230,15 +247,19 @@ __global__ __launch_bounds__(256) void bwd8_kernel(Bwd8Args a) {
     }
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
-      const int8_t* src = okB[i] ? srcB[i] + (long)nb * K : srcB[i];
+      const int8_t* src = okB[i] ? srcB[i] + (long)nb * crs : srcB[i];
       if (tail && nb + nB[i] >= N) src = zero_chunk(lane);
-      lds_dma16(src, base + ASZ + (wid * BI + i) * RPI * BN);
+      lds_dma16(src, base + ASZ + (wid * BI + i) * RPI * RB);
     }
 #pragma unroll
     for (int i = 0; i < AUXI; ++i) {
       const int8_t* src = okX[i] ? srcX[i] + 4L * nb : srcX[i];
       if (tail && nb + nX[i] >= N) src = zero_chunk(lane);
       lds_dma16(src, base + ASZ + BSZ + (wid * AUXI + i) * 1024);
+    }
+    if constexpr (W4) {
+      const int n = nb + scn;
+      scr = a.sc4[(long)(n < N ? n : N - 1) * (K / 128) + k0 / 128];
     }
   };
 
@@ -278,6 +299,10 @@ __global__ __launch_bounds__(256) void bwd8_kernel(Bwd8Args a) {
   int slot = 0;
   for (int kt = 0; kt < nk; ++kt) {
     wait_stages<LPS, 0, S - 2>(nk - 1 - kt);
+    if constexpr (W4) {                              // the stage's scales, as float
+      if (lane < 16) SCs[scn] = (float)__builtin_bit_cast(_Float16, scr);
+      __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+    }
     __builtin_amdgcn_s_barrier();                    // stage kt landed; CB, BU free
     if (kt + S - 1 < nk) issue(kt + S - 1, slot == 0 ? S - 1 : slot - 1);
     const int8_t* As = ring + slot * STG;
@@ -285,7 +310,26 @@ __global__ __launch_bounds__(256) void bwd8_kernel(Bwd8Args a) {
     const float* Xa = reinterpret_cast<const float*>(Bs + BSZ);
 
     // CB[k][n] = bf16(q[n][k] sw[n]) for the 4 n of nq and 4 k per quad
-    {
+    // (4-bit: bf16(q[n][k] sc[n][k0 / 128]) for the 4 n of nq and 8 k)
+    if constexpr (W4) {
+      const f32x4 scv = *reinterpret_cast<const f32x4*>(SCs + 4 * nq);
+      const int kq8 = kq0;                           // k in [8 kq8, 8 kq8 + 8)
+      uint32_t raw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = 4 * nq + i;
+        raw[i] = *reinterpret_cast<const uint32_t*>(Bs + n * RB + (((kq8 >> 2) ^ code_swz<RB>(n)) << 4) + (kq8 & 3) * 4);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v0 = (float)(((int)(raw[0] << (28 - 4 * e))) >> 28) * scv.x;
+        const float v1 = (float)(((int)(raw[1] << (28 - 4 * e))) >> 28) * scv.y;
+        const float v2 = (float)(((int)(raw[2] << (28 - 4 * e))) >> 28) * scv.z;
+        const float v3 = (float)(((int)(raw[3] << (28 - 4 * e))) >> 28) * scv.w;
+        *reinterpret_cast<u32x2*>(CB + swz128(8 * kq8 + e, nq >> 1) + (nq & 1) * 8) =
+            u32x2{pk_bf16(v0, v1), pk_bf16(v2, v3)};
+      }
+    } else {
       const f32x4 swv = *reinterpret_cast<const f32x4*>(Xa + 4 * nq);
 #pragma unroll
       for (int h = 0; h < BN / 64; ++h) {
@@ -294,7 +338,7 @@ __global__ __launch_bounds__(256) void bwd8_kernel(Bwd8Args a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int n = 4 * nq + i;
-          raw[i] = *reinterpret_cast<const int*>(Bs + n * BN + ((((kcol >> 4) ^ code_swz<BN>(n))) << 4) + (kcol & 15));
+          raw[i] = *reinterpret_cast<const int*>(Bs + n * RB + ((((kcol >> 4) ^ code_swz<RB>(n))) << 4) + (kcol & 15));
         }
 #pragma unroll
         for (int kk2 = 0; kk2 < 4; ++kk2) {
@@ -306,13 +350,13 @@ __global__ __launch_bounds__(256) void bwd8_kernel(Bwd8Args a) {
               u32x2{pk_bf16(v0, v1), pk_bf16(v2, v3)};
         }
       }
-      // BU[j][n] = bf16(B[j][n]), 2 n per entry
+    }
+    // BU[j][n] = bf16(B[j][n]), 2 n per entry
 #pragma unroll
-      for (int e = tid; e < R * 32; e += 256) {
-        const int j = e >> 5, p = e & 31;
-        const f32x2 b = *reinterpret_cast<const f32x2*>(Xa + 64 * (1 + j) + 2 * p);
-        *reinterpret_cast<uint32_t*>(BU + swz128(j, p >> 2) + (p & 3) * 4) = pk_bf16(b.x, b.y);
-      }
+    for (int e = tid; e < R * 32; e += 256) {
+      const int j = e >> 5, p = e & 31;
+      const f32x2 b = *reinterpret_cast<const f32x2*>(Xa + 64 * (1 + j) + 2 * p);
+      *reinterpret_cast<uint32_t*>(BU + swz128(j, p >> 2) + (p & 3) * 4) = pk_bf16(b.x, b.y);
     }
     __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
     __builtin_amdgcn_s_barrier();                    // CB, BU visible
@@ -456,34 +500,45 @@ __global__ __launch_bounds__(256) void bwd8_kernel(Bwd8Args a) {
   epilogue_lowrank<BM, BN, R, false>(acc, E, M, K, m0, k0, wm * (BM / 2), wn * (BN / 2), a.s, a.dx);
 }
 
-template <int BM, int BN, int S>
-void launch_tiles(Bwd8Args a, hipStream_t st) {
+template <bool W4, int BM, int BN, int S>
+void launch_tiles(BwdArgs a, hipStream_t st) {
   a.tiles_x = (a.K + BN - 1) / BN;
   const dim3 grid((unsigned)(a.tiles_x * ((a.M + BM - 1) / BM)));
-  if (a.r <= 4) bwd8_kernel<BM, BN, S, 4><<<grid, 256, 0, st>>>(a);
-  else if (a.r <= 8) bwd8_kernel<BM, BN, S, 8><<<grid, 256, 0, st>>>(a);
-  else if (a.r <= 16) bwd8_kernel<BM, BN, S, 16><<<grid, 256, 0, st>>>(a);
-  else bwd8_kernel<BM, BN, S, 32><<<grid, 256, 0, st>>>(a);
+  if (a.r <= 4) bwd_kernel<W4, BM, BN, S, 4><<<grid, 256, 0, st>>>(a);
+  else if (a.r <= 8) bwd_kernel<W4, BM, BN, S, 8><<<grid, 256, 0, st>>>(a);
+  else if (a.r <= 16) bwd_kernel<W4, BM, BN, S, 16><<<grid, 256, 0, st>>>(a);
+  else bwd_kernel<W4, BM, BN, S, 32><<<grid, 256, 0, st>>>(a);
 }
 
 }  // namespace
 
-int bwd8_row_block(int M, int K) {
-  const long t64 = (long)((M + 63) / 64) * ((K + 63) / 64);
-  return t64 <= 512 ? 64 : 128;
+int bwd_row_block(int fmt, int M, int K) {
+  // int8: 64 x 64 tiles while they make at most two blocks per compute unit,
+  // else 128 x 128; 4-bit: 128 columns (one scale group), 64 or 128 rows
+  const int bn = fmt == 0 ? 64 : 128;
+  const long t = (long)((M + 63) / 64) * ((K + bn - 1) / bn);
+  return t <= 512 ? 64 : 128;
 }
 
-void launch_bwd_w8_fused(int M, int K, int N, const uint16_t* dy,
-                         const int8_t* codes, const float* sw, const float* B,
-                         const float* A, const float* t, const uint16_t* x,
-                         int r, float s, uint16_t* dx, float* partA, float* partB,
-                         hipStream_t st) {
-  Bwd8Args a{};
-  a.M = M; a.K = K; a.N = N; a.dy = dy; a.codes = codes; a.sw = sw; a.B = B;
-  a.A = A; a.t = t; a.x = x; a.r = r; a.s = s; a.dx = dx; a.partA = partA;
+void launch_bwd_fused(int fmt, int M, int K, int N, const uint16_t* dy,
+                      const void* codes, const void* scales, const float* B,
+                      const float* A, const float* t, const uint16_t* x, int r,
+                      float s, uint16_t* dx, float* partA, float* partB,
+                      hipStream_t st) {
+  BwdArgs a{};
+  a.M = M; a.K = K; a.N = N; a.dy = dy; a.codes = static_cast<const int8_t*>(codes);
+  a.B = B; a.A = A; a.t = t; a.x = x; a.r = r; a.s = s; a.dx = dx; a.partA = partA;
   a.partB = partB;
-  if (bwd8_row_block(M, K) == 64) launch_tiles<64, 64, 3>(a, st);
-  else launch_tiles<128, 128, 2>(a, st);
+  const int bm = bwd_row_block(fmt, M, K);
+  if (fmt == 0) {
+    a.sw = static_cast<const float*>(scales);
+    if (bm == 64) launch_tiles<false, 64, 64, 3>(a, st);
+    else launch_tiles<false, 128, 128, 2>(a, st);
+  } else {
+    a.sc4 = static_cast<const uint16_t*>(scales);
+    if (bm == 64) launch_tiles<true, 64, 128, 2>(a, st);
+    else launch_tiles<true, 128, 128, 2>(a, st);
+  }
 }
 
 }  // namespace qlora

@@ -1,0 +1,220 @@
+// Forward product of the frozen 4-bit layer on v_mfma_f32_16x16x32_bf16:
+//
+//   y[m, n] = fma(s, sum_j t[m, j] B[j, n], sum_k x[m, k] deq4[k, n])
+//   deq4[k, n] = q[n, k] sc[n, k / 128]
+//
+// ("How to fine-tune the 4-bit model?": the frozen weight is dequantized
+// and multiplied in float; "Simplified Int4Variable quantization": two 4-bit
+// values per byte. "Parameter-efficient fine-tuning of GPT-2 with LoRA",
+// "LoRA equation" and "Create LoRA layer": the adapter term, scaled by
+// alpha / rank.)
+//
+// A stage covers one 128-wide group of k, so one fp16 scale per output
+// column applies to the whole stage. Three tiles move global -> LDS without
+// registers (ring.hpp): the x rows (bf16, 256-byte rows swizzled by 16-byte
+// chunk ^ (row % 16)), the packed codes [BN n][64 bytes] (chunk-swizzled),
+// and, once before the loop, the block's scales [BN][K / 128] (a contiguous
+// slab of the scale array). Once a stage has landed the block converts its
+// codes in one cooperative pass, every nibble once: CB [BN n][128 k] =
+// bf16(q sc), stored like the x rows. The MFMA loop then reads both operands
+// with plain 16-byte LDS reads. The adapter term runs in the epilogue on
+// v_mfma_f32_16x16x4_f32 (ring.hpp).
+#include "launch.hpp"
+#include "ring.hpp"
+
+namespace qlora {
+
+namespace {
+
+constexpr int kCUs = 256;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+struct W4Args {
+  int M, N, K;
+  const uint16_t* x;        // [M, K] bf16
+  const uint8_t* packed;    // [N, K / 2], low nibble = even k
+  const _Float16* scales;   // [N, K / 128]
+  const float* t;           // [M, r]
+  const float* B;           // [r, N]
+  int r;
+  float s;
+  uint16_t* y;              // [M, N] bf16
+  int tiles_x;
+};
+
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// Byte offset of logical 16-byte chunk c of row `row` in a 256-byte-row tile.
+__device__ __forceinline__ int swz256(int row, int c) {
+  return row * 256 + ((c ^ (row & 15)) << 4);
+}
+
+// Two's-complement nibble e (0..7) of a packed word, as a float.
+__device__ __forceinline__ float nibble(uint32_t w, int e) {
+  return (float)(((int)(w << (28 - 4 * e))) >> 28);
+}
+
+// G: the largest number of 128-wide k groups the block's scale slab holds.
+template <int BM, int BN, int S, int R, int G>
+__global__ __launch_bounds__(256) void fwd_w4_kernel(W4Args a) {
+  constexpr int BK = 128;                          // k per stage = one scale group
+  constexpr int ASZ = BM * 256, BSZ = BN * 64, STG = ASZ + BSZ;
+  constexpr int AI = BM / 16, BI = BN / 64, LPS = AI + BI;   // DMA per wave per stage
+  constexpr int FM = BM / 32, FN = BN / 32;
+  constexpr int CBSZ = BN * 256;
+  static_assert(BN == 128, "code rows of 64 bytes: 16 rows per DMA instruction, 2 threads per row");
+  static_assert(EpiOps<BM, BN, R, false>::kFloats * 4 <= S * STG, "epilogue fits in the ring");
+  const int K = a.K, M = a.M, N = a.N;
+  const int ngrp = K / BK;
+  static_assert(BN * G * 2 % 1024 == 0, "the scale slab takes whole 1 KB DMA instructions");
+  // scales of the block's columns: [BN][ngrp] fp16, ngrp <= G
+  __shared__ __attribute__((aligned(1024))) int8_t lds[S * STG + CBSZ + BN * G * 2];
+  int8_t* ring = lds;
+  int8_t* CB = lds + S * STG;
+  const _Float16* SC = reinterpret_cast<const _Float16*>(lds + S * STG + CBSZ);
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = wave_id();
+  const int wm = wid >> 1, wn = wid & 1;
+  const int m0 = ((int)blockIdx.x / a.tiles_x) * BM, n0 = ((int)blockIdx.x % a.tiles_x) * BN;
+  const int nk = ngrp;
+
+  EpiOps<BM, BN, R, false> ep;
+  ep.load(M, N, m0, n0, a.r, a.t, a.B, N, 1, nullptr, nullptr);
+
+  // the block's scale slab: rows n0 .. n0 + BN of [N][ngrp], contiguous
+  {
+    const int bytes = BN * ngrp * 2;                // multiple of 16 (ngrp >= 1, BN = 128)
+    const int8_t* src0 = reinterpret_cast<const int8_t*>(a.scales) + (long)n0 * ngrp * 2;
+    const long valid = ((long)N - n0) * ngrp * 2;    // bytes that exist past src0
+    for (int o = wid * 1024; o < bytes; o += 4096) {
+      const int e = o + lane * 16;
+      const int8_t* src = (e < bytes && e < valid) ? src0 + e : zero_chunk(lane);
+      lds_dma16(src, lds + S * STG + CBSZ + o);
+    }
+  }
+  auto issue = [&](int kt, int slot) {
+    int8_t* base = ring + slot * STG;
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+      const int rb = (wid * AI + i) * 4, row = rb + (lane >> 4);
+      const int c = (lane & 15) ^ (row & 15);
+      const int gm = m0 + row, gk = kt * BK + c * 8;
+      lds_dma16(a.x + (long)(gm < M ? gm : M - 1) * K + gk, base + rb * 256);
+    }
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const int rb = (wid * BI + i) * 16, row = rb + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3), gn = n0 + row;
+      const uint8_t* src = gn < N ? a.packed + (long)gn * (K / 2) + kt * 64 + c * 16
+                                  : reinterpret_cast<const uint8_t*>(zero_chunk(lane));
+      lds_dma16(src, base + ASZ + rb * 64);
+    }
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st)
+    if (st < nk) issue(st, st);
+  // The scale slab went out before stage 0 (its per-wave instruction count
+  // may differ): loads complete in issue order, so every wave's share has
+  // landed once its stage 0 has, and the first barrier covers all waves.
+
+  const int crow = tid >> 1, chalf = tid & 1;        // conversion: row n, 64 k half
+  int slot = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_stages<LPS, 0, S - 2>(nk - 1 - kt);
+    __builtin_amdgcn_s_barrier();                    // stage kt landed; CB free
+    if (kt + S - 1 < nk) issue(kt + S - 1, slot == 0 ? S - 1 : slot - 1);
+    const int8_t* As = ring + slot * STG;
+    const int8_t* Bs = As + ASZ;
+
+    // CB[n][k] = bf16(q[n][k] sc[n][kt]) for row crow, k in [64 chalf, 64 chalf + 64)
+    {
+      const float sc = (float)SC[crow * ngrp + kt];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = 2 * chalf + h;                 // 16-byte chunk of packed codes
+        const u32x4 w = *reinterpret_cast<const u32x4*>(Bs + crow * 64 + ((c ^ ((crow >> 2) & 3)) << 4));
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int kc = 4 * c + d;                  // 16-byte chunk of CB (8 k)
+          const u32x4 o = {pk_bf16(nibble(w[d], 0) * sc, nibble(w[d], 1) * sc),
+                           pk_bf16(nibble(w[d], 2) * sc, nibble(w[d], 3) * sc),
+                           pk_bf16(nibble(w[d], 4) * sc, nibble(w[d], 5) * sc),
+                           pk_bf16(nibble(w[d], 6) * sc, nibble(w[d], 7) * sc)};
+          *reinterpret_cast<u32x4*>(CB + swz256(crow, kc)) = o;
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+    __builtin_amdgcn_s_barrier();                    // CB visible
+
+#pragma unroll
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      const int c = kk * 4 + (lane >> 4);
+      bf16x8 af[FM], bf[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(As + swz256(wm * (BM / 2) + i * 16 + (lane & 15), c));
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bf[j] = *reinterpret_cast<const bf16x8*>(CB + swz256(wn * (BN / 2) + j * 16 + (lane & 15), c));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    slot = slot == S - 1 ? 0 : slot + 1;
+  }
+
+  float* E = reinterpret_cast<float*>(ring);
+  __syncthreads();
+  ep.store(E, M, N, m0, n0, a.r);
+  __syncthreads();
+  epilogue_lowrank<BM, BN, R, false>(acc, E, M, N, m0, n0, wm * (BM / 2), wn * (BN / 2), a.s, a.y);
+}
+
+template <int BM, int S, int G>
+void launch_tiles(W4Args a, hipStream_t st) {
+  constexpr int BN = 128;
+  a.tiles_x = (a.N + BN - 1) / BN;
+  const dim3 grid((unsigned)(a.tiles_x * ((a.M + BM - 1) / BM)));
+  if (a.r <= 4) fwd_w4_kernel<BM, BN, S, 4, G><<<grid, 256, 0, st>>>(a);
+  else if (a.r <= 8) fwd_w4_kernel<BM, BN, S, 8, G><<<grid, 256, 0, st>>>(a);
+  else if (a.r <= 16) fwd_w4_kernel<BM, BN, S, 16, G><<<grid, 256, 0, st>>>(a);
+  else fwd_w4_kernel<BM, BN, S, 32, G><<<grid, 256, 0, st>>>(a);
+}
+
+template <int BM, int S>
+void launch_groups(const W4Args& a, hipStream_t st) {
+  const int ngrp = a.K / 128;                      // validated: <= kW4MaxGroups
+  if (ngrp <= 8) launch_tiles<BM, S, 8>(a, st);
+  else if (ngrp <= 32) launch_tiles<BM, S, 32>(a, st);
+  else launch_tiles<BM, S, kW4MaxGroups>(a, st);
+}
+
+}  // namespace
+
+void launch_gemm_fwd_w4(int M, int N, int K, const uint16_t* x,
+                        const uint8_t* packed, const _Float16* scales,
+                        const float* t, const float* B, int r, float s,
+                        uint16_t* y, hipStream_t st) {
+  W4Args a{};
+  a.M = M; a.N = N; a.K = K; a.x = x; a.packed = packed; a.scales = scales;
+  a.t = t; a.B = B; a.r = r; a.s = s; a.y = y;
+  const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
+  if (t128 >= kCUs) launch_groups<128, 2>(a, st);
+  else launch_groups<64, 2>(a, st);
+}
+
+}  // namespace qlora

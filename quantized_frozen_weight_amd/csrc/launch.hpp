@@ -26,6 +26,10 @@ void launch_gemm_fwd_w8(int dtype, int M, int N, int K, const int8_t* xq,
                         const int8_t* codes, const float* sx, const float* sw,
                         const float* t, const float* B, int r, float s,
                         void* y, int32_t* acc_out, hipStream_t st);
+// 4-bit weights: the products hold the scales of up to this many 128-wide k
+// groups per block in LDS (K <= 16384).
+constexpr int kW4MaxGroups = 128;
+
 // y = x deq4(W) + s * t B   (bf16 x and y)
 void launch_gemm_fwd_w4(int M, int N, int K, const uint16_t* x,
                         const uint8_t* packed, const _Float16* scales,
@@ -48,24 +52,20 @@ SkinnyJobs make_adapter_grad_jobs(int M, int r, float s, const float* t,
 void launch_skinny_stage1(int dtype, const SkinnyJobs& p, hipStream_t st);
 void launch_skinny_stage2(const SkinnyJobs& p, hipStream_t st);
 
-// int8 weights, bf16: dx = dy deq(W)^T + s u A^T with u = dy B^T computed in
-// the same launch, plus per-row-block partial sums of dA (partA [blocks, r, K])
-// and dB (partB [blocks, r, N]); blocks = ceil(M / bwd8_row_block(M, K)).
-int bwd8_row_block(int M, int K);
-void launch_bwd_w8_fused(int M, int K, int N, const uint16_t* dy,
-                         const int8_t* codes, const float* sw, const float* B,
-                         const float* A, const float* t, const uint16_t* x,
-                         int r, float s, uint16_t* dx, float* partA, float* partB,
-                         hipStream_t st);
+// bf16 backward, int8 (fmt 0: codes [N, K], scales float [N]) or 4-bit
+// (fmt 1: packed [N, K/2], scales fp16 [N, K/128]) weights:
+// dx = dy deq(W)^T + s u A^T with u = dy B^T computed in the same launch,
+// plus per-row-block partial sums of dA (partA [blocks, r, K]) and dB
+// (partB [blocks, r, N]); blocks = ceil(M / bwd_row_block(fmt, M, K)).
+int bwd_row_block(int fmt, int M, int K);
+void launch_bwd_fused(int fmt, int M, int K, int N, const uint16_t* dy,
+                      const void* codes, const void* scales, const float* B,
+                      const float* A, const float* t, const uint16_t* x, int r,
+                      float s, uint16_t* dx, float* partA, float* partB,
+                      hipStream_t st);
 // dx = dy (codes * sw)^T + s u A^T in float32
 void launch_gemm_dx_f32(int M, int K, int N, const float* dy,
                         const int8_t* codes, const float* sw, const float* u,
                         const float* A, int r, float s, float* dx,
                         hipStream_t st);
-// dx = dy deq4(W)^T + s u A^T   (bf16)
-void launch_gemm_dx_w4(int M, int K, int N, const uint16_t* dy,
-                       const uint8_t* packed, const _Float16* scales,
-                       const float* u, const float* A, int r, float s,
-                       uint16_t* dx, const SkinnyJobs* sk, hipStream_t st);
-
 }  // namespace qlora
