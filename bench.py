@@ -269,7 +269,8 @@ def dominant_kernel_roofline(w, layers, step, torch):
     In one eager step the library launches each layer's backward kernel 20
     times back to back (same inputs, same outputs) between two HIP events
     that it records on the stream it launches on; the average duration is
-    the summed intervals over all launches. Algorithmic work per launch of the fused int8
+    the summed intervals over all launches. Peak: dense bf16 MFMA (float32
+    vector peak for the float32 workload). Algorithmic work per launch of the fused int8
     backward: 2 M K N for dx, 2 M N r each for u and dB, 2 M K r each for dA
     and the rank-r term of dx, i.e. 2 M K N + 4 M r (N + K) flops; peak: dense
     bf16 MFMA.
@@ -286,7 +287,13 @@ def dominant_kernel_roofline(w, layers, step, torch):
     tot_ms = sum(a.elapsed_time(b) for a, b in pairs)
     launches = n * repeats
     avg_ms = tot_ms / launches
-    flops = sum(2.0 * w.M * l.K * l.N + 4.0 * w.M * w.r * (l.N + l.K) for l in layers) / n
+    if w.dtype == "bf16":   # fused backward: dx, u, dB, dA, s u A^T
+        flops = sum(2.0 * w.M * l.K * l.N + 4.0 * w.M * w.r * (l.N + l.K) for l in layers) / n
+        kernel = ("bwd_kernel (fused backward: dx, u, dA and dB partial sums, "
+                  f"bf16 MFMA, {w.wfmt} weights)")
+    else:                   # float32 input gradient: dy deq(W)^T + s u A^T
+        flops = sum(2.0 * w.M * l.K * l.N + 2.0 * w.M * w.r * l.K for l in layers) / n
+        kernel = "dx_f32_kernel (float32 input gradient)"
     achieved = flops / (avg_ms * 1e-3) / 1e12
     peak = PEAK["bf16" if w.dtype == "bf16" else "f32"] / 1e12
     traffic = None
@@ -294,7 +301,7 @@ def dominant_kernel_roofline(w, layers, step, torch):
             and kernel_sources_sha256(TRAFFIC["sources"]) == TRAFFIC["sha256"]):
         traffic = TRAFFIC["bytes_per_launch"]
     return {
-        "kernel": "bwd8_kernel (fused int8 backward: dx, u, dA and dB partial sums, bf16 MFMA)",
+        "kernel": kernel,
         "bound": "mfma",
         "achieved": round(achieved, 2),
         "peak": peak,

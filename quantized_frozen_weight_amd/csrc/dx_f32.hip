@@ -3,7 +3,7 @@
 // gradient needs the product with the transposed quantized matrix):
 //     dx[m, k] = sum_n (dy[m, n] * sw[n]) q[n, k] + s sum_j u[m, j] A[k, j]
 // Plain LDS-tiled FMA kernel, no reduced-precision rounding anywhere; used
-// for the float32 compute dtype.
+// for the float32 compute dtype (small layers).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -12,58 +12,66 @@ namespace qlora {
 namespace {
 
 // ---------------------------------------------------------------------------
-// float32 input gradient: 64 x 64 output tile, 16-wide contraction slices,
-// each thread a 4 x 4 register tile. dy * sw is formed once per element (one
-// float32 rounding), then multiplied by the exact integer code.
+// 32 x 32 output tile per block (small layers still spread over many compute
+// units), contraction in slices of 32 n, each thread a 2 x 2 register tile.
+// The next slice is fetched into registers while the current one is used.
+// dy * sw is formed once per element (one float32 rounding), then multiplied
+// by the exact integer code.
 // ---------------------------------------------------------------------------
+constexpr int kT = 32;
+
 __global__ __launch_bounds__(256) void gemm_dx_f32_kernel(
     int M, int K, int N, const float* __restrict__ dy,
     const int8_t* __restrict__ codes, const float* __restrict__ sw,
     const float* __restrict__ u, const float* __restrict__ A, int r, float s,
     float* __restrict__ dx) {
-  __shared__ float Ds[16][64 + 4];   // [n][m]
-  __shared__ float Ws[16][64 + 4];   // [n][k]
+  __shared__ float Ds[kT][kT + 1];   // [n][m]
+  __shared__ float Ws[kT][kT + 1];   // [n][k]
   const int tid = threadIdx.x;
-  const int m0 = blockIdx.y * 64, k0 = blockIdx.x * 64;
-  const int tm = tid >> 4, tk = tid & 15;
-  float acc[4][4] = {};
-  for (int n0 = 0; n0 < N; n0 += 16) {
-    {
-      const int ml = tid >> 2, nq = (tid & 3) * 4;
-      const int gm = m0 + ml;
+  const int m0 = blockIdx.y * kT, k0 = blockIdx.x * kT;
+  const int tm = tid >> 4, tk = tid & 15;      // outputs rows 2 tm + i, cols 2 tk + j
+  // loader roles: dy element (ml, 4 n), codes (nl, 4 k)
+  const int lm = tid >> 3, ln = (tid & 7) * 4;
+  const int wn = tid >> 3, wk = (tid & 7) * 4;
+  float dv[4];
+  uint32_t wv;
+  auto fetch = [&](int n0) {
+    const int gm = m0 + lm;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int gn = n0 + nq + i;
-        Ds[nq + i][ml] = (gm < M && gn < N) ? dy[(long)gm * N + gn] * sw[gn] : 0.f;
-      }
-      const int nl = tid >> 4, kq = (tid & 15) * 4;
-      const int gn = n0 + nl, gk = k0 + kq;
-      uint32_t w = (gn < N && gk < K)
-                       ? *reinterpret_cast<const uint32_t*>(codes + (long)gn * K + gk) : 0u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        Ws[nl][kq + i] = (float)(((int)(w << (24 - 8 * i))) >> 24);
+    for (int i = 0; i < 4; ++i) {
+      const int gn = n0 + ln + i;
+      dv[i] = (gm < M && gn < N) ? dy[(long)gm * N + gn] * sw[gn] : 0.f;
     }
+    const int gn = n0 + wn, gk = k0 + wk;
+    wv = (gn < N && gk < K) ? *reinterpret_cast<const uint32_t*>(codes + (long)gn * K + gk) : 0u;
+  };
+  float acc[2][2] = {};
+  fetch(0);
+  for (int n0 = 0; n0 < N; n0 += kT) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Ds[ln + i][lm] = dv[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Ws[wn][wk + i] = (float)(((int)(wv << (24 - 8 * i))) >> 24);
     __syncthreads();
+    if (n0 + kT < N) fetch(n0 + kT);
 #pragma unroll
-    for (int n = 0; n < 16; ++n) {
-      float a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { a[i] = Ds[n][4 * tm + i]; b[i] = Ws[n][4 * tk + i]; }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+    for (int n = 0; n < kT; ++n) {
+      const float a0 = Ds[n][2 * tm], a1 = Ds[n][2 * tm + 1];
+      const float b0 = Ws[n][2 * tk], b1 = Ws[n][2 * tk + 1];
+      acc[0][0] = __builtin_fmaf(a0, b0, acc[0][0]);
+      acc[0][1] = __builtin_fmaf(a0, b1, acc[0][1]);
+      acc[1][0] = __builtin_fmaf(a1, b0, acc[1][0]);
+      acc[1][1] = __builtin_fmaf(a1, b1, acc[1][1]);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + 4 * tm + i;
+  for (int i = 0; i < 2; ++i) {
+    const int m = m0 + 2 * tm + i;
     if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = k0 + 4 * tk + j;
+    for (int j = 0; j < 2; ++j) {
+      const int k = k0 + 2 * tk + j;
       if (k >= K) continue;
       float low = 0.f;
       for (int jj = 0; jj < r; ++jj)
@@ -79,7 +87,7 @@ void launch_gemm_dx_f32(int M, int K, int N, const float* dy,
                         const int8_t* codes, const float* sw, const float* u,
                         const float* A, int r, float s, float* dx,
                         hipStream_t st) {
-  dim3 grid((K + 63) / 64, (M + 63) / 64);
+  dim3 grid((K + kT - 1) / kT, (M + kT - 1) / kT);
   gemm_dx_f32_kernel<<<grid, 256, 0, st>>>(M, K, N, dy, codes, sw, u, A, r, s,
                                            dx);
 }
