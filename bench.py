@@ -238,8 +238,8 @@ def describe(w):
 TRAFFIC = {
     "workload": 2,
     "sources": ["gemm_bwd.hip", "ring.hpp", "common.hpp", "launch.hpp"],
-    "sha256": "aec4628696117355716e5139c02c3e84230f5efc323812ba0a01631f3bd514e1",
-    "bytes_per_launch": 25014439,
+    "sha256": "6a6f6e61d424c36eac291653374c6a2d177e910bb12a555d8209bc8c641a84e1",
+    "bytes_per_launch": 25010441,
 }
 
 

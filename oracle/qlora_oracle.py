@@ -323,8 +323,31 @@ def fwd_w4(x, packed, scales, A, B, alpha: float, dtype: str):
 # ---------------------------------------------------------------------------
 
 
+def merged_weight_w8(codes, sw, A, B, alpha: float) -> np.ndarray:
+    """The adapter folded into the frozen weight, as float32 [K, N]
+    ([GPT-2 LoRA] "Merge weights and generate text!": the merged kernel is
+    the frozen kernel plus the adapter product; here scaled by s as in the
+    forward):
+
+        W'[k, n] = fl32( deq(W)[k, n] + s * sum_j A[k, j] B[j, n] )
+
+    evaluated in float64 with a fixed operation sequence: deq = q * sw and
+    every A B product are exact in float64; the r products are added in
+    index order; then one multiply by s, one add, and one rounding to
+    float32."""
+    A64 = np.asarray(A, F64)
+    B64 = np.asarray(B, F64)
+    K, r = A64.shape
+    acc = np.zeros((K, B64.shape[1]), F64)
+    for j in range(r):
+        acc = acc + A64[:, j:j + 1] * B64[j:j + 1, :]
+    s = F64(lora_scale(alpha, r))
+    return (dequant_w8(codes, sw) + s * acc).astype(F32)
+
+
 def merge_w8(codes, sw, A, B, alpha: float):
-    """Dequantize, add s A B, re-quantize with the same int8 rule."""
-    s = lora_scale(alpha, np.asarray(A).shape[1])
-    W = dequant_w8(codes, sw) + s * (np.asarray(A, F64) @ np.asarray(B, F64))
-    return quantize_w8(round_f32(W))
+    """Merge the adapter into the int8 weight: W' (merged_weight_w8),
+    re-quantized with the same per-channel int8 rule. Lossy: the merged codes
+    are W' rounded to its own channel grid ([QLoRA-like] results-table
+    footnote: merging LoRA into int8 kernels changes the outputs)."""
+    return quantize_w8(merged_weight_w8(codes, sw, A, B, alpha))

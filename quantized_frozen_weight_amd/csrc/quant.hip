@@ -18,22 +18,33 @@ __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, long n) {
 // ---------------------------------------------------------------------------
 // int8 weights, per output channel n (a column of W [K, N]).
 // Pass 1: column abs-max as ordered bits, combined across K-slices with an
-// integer atomic max (order-independent, hence deterministic).
+// integer atomic max (order-independent, hence deterministic). A thread
+// covers 4 adjacent columns (N % 16 == 0) of an 8-row slice, all 8 row loads
+// in flight at once.
 // ---------------------------------------------------------------------------
-constexpr int kColmaxRows = 256;
+constexpr int kColmaxRows = 8;
 
 __global__ __launch_bounds__(256) void w8_colmax_kernel(
     const float* __restrict__ W, int K, int N, uint32_t* __restrict__ amax) {
-  int n = blockIdx.x * 256 + threadIdx.x;
+  const int n = 4 * (blockIdx.x * 256 + threadIdx.x);
   if (n >= N) return;
-  int k0 = blockIdx.y * kColmaxRows;
-  int k1 = min(K, k0 + kColmaxRows);
-  uint32_t m = 0;
-  for (int k = k0; k < k1; ++k) {
-    uint32_t b = abs_bits(W[(long)k * N + n]);
-    m = b > m ? b : m;
+  const int k0 = blockIdx.y * kColmaxRows;
+  f32x4 v[kColmaxRows];
+#pragma unroll
+  for (int i = 0; i < kColmaxRows; ++i) {
+    const int k = k0 + i < K ? k0 + i : K - 1;     // repeats of a real row do not change a max
+    v[i] = *reinterpret_cast<const f32x4*>(W + (long)k * N + n);
   }
-  atomicMax(amax + n, m);
+  uint32_t m[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < kColmaxRows; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t b = abs_bits(v[i][c]);
+      m[c] = b > m[c] ? b : m[c];
+    }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) atomicMax(amax + n + c, m[c]);
 }
 
 // Pass 2: codes for a 64(k) x 64(n) tile, transposed through LDS so that the
@@ -75,7 +86,7 @@ void launch_quantize_w8(const float* W, int K, int N, int8_t* codes,
                         float* scales, hipStream_t st) {
   uint32_t* amax = reinterpret_cast<uint32_t*>(scales);
   fill_u32_kernel<<<dim3((N + 255) / 256), 256, 0, st>>>(amax, 0u, N);
-  w8_colmax_kernel<<<dim3((N + 255) / 256, (K + kColmaxRows - 1) / kColmaxRows),
+  w8_colmax_kernel<<<dim3((N + 1023) / 1024, (K + kColmaxRows - 1) / kColmaxRows),
                      256, 0, st>>>(W, K, N, amax);
   w8_codes_kernel<<<dim3((N + 63) / 64, (K + 63) / 64), 256, 0, st>>>(
       W, K, N, amax, codes);

@@ -184,6 +184,52 @@ def test_merge_with_zero_B_keeps_codes():
     assert np.all(np.abs(s2 - sw) <= np.abs(np.nextafter(sw, F32(1)) - sw))
 
 
+@pytest.mark.parametrize("seed,r", [(21, 1), (22, 3)])
+def test_merged_weight_is_the_nearest_float32(seed, r):
+    """W' is the float32 nearest to the exact deq(W) + s A B (checked with
+    rational arithmetic), for every element of a small layer."""
+    rng = np.random.default_rng(seed)
+    K, N, alpha = 6, 5, 8.0
+    W = (rng.standard_normal((K, N)) * 0.05).astype(F32)
+    A = (rng.standard_normal((K, r)) * 0.3).astype(F32)
+    B = (rng.standard_normal((r, N)) * 0.3).astype(F32)
+    codes, sw = O.quantize_w8(W)
+    Wm = O.merged_weight_w8(codes, sw, A, B, alpha)
+    s = Fraction(float(np.float32(alpha) / np.float32(r)))
+    for k in range(K):
+        for n in range(N):
+            exact = int(codes[n, k]) * Fraction(float(sw[n])) + s * sum(
+                Fraction(float(A[k, j])) * Fraction(float(B[j, n])) for j in range(r))
+            got = Fraction(float(Wm[k, n]))
+            lo = Fraction(float(np.nextafter(Wm[k, n], np.float32(-np.inf))))
+            hi = Fraction(float(np.nextafter(Wm[k, n], np.float32(np.inf))))
+            # nearest: no neighbouring float32 is strictly closer
+            assert abs(got - exact) <= abs(lo - exact) and abs(got - exact) <= abs(hi - exact)
+
+
+def test_merge_error_bound_and_merged_forward():
+    """The merged codes are W' on its own channel grid (error <= half a step,
+    plus the slack of the float32 quantizer), so the merged forward stays
+    within that bound of the unmerged float product."""
+    rng = np.random.default_rng(23)
+    K, N, r, alpha = 48, 24, 4, 16.0
+    W = (rng.standard_normal((K, N)) * 0.05).astype(F32)
+    A = (rng.standard_normal((K, r)) * 0.05).astype(F32)
+    B = (rng.standard_normal((r, N)) * 0.05).astype(F32)
+    codes, sw = O.quantize_w8(W)
+    Wm = O.merged_weight_w8(codes, sw, A, B, alpha).astype(np.float64)
+    c2, s2 = O.merge_w8(codes, sw, A, B, alpha)
+    step = s2.astype(np.float64)[None, :]
+    assert np.all(np.abs(O.dequant_w8(c2, s2) - Wm) <= step * (0.5 + 2.0 ** -15))
+    assert np.all(np.abs(c2).max(axis=1) == 127)
+    x = rng.standard_normal((5, K)).astype(np.float64)
+    s = float(np.float32(alpha) / np.float32(r))
+    unmerged = x @ O.dequant_w8(codes, sw) + s * (x @ A.astype(np.float64)) @ B.astype(np.float64)
+    merged = x @ O.dequant_w8(c2, s2)
+    bound = np.abs(x) @ np.ones((K, 1)) * step * (0.5 + 2.0 ** -15) + 1e-12 * np.abs(unmerged).max()
+    assert np.all(np.abs(merged - unmerged) <= bound + 1e-6 * np.abs(unmerged))
+
+
 def test_rounded_outputs_are_nearest():
     x, W, A, B, dy = _tiny(9, M=4, K=16, N=8, r=2)
     codes, sw = O.quantize_w8(W)
