@@ -126,6 +126,24 @@ def main():
     torch.cuda.synchronize()
     quantize_ms = e0.elapsed_time(e1)
 
+    # merging the trained adapter into the int8 weight (one-time, after
+    # training; not part of the step), into separate buffers
+    merge_ms = None
+    if w.wfmt == "w8":
+        outs = [(torch.empty_like(l.codes), torch.empty_like(l.scales)) for l in layers]
+
+        def merge_all():
+            for l, (c, sc) in zip(layers, outs):
+                check(lib.qlora_merge(ctypes.byref(l.cs), c.data_ptr(), sc.data_ptr(), stream),
+                      "merge")
+        merge_all()
+        torch.cuda.synchronize()
+        e0.record()
+        merge_all()
+        e1.record()
+        torch.cuda.synchronize()
+        merge_ms = e0.elapsed_time(e1)
+
     def step(ev_b=None, repeats=1):
         st = torch.cuda.current_stream().cuda_stream
         for i, l in enumerate(layers):
@@ -215,6 +233,7 @@ def main():
         "wall_ms_per_step": round(wall_ms, 5),
         "eager_ms_per_step": round(eager_ms, 5),
         "quantize_ms": round(quantize_ms, 4),
+        "merge_ms": None if merge_ms is None else round(merge_ms, 4),
         "roofline": roof,
         "cpu_baseline": cpu,
     }
@@ -233,22 +252,25 @@ def describe(w):
 # HBM traffic of the dominant kernel per launch on the benchmarked workload,
 # from two rocprofv3 counter passes (FETCH_SIZE, then WRITE_SIZE, KiB per
 # dispatch), each divided by what the same counter reads per KiB of a plain
-# 256 MiB device copy in the same run. Valid only for the kernel sources it
-# was taken on (their SHA-256); otherwise reported as null.
+# 256 MiB device copy in the same run. Valid only for the kernel's device
+# code it was taken on: the SHA-256 of the sources that define that kernel
+# and of the compiler flags; otherwise reported as null.
 TRAFFIC = {
     "workload": 2,
-    "sources": ["gemm_bwd.hip", "ring.hpp", "common.hpp", "launch.hpp"],
-    "sha256": "6a6f6e61d424c36eac291653374c6a2d177e910bb12a555d8209bc8c641a84e1",
+    "sources": ["gemm_bwd.hip", "ring.hpp", "common.hpp"],
+    "sha256": "c4a7bf8667353e2e323767aa9cf6fb34b2742426651b072c50e10af9f4d53aad",
     "bytes_per_launch": 25010441,
 }
 
 
 def kernel_sources_sha256(names):
     import hashlib
+    from quantized_frozen_weight_amd import build_lib
     h = hashlib.sha256()
     for n in names:
         with open(os.path.join(ROOT, "quantized_frozen_weight_amd", "csrc", n), "rb") as f:
             h.update(f.read())
+    h.update(" ".join(build_lib.HIPCC_FLAGS).encode())
     return h.hexdigest()
 
 

@@ -165,6 +165,20 @@ int qlora_bwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
                     float* dB, void* ws, size_t ws_bytes, void* stream,
                     int repeats, void* ev_start, void* ev_stop);
 
+/* Merge the trained adapter into the frozen int8 weight ("Parameter-efficient
+ * fine-tuning of GPT-2 with LoRA", "Merge weights and generate text!": the
+ * merged kernel is the frozen kernel plus the adapter product; "Introduce
+ * QLoRA-like technique", results-table footnote: merging into int8 kernels
+ * is lossy, the merged layer's outputs differ from the unmerged ones):
+ *   W'[k, n] = float32( q[n, k] sw[n] + s sum_j A[k, j] B[j, n] ),
+ * evaluated in float64 with a fixed sequence (exact products, the r terms
+ * added in index order, one multiply by s, one add, one rounding), then
+ * quantized with the qlora_quantize int8 rule into codes_out int8 [N, K] and
+ * scales_out float32 [N] (device memory, 16-byte aligned, not overlapping L's
+ * buffers). QLORA_W8 only (QLORA_EUNSUPPORTED otherwise). */
+int qlora_merge(const qlora_linear* L, void* codes_out, void* scales_out,
+                void* stream);
+
 /* Test hook: the forward's per-row activation quantizer alone. x [M, K] in
  * the compute dtype -> xq int8 [M, K], sx float32 [M]. Same kernel as
  * qlora_fwd. */

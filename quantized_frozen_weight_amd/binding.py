@@ -51,6 +51,7 @@ EXPORTS = (
     "qlora_status_str", "qlora_weight_bytes", "qlora_quantize",
     "qlora_fwd_workspace", "qlora_fwd", "qlora_bwd_workspace", "qlora_bwd",
     "qlora_quantize_rows", "qlora_fwd_acc", "qlora_fwd_timed", "qlora_bwd_timed",
+    "qlora_merge",
 )
 
 
@@ -79,6 +80,7 @@ def lib() -> ctypes.CDLL:
     L.qlora_fwd_acc.argtypes = [plin, i, i, vp, vp, vp, sz, vp]
     L.qlora_fwd_timed.argtypes = [plin, i, i, vp, vp, vp, vp, sz, vp, i, vp, vp]
     L.qlora_bwd_timed.argtypes = [plin, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp, i, vp, vp]
+    L.qlora_merge.argtypes = [plin, vp, vp, vp]
     for name in EXPORTS[1:]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -154,6 +156,18 @@ def qlora_quantize(W, fmt: str = "w8"):
     W = W.contiguous()
     _check(lib().qlora_quantize(_ptr(W), K, N, _FMT[fmt], _ptr(codes), _ptr(scales),
                                 _stream()), "qlora_quantize")
+    return codes, scales
+
+
+def qlora_merge(layer: QLinear):
+    """The adapter merged into the layer's int8 weight, re-quantized: new
+    (codes int8 [N, K], scales float32 [N]) on the layer's device."""
+    import torch
+    codes = torch.empty((layer.N, layer.K), dtype=torch.int8, device=layer.codes.device)
+    scales = torch.empty((layer.N,), dtype=torch.float32, device=layer.codes.device)
+    s = layer.cstruct()
+    _check(lib().qlora_merge(ctypes.byref(s), _ptr(codes), _ptr(scales), _stream()),
+           "qlora_merge")
     return codes, scales
 
 

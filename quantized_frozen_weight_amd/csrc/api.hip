@@ -283,6 +283,31 @@ int qlora_bwd(const qlora_linear* L, int M, int dtype, const void* x,
                          stream, 1, nullptr, nullptr);
 }
 
+int qlora_merge(const qlora_linear* L, void* codes_out, void* scales_out,
+                void* stream) {
+  int st = check_linear(L, 1, QLORA_BF16);
+  if (st) return st;
+  if (L->fmt != QLORA_W8) return QLORA_EUNSUPPORTED;
+  if (!codes_out || !scales_out || !aligned16(codes_out) || !aligned16(scales_out))
+    return QLORA_EINVAL;
+  const size_t cb = (size_t)L->N * L->K, sb = (size_t)L->N * 4;
+  auto overlaps = [](const void* a, size_t na, const void* b, size_t nb) {
+    const char* x = static_cast<const char*>(a);
+    const char* y = static_cast<const char*>(b);
+    return x < y + nb && y < x + na;
+  };
+  if (overlaps(codes_out, cb, L->codes, cb) || overlaps(codes_out, cb, L->scales, sb) ||
+      overlaps(scales_out, sb, L->codes, cb) || overlaps(scales_out, sb, L->scales, sb) ||
+      overlaps(codes_out, cb, scales_out, sb))
+    return QLORA_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  launch_merge_w8(static_cast<const int8_t*>(L->codes), static_cast<const float*>(L->scales),
+                  L->A, L->B, L->K, L->N, L->r, lora_s(L),
+                  static_cast<int8_t*>(codes_out), static_cast<float*>(scales_out), s);
+  return launch_status();
+}
+
 int qlora_quantize_rows(const void* x, int M, int K, int dtype, int8_t* xq,
                         float* sx, void* stream) {
   int st = check_dtype(dtype);

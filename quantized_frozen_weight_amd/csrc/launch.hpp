@@ -15,6 +15,11 @@ void launch_quantize_w8(const float* W, int K, int N, int8_t* codes,
                         float* scales, hipStream_t st);
 void launch_quantize_w4(const float* W, int K, int N, uint8_t* packed,
                         _Float16* scales, hipStream_t st);
+// int8 weight with the adapter merged in, re-quantized (r <= 32); the
+// outputs must not overlap the inputs.
+void launch_merge_w8(const int8_t* codes, const float* sw, const float* A,
+                     const float* B, int K, int N, int r, float s,
+                     int8_t* codes_out, float* scales_out, hipStream_t st);
 
 void launch_rowquant(int dtype, const void* x, int M, int K, const float* A,
                      int r, int8_t* xq, float* sx, float* t, hipStream_t st);

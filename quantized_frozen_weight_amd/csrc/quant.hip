@@ -82,6 +82,117 @@ __global__ void w8_scales_kernel(uint32_t* __restrict__ amax_then_scale, int N) 
   amax_then_scale[n] = __float_as_uint(p.scale);
 }
 
+// ---------------------------------------------------------------------------
+// Merging the adapter into the int8 weight ("Parameter-efficient fine-tuning
+// of GPT-2 with LoRA", "Merge weights and generate text!": the merged kernel
+// is the frozen one plus the adapter product; "Introduce QLoRA-like
+// technique", results-table footnote: merging into int8 is lossy):
+//
+//   W'[k, n] = fl32( q[n, k] sw[n] + s sum_j A[k, j] B[j, n] )
+//
+// evaluated in float64 with a fixed sequence: q sw and every A B product are
+// exact; the r products are added in index order; one multiply by s, one
+// add, one rounding to float32 (explicitly rounded operations, no fused
+// multiply-add). W' is then quantized with the int8 rule above. A 64 n x 64 k
+// tile per block; a thread owns 16 consecutive k of one row n (one 16-byte
+// code load and, in pass 2, one 16-byte code store). W' is recomputed in
+// pass 2 rather than stored.
+// ---------------------------------------------------------------------------
+struct MergeSrc {
+  const int8_t* codes;   // [N, K]
+  const float* sw;       // [N]
+  const float* A;        // [K, r]
+  const float* B;        // [r, N]
+  int K, N, r;
+  double s;
+};
+
+constexpr int kMergeMaxR = 32;
+
+// W' for the thread's 16 k of row n: A [64 k][r] and B [r][64 n] of the tile
+// are in LDS.
+__device__ __forceinline__ void merged_row16(const MergeSrc& p, const float (*As)[kMergeMaxR + 1],
+                                             const float (*Bs)[64], int nl, int kl0, u32x4 qraw,
+                                             float swn, float w[16]) {
+  const int8_t* q = reinterpret_cast<const int8_t*>(&qraw);
+  const double sw64 = (double)swn;
+  for (int i = 0; i < 16; ++i) {
+    double acc = 0.0;
+    for (int j = 0; j < p.r; ++j)
+      acc = __dadd_rn(acc, __dmul_rn((double)As[kl0 + i][j], (double)Bs[j][nl]));
+    const double d = __dmul_rn((double)q[i], sw64);            // exact
+    w[i] = __double2float_rn(__dadd_rn(d, __dmul_rn(p.s, acc)));
+  }
+}
+
+template <bool CODES>
+__global__ __launch_bounds__(256) void merge_kernel(MergeSrc p, uint32_t* __restrict__ amax,
+                                                    int8_t* __restrict__ codes_out) {
+  __shared__ float As[64][kMergeMaxR + 1];
+  __shared__ float Bs[kMergeMaxR][64];
+  const int n0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+  const int tid = threadIdx.x, K = p.K, N = p.N, r = p.r;
+  for (int e = tid; e < 64 * r; e += 256) {
+    const int kl = e / r, j = e % r, k = k0 + kl;
+    As[kl][j] = k < K ? p.A[(long)k * r + j] : 0.f;
+  }
+  for (int e = tid; e < 64 * r; e += 256) {
+    const int j = e / 64, nl = e % 64, n = n0 + nl;
+    Bs[j][nl] = n < N ? p.B[(long)j * N + n] : 0.f;
+  }
+  __syncthreads();
+  const int nl = tid >> 2, kl0 = (tid & 3) * 16;
+  const int n = n0 + nl, k = k0 + kl0;
+  const bool live = n < N && k < K;                 // K % 16 == 0: 16 k all in or out
+  u32x4 qraw = {0u, 0u, 0u, 0u};
+  float swn = 0.f;
+  if (live) {
+    qraw = *reinterpret_cast<const u32x4*>(p.codes + (long)n * K + k);
+    swn = p.sw[n];
+  }
+  float w[16];
+  merged_row16(p, As, Bs, nl, kl0, qraw, swn, w);
+  if constexpr (!CODES) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t b = abs_bits(w[i]);
+      m = b > m ? b : m;
+    }
+    // the 4 threads of a row are adjacent lanes
+    m = max(m, (uint32_t)__shfl_xor((int)m, 1, kWave));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 2, kWave));
+    if (live && (tid & 3) == 0) atomicMax(amax + n, m);
+  } else {
+    if (!live) return;
+    const QuantParams qp = absmax_params(amax[n], 127.f);
+    uint32_t o[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int c = qp.live ? quant_code(w[4 * d + b], qp.inv, 127.f) : 0;
+        v |= (uint32_t)(uint8_t)(int8_t)c << (8 * b);
+      }
+      o[d] = v;
+    }
+    *reinterpret_cast<u32x4*>(codes_out + (long)n * K + k) = u32x4{o[0], o[1], o[2], o[3]};
+  }
+}
+
+void launch_merge_w8(const int8_t* codes, const float* sw, const float* A,
+                     const float* B, int K, int N, int r, float s,
+                     int8_t* codes_out, float* scales_out, hipStream_t st) {
+  MergeSrc p{codes, sw, A, B, K, N, r, (double)s};
+  uint32_t* amax = reinterpret_cast<uint32_t*>(scales_out);
+  fill_u32_kernel<<<dim3((N + 255) / 256), 256, 0, st>>>(amax, 0u, N);
+  const dim3 grid((N + 63) / 64, (K + 63) / 64);
+  merge_kernel<false><<<grid, 256, 0, st>>>(p, amax, nullptr);
+  merge_kernel<true><<<grid, 256, 0, st>>>(p, amax, codes_out);
+  w8_scales_kernel<<<dim3((N + 255) / 256), 256, 0, st>>>(amax, N);
+}
+
 void launch_quantize_w8(const float* W, int K, int N, int8_t* codes,
                         float* scales, hipStream_t st) {
   uint32_t* amax = reinterpret_cast<uint32_t*>(scales);

@@ -153,6 +153,11 @@ def test_calls_fail_before_launch(lib):
     assert lib.qlora_quantize_rows(FAKE, 4, 24, Q.QLORA_BF16, FAKE, FAKE, None) == Q.QLORA_EINVAL
     assert lib.qlora_fwd_acc(ctypes.byref(_lin(fmt=Q.QLORA_W4G128)), 64, Q.QLORA_BF16,
                              FAKE, FAKE, FAKE, 1 << 30, None) == Q.QLORA_EUNSUPPORTED
+    # merge: int8 only, outputs must not overlap the inputs
+    assert lib.qlora_merge(ctypes.byref(_lin(fmt=Q.QLORA_W4G128)), FAKE + 4096, FAKE + 8192,
+                           None) == Q.QLORA_EUNSUPPORTED
+    assert lib.qlora_merge(ctypes.byref(lin), FAKE, FAKE + (1 << 20), None) == Q.QLORA_EINVAL
+    assert lib.qlora_merge(ctypes.byref(lin), None, FAKE + (1 << 20), None) == Q.QLORA_EINVAL
     # the timed variants need at least one launch of the product kernel
     assert lib.qlora_fwd_timed(ctypes.byref(lin), 64, Q.QLORA_BF16, FAKE, FAKE, None, FAKE,
                                need, None, 0, None, None) == Q.QLORA_EINVAL

@@ -233,6 +233,52 @@ def test_deterministic_and_frozen():
     assert torch.equal(A0, case.lin.A) and torch.equal(B0, case.lin.B)
 
 
+def check_merge(case: Case):
+    c, sw, _ = case.oracle_weights()
+    mc, ms = Q.qlora_merge(case.lin)
+    torch.cuda.synchronize()
+    oc, osw = O.merge_w8(c, sw, case.A, case.B, case.w.alpha)
+    assert np.array_equal(to_numpy(mc), oc), "merged codes differ"
+    assert same_bits_f32(to_numpy(ms), osw), "merged scales differ"
+
+
+# merging the adapter into the int8 weight: full layers of three workloads
+@pytest.mark.parametrize("cid,layer", [(2, 0), (3, 1), (4, 2)])
+def test_merge_full_layer(cid, layer):
+    w = WL.WORKLOADS[cid]
+    say(f"merge: workload {cid} ({w.name}) layer {layer} K,N={w.layers[layer]} r={w.r}")
+    case = Case(w, layer, M=1)
+    check_weights(case)
+    check_merge(case)
+
+
+@pytest.mark.parametrize("K,N,r", [(784, 272, 1), (16, 16, 32), (128, 144, 3)])
+def test_merge_ragged(K, N, r):
+    w = WL.small(2, 1, K, N, r)
+    say(f"merge ragged: K={K} N={N} r={r}")
+    case = Case(w, 0)
+    check_weights(case)
+    check_merge(case)
+
+
+def test_merge_zero_channel():
+    """A channel whose weight column and adapter column are both zero stays
+    all-zero with scale 0 after the merge."""
+    w = WL.small(2, 1, 256, 64, 4)
+    say("merge: zero channel")
+    W = WL.weight(w, 0).copy()
+    W[:, 5] = 0.0
+    case = Case(w, 0, W=W)
+    B = case.B.copy()
+    B[:, 5] = 0.0
+    case.B = B
+    case.lin = Q.QLinear(case.K, case.N, w.r, w.alpha, w.wfmt, case.lin.codes, case.lin.scales,
+                         case.lin.A, dev(B))
+    check_merge(case)
+    mc, ms = Q.qlora_merge(case.lin)
+    assert to_numpy(ms)[5] == 0.0 and not to_numpy(mc)[5].any()
+
+
 def test_timed_repeats_are_identical():
     """The timed entry points launch the product kernel several times; every
     launch rewrites the same outputs, so results match the plain call bit for
