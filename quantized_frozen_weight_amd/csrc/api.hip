@@ -250,7 +250,7 @@ int qlora_bwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
                        static_cast<uint16_t*>(dx), partA, partB, s);
     mark(ev_stop, s);
     SkinnyJobs sk{};
-    const int bm = bwd_row_block(w8 ? 0 : 1, M, L->K);
+    const int bm = bwd_row_block(w8 ? 0 : 1, M, L->K, L->r);
     sk.njobs = 2; sk.M = M; sk.r = L->r; sk.s = sc;
     sk.nsplit = (M + bm - 1) / bm;
     sk.partial[0] = partB; sk.C[0] = L->N; sk.out[0] = dB; sk.transpose[0] = 0;

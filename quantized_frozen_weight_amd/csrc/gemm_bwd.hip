@@ -18,8 +18,8 @@
 // The stage ring (ring.hpp) carries three tiles per stage, all moved
 // global -> LDS without registers: the dy rows (swizzled 128-byte rows), the
 // codes [64 n][BN k] in their stored layout (chunk-swizzled), and an aux tile
-// with sw[n] and the adapter's B columns for those n. Once a stage has
-// landed, the whole block converts it in one cooperative pass (every code
+// with the stage's weight scales and the adapter's B columns for those n.
+// Once a stage has landed it is converted in one cooperative pass (every code
 // read and widened once, not once per wave that uses it):
 //   * CB [BN k][64 n] = bf16(deq(W)[k, n]), the transposed dequantized
 //     weight, as swizzled 128-byte rows (4-bit: the nibbles unpacked and
@@ -30,13 +30,22 @@
 //   * u  += dy BU^T, one MFMA per row block (the two column waves of a row
 //     split the row blocks);
 //   * dB: the block whose column index equals the stage index modulo the
-//     column-tile count adds t^T dy over its rows for the stage's 64 n on the
-//     vector ALUs in float32 (t exact), giving one partial per row block.
+//     column-tile count adds t^T dy over its rows for the stage's 64 n
+//     (dy^T through transposing LDS reads, t rounded to bf16), giving one
+//     partial per row block.
 // After the loop u goes to LDS; the dA partial over the block's rows is a
 // float32 vector-ALU sum of x (a tile loaded into LDS) times u; the dx
 // epilogue adds s u A^T on v_mfma_f32_16x16x4_f32. The partials of dA and dB
 // are added in row-block order by a small second launch. No atomics:
 // results are bitwise reproducible.
+//
+// Two block shapes share this scheme:
+//   * 64-row tiles, 512 threads in two roles (producer waves load and
+//     convert stage kt + 1 while consumer waves multiply stage kt), for
+//     shapes with at most two such tiles per compute unit;
+//   * 128 x 128 tiles, 256 threads that all do every step, for larger shapes,
+//     where sharing each loaded tile among more outputs matters more than
+//     overlapping the steps.
 #include "launch.hpp"
 #include "ring.hpp"
 
@@ -123,8 +132,475 @@ __device__ __forceinline__ float tile_bf16(const int8_t* tile, int row, int e) {
 }
 
 // W4: 4-bit weights (two codes per byte, fp16 scale per 128 k); else int8.
+// S: ring slots (at least 3: stage kt is multiplied while stage kt + 1 is
+// converted and the later stages are in flight).
+//
+// 512 threads in two roles. Waves 0-3 (consumers) own the accumulators and
+// run the products; waves 4-7 (producers) issue every direct-to-LDS load and
+// convert the codes. In iteration kt the consumers multiply stage kt while
+// the producers refill the ring with stage kt + S - 1 and convert stage
+// kt + 1 into the other buffer, so a compute unit overlaps the matrix work
+// of one wave with the vector work of the other on each SIMD. One barrier
+// per stage hands the buffers over.
 template <bool W4, int BM, int BN, int S, int R>
-__global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
+  constexpr int KC = 64;                              // n per stage
+  constexpr int RB = W4 ? BN / 2 : BN;                // code bytes per row of n
+  // aux tile: a header with the stage's weight scales (int8: sw[n], 64
+  // floats; 4-bit: for each n the 16-byte chunk of the scale array that holds
+  // sc[n][k0 / 128]), then the B columns [R][64] float
+  constexpr int HDR = W4 ? 1024 : 256;
+  constexpr int AUXI = (HDR + R * 256 + 4095) / 4096;  // aux DMA instructions per producer wave
+  constexpr int ASZ = BM * 128, BSZ = KC * RB, XSZ = 4 * AUXI * 1024;
+  constexpr int STG = ASZ + BSZ + XSZ;
+  // per producer wave and stage: dy rows, code rows, aux
+  constexpr int AI = BM / 32, BI = RB / 64, LPS = AI + BI + AUXI;
+  constexpr int FM = BM / 32, FN = BN / 32;
+  constexpr int RPI = 1024 / RB, CPR = RB / 16;
+  static_assert(RB == 64 || RB == 128, "code rows of 64 or 128 bytes");
+  static_assert(S >= 3, "stage kt + 1 is resident while stage kt is used");
+  static_assert(!W4 || BN == 128, "4-bit: one 128-wide k group per block");
+  constexpr int UCB = (R + 15) / 16;                  // u column blocks of 16
+  constexpr bool XPRE = BM * BN * 2 <= 8192;          // x tile kept outside the ring
+  constexpr int CBSZ = BN * 128;                      // converted codes [BN][64] bf16
+  constexpr int BUSZ = UCB * 16 * 128;                // converted B [16 UCB][64] bf16
+  constexpr int TSZ = BM * R * 4;                     // t tile (pitch r)
+  constexpr int XTSZ = BM * BN * 2;
+  constexpr int AQSZ = BN * R * 4;                    // the block's rows of A [BN][r]
+  constexpr int EFL = (BM + BN) * R;                  // epilogue floats: U [BM][R], A^T [R][BN]
+  static_assert(EFL * 4 + (XPRE ? 0 : XTSZ) <= S * STG, "epilogue and x tile fit in the ring");
+  // One LDS array for everything: with a second __shared__ object the
+  // compiler can no longer tell that the ring's reads do not wait on the
+  // direct-to-LDS loads still in flight, and waits for all of them.
+  // Converted codes and B are double-buffered: buffer kt % 2 feeds the
+  // products of stage kt while stage kt + 1 is converted into the other.
+  __shared__ __attribute__((aligned(1024))) int8_t ring[S * STG + 2 * CBSZ + 2 * BUSZ + TSZ + AQSZ + (XPRE ? XTSZ : 0)];
+  int8_t* CB0 = ring + S * STG;
+  int8_t* BU0 = CB0 + 2 * CBSZ;
+  float* Ts = reinterpret_cast<float*>(BU0 + 2 * BUSZ);                        // [BM][r]
+  const float* Aq = reinterpret_cast<const float*>(BU0 + 2 * BUSZ + TSZ);    // [BN][r]
+  int8_t* Xs = XPRE ? BU0 + 2 * BUSZ + TSZ + AQSZ : ring + EFL * 4;            // [BM][BN] bf16
+
+  const int lane = threadIdx.x & 63, wid = wave_id();
+  const bool producer = wid >= 4;
+  const int pw = wid - 4;                             // producer wave 0..3
+  const int ptid = (int)threadIdx.x - 256;            // producer thread 0..255
+  const int ctid = threadIdx.x;                       // consumer thread 0..255
+  const int wm = (wid >> 1) & 1, wn = wid & 1;        // consumer wave position
+  const int mt = (int)blockIdx.x / a.tiles_x, kt_blk = (int)blockIdx.x % a.tiles_x;
+  const int m0 = mt * BM, k0 = kt_blk * BN;
+  const int M = a.M, K = a.K, N = a.N, r = a.r;
+  const int nk = (N + KC - 1) / KC;
+  const int G = K / 128;                              // 4-bit: scale groups per row
+
+  // consumers: t rows of the block (for dB), then A^T of the block's columns
+  // (for the epilogue); masks are applied when stored
+  constexpr int NT = (BM * R + 255) / 256;
+  float tv[NT];
+  if (!producer) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int e = ctid + 256 * i, row = e / R, j = e % R, gm = m0 + row;
+      tv[i] = a.t[(long)(gm < M ? gm : M - 1) * r + (j < r ? j : r - 1)];
+    }
+  }
+
+  // producers: x tile [BM][BN] bf16 as swizzled 128-byte rows (64 columns
+  // per row half)
+  auto issue_x = [&]() {
+    constexpr int RH = BN / 64;                        // 128-byte halves per row
+#pragma unroll
+    for (int i = 0; i < BM * RH / 32; ++i) {
+      const int rb = (pw * (BM * RH / 32) + i) * 8, hrow = rb + (lane >> 3);
+      const int row = hrow / RH, half = hrow % RH;
+      const int c = (lane & 7) ^ ((hrow >> 1) & 7);
+      const int gm = m0 + row, gk = k0 + half * 64 + c * 8;
+      const void* src = gk < K ? (const void*)(a.x + (long)(gm < M ? gm : M - 1) * K + gk)
+                               : (const void*)zero_chunk(lane);
+      lds_dma16(src, Xs + rb * 128);
+    }
+  };
+
+  // Producers' per-lane sources of the stage loads at stage 0; stage kt
+  // moves each by kt * 64 n. Lanes whose chunk is outside the operand point
+  // at the zero page and do not move. Only a ragged last stage needs the n
+  // bound checked.
+  const int8_t* srcA[AI];
+  int nA[AI];                                          // first n of the lane's chunk
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int row = pw * (BM / 4) + i * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7), gm = m0 + row;
+    nA[i] = c * 8;
+    srcA[i] = reinterpret_cast<const int8_t*>(a.dy + (long)(gm < M ? gm : M - 1) * N + c * 8);
+  }
+  const long crs = W4 ? K / 2 : K;                    // code bytes per row in memory
+  const int8_t* srcB[BI];
+  int nB[BI];
+  bool okB[BI];
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int row = (pw * BI + i) * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ code_swz<RB>(row), gk = (W4 ? k0 / 2 : k0) + c * 16;
+    nB[i] = row;
+    okB[i] = gk < crs;
+    srcB[i] = okB[i] ? a.codes + (long)row * crs + gk : zero_chunk(lane);
+  }
+  // aux chunk ci of the tile: header chunks first, then B [j][64 n] in
+  // 4-float chunks; the source moves by adv bytes per n of the stage
+  const int8_t* srcX[AUXI];
+  int nX[AUXI], advX[AUXI];
+  bool okX[AUXI];
+#pragma unroll
+  for (int i = 0; i < AUXI; ++i) {
+    const int ci = (pw * AUXI + i) * 64 + lane;
+    if (ci < HDR / 16) {
+      if constexpr (W4) {
+        // n = ci: the aligned 16 bytes around sc[n][k0 / 128]
+        const long byte = 2L * ((long)ci * G + k0 / 128);
+        nX[i] = ci;
+        advX[i] = 2 * G;
+        okX[i] = true;
+        srcX[i] = reinterpret_cast<const int8_t*>(a.sc4) + (byte & ~15L);
+      } else {
+        nX[i] = 4 * ci;
+        advX[i] = 4;
+        okX[i] = true;
+        srcX[i] = reinterpret_cast<const int8_t*>(a.sw + 4 * ci);
+      }
+    } else {
+      const int e = (ci - HDR / 16) * 4, j = e / 64, nn = e % 64;
+      nX[i] = nn;
+      advX[i] = 4;
+      okX[i] = j < r;
+      srcX[i] = j < r ? reinterpret_cast<const int8_t*>(a.B + (long)j * N + nn) : zero_chunk(lane);
+    }
+  }
+  auto issue = [&](int kt, int slot) {
+    int8_t* base = ring + slot * STG;
+    const int nb = kt * KC;
+    const bool tail = nb + KC > N;
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+      const int8_t* src = srcA[i] + 2L * nb;
+      if (tail && nb + nA[i] >= N) src = zero_chunk(lane);
+      lds_dma16(src, base + (pw * (BM / 4) + i * 8) * 128);
+    }
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const int8_t* src = okB[i] ? srcB[i] + (long)nb * crs : srcB[i];
+      if (tail && nb + nB[i] >= N) src = zero_chunk(lane);
+      lds_dma16(src, base + ASZ + (pw * BI + i) * RPI * RB);
+    }
+#pragma unroll
+    for (int i = 0; i < AUXI; ++i) {
+      const int8_t* src = okX[i] ? srcX[i] + (long)advX[i] * nb : srcX[i];
+      if (tail && nb + nX[i] >= N) src = zero_chunk(lane);
+      lds_dma16(src, base + ASZ + BSZ + (pw * AUXI + i) * 1024);
+    }
+  };
+
+  // producers' cooperative conversion: thread -> n quad nq, k quads kq0 + 16 h
+  const int nq = ptid & 15, kq0 = (ptid >> 4) & 15;
+  // 4-bit: byte offset of sc[n][k0 / 128] inside the header chunk of n, for
+  // the thread's 4 n
+  int soff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) soff[i] = 16 * (4 * nq + i) + ((2 * ((4 * nq + i) * G + k0 / 128)) & 15);
+
+  // Conversion of the stage in ring slot `slot` into buffer `buf`:
+  //   CB[k][n] = bf16(q[n][k] sw[n]) for the 4 n of nq and 4 k per quad
+  //   (4-bit: bf16(q[n][k] sc[n][k0 / 128]) for the 4 n of nq and 8 k);
+  //   BU[j][n] = bf16(B[j][n]), 2 n per entry.
+  constexpr int NBU = (R * 32 + 255) / 256;
+  auto convert = [&](int slot, int buf) {
+    const int8_t* Bs = ring + slot * STG + ASZ;
+    const int8_t* Xb = Bs + BSZ;
+    const float* Xa = reinterpret_cast<const float*>(Xb);
+    int8_t* CB = CB0 + buf * CBSZ;
+    int8_t* BU = BU0 + buf * BUSZ;
+    f32x2 bq[NBU];
+#pragma unroll
+    for (int q = 0; q < NBU; ++q) {
+      const int e = ptid + 256 * q;
+      const int j = e >> 5, p = e & 31;
+      if (e < R * 32) bq[q] = *reinterpret_cast<const f32x2*>(Xa + HDR / 4 + 64 * j + 2 * p);
+    }
+    if constexpr (W4) {
+      float sc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[i] = (float)*reinterpret_cast<const _Float16*>(Xb + soff[i]);
+      const int kq8 = kq0;                           // k in [8 kq8, 8 kq8 + 8)
+      uint32_t raw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = 4 * nq + i;
+        raw[i] = *reinterpret_cast<const uint32_t*>(Bs + n * RB + (((kq8 >> 2) ^ code_swz<RB>(n)) << 4) + (kq8 & 3) * 4);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v0 = (float)(((int)(raw[0] << (28 - 4 * e))) >> 28) * sc[0];
+        const float v1 = (float)(((int)(raw[1] << (28 - 4 * e))) >> 28) * sc[1];
+        const float v2 = (float)(((int)(raw[2] << (28 - 4 * e))) >> 28) * sc[2];
+        const float v3 = (float)(((int)(raw[3] << (28 - 4 * e))) >> 28) * sc[3];
+        *reinterpret_cast<u32x2*>(CB + swz128(8 * kq8 + e, nq >> 1) + (nq & 1) * 8) =
+            u32x2{pk_bf16(v0, v1), pk_bf16(v2, v3)};
+      }
+    } else {
+      const f32x4 swv = *reinterpret_cast<const f32x4*>(Xa + 4 * nq);
+#pragma unroll
+      for (int h = 0; h < BN / 64; ++h) {
+        const int kcol = 4 * (kq0 + 16 * h);
+        int raw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = 4 * nq + i;
+          raw[i] = *reinterpret_cast<const int*>(Bs + n * RB + ((((kcol >> 4) ^ code_swz<RB>(n))) << 4) + (kcol & 15));
+        }
+#pragma unroll
+        for (int kk2 = 0; kk2 < 4; ++kk2) {
+          const float v0 = (float)(int8_t)(raw[0] >> (8 * kk2)) * swv.x;
+          const float v1 = (float)(int8_t)(raw[1] >> (8 * kk2)) * swv.y;
+          const float v2 = (float)(int8_t)(raw[2] >> (8 * kk2)) * swv.z;
+          const float v3 = (float)(int8_t)(raw[3] >> (8 * kk2)) * swv.w;
+          *reinterpret_cast<u32x2*>(CB + swz128(kcol + kk2, nq >> 1) + (nq & 1) * 8) =
+              u32x2{pk_bf16(v0, v1), pk_bf16(v2, v3)};
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NBU; ++q) {
+      const int e = ptid + 256 * q;
+      const int j = e >> 5, p = e & 31;
+      if (e < R * 32) *reinterpret_cast<uint32_t*>(BU + swz128(j, p >> 2) + (p & 3) * 4) = pk_bf16(bq[q].x, bq[q].y);
+    }
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 uacc[(FM + 1) / 2][UCB];
+#pragma unroll
+  for (int i = 0; i < (FM + 1) / 2; ++i)
+#pragma unroll
+    for (int j = 0; j < UCB; ++j) uacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (producer) {
+    // the block's rows of A, contiguous in memory: (K - k0 or BN) * r floats
+    {
+      const int rows = K - k0 < BN ? K - k0 : BN;
+      const int bytes = rows * r * 4;                // a multiple of 16
+      const int8_t* src0 = reinterpret_cast<const int8_t*>(a.A + (long)k0 * r);
+      for (int o = pw * 1024; o < AQSZ; o += 4096) {
+        const int e = o + lane * 16;
+        lds_dma16(e < bytes ? src0 + e : zero_chunk(lane), const_cast<float*>(Aq) + o / 4);
+      }
+    }
+    if constexpr (XPRE) issue_x();
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st)
+      if (st < nk) issue(st, st);
+    // BU rows past the rank stay zero for good
+    for (int e = R * 32 + ptid; e < UCB * 16 * 32; e += 256) {   // 4-byte pairs
+      const int off = swz128(e / 32, (e % 32) >> 2) + (e & 3) * 4;
+      *reinterpret_cast<uint32_t*>(BU0 + off) = 0u;
+      *reinterpret_cast<uint32_t*>(BU0 + BUSZ + off) = 0u;
+    }
+    // stage 0 landed (later prologue stages may still be in flight)
+    wait_stages<LPS, 0, S - 2>(nk - 1);
+  } else {
+    // t tile into LDS (pitch r)
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int e = ctid + 256 * i, row = e / R, j = e % R;
+      if (e < BM * R && j < r) Ts[row * r + j] = m0 + row < M ? tv[i] : 0.f;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+  __builtin_amdgcn_s_barrier();
+  if (producer) convert(0, 0);
+
+  const int rows_here = M - m0 < BM ? M - m0 : BM;
+  // dB operand: t as bf16, lane -> rank (lane % 16), rows 32 c + 8 (lane / 16) + e
+  // (read back from LDS at the block's first dB stage)
+  bf16x8 tfr[UCB][BM / 32];
+  bool tfr_ready = false;
+
+  int slot = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    // producers: stage kt + 1 landed and buffer kt % 2 written; then every
+    // wave is done with stage kt - 1 (its slot and buffer (kt + 1) % 2)
+    if (producer) wait_stages<LPS, 0, S - 3>(nk - 2 - kt);
+    __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+    __builtin_amdgcn_s_barrier();
+    const int pslot = slot == 0 ? S - 1 : slot - 1;  // slot of stage kt - 1 = kt + S - 1
+    const int nslot = slot == S - 1 ? 0 : slot + 1;  // slot of stage kt + 1
+    if (producer) {
+      if (kt + S - 1 < nk) issue(kt + S - 1, pslot);
+      if (kt + 1 < nk) convert(nslot, (kt + 1) & 1);
+    } else {
+      const int8_t* As = ring + slot * STG;
+      const int8_t* CB = CB0 + (kt & 1) * CBSZ;
+      const int8_t* BU = BU0 + (kt & 1) * BUSZ;
+      constexpr int KS = KC / 32;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const int c = kk * 4 + (lane >> 4);
+        bf16x8 af[FM], bf[FN], bu[UCB];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          af[i] = *reinterpret_cast<const bf16x8*>(As + swz128(wm * (BM / 2) + i * 16 + (lane & 15), c));
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          bf[j] = *reinterpret_cast<const bf16x8*>(CB + swz128(wn * (BN / 2) + j * 16 + (lane & 15), c));
+#pragma unroll
+        for (int cb = 0; cb < UCB; ++cb)
+          bu[cb] = *reinterpret_cast<const bf16x8*>(BU + swz128(cb * 16 + (lane & 15), c));
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int cb = 0; cb < UCB; ++cb)
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+            if ((i & 1) == wn)
+              uacc[i >> 1][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bu[cb], uacc[i >> 1][cb], 0, 0, 0);
+      }
+      // dB partial for this stage's 64 n over the block's rows (one block
+      // per row block and stage), on the matrix cores: consumer wave w takes
+      // n in [16 w, 16 w + 16); dB^T[n][j] = sum_m dy[m][n] t[m][j]. The dy^T
+      // operand comes from the dy tile through transposing reads: in each
+      // 16-lane group, lanes 4 i + p fetch the 4 n at 16 w + 4 p of row i,
+      // and lane q receives n = 16 w + q of rows 0..3.
+      if (kt % a.tiles_x == kt_blk) {
+        if (!tfr_ready) {
+          tfr_ready = true;
+#pragma unroll
+          for (int cb = 0; cb < UCB; ++cb) {
+            const int j = cb * 16 + (lane & 15);
+#pragma unroll
+            for (int c = 0; c < BM / 32; ++c) {
+              float v[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const int m = 32 * c + 8 * (lane >> 4) + e;
+                v[e] = j < r ? Ts[m * r + (j < r ? j : 0)] : 0.f;
+              }
+              tfr[cb][c] = __builtin_bit_cast(bf16x8, u32x4{pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]),
+                                                             pk_bf16(v[4], v[5]), pk_bf16(v[6], v[7])});
+            }
+          }
+        }
+        constexpr int NRD = 2 * (BM / 32);
+        uint32_t tra[NRD];
+        uint64_t trv[NRD];
+        const int q = lane & 15, i4 = q >> 2, p4 = q & 3;
+#pragma unroll
+        for (int c = 0; c < BM / 32; ++c)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int m = 32 * c + 8 * (lane >> 4) + 4 * h + i4;
+            const int n = 16 * wid + 4 * p4;
+            tra[2 * c + h] = lds_addr(As + swz128(m, n >> 3) + (n & 7) * 2);
+          }
+        tr16_reads<NRD>(tra, trv);
+        f32x4 dbacc[UCB];
+#pragma unroll
+        for (int cb = 0; cb < UCB; ++cb) dbacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < BM / 32; ++c) {
+          const bf16x8 dyT = __builtin_bit_cast(bf16x8, u32x4{(uint32_t)trv[2 * c], (uint32_t)(trv[2 * c] >> 32),
+                                                              (uint32_t)trv[2 * c + 1], (uint32_t)(trv[2 * c + 1] >> 32)});
+#pragma unroll
+          for (int cb = 0; cb < UCB; ++cb)
+            dbacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dyT, tfr[cb][c], dbacc[cb], 0, 0, 0);
+        }
+#pragma unroll
+        for (int cb = 0; cb < UCB; ++cb) {
+          const int j = cb * 16 + (lane & 15);
+          if (j < r) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+              const int gn = kt * KC + 16 * wid + 4 * (lane >> 4) + ii;
+              if (gn < N) a.partB[((long)mt * r + j) * N + gn] = dbacc[cb][ii];
+            }
+          }
+        }
+      }
+    }
+    slot = nslot;
+  }
+
+  // ---- after the contraction: u to LDS, x tile, then the dA partial
+  // (producers) beside the dx epilogue (consumers) ----
+  float* E = reinterpret_cast<float*>(ring);             // U [BM][R] | A^T [R][BN]
+  __syncthreads();                                        // ring released
+  if (producer) {
+    if constexpr (!XPRE) issue_x();
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if ((i & 1) != wn) continue;
+#pragma unroll
+      for (int cb = 0; cb < UCB; ++cb) {
+        const int j = cb * 16 + (lane & 15);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int ml = wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + ii;
+          if (j < R) E[ml * R + j] = j < r ? uacc[i >> 1][cb][ii] : 0.f;
+        }
+      }
+    }
+  }
+  // A^T of the block's columns into the epilogue layout (from LDS)
+  for (int e = threadIdx.x; e < BN * R; e += 512) {
+    const int j = e / BN, col = e % BN;
+    E[BM * R + e] = (j < r && k0 + col < K) ? Aq[col * r + (j < r ? j : 0)] : 0.f;
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+
+  if (producer) {
+    // dA partial: thread -> column k = ptid % BN, ranks jb + (256 / BN) jj
+    constexpr int TPK = 256 / BN, JPT = R / TPK;
+    const int kl = ptid % BN, jb = ptid / BN;
+    float da[JPT];
+#pragma unroll
+    for (int jj = 0; jj < JPT; ++jj) da[jj] = 0.f;
+#pragma unroll 8
+    for (int m = 0; m < rows_here; ++m) {
+      const int hrow = m * (BN / 64) + kl / 64;
+      const float xv = tile_bf16(Xs, hrow, kl % 64);
+#pragma unroll
+      for (int jj = 0; jj < JPT; ++jj) da[jj] = __builtin_fmaf(xv, E[m * R + jb + TPK * jj], da[jj]);
+    }
+    if (k0 + kl < K) {
+#pragma unroll
+      for (int jj = 0; jj < JPT; ++jj) {
+        const int j = jb + TPK * jj;
+        if (j < r) a.partA[((long)mt * r + j) * K + k0 + kl] = da[jj];
+      }
+    }
+  } else {
+    epilogue_lowrank<BM, BN, R, false>(acc, E, M, K, m0, k0, wm * (BM / 2), wn * (BN / 2), a.s, a.dx);
+  }
+}
+
+
+
+// Wide tiles (128 x 128, 256 threads): every wave issues its share of the
+// stage loads, converts its share of the codes and multiplies, with two
+// barriers per stage. At this tile size the dy and code tiles are each shared
+// by twice the outputs of a 64-row tile, which halves the load traffic per
+// product, and the whole block's registers serve one role.
+// W4: 4-bit weights (two codes per byte, fp16 scale per 128 k, carried one
+// stage ahead in a register); else int8.
+template <bool W4, int BM, int BN, int S, int R>
+__global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
   constexpr int KC = 64;                              // n per stage
   constexpr int RB = W4 ? BN / 2 : BN;                // code bytes per row of n
   constexpr int AUXI = ((1 + R) * 256 + 4095) / 4096;  // aux DMA instructions per wave
@@ -500,24 +976,36 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
   epilogue_lowrank<BM, BN, R, false>(acc, E, M, K, m0, k0, wm * (BM / 2), wn * (BN / 2), a.s, a.dx);
 }
 
-template <bool W4, int BM, int BN, int S>
-void launch_tiles(BwdArgs a, hipStream_t st) {
+
+template <bool W4, int BN, int S>
+void launch_pc(BwdArgs a, hipStream_t st) {
+  constexpr int BM = 64;
   a.tiles_x = (a.K + BN - 1) / BN;
   const dim3 grid((unsigned)(a.tiles_x * ((a.M + BM - 1) / BM)));
-  if (a.r <= 4) bwd_kernel<W4, BM, BN, S, 4><<<grid, 256, 0, st>>>(a);
-  else if (a.r <= 8) bwd_kernel<W4, BM, BN, S, 8><<<grid, 256, 0, st>>>(a);
-  else if (a.r <= 16) bwd_kernel<W4, BM, BN, S, 16><<<grid, 256, 0, st>>>(a);
-  else bwd_kernel<W4, BM, BN, S, 32><<<grid, 256, 0, st>>>(a);
+  if (a.r <= 4) bwd_pc_kernel<W4, BM, BN, S, 4><<<grid, 512, 0, st>>>(a);
+  else if (a.r <= 8) bwd_pc_kernel<W4, BM, BN, S, 8><<<grid, 512, 0, st>>>(a);
+  else if (a.r <= 16) bwd_pc_kernel<W4, BM, BN, S, 16><<<grid, 512, 0, st>>>(a);
+  else bwd_pc_kernel<W4, BM, BN, S, 32><<<grid, 512, 0, st>>>(a);
+}
+
+template <bool W4>
+void launch_wide(BwdArgs a, hipStream_t st) {
+  constexpr int BM = 128, BN = 128, S = 2;
+  a.tiles_x = (a.K + BN - 1) / BN;
+  const dim3 grid((unsigned)(a.tiles_x * ((a.M + BM - 1) / BM)));
+  if (a.r <= 4) bwd_wide_kernel<W4, BM, BN, S, 4><<<grid, 256, 0, st>>>(a);
+  else if (a.r <= 8) bwd_wide_kernel<W4, BM, BN, S, 8><<<grid, 256, 0, st>>>(a);
+  else if (a.r <= 16) bwd_wide_kernel<W4, BM, BN, S, 16><<<grid, 256, 0, st>>>(a);
+  else bwd_wide_kernel<W4, BM, BN, S, 32><<<grid, 256, 0, st>>>(a);
 }
 
 }  // namespace
 
-int bwd_row_block(int fmt, int M, int K) {
-  // int8: 64 x 64 tiles while they make at most two blocks per compute unit,
-  // else 128 x 128; 4-bit: 128 columns (one scale group), 64 or 128 rows
+int bwd_row_block(int fmt, int M, int K, int r) {
+  (void)r;
   const int bn = fmt == 0 ? 64 : 128;
-  const long t = (long)((M + 63) / 64) * ((K + bn - 1) / bn);
-  return t <= 512 ? 64 : 128;
+  const long t64 = (long)((M + 63) / 64) * ((K + bn - 1) / bn);
+  return t64 <= 512 ? 64 : 128;
 }
 
 void launch_bwd_fused(int fmt, int M, int K, int N, const uint16_t* dy,
@@ -529,15 +1017,17 @@ void launch_bwd_fused(int fmt, int M, int K, int N, const uint16_t* dy,
   a.M = M; a.K = K; a.N = N; a.dy = dy; a.codes = static_cast<const int8_t*>(codes);
   a.B = B; a.A = A; a.t = t; a.x = x; a.r = r; a.s = s; a.dx = dx; a.partA = partA;
   a.partB = partB;
-  const int bm = bwd_row_block(fmt, M, K);
+  // 64-row tiles (producer/consumer) while they make at most two blocks per
+  // compute unit, else the wide 128 x 128 tiles
+  const bool small = bwd_row_block(fmt, M, K, r) == 64;
   if (fmt == 0) {
     a.sw = static_cast<const float*>(scales);
-    if (bm == 64) launch_tiles<false, 64, 64, 3>(a, st);
-    else launch_tiles<false, 128, 128, 2>(a, st);
+    if (small) launch_pc<false, 64, 3>(a, st);
+    else launch_wide<false>(a, st);
   } else {
     a.sc4 = static_cast<const uint16_t*>(scales);
-    if (bm == 64) launch_tiles<true, 64, 128, 2>(a, st);
-    else launch_tiles<true, 128, 128, 2>(a, st);
+    if (small) launch_pc<true, 128, 3>(a, st);
+    else launch_wide<true>(a, st);
   }
 }
 

@@ -61,8 +61,8 @@ void launch_skinny_stage2(const SkinnyJobs& p, hipStream_t st);
 // (fmt 1: packed [N, K/2], scales fp16 [N, K/128]) weights:
 // dx = dy deq(W)^T + s u A^T with u = dy B^T computed in the same launch,
 // plus per-row-block partial sums of dA (partA [blocks, r, K]) and dB
-// (partB [blocks, r, N]); blocks = ceil(M / bwd_row_block(fmt, M, K)).
-int bwd_row_block(int fmt, int M, int K);
+// (partB [blocks, r, N]); blocks = ceil(M / bwd_row_block(fmt, M, K, r)).
+int bwd_row_block(int fmt, int M, int K, int r);
 void launch_bwd_fused(int fmt, int M, int K, int N, const uint16_t* dy,
                       const void* codes, const void* scales, const float* B,
                       const float* A, const float* t, const uint16_t* x, int r,
