@@ -586,7 +586,10 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
       }
     }
   } else {
-    epilogue_lowrank<BM, BN, R, false>(acc, E, M, K, m0, k0, wm * (BM / 2), wn * (BN / 2), a.s, a.dx);
+    // output staging strips in the converted-code buffers, free after the loop
+    static_assert(4 * epi_strip_bytes<uint16_t, FN>() <= 2 * CBSZ, "staging strips fit");
+    epilogue_lowrank<BM, BN, R, false>(acc, E, M, K, m0, k0, wm * (BM / 2), wn * (BN / 2), a.s, a.dx,
+                                       CB0 + wid * epi_strip_bytes<uint16_t, FN>());
   }
 }
 
@@ -973,7 +976,10 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
     }
   }
 
-  epilogue_lowrank<BM, BN, R, false>(acc, E, M, K, m0, k0, wm * (BM / 2), wn * (BN / 2), a.s, a.dx);
+  // output staging strips in the converted-code buffer, free after the loop
+  static_assert(4 * epi_strip_bytes<uint16_t, FN>() <= CBSZ, "staging strips fit");
+  epilogue_lowrank<BM, BN, R, false>(acc, E, M, K, m0, k0, wm * (BM / 2), wn * (BN / 2), a.s, a.dx,
+                                     CB + wid * epi_strip_bytes<uint16_t, FN>());
 }
 
 

@@ -45,7 +45,10 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
   constexpr int BK = 128, ASZ = BM * BK, STG = (BM + BN) * BK;
   constexpr int AI = BM / 32, BI = BN / 32, LPS = AI + BI;   // loads per wave per stage
   constexpr int FM = BM / 32, FN = BN / 32;
-  static_assert(EpiOps<BM, BN, R, true>::kFloats * 4 <= S * STG, "epilogue fits in the ring");
+  // after the loop the ring holds the epilogue operands, then one output
+  // staging strip per wave
+  constexpr int EPB = (EpiOps<BM, BN, R, true>::kFloats * 4 + 15) / 16 * 16;
+  static_assert(EPB + 4 * epi_strip_bytes<OutT, FN>() <= S * STG, "epilogue fits in the ring");
   __shared__ __attribute__((aligned(1024))) int8_t ring[S * STG];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = wave_id();
@@ -131,7 +134,8 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
     ep.store(E, M, N, m0, n0, a.r);
     __syncthreads();
     epilogue_lowrank<BM, BN, R, true>(acc, E, M, N, m0, n0, wm * (BM / 2), wn * (BN / 2),
-                                      a.s, reinterpret_cast<OutT*>(a.y));
+                                      a.s, reinterpret_cast<OutT*>(a.y),
+                                      ring + EPB + wid * epi_strip_bytes<OutT, FN>());
   }
 }
 

@@ -67,7 +67,10 @@ __global__ __launch_bounds__(256) void fwd_w4_kernel(W4Args a) {
   constexpr int FM = BM / 32, FN = BN / 32;
   constexpr int CBSZ = BN * 256;
   static_assert(BN == 128, "code rows of 64 bytes: 16 rows per DMA instruction, 2 threads per row");
-  static_assert(EpiOps<BM, BN, R, false>::kFloats * 4 <= S * STG, "epilogue fits in the ring");
+  // after the loop the ring holds the epilogue operands, then one output
+  // staging strip per wave
+  constexpr int EPB = (EpiOps<BM, BN, R, false>::kFloats * 4 + 15) / 16 * 16;
+  static_assert(EPB + 4 * epi_strip_bytes<uint16_t, FN>() <= S * STG, "epilogue fits in the ring");
   const int K = a.K, M = a.M, N = a.N;
   const int ngrp = K / BK;
   static_assert(BN * G * 2 % 1024 == 0, "the scale slab takes whole 1 KB DMA instructions");
@@ -181,7 +184,8 @@ __global__ __launch_bounds__(256) void fwd_w4_kernel(W4Args a) {
   __syncthreads();
   ep.store(E, M, N, m0, n0, a.r);
   __syncthreads();
-  epilogue_lowrank<BM, BN, R, false>(acc, E, M, N, m0, n0, wm * (BM / 2), wn * (BN / 2), a.s, a.y);
+  epilogue_lowrank<BM, BN, R, false>(acc, E, M, N, m0, n0, wm * (BM / 2), wn * (BN / 2), a.s, a.y,
+                                     ring + EPB + wid * epi_strip_bytes<uint16_t, FN>());
 }
 
 template <int BM, int S, int G>

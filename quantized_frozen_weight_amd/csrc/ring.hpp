@@ -140,13 +140,26 @@ template <int BM, int BN, int R, bool SCALED> struct EpiOps {
   }
 };
 
+// LDS bytes of one wave's output staging strip in epilogue_lowrank: 16 rows
+// of FN * 16 outputs, each row padded by 16 bytes (so that the four row
+// groups of one write instruction fall in different banks).
+template <typename OutT, int FN>
+constexpr int epi_strip_bytes() {
+  return 16 * (FN * 16 * (int)sizeof(OutT) + 16);
+}
+
 // Apply the epilogue to a wave's FM x FN grid of 16 x 16 accumulator blocks
 // whose top-left output is (wr0, wc0) inside the tile (the lane holds rows
-// 4 (lane / 16) + ii of column lane % 16 of each block).
+// 4 (lane / 16) + ii of column lane % 16 of each block). The results leave
+// through `strip` (epi_strip_bytes<OutT, FN>() of LDS owned by this wave):
+// one 16-row strip at a time is written there in the accumulator layout and
+// read back as 16-byte pieces of rows, so each global store instruction
+// writes whole 16-byte runs of a row instead of one element per lane.
 template <int BM, int BN, int R, bool SCALED, typename OutT, typename AccT, int FM, int FN>
 __device__ __forceinline__ void epilogue_lowrank(const AccT (&acc)[FM][FN], const float* E,
                                                  int M, int N, int m0, int n0, int wr0,
-                                                 int wc0, float s, OutT* __restrict__ out) {
+                                                 int wc0, float s, OutT* __restrict__ out,
+                                                 int8_t* strip) {
   const int lane = threadIdx.x & 63;
   const float* ts = E;
   const float* qs = E + BM * R;
@@ -173,22 +186,35 @@ __device__ __forceinline__ void epilogue_lowrank(const AccT (&acc)[FM][FN], cons
       for (int jn = 0; jn < FN; ++jn)
         low[i][jn] = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[i], qb[jn], low[i][jn], 0, 0, 0);
   }
+  constexpr int ROWB = FN * 16 * (int)sizeof(OutT);   // bytes of one strip row
+  constexpr int PITCH = ROWB + 16;
+  constexpr int CPR = ROWB / 16;                      // 16-byte pieces per row
+  constexpr int EPC = 16 / (int)sizeof(OutT);         // outputs per piece
+  static_assert(CPR * 16 % 64 == 0, "whole pieces per lane");
 #pragma unroll
-  for (int jn = 0; jn < FN; ++jn) {
-    const int nl = wc0 + jn * 16 + (lane & 15);
-    const int n = n0 + nl;
-    const float csn = SCALED ? csv[nl] : 1.f;
+  for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int jn = 0; jn < FN; ++jn) {
+      const int nl = wc0 + jn * 16 + (lane & 15);
+      const float csn = SCALED ? csv[nl] : 1.f;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const int ml = wr0 + i * 16 + (lane >> 4) * 4 + ii;
-        const int m = m0 + ml;
-        const float base = SCALED ? (float)acc[i][jn][ii] * (rsv[ml] * csn)
+        const int rl = (lane >> 4) * 4 + ii;             // row inside the strip
+        const float base = SCALED ? (float)acc[i][jn][ii] * (rsv[wr0 + i * 16 + rl] * csn)
                                   : (float)acc[i][jn][ii];
-        if (m < M && n < N) store_out(out + (long)m * N + n, __builtin_fmaf(s, low[i][jn][ii], base));
+        store_out(reinterpret_cast<OutT*>(strip + rl * PITCH) + jn * 16 + (lane & 15),
+                  __builtin_fmaf(s, low[i][jn][ii], base));
       }
     }
+    __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());          // the strip is written
+#pragma unroll
+    for (int p = 0; p < CPR * 16 / 64; ++p) {
+      const int q = lane + 64 * p, rl = q / CPR, cq = q % CPR;
+      const int m = m0 + wr0 + i * 16 + rl, n = n0 + wc0 + cq * EPC;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(strip + rl * PITCH + cq * 16);
+      if (m < M && n < N) *reinterpret_cast<u32x4*>(out + (long)m * N + n) = v;
+    }
+    __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());          // read back before the next strip
   }
 }
 
