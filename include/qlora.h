@@ -147,6 +147,24 @@ int qlora_bwd(const qlora_linear* L, int M, int dtype, const void* x,
               const void* dy, const float* t_saved, void* dx, float* dA,
               float* dB, void* ws, size_t ws_bytes, void* stream);
 
+/* qlora_bwd in two calls, for callers that take the adapter gradients off the
+ * path that carries dx to the next layer (for instance onto a second stream,
+ * the way weight gradients are usually overlapped with the rest of a
+ * backward pass). Same arithmetic, bitwise the same results:
+ *   - qlora_bwd_partial writes dx (skipped if NULL) and leaves fixed-order
+ *     per-row-block partial sums of dB and dA in ws;
+ *   - qlora_bwd_finish adds those partial sums, in row-block order, times s,
+ *     into dB and dA.
+ * Both take the same L, M, dtype and workspace (qlora_bwd_workspace bytes).
+ * The caller orders them: finish must run after partial's work on ws has
+ * completed, and nothing else may write ws in between. Arguments and errors
+ * as for qlora_bwd; each call validates its own arguments. */
+int qlora_bwd_partial(const qlora_linear* L, int M, int dtype, const void* x,
+                      const void* dy, const float* t_saved, void* dx, void* ws,
+                      size_t ws_bytes, void* stream);
+int qlora_bwd_finish(const qlora_linear* L, int M, int dtype, float* dA,
+                     float* dB, void* ws, size_t ws_bytes, void* stream);
+
 /* qlora_fwd / qlora_bwd with timing marks, for timing the call's main
  * product kernel live: the int8 or 4-bit forward product; the fused int8
  * backward (dx, u and the adapter-gradient partial sums) or, on the other

@@ -51,7 +51,7 @@ EXPORTS = (
     "qlora_status_str", "qlora_weight_bytes", "qlora_quantize",
     "qlora_fwd_workspace", "qlora_fwd", "qlora_bwd_workspace", "qlora_bwd",
     "qlora_quantize_rows", "qlora_fwd_acc", "qlora_fwd_timed", "qlora_bwd_timed",
-    "qlora_merge",
+    "qlora_merge", "qlora_bwd_partial", "qlora_bwd_finish",
 )
 
 
@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
     L.qlora_fwd_timed.argtypes = [plin, i, i, vp, vp, vp, vp, sz, vp, i, vp, vp]
     L.qlora_bwd_timed.argtypes = [plin, i, i, vp, vp, vp, vp, vp, vp, vp, sz, vp, i, vp, vp]
     L.qlora_merge.argtypes = [plin, vp, vp, vp]
+    L.qlora_bwd_partial.argtypes = [plin, i, i, vp, vp, vp, vp, vp, sz, vp]
+    L.qlora_bwd_finish.argtypes = [plin, i, i, vp, vp, vp, sz, vp]
     for name in EXPORTS[1:]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -232,6 +234,42 @@ def qlora_bwd(layer: QLinear, x, dy, t=None, need_dx: bool = True, dx=None,
                            _ptr(ws), ws.numel() * ws.element_size(), _stream()),
            "qlora_bwd")
     return (dx if need_dx else None), dA, dB
+
+
+def qlora_bwd_partial(layer: QLinear, x, dy, t=None, need_dx: bool = True, dx=None,
+                      ws=None, stream=None):
+    """First half of qlora_bwd: dx (or None) and the adapter-gradient partial
+    sums, which stay in the returned workspace for qlora_bwd_finish."""
+    import torch
+    M = x.shape[0]
+    dt = _dtype_code(x)
+    if need_dx and dx is None:
+        dx = torch.empty((M, layer.K), dtype=x.dtype, device=x.device)
+    ws = _workspace(qlora_bwd_workspace(layer, M, dt), x.device, ws)
+    s = layer.cstruct()
+    _check(lib().qlora_bwd_partial(ctypes.byref(s), M, dt, _ptr(x), _ptr(dy), _ptr(t),
+                                   _ptr(dx) if need_dx else None, _ptr(ws),
+                                   ws.numel() * ws.element_size(),
+                                   _stream() if stream is None else stream.cuda_stream),
+           "qlora_bwd_partial")
+    return (dx if need_dx else None), ws
+
+
+def qlora_bwd_finish(layer: QLinear, M: int, dtype, ws, dA=None, dB=None, stream=None):
+    """Second half of qlora_bwd: dA [K, r] and dB [r, N] from the partial sums
+    that qlora_bwd_partial left in ws. dtype: the activations' torch dtype."""
+    import torch
+    dt = QLORA_F32 if dtype == torch.float32 else QLORA_BF16
+    if dA is None:
+        dA = torch.empty((layer.K, layer.r), dtype=torch.float32, device=ws.device)
+    if dB is None:
+        dB = torch.empty((layer.r, layer.N), dtype=torch.float32, device=ws.device)
+    s = layer.cstruct()
+    _check(lib().qlora_bwd_finish(ctypes.byref(s), M, dt, _ptr(dA), _ptr(dB), _ptr(ws),
+                                  ws.numel() * ws.element_size(),
+                                  _stream() if stream is None else stream.cuda_stream),
+           "qlora_bwd_finish")
+    return dA, dB
 
 
 def qlora_quantize_rows(x):

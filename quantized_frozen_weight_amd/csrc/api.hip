@@ -103,6 +103,21 @@ int launch_status() {
   return e == hipSuccess ? QLORA_OK : QLORA_EHIP;
 }
 
+// Row-block count of the adapter-gradient partial sums: the fused bf16
+// backward's row tile; the other paths split the rows the same way so that
+// the combine needs nothing but (L, M, dtype).
+int bwd_splits(const qlora_linear* L, int M) {
+  const int bm = bwd_row_block(L->fmt == QLORA_W8 ? 0 : 1, M, L->K, L->r);
+  return (M + bm - 1) / bm;
+}
+
+int bwd_check_ws(const qlora_linear* L, int M, int dtype, void* ws, size_t ws_bytes) {
+  const BwdLayout w = bwd_layout(L, M, dtype);
+  if (ws_bytes < w.total || !ws || !aligned16(ws)) return QLORA_EWORKSPACE;
+  return QLORA_OK;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -215,18 +230,19 @@ int qlora_bwd_workspace(const qlora_linear* L, int M, int dtype, size_t* bytes) 
   return QLORA_OK;
 }
 
-int qlora_bwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
-                    const void* dy, const float* t_saved, void* dx, float* dA,
-                    float* dB, void* ws, size_t ws_bytes, void* stream,
-                    int repeats, void* ev_start, void* ev_stop) {
+int qlora_bwd_partial_timed(const qlora_linear* L, int M, int dtype, const void* x,
+                            const void* dy, const float* t_saved, void* dx, void* ws,
+                            size_t ws_bytes, void* stream, int repeats, void* ev_start,
+                            void* ev_stop) {
   int st = check_linear(L, M, dtype);
   if (st) return st;
   if (repeats < 1) return QLORA_EINVAL;
-  if (!x || !dy || !dA || !dB) return QLORA_EINVAL;
-  if (!aligned16(x) || !aligned16(dy) || !aligned16(dA) || !aligned16(dB)) return QLORA_EINVAL;
+  if (!x || !dy) return QLORA_EINVAL;
+  if (!aligned16(x) || !aligned16(dy)) return QLORA_EINVAL;
   if ((t_saved && !aligned16(t_saved)) || (dx && !aligned16(dx))) return QLORA_EINVAL;
+  st = bwd_check_ws(L, M, dtype, ws, ws_bytes);
+  if (st) return st;
   const BwdLayout w = bwd_layout(L, M, dtype);
-  if (ws_bytes < w.total || !ws || !aligned16(ws)) return QLORA_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float sc = lora_s(L);
   float* u = reinterpret_cast<float*>(at(ws, w.u));
@@ -249,18 +265,14 @@ int qlora_bwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
                        static_cast<const uint16_t*>(x), L->r, sc,
                        static_cast<uint16_t*>(dx), partA, partB, s);
     mark(ev_stop, s);
-    SkinnyJobs sk{};
-    const int bm = bwd_row_block(w8 ? 0 : 1, M, L->K, L->r);
-    sk.njobs = 2; sk.M = M; sk.r = L->r; sk.s = sc;
-    sk.nsplit = (M + bm - 1) / bm;
-    sk.partial[0] = partB; sk.C[0] = L->N; sk.out[0] = dB; sk.transpose[0] = 0;
-    sk.partial[1] = partA; sk.C[1] = L->K; sk.out[1] = dA; sk.transpose[1] = 1;
-    launch_skinny_stage2(sk, s);
     return launch_status();
   }
   launch_bwd_rows(dtype, dy, M, L->N, L->B, L->r, nullptr, nullptr, u, s);
-  const SkinnyJobs sk = make_adapter_grad_jobs(M, L->r, sc, t, dy, L->N, dB, partB,
-                                               u, x, L->K, dA, partA);
+  SkinnyJobs sk = make_adapter_grad_jobs(M, L->r, sc, t, dy, L->N, nullptr, partB,
+                                         u, x, L->K, nullptr, partA);
+  sk.nsplit = bwd_splits(L, M);
+  sk.rows_per_split = (M + sk.nsplit - 1) / sk.nsplit;
+  sk.rows_per_split = (sk.rows_per_split + 3) / 4 * 4;
   // float32 compute (int8 weights): the adapter-gradient stage 1, then the
   // float32 input gradient; or no input gradient at all
   launch_skinny_stage1(dtype, sk, s);
@@ -272,8 +284,48 @@ int qlora_bwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
                          static_cast<const float*>(L->scales), u, L->A, L->r,
                          sc, static_cast<float*>(dx), s);
   mark(ev_stop, s);
-  launch_skinny_stage2(sk, s);
   return launch_status();
+}
+
+int qlora_bwd_partial(const qlora_linear* L, int M, int dtype, const void* x,
+                      const void* dy, const float* t_saved, void* dx, void* ws,
+                      size_t ws_bytes, void* stream) {
+  return qlora_bwd_partial_timed(L, M, dtype, x, dy, t_saved, dx, ws, ws_bytes, stream,
+                                 1, nullptr, nullptr);
+}
+
+int qlora_bwd_finish(const qlora_linear* L, int M, int dtype, float* dA, float* dB,
+                     void* ws, size_t ws_bytes, void* stream) {
+  int st = check_linear(L, M, dtype);
+  if (st) return st;
+  if (!dA || !dB || !aligned16(dA) || !aligned16(dB)) return QLORA_EINVAL;
+  st = bwd_check_ws(L, M, dtype, ws, ws_bytes);
+  if (st) return st;
+  const BwdLayout w = bwd_layout(L, M, dtype);
+  (void)hipGetLastError();
+  SkinnyJobs sk{};
+  sk.njobs = 2; sk.M = M; sk.r = L->r; sk.s = lora_s(L);
+  sk.nsplit = bwd_splits(L, M);
+  sk.partial[0] = reinterpret_cast<float*>(at(ws, w.pB)); sk.C[0] = L->N;
+  sk.out[0] = dB; sk.transpose[0] = 0;
+  sk.partial[1] = reinterpret_cast<float*>(at(ws, w.pA)); sk.C[1] = L->K;
+  sk.out[1] = dA; sk.transpose[1] = 1;
+  launch_skinny_stage2(sk, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int qlora_bwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
+                    const void* dy, const float* t_saved, void* dx, float* dA,
+                    float* dB, void* ws, size_t ws_bytes, void* stream,
+                    int repeats, void* ev_start, void* ev_stop) {
+  // both halves are validated before either is enqueued
+  int st = check_linear(L, M, dtype);
+  if (st) return st;
+  if (!dA || !dB || !aligned16(dA) || !aligned16(dB)) return QLORA_EINVAL;
+  st = qlora_bwd_partial_timed(L, M, dtype, x, dy, t_saved, dx, ws, ws_bytes, stream,
+                               repeats, ev_start, ev_stop);
+  if (st) return st;
+  return qlora_bwd_finish(L, M, dtype, dA, dB, ws, ws_bytes, stream);
 }
 
 int qlora_bwd(const qlora_linear* L, int M, int dtype, const void* x,

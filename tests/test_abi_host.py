@@ -163,6 +163,19 @@ def test_calls_fail_before_launch(lib):
                                need, None, 0, None, None) == Q.QLORA_EINVAL
     assert lib.qlora_bwd_timed(ctypes.byref(lin), 64, Q.QLORA_BF16, FAKE, FAKE, None, FAKE,
                                FAKE, FAKE, FAKE, n.value, None, 0, None, None) == Q.QLORA_EINVAL
+    # the two halves of the backward validate their own arguments
+    assert lib.qlora_bwd_partial(ctypes.byref(lin), 64, Q.QLORA_BF16, None, FAKE, None, FAKE,
+                                 FAKE, n.value, None) == Q.QLORA_EINVAL
+    assert lib.qlora_bwd_partial(ctypes.byref(lin), 64, Q.QLORA_BF16, FAKE, FAKE, None, FAKE,
+                                 FAKE, n.value - 1, None) == Q.QLORA_EWORKSPACE
+    assert lib.qlora_bwd_finish(ctypes.byref(lin), 64, Q.QLORA_BF16, None, FAKE, FAKE,
+                                n.value, None) == Q.QLORA_EINVAL
+    assert lib.qlora_bwd_finish(ctypes.byref(lin), 64, Q.QLORA_BF16, FAKE, FAKE + 2, FAKE,
+                                n.value, None) == Q.QLORA_EINVAL
+    assert lib.qlora_bwd_finish(ctypes.byref(lin), 64, Q.QLORA_BF16, FAKE, FAKE, FAKE,
+                                n.value - 1, None) == Q.QLORA_EWORKSPACE
+    assert lib.qlora_bwd_finish(ctypes.byref(lin), 0, Q.QLORA_BF16, FAKE, FAKE, FAKE,
+                                n.value, None) == Q.QLORA_EINVAL
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

@@ -314,6 +314,44 @@ def test_timed_repeats_are_identical():
                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
 
 
+def _bits(a):
+    return a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32)
+
+
+SPLIT = [
+    (1, None, True),                      # float32 path (row pass, stage 1, float32 dx)
+    ((2, 257, 1024, 1040, 8), None, True),  # 64-row tiles, ragged rows
+    ((2, 256, 1024, 1024, 8), None, False),  # no input gradient
+    (3, 0, True),                         # 128 x 128 tiles (gpt2 qkv, full size)
+    ((5, 512, 1024, 512, 4), None, True),  # 4-bit, 64-row tiles
+    (5, 0, True),                         # 4-bit, 128 x 128 tiles (full size)
+]
+
+
+@pytest.mark.parametrize("spec,layer,need_dx", SPLIT)
+def test_split_backward_matches_one_call(spec, layer, need_dx):
+    """qlora_bwd_partial on one stream and qlora_bwd_finish on another give
+    qlora_bwd's results bit for bit."""
+    w = WL.small(*spec) if isinstance(spec, tuple) else WL.WORKLOADS[spec]
+    case = Case(w, layer or 0)
+    say(f"split backward: {w.name} M={case.M} K,N={case.K},{case.N} r={w.r} {w.dtype} {w.wfmt} dx={need_dx}")
+    _, t = Q.qlora_fwd(case.lin, case.x_t)
+    dx1, dA1, dB1 = Q.qlora_bwd(case.lin, case.x_t, case.dy_t, t=t, need_dx=need_dx)
+    side = torch.cuda.Stream()
+    dx2, ws = Q.qlora_bwd_partial(case.lin, case.x_t, case.dy_t, t=t, need_dx=need_dx)
+    side.wait_stream(torch.cuda.current_stream())
+    dA2, dB2 = Q.qlora_bwd_finish(case.lin, case.M, case.x_t.dtype, ws, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert (dx2 is None) == (not need_dx)
+    if need_dx:
+        assert torch.equal(_bits(dx1), _bits(dx2)), "dx differs"
+    assert torch.equal(_bits(dA1), _bits(dA2)), "dA differs"
+    assert torch.equal(_bits(dB1), _bits(dB2)), "dB differs"
+    # and both agree with the oracle
+    check_bwd(case, t, need_dx=need_dx)
+
+
 def test_mlp_stack_all_layers():
     """The 32-layer MLP workload exactly as the benchmark runs it: forward
     0..31, then backward 31..0, one stream, per-layer parity."""
