@@ -44,7 +44,10 @@ Readings taken where the pages are silent (each listed in the design doc):
   f16(absmax / 7), codes = round-half-even(w * (1 / scale)) in [-7, 7] against
   the stored scale, two's-complement nibbles packed along K with the even k in
   the low nibble; the forward multiplies the (unquantized) activations by the
-  dequantized weight.
+  dequantized weight;
+* 4-bit integer forward (the alternative): activations quantized per row as
+  above, exact int8 x int4 sums per 128-wide group, each weighted by its fp16
+  scale, the total by the row scale; adapter term as in the float forward.
 
 Layouts: W [K, N] float32 (the pages' kernel orientation); int8 codes [N, K]
 (one output channel per row, K contiguous) with scales [N]; 4-bit codes
@@ -313,6 +316,50 @@ def fwd_w4_f64(x, packed, scales, A, B, alpha: float):
 
 def fwd_w4(x, packed, scales, A, B, alpha: float, dtype: str):
     y, t = fwd_w4_f64(x, packed, scales, A, B, alpha)
+    return round_to(y, dtype), round_f32(t)
+
+
+# ---------------------------------------------------------------------------
+# Integer forward of the 4-bit layer with int8 activations: an alternative to
+# the dequantized float product above. The activations are quantized per row
+# with the int8 rule; each 128-wide group of the contraction is an exact
+# integer sum of int8 x int4 products, and each group's sum is weighted by
+# its fp16 scale. ([llm-light] "Simplified Int4Variable quantization": two
+# int4 codes per byte; [4-bit issue]: narrow frozen weights under a float
+# adapter and the arithmetic intensity they buy; [QLoRA-like] Highlights: the
+# int8 x int8 integer product the int8 path already uses.)
+# ---------------------------------------------------------------------------
+
+
+def int4_group_acc(xq, packed) -> np.ndarray:
+    """acc[g, m, n] = sum over k in group g of xq[m, k] * q[n, k], int64, exact."""
+    q = unpack_nibbles(packed).astype(np.int64)          # [N, K]
+    xq = np.asarray(xq).astype(np.int64)                 # [M, K]
+    N, K = q.shape
+    G = K // GROUP
+    acc = np.empty((G, xq.shape[0], N), np.int64)
+    for g in range(G):
+        ks = slice(g * GROUP, (g + 1) * GROUP)
+        acc[g] = xq[:, ks] @ q[:, ks].T
+    return acc
+
+
+def fwd_a8w4_f64(x, packed, scales, A, B, alpha: float):
+    """Unrounded integer 4-bit forward. Returns (y64, t64, xq, sx):
+    y[m, n] = sx[m] * sum_g sc[n, g] acc[g, m, n] + s sum_j t[m, j] B[j, n]."""
+    x32 = np.asarray(x, F32)
+    xq, sx = quantize_rows(x32)
+    acc = int4_group_acc(xq, packed).astype(F64)          # exact in float64
+    sc = np.asarray(scales, dtype=np.float16).astype(F64)  # [N, G]
+    base = np.einsum("gmn,ng->mn", acc, sc)
+    t = lora_down(x32.astype(F64), A)
+    s = lora_scale(alpha, np.asarray(A).shape[1])
+    y = sx.astype(F64)[:, None] * base + s * (t @ np.asarray(B, F64))
+    return y, t, xq, sx
+
+
+def fwd_a8w4(x, packed, scales, A, B, alpha: float, dtype: str):
+    y, t, _, _ = fwd_a8w4_f64(x, packed, scales, A, B, alpha)
     return round_to(y, dtype), round_f32(t)
 
 
