@@ -144,6 +144,31 @@ def main():
         torch.cuda.synchronize()
         merge_ms = e0.elapsed_time(e1)
 
+    # 4-bit layers: the forward alone per step, with the dequantized bf16
+    # product (what the step uses) and with the integer int8 x int4 product
+    fwd_ms = fwd_a8w4_ms = None
+    if w.wfmt == "w4g128":
+        st0 = torch.cuda.current_stream().cuda_stream
+
+        def fwd_all(fn):
+            for l in layers:
+                check(fn(ctypes.byref(l.cs), M, l.dt, l.x.data_ptr(), l.y.data_ptr(),
+                         l.t.data_ptr(), wsp, ws_bytes, st0), "fwd")
+
+        for fn_name in ("qlora_fwd", "qlora_fwd_a8w4"):
+            fn = getattr(lib, fn_name)
+            fwd_all(fn)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(20):
+                fwd_all(fn)
+            e1.record()
+            torch.cuda.synchronize()
+            if fn_name == "qlora_fwd":
+                fwd_ms = e0.elapsed_time(e1) / 20
+            else:
+                fwd_a8w4_ms = e0.elapsed_time(e1) / 20
+
     def step(ev_b=None, repeats=1):
         st = torch.cuda.current_stream().cuda_stream
         for i, l in enumerate(layers):
@@ -234,6 +259,8 @@ def main():
         "eager_ms_per_step": round(eager_ms, 5),
         "quantize_ms": round(quantize_ms, 4),
         "merge_ms": None if merge_ms is None else round(merge_ms, 4),
+        "fwd_ms": None if fwd_ms is None else round(fwd_ms, 4),
+        "fwd_a8w4_ms": None if fwd_a8w4_ms is None else round(fwd_a8w4_ms, 4),
         "roofline": roof,
         "cpu_baseline": cpu,
     }

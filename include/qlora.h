@@ -131,6 +131,23 @@ int qlora_fwd_workspace(const qlora_linear* L, int M, int dtype,
 int qlora_fwd(const qlora_linear* L, int M, int dtype, const void* x, void* y,
               float* t_save, void* ws, size_t ws_bytes, void* stream);
 
+/* Integer forward of a QLORA_W4G128 layer with int8 activations, the
+ * alternative to qlora_fwd's dequantized bf16 product ("Simplified
+ * Int4Variable quantization": two 4-bit codes per byte; "How to fine-tune the
+ * 4-bit model?": narrow weights raise the arithmetic intensity). x is
+ * quantized per row exactly as for QLORA_W8 layers (xq, sx); then
+ *   y[m, n] = sx[m] sum_g sc[n, g] (sum_{k in group g} xq[m, k] q[n, k])
+ *             + s (t B)[m, n],
+ * each group's sum an exact int32, the weighting and the sum over groups in
+ * float32, y rounded once to bf16. t_save as for qlora_fwd. The workspace is
+ * qlora_fwd_workspace's. QLORA_W8 layers -> QLORA_EUNSUPPORTED (their
+ * qlora_fwd already is the integer product); bf16 activations only. The
+ * backward is qlora_bwd's (the activation quantizer is passed straight
+ * through). */
+int qlora_fwd_a8w4(const qlora_linear* L, int M, int dtype, const void* x,
+                   void* y, float* t_save, void* ws, size_t ws_bytes,
+                   void* stream);
+
 /* Workspace needed by qlora_bwd for M rows. */
 int qlora_bwd_workspace(const qlora_linear* L, int M, int dtype,
                         size_t* bytes);

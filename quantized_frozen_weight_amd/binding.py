@@ -51,7 +51,7 @@ EXPORTS = (
     "qlora_status_str", "qlora_weight_bytes", "qlora_quantize",
     "qlora_fwd_workspace", "qlora_fwd", "qlora_bwd_workspace", "qlora_bwd",
     "qlora_quantize_rows", "qlora_fwd_acc", "qlora_fwd_timed", "qlora_bwd_timed",
-    "qlora_merge", "qlora_bwd_partial", "qlora_bwd_finish",
+    "qlora_merge", "qlora_bwd_partial", "qlora_bwd_finish", "qlora_fwd_a8w4",
 )
 
 
@@ -83,6 +83,7 @@ def lib() -> ctypes.CDLL:
     L.qlora_merge.argtypes = [plin, vp, vp, vp]
     L.qlora_bwd_partial.argtypes = [plin, i, i, vp, vp, vp, vp, vp, sz, vp]
     L.qlora_bwd_finish.argtypes = [plin, i, i, vp, vp, vp, sz, vp]
+    L.qlora_fwd_a8w4.argtypes = [plin, i, i, vp, vp, vp, vp, sz, vp]
     for name in EXPORTS[1:]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -211,6 +212,24 @@ def qlora_fwd(layer: QLinear, x, save_t: bool = True, y=None, t=None, ws=None):
     _check(lib().qlora_fwd(ctypes.byref(s), M, dt, _ptr(x), _ptr(y),
                            _ptr(t) if save_t else None, _ptr(ws),
                            ws.numel() * ws.element_size(), _stream()), "qlora_fwd")
+    return y, (t if save_t else None)
+
+
+def qlora_fwd_a8w4(layer: QLinear, x, save_t: bool = True, y=None, t=None, ws=None):
+    """Integer forward of a 4-bit layer with int8 activations: (y, t or None)."""
+    import torch
+    M = x.shape[0]
+    dt = _dtype_code(x)
+    if y is None:
+        y = torch.empty((M, layer.N), dtype=x.dtype, device=x.device)
+    if save_t and t is None:
+        t = torch.empty((M, layer.r), dtype=torch.float32, device=x.device)
+    ws = _workspace(qlora_fwd_workspace(layer, M, dt), x.device, ws)
+    s = layer.cstruct()
+    _check(lib().qlora_fwd_a8w4(ctypes.byref(s), M, dt, _ptr(x), _ptr(y),
+                                _ptr(t) if save_t else None, _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream()),
+           "qlora_fwd_a8w4")
     return y, (t if save_t else None)
 
 

@@ -61,10 +61,10 @@ struct FwdLayout {
 FwdLayout fwd_layout(const qlora_linear* L, int M) {
   FwdLayout w{};
   size_t off = 0;
-  if (L->fmt == QLORA_W8) {
-    w.xq = off; off = align_up(off + (size_t)M * L->K);
-    w.sx = off; off = align_up(off + (size_t)M * 4);
-  }
+  // activation codes and scales: the int8 product, and the integer forward
+  // of 4-bit layers
+  w.xq = off; off = align_up(off + (size_t)M * L->K);
+  w.sx = off; off = align_up(off + (size_t)M * 4);
   w.t = off; off = align_up(off + (size_t)M * L->r * 4);
   w.total = off;
   return w;
@@ -220,6 +220,27 @@ int qlora_fwd(const qlora_linear* L, int M, int dtype, const void* x, void* y,
               float* t_save, void* ws, size_t ws_bytes, void* stream) {
   return qlora_fwd_timed(L, M, dtype, x, y, t_save, ws, ws_bytes, stream, 1,
                          nullptr, nullptr);
+}
+
+int qlora_fwd_a8w4(const qlora_linear* L, int M, int dtype, const void* x, void* y,
+                   float* t_save, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_linear(L, M, dtype);
+  if (st) return st;
+  if (L->fmt != QLORA_W4G128) return QLORA_EUNSUPPORTED;
+  if (!x || !y || !aligned16(x) || !aligned16(y)) return QLORA_EINVAL;
+  if (t_save && !aligned16(t_save)) return QLORA_EINVAL;
+  const FwdLayout w = fwd_layout(L, M);
+  if (ws_bytes < w.total || !ws || !aligned16(ws)) return QLORA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* t = t_save ? t_save : reinterpret_cast<float*>(at(ws, w.t));
+  int8_t* xq = reinterpret_cast<int8_t*>(at(ws, w.xq));
+  float* sx = reinterpret_cast<float*>(at(ws, w.sx));
+  (void)hipGetLastError();
+  launch_rowquant(dtype, x, M, L->K, L->A, L->r, xq, sx, t, s);
+  launch_gemm_fwd_a8w4(M, L->N, L->K, xq, sx, static_cast<const uint8_t*>(L->codes),
+                       static_cast<const _Float16*>(L->scales), t, L->B, L->r, lora_s(L),
+                       static_cast<uint16_t*>(y), s);
+  return launch_status();
 }
 
 int qlora_bwd_workspace(const qlora_linear* L, int M, int dtype, size_t* bytes) {

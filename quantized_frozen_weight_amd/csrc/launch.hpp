@@ -36,6 +36,12 @@ void launch_gemm_fwd_w8(int dtype, int M, int N, int K, const int8_t* xq,
 constexpr int kW4MaxGroups = 128;
 
 // y = x deq4(W) + s * t B   (bf16 x and y)
+// 4-bit weights with int8 activations: exact int8 x int4 sums per 128-wide
+// group, weighted by the group's fp16 scale, times sx[m], plus s t B (bf16 y)
+void launch_gemm_fwd_a8w4(int M, int N, int K, const int8_t* xq, const float* sx,
+                          const uint8_t* packed, const _Float16* scales,
+                          const float* t, const float* B, int r, float s,
+                          uint16_t* y, hipStream_t st);
 void launch_gemm_fwd_w4(int M, int N, int K, const uint16_t* x,
                         const uint8_t* packed, const _Float16* scales,
                         const float* t, const float* B, int r, float s,

@@ -91,9 +91,9 @@ template <int BM, int BN, int R, bool SCALED> struct EpiOps {
   float t[NT], q[NQ], rs, cs;
 
   // P float32 [M, r]; Q(j, n) = Q[j * ldj + n * ldn]; rsrc [M] / csrc [N]
-  // read when SCALED. Nothing here consumes the loaded values: a use would
-  // make the wave wait for these loads before the main loop starts. The
-  // masks are applied by store().
+  // read when SCALED (csrc NULL: column scale 1). Nothing here consumes the
+  // loaded values: a use would make the wave wait for these loads before the
+  // main loop starts. The masks are applied by store().
   __device__ __forceinline__ void load(int M, int N, int m0, int n0, int r,
                                        const float* __restrict__ P,
                                        const float* __restrict__ Q, long ldj, long ldn,
@@ -115,7 +115,7 @@ template <int BM, int BN, int R, bool SCALED> struct EpiOps {
     if constexpr (SCALED) {
       const int im = m0 + (tid < BM ? tid : BM - 1), in = n0 + (tid < BN ? tid : BN - 1);
       rs = rsrc[im < M ? im : M - 1];
-      cs = csrc[in < N ? in : N - 1];
+      cs = csrc != nullptr ? csrc[in < N ? in : N - 1] : 1.f;   // no column scale: 1
     }
   }
 

@@ -163,6 +163,17 @@ def test_calls_fail_before_launch(lib):
                                need, None, 0, None, None) == Q.QLORA_EINVAL
     assert lib.qlora_bwd_timed(ctypes.byref(lin), 64, Q.QLORA_BF16, FAKE, FAKE, None, FAKE,
                                FAKE, FAKE, FAKE, n.value, None, 0, None, None) == Q.QLORA_EINVAL
+    # the integer 4-bit forward: 4-bit layers only
+    assert lib.qlora_fwd_a8w4(ctypes.byref(lin), 64, Q.QLORA_BF16, FAKE, FAKE, None, FAKE,
+                              need, None) == Q.QLORA_EUNSUPPORTED
+    lin4 = _lin(fmt=Q.QLORA_W4G128)
+    st4, need4 = _fwd_ws(lib, lin4)
+    assert lib.qlora_fwd_a8w4(ctypes.byref(lin4), 64, Q.QLORA_BF16, FAKE, FAKE, None, FAKE,
+                              need4 - 1, None) == Q.QLORA_EWORKSPACE
+    assert lib.qlora_fwd_a8w4(ctypes.byref(lin4), 64, Q.QLORA_F32, FAKE, FAKE, None, FAKE,
+                              need4, None) == Q.QLORA_EUNSUPPORTED
+    assert lib.qlora_fwd_a8w4(ctypes.byref(lin4), 64, Q.QLORA_BF16, None, FAKE, None, FAKE,
+                              need4, None) == Q.QLORA_EINVAL
     # the two halves of the backward validate their own arguments
     assert lib.qlora_bwd_partial(ctypes.byref(lin), 64, Q.QLORA_BF16, None, FAKE, None, FAKE,
                                  FAKE, n.value, None) == Q.QLORA_EINVAL

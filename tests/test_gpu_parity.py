@@ -352,6 +352,51 @@ def test_split_backward_matches_one_call(spec, layer, need_dx):
     check_bwd(case, t, need_dx=need_dx)
 
 
+A8W4 = [
+    (5, 0),                          # the 4096 x 4096 layer, 2048 rows (128 x 128 tiles)
+    ((5, 257, 384, 272, 3), 0),      # ragged rows and columns, 64-row tiles
+    ((5, 64, 128, 16, 32), 0),       # one group, one column block, rank 32
+    ((5, 130, 2048, 400, 1), 0),     # 16 groups, rank 1
+]
+
+
+@pytest.mark.parametrize("spec,layer", A8W4)
+def test_a8w4_forward(spec, layer):
+    """Integer 4-bit forward (int8 activations) against the oracle's."""
+    w = WL.small(*spec) if isinstance(spec, tuple) else WL.WORKLOADS[spec]
+    case = Case(w, layer)
+    say(f"a8w4 forward: {w.name} M={case.M} K,N={case.K},{case.N} r={w.r}")
+    y, t = Q.qlora_fwd_a8w4(case.lin, case.x_t)
+    torch.cuda.synchronize()
+    p, sc, _ = case.oracle_weights()
+    oy, ot = O.fwd_a8w4(case.x, p, sc, case.A, case.B, w.alpha, w.dtype)
+    assert_close(to_numpy(y), oy, RTOL[w.dtype], "y")
+    assert_close(to_numpy(t), ot, RTOL[w.dtype], "t")
+
+
+@pytest.mark.parametrize("M,N", [(64, 144), (2048, 2048)])
+def test_a8w4_exact_on_the_integer_grid(M, N):
+    """Integer activation rows whose abs-max is 127 (row scale 1), weights
+    q / 8 with a 7 in every group (scale 1/8), B = 0: every step is exact in
+    float32, so y must be the oracle's bf16 rounding bit for bit."""
+    K = 384
+    rng = np.random.default_rng(7)
+    q = rng.integers(-7, 8, (K, N))
+    q[::128, :] = 7
+    W = (q / 8.0).astype(np.float32)
+    x = rng.integers(-127, 128, (M, K)).astype(np.float32)
+    x[:, 0] = 127.0
+    w = WL.small(5, M, K, N, 4)
+    say(f"a8w4 exact grid: M={M} K={K} N={N}")
+    case = Case(w, 0, W=W, x32=x, zero_B=True)
+    y, _ = Q.qlora_fwd_a8w4(case.lin, case.x_t)
+    torch.cuda.synchronize()
+    p, sc, _ = case.oracle_weights()
+    assert np.all(sc.astype(np.float32) == 0.125)
+    oy, _ = O.fwd_a8w4(case.x, p, sc, case.A, case.B, w.alpha, w.dtype)
+    assert same_bits_f32(to_numpy(y), oy), "y differs from the exact result"
+
+
 def test_mlp_stack_all_layers():
     """The 32-layer MLP workload exactly as the benchmark runs it: forward
     0..31, then backward 31..0, one stream, per-layer parity."""
