@@ -45,6 +45,8 @@ Readings taken where the pages are silent (each listed in the design doc):
   the stored scale, two's-complement nibbles packed along K with the even k in
   the low nibble; the forward multiplies the (unquantized) activations by the
   dequantized weight;
+* multi-head layers: output n = head * hd + d; W [heads, K, hd] and B, dB
+  [heads, r, hd] are the plain [K, N] and [r, N] arrays with that column map;
 * 4-bit integer forward (the alternative): activations quantized per row as
   above, exact int8 x int4 sums per 128-wide group, each weighted by its fp16
   scale, the total by the row scale; adapter term as in the float forward.
@@ -317,6 +319,29 @@ def fwd_w4_f64(x, packed, scales, A, B, alpha: float):
 def fwd_w4(x, packed, scales, A, B, alpha: float, dtype: str):
     y, t = fwd_w4_f64(x, packed, scales, A, B, alpha)
     return round_to(y, dtype), round_f32(t)
+
+
+# ---------------------------------------------------------------------------
+# Multi-head layouts ([GPT-2 LoRA] "Create LoRA layer": the attention
+# projections are EinsumDense layers whose output is [heads, head_dim], and
+# the adapter's B keeps that per-head output shape; [QLoRA-like] Highlights:
+# frozen int8 EinsumDense kernels). Output n of the layer is head n // hd,
+# position n % hd; the layer itself is the plain one on the mapped tensors.
+# ---------------------------------------------------------------------------
+
+
+def heads_to_plain(T) -> np.ndarray:
+    """[heads, rows, hd] -> [rows, heads * hd] (column n = head * hd + d)."""
+    T = np.asarray(T)
+    H, rows, hd = T.shape
+    return np.transpose(T, (1, 0, 2)).reshape(rows, H * hd)
+
+
+def plain_to_heads(T, heads: int) -> np.ndarray:
+    """[rows, N] -> [heads, rows, N / heads]; inverse of heads_to_plain."""
+    T = np.asarray(T)
+    rows, N = T.shape
+    return np.ascontiguousarray(np.transpose(T.reshape(rows, heads, N // heads), (1, 0, 2)))
 
 
 # ---------------------------------------------------------------------------
