@@ -44,6 +44,16 @@
  *   x, dx  [M, K] in the compute dtype;  y, dy  [M, N] in the compute dtype
  *   A, dA  float32 [K, r];               B, dB  float32 [r, N]
  *   t      float32 [M, r]  (t = x A, unscaled; saved by the forward)
+ *   Multi-head layers ("Parameter-efficient fine-tuning of GPT-2 with LoRA",
+ *   "Create LoRA layer": the attention projections are EinsumDense layers and
+ *   the adapter's B keeps their per-head output shape; "Introduce QLoRA-like
+ *   technique": frozen int8 EinsumDense kernels): with heads > 1 the N
+ *   outputs are heads x hd (n = head * hd + d, hd = N / heads) and
+ *     W      float32 [heads, K, hd]       (input to qlora_quantize_heads)
+ *     B, dB  float32 [heads, r, hd]
+ *   while codes, scales, A, dA, x, y, dx and dy keep the layouts above. A
+ *   projection whose heads are on the input side ([heads, hd, N] kernels) is
+ *   a plain layer with K = heads * hd.
  *
  * Conventions shared by every entry point:
  *   - The library never allocates, frees or synchronizes. Work is enqueued on
@@ -99,7 +109,9 @@ typedef struct {
   const void* codes;      /* see "Layouts" */
   const void* scales;     /* see "Layouts" */
   const float* A;         /* [K, r] */
-  const float* B;         /* [r, N] */
+  const float* B;         /* [r, N], or [heads, r, N / heads] */
+  int32_t heads;          /* 0 or 1: one head; else N / heads must be a
+                             multiple of 64 (EUNSUPPORTED otherwise) */
 } qlora_linear;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -119,6 +131,13 @@ int qlora_weight_bytes(int K, int N, int fmt, size_t* codes_bytes,
  * the NaN reaches every output that uses it. W is only read. */
 int qlora_quantize(const float* W, int K, int N, int fmt, void* codes,
                    void* scales, void* stream);
+
+/* qlora_quantize for a multi-head weight W [heads, K, N / heads] (see
+ * Layouts): the same codes and scales as qlora_quantize of the equivalent
+ * [K, N] matrix. heads must divide N and N / heads be a multiple of 64
+ * (EINVAL / EUNSUPPORTED otherwise); heads = 1 is qlora_quantize. */
+int qlora_quantize_heads(const float* W, int heads, int K, int N, int fmt,
+                         void* codes, void* scales, void* stream);
 
 /* Workspace needed by qlora_fwd / qlora_fwd_acc for M rows. */
 int qlora_fwd_workspace(const qlora_linear* L, int M, int dtype,

@@ -42,6 +42,7 @@ class qlora_linear(ctypes.Structure):
         ("scales", ctypes.c_void_p),
         ("A", ctypes.c_void_p),
         ("B", ctypes.c_void_p),
+        ("heads", ctypes.c_int32),
     ]
 
 
@@ -52,6 +53,7 @@ EXPORTS = (
     "qlora_fwd_workspace", "qlora_fwd", "qlora_bwd_workspace", "qlora_bwd",
     "qlora_quantize_rows", "qlora_fwd_acc", "qlora_fwd_timed", "qlora_bwd_timed",
     "qlora_merge", "qlora_bwd_partial", "qlora_bwd_finish", "qlora_fwd_a8w4",
+    "qlora_quantize_heads",
 )
 
 
@@ -84,6 +86,7 @@ def lib() -> ctypes.CDLL:
     L.qlora_bwd_partial.argtypes = [plin, i, i, vp, vp, vp, vp, vp, sz, vp]
     L.qlora_bwd_finish.argtypes = [plin, i, i, vp, vp, vp, sz, vp]
     L.qlora_fwd_a8w4.argtypes = [plin, i, i, vp, vp, vp, vp, sz, vp]
+    L.qlora_quantize_heads.argtypes = [vp, i, i, i, i, vp, vp, vp]
     for name in EXPORTS[1:]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -135,18 +138,31 @@ class QLinear:
     codes: object     # int8 [N, K]  or uint8 [N, K/2]
     scales: object    # float32 [N] or float16 [N, K/128]
     A: object         # float32 [K, r]
-    B: object         # float32 [r, N]
+    B: object         # float32 [r, N], or [heads, r, N / heads]
+    heads: int = 1
 
     def cstruct(self) -> qlora_linear:
         return qlora_linear(self.K, self.N, self.r, float(self.alpha), _FMT[self.fmt],
                             _ptr(self.codes), _ptr(self.scales), _ptr(self.A),
-                            _ptr(self.B))
+                            _ptr(self.B), int(self.heads))
+
+
+def _b_shape(layer: QLinear):
+    """Shape of B and dB: [r, N], or [heads, r, N / heads]."""
+    if layer.heads > 1:
+        return (layer.heads, layer.r, layer.N // layer.heads)
+    return (layer.r, layer.N)
 
 
 def qlora_quantize(W, fmt: str = "w8"):
-    """W float32 [K, N] on the GPU -> (codes, scales) in the library's layout."""
+    """W float32 [K, N], or per head [heads, K, hd] (N = heads * hd), on the
+    GPU -> (codes, scales) in the library's layout."""
     import torch
-    K, N = W.shape
+    if W.dim() == 3:
+        heads, K, hd = W.shape
+        N = heads * hd
+    else:
+        heads, (K, N) = 1, W.shape
     cb, sb = qlora_weight_bytes(K, N, fmt)
     if fmt == "w8":
         codes = torch.empty((N, K), dtype=torch.int8, device=W.device)
@@ -157,8 +173,8 @@ def qlora_quantize(W, fmt: str = "w8"):
     assert codes.numel() * codes.element_size() == cb
     assert scales.numel() * scales.element_size() == sb
     W = W.contiguous()
-    _check(lib().qlora_quantize(_ptr(W), K, N, _FMT[fmt], _ptr(codes), _ptr(scales),
-                                _stream()), "qlora_quantize")
+    _check(lib().qlora_quantize_heads(_ptr(W), heads, K, N, _FMT[fmt], _ptr(codes),
+                                      _ptr(scales), _stream()), "qlora_quantize_heads")
     return codes, scales
 
 
@@ -244,7 +260,7 @@ def qlora_bwd(layer: QLinear, x, dy, t=None, need_dx: bool = True, dx=None,
     if dA is None:
         dA = torch.empty((layer.K, layer.r), dtype=torch.float32, device=x.device)
     if dB is None:
-        dB = torch.empty((layer.r, layer.N), dtype=torch.float32, device=x.device)
+        dB = torch.empty(_b_shape(layer), dtype=torch.float32, device=x.device)
     nbytes = qlora_bwd_workspace(layer, M, dt)
     ws = _workspace(nbytes, x.device, ws)
     s = layer.cstruct()
@@ -282,7 +298,7 @@ def qlora_bwd_finish(layer: QLinear, M: int, dtype, ws, dA=None, dB=None, stream
     if dA is None:
         dA = torch.empty((layer.K, layer.r), dtype=torch.float32, device=ws.device)
     if dB is None:
-        dB = torch.empty((layer.r, layer.N), dtype=torch.float32, device=ws.device)
+        dB = torch.empty(_b_shape(layer), dtype=torch.float32, device=ws.device)
     s = layer.cstruct()
     _check(lib().qlora_bwd_finish(ctypes.byref(s), M, dt, _ptr(dA), _ptr(dB), _ptr(ws),
                                   ws.numel() * ws.element_size(),

@@ -45,10 +45,17 @@ int check_linear(const qlora_linear* L, int M, int dtype) {
     if (dtype != QLORA_BF16) return QLORA_EUNSUPPORTED;
     if (L->K > 128 * kW4MaxGroups) return QLORA_EUNSUPPORTED;
   }
+  if (L->heads < 0 || (L->heads > 1 && L->N % L->heads)) return QLORA_EINVAL;
+  if (L->heads > 1 && (L->N / L->heads) % 64) return QLORA_EUNSUPPORTED;
   const void* ptrs[4] = {L->codes, L->scales, L->A, L->B};
   for (const void* p : ptrs)
     if (p == nullptr || !aligned16(p)) return QLORA_EINVAL;
   return QLORA_OK;
+}
+
+// Head width of B / dB (and of W at quantization): N for a one-head layer.
+inline int head_width(const qlora_linear* L) {
+  return L->heads > 1 ? L->N / L->heads : L->N;
 }
 
 inline float lora_s(const qlora_linear* L) {
@@ -155,18 +162,26 @@ int qlora_weight_bytes(int K, int N, int fmt, size_t* codes_bytes,
 
 int qlora_quantize(const float* W, int K, int N, int fmt, void* codes,
                    void* scales, void* stream) {
+  return qlora_quantize_heads(W, 1, K, N, fmt, codes, scales, stream);
+}
+
+int qlora_quantize_heads(const float* W, int heads, int K, int N, int fmt,
+                         void* codes, void* scales, void* stream) {
   size_t cb, sb;
   int st = qlora_weight_bytes(K, N, fmt, &cb, &sb);
   if (st) return st;
+  if (heads < 1 || N % heads) return QLORA_EINVAL;
+  if (heads > 1 && (N / heads) % 64) return QLORA_EUNSUPPORTED;
+  const int hd = N / heads;
   if (!W || !codes || !scales || !aligned16(W) || !aligned16(codes) || !aligned16(scales))
     return QLORA_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (fmt == QLORA_W8)
-    launch_quantize_w8(W, K, N, static_cast<int8_t*>(codes),
+    launch_quantize_w8(W, K, N, hd, static_cast<int8_t*>(codes),
                        static_cast<float*>(scales), s);
   else
-    launch_quantize_w4(W, K, N, static_cast<uint8_t*>(codes),
+    launch_quantize_w4(W, K, N, hd, static_cast<uint8_t*>(codes),
                        static_cast<_Float16*>(scales), s);
   return launch_status();
 }
@@ -200,7 +215,7 @@ int qlora_fwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
     for (int rep = 0; rep < repeats; ++rep)
       launch_gemm_fwd_w8(dtype, M, L->N, L->K, xq,
                          static_cast<const int8_t*>(L->codes), sx,
-                         static_cast<const float*>(L->scales), t, L->B, L->r,
+                         static_cast<const float*>(L->scales), t, L->B, head_width(L), L->r,
                          lora_s(L), y, nullptr, s);
     mark(ev_stop, s);
   } else {
@@ -209,7 +224,7 @@ int qlora_fwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
     for (int rep = 0; rep < repeats; ++rep)
       launch_gemm_fwd_w4(M, L->N, L->K, static_cast<const uint16_t*>(x),
                          static_cast<const uint8_t*>(L->codes),
-                         static_cast<const _Float16*>(L->scales), t, L->B, L->r,
+                         static_cast<const _Float16*>(L->scales), t, L->B, head_width(L), L->r,
                          lora_s(L), static_cast<uint16_t*>(y), s);
     mark(ev_stop, s);
   }
@@ -238,7 +253,7 @@ int qlora_fwd_a8w4(const qlora_linear* L, int M, int dtype, const void* x, void*
   (void)hipGetLastError();
   launch_rowquant(dtype, x, M, L->K, L->A, L->r, xq, sx, t, s);
   launch_gemm_fwd_a8w4(M, L->N, L->K, xq, sx, static_cast<const uint8_t*>(L->codes),
-                       static_cast<const _Float16*>(L->scales), t, L->B, L->r, lora_s(L),
+                       static_cast<const _Float16*>(L->scales), t, L->B, head_width(L), L->r, lora_s(L),
                        static_cast<uint16_t*>(y), s);
   return launch_status();
 }
@@ -282,13 +297,13 @@ int qlora_bwd_partial_timed(const qlora_linear* L, int M, int dtype, const void*
     mark(ev_start, s);
     for (int rep = 0; rep < repeats; ++rep)
       launch_bwd_fused(w8 ? 0 : 1, M, L->K, L->N, static_cast<const uint16_t*>(dy),
-                       L->codes, L->scales, L->B, L->A, t,
+                       L->codes, L->scales, L->B, head_width(L), L->A, t,
                        static_cast<const uint16_t*>(x), L->r, sc,
                        static_cast<uint16_t*>(dx), partA, partB, s);
     mark(ev_stop, s);
     return launch_status();
   }
-  launch_bwd_rows(dtype, dy, M, L->N, L->B, L->r, nullptr, nullptr, u, s);
+  launch_bwd_rows(dtype, dy, M, L->N, L->B, head_width(L), L->r, nullptr, nullptr, u, s);
   SkinnyJobs sk = make_adapter_grad_jobs(M, L->r, sc, t, dy, L->N, nullptr, partB,
                                          u, x, L->K, nullptr, partA);
   sk.nsplit = bwd_splits(L, M);
@@ -328,7 +343,7 @@ int qlora_bwd_finish(const qlora_linear* L, int M, int dtype, float* dA, float* 
   sk.njobs = 2; sk.M = M; sk.r = L->r; sk.s = lora_s(L);
   sk.nsplit = bwd_splits(L, M);
   sk.partial[0] = reinterpret_cast<float*>(at(ws, w.pB)); sk.C[0] = L->N;
-  sk.out[0] = dB; sk.transpose[0] = 0;
+  sk.out[0] = dB; sk.transpose[0] = 0; sk.hd0 = head_width(L);
   sk.partial[1] = reinterpret_cast<float*>(at(ws, w.pA)); sk.C[1] = L->K;
   sk.out[1] = dA; sk.transpose[1] = 1;
   launch_skinny_stage2(sk, static_cast<hipStream_t>(stream));
@@ -376,7 +391,7 @@ int qlora_merge(const qlora_linear* L, void* codes_out, void* scales_out,
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   launch_merge_w8(static_cast<const int8_t*>(L->codes), static_cast<const float*>(L->scales),
-                  L->A, L->B, L->K, L->N, L->r, lora_s(L),
+                  L->A, L->B, head_width(L), L->K, L->N, L->r, lora_s(L),
                   static_cast<int8_t*>(codes_out), static_cast<float*>(scales_out), s);
   return launch_status();
 }
@@ -410,7 +425,7 @@ int qlora_fwd_acc(const qlora_linear* L, int M, int dtype, const void* x,
   launch_rowquant(dtype, x, M, L->K, nullptr, 1, xq, sx, nullptr, s);
   launch_gemm_fwd_w8(dtype, M, L->N, L->K, xq,
                      static_cast<const int8_t*>(L->codes), sx,
-                     static_cast<const float*>(L->scales), nullptr, L->B,
+                     static_cast<const float*>(L->scales), nullptr, L->B, head_width(L),
                      L->r, 0.f, nullptr, acc, s);
   return launch_status();
 }

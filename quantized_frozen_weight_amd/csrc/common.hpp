@@ -67,6 +67,16 @@ __device__ __forceinline__ void store_out(uint16_t* p, float v) {
   *p = (uint16_t)f32_to_bf16(v);
 }
 
+// ---- multi-head layouts ---------------------------------------------------
+// Element (row, n) of an array stored [heads][rows][hd] with heads = N / hd,
+// n = head * hd + d ("Parameter-efficient fine-tuning of GPT-2 with LoRA",
+// "Create LoRA layer": the adapter's B keeps the attention projection's
+// per-head output shape). With hd = N it is the plain row-major [rows][N].
+__device__ __forceinline__ long head_index(int row, int n, int rows, int hd) {
+  const int h = n / hd;
+  return ((long)h * rows + row) * hd + (n - h * hd);
+}
+
 // ---- wave reductions ---------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -39,7 +39,8 @@ struct A8W4Args {
   const uint8_t* packed;    // [N, K / 2], low nibble = even k
   const _Float16* scales;   // [N, K / 128]
   const float* t;           // [M, r]
-  const float* B;           // [r, N]
+  const float* B;           // [r, N], or [heads, r, hd]
+  int hd;                   // head width (N: one head)
   int r;
   float s;
   uint16_t* y;              // [M, N] bf16
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(256) void fwd_a8w4_kernel(A8W4Args a) {
 
   // epilogue operands: t, B, and the row scales sx (no column scale)
   EpiOps<BM, BN, R, true> ep;
-  ep.load(M, N, m0, n0, a.r, a.t, a.B, N, 1, a.sx, nullptr);
+  ep.load(M, N, m0, n0, a.r, a.t, a.B, a.hd, a.sx, nullptr);
 
   // the block's scale slab: rows n0 .. n0 + BN of [N][ngrp], contiguous
   {
@@ -212,11 +213,11 @@ void launch_groups(const A8W4Args& a, hipStream_t st) {
 
 void launch_gemm_fwd_a8w4(int M, int N, int K, const int8_t* xq, const float* sx,
                           const uint8_t* packed, const _Float16* scales,
-                          const float* t, const float* B, int r, float s,
+                          const float* t, const float* B, int hd, int r, float s,
                           uint16_t* y, hipStream_t st) {
   A8W4Args a{};
   a.M = M; a.N = N; a.K = K; a.xq = xq; a.sx = sx; a.packed = packed; a.scales = scales;
-  a.t = t; a.B = B; a.r = r; a.s = s; a.y = y;
+  a.t = t; a.B = B; a.hd = hd; a.r = r; a.s = s; a.y = y;
   const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
   if (t128 >= kCUs) launch_groups<128, 2>(a, st);
   else launch_groups<64, 3>(a, st);

@@ -62,7 +62,8 @@ struct BwdArgs {
   const int8_t* codes;     // int8 [N, K], or packed 4-bit [N, K / 2]
   const float* sw;         // int8: channel scales [N]
   const uint16_t* sc4;     // 4-bit: fp16 group scales [N, K / 128] (bit patterns)
-  const float* B;          // [r, N]
+  const float* B;          // [r, N], or [heads, r, hd]
+  int hd;                  // head width of B (N: one head)
   const float* A;          // [K, r]
   const float* t;          // [M, r]
   const uint16_t* x;       // [M, K] bf16
@@ -247,7 +248,9 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
     srcB[i] = okB[i] ? a.codes + (long)row * crs + gk : zero_chunk(lane);
   }
   // aux chunk ci of the tile: header chunks first, then B [j][64 n] in
-  // 4-float chunks; the source moves by adv bytes per n of the stage
+  // 4-float chunks; a header source moves by adv bytes per n of the stage, a
+  // B source (adv 0) by the stage's offset in B (a stage of 64 n lies inside
+  // one head: the head width is a multiple of 64)
   const int8_t* srcX[AUXI];
   int nX[AUXI], advX[AUXI];
   bool okX[AUXI];
@@ -271,9 +274,9 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
     } else {
       const int e = (ci - HDR / 16) * 4, j = e / 64, nn = e % 64;
       nX[i] = nn;
-      advX[i] = 4;
+      advX[i] = 0;
       okX[i] = j < r;
-      srcX[i] = j < r ? reinterpret_cast<const int8_t*>(a.B + (long)j * N + nn) : zero_chunk(lane);
+      srcX[i] = j < r ? reinterpret_cast<const int8_t*>(a.B + (long)j * a.hd + nn) : zero_chunk(lane);
     }
   }
   auto issue = [&](int kt, int slot) {
@@ -292,9 +295,10 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
       if (tail && nb + nB[i] >= N) src = zero_chunk(lane);
       lds_dma16(src, base + ASZ + (pw * BI + i) * RPI * RB);
     }
+    const long boff = 4 * head_index(0, nb, r, a.hd);   // bytes: B column nb, rank 0
 #pragma unroll
     for (int i = 0; i < AUXI; ++i) {
-      const int8_t* src = okX[i] ? srcX[i] + (long)advX[i] * nb : srcX[i];
+      const int8_t* src = okX[i] ? srcX[i] + (advX[i] ? (long)advX[i] * nb : boff) : srcX[i];
       if (tail && nb + nX[i] >= N) src = zero_chunk(lane);
       lds_dma16(src, base + ASZ + BSZ + (pw * AUXI + i) * 1024);
     }
@@ -697,18 +701,22 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
     okB[i] = gk < crs;
     srcB[i] = okB[i] ? a.codes + (long)row * crs + gk : zero_chunk(lane);
   }
+  // aux chunks: sw (row -1), then B [j][64 n]; sw moves by 4 bytes per n of
+  // the stage, B by the stage's offset in B (a stage of 64 n lies inside one
+  // head: the head width is a multiple of 64)
   const int8_t* srcX[AUXI];
   int nX[AUXI];
-  bool okX[AUXI];
+  bool okX[AUXI], isB[AUXI];
 #pragma unroll
   for (int i = 0; i < AUXI; ++i) {
     const int e = ((wid * AUXI + i) * 64 + lane) * 4;   // aux float index
     const int j = e / 64 - 1, nn = e % 64;
     nX[i] = nn;
+    isB[i] = j >= 0;
     okX[i] = j < r;
     okX[i] = okX[i] && !(W4 && j < 0);                 // 4-bit: no channel scales
     srcX[i] = j < 0 ? (W4 ? zero_chunk(lane) : reinterpret_cast<const int8_t*>(a.sw + nn))
-                    : (j < r ? reinterpret_cast<const int8_t*>(a.B + (long)j * N + nn) : zero_chunk(lane));
+                    : (j < r ? reinterpret_cast<const int8_t*>(a.B + (long)j * a.hd + nn) : zero_chunk(lane));
   }
   // 4-bit: lane l of wave w loads the scale of n = 16 w + l % 16 of the
   // stage (k group k0 / 128); kept as raw bits until the stage has landed
@@ -730,9 +738,10 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
       if (tail && nb + nB[i] >= N) src = zero_chunk(lane);
       lds_dma16(src, base + ASZ + (wid * BI + i) * RPI * RB);
     }
+    const long boff = 4 * head_index(0, nb, r, a.hd);   // bytes: B column nb, rank 0
 #pragma unroll
     for (int i = 0; i < AUXI; ++i) {
-      const int8_t* src = okX[i] ? srcX[i] + 4L * nb : srcX[i];
+      const int8_t* src = okX[i] ? srcX[i] + (isB[i] ? boff : 4L * nb) : srcX[i];
       if (tail && nb + nX[i] >= N) src = zero_chunk(lane);
       lds_dma16(src, base + ASZ + BSZ + (wid * AUXI + i) * 1024);
     }
@@ -1015,13 +1024,13 @@ int bwd_row_block(int fmt, int M, int K, int r) {
 }
 
 void launch_bwd_fused(int fmt, int M, int K, int N, const uint16_t* dy,
-                      const void* codes, const void* scales, const float* B,
+                      const void* codes, const void* scales, const float* B, int hd,
                       const float* A, const float* t, const uint16_t* x, int r,
                       float s, uint16_t* dx, float* partA, float* partB,
                       hipStream_t st) {
   BwdArgs a{};
   a.M = M; a.K = K; a.N = N; a.dy = dy; a.codes = static_cast<const int8_t*>(codes);
-  a.B = B; a.A = A; a.t = t; a.x = x; a.r = r; a.s = s; a.dx = dx; a.partA = partA;
+  a.B = B; a.hd = hd; a.A = A; a.t = t; a.x = x; a.r = r; a.s = s; a.dx = dx; a.partA = partA;
   a.partB = partB;
   // 64-row tiles (producer/consumer) while they make at most two blocks per
   // compute unit, else the wide 128 x 128 tiles

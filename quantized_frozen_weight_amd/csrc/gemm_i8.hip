@@ -32,7 +32,8 @@ struct I8Args {
   const float* sx;       // [M]
   const float* sw;       // [N]
   const float* t;        // [M, r]
-  const float* B;        // [r, N]
+  const float* B;        // [r, N], or [heads, r, hd]
+  int hd;                // head width (N: one head)
   int r;
   float s;
   void* y;               // [M, N] float32 or bfloat16
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
   const int nk = (K + BK - 1) / BK;
 
   EpiOps<BM, BN, R, true> ep;
-  if constexpr (!ACC_OUT) ep.load(M, N, m0, n0, a.r, a.t, a.B, N, 1, a.sx, a.sw);
+  if constexpr (!ACC_OUT) ep.load(M, N, m0, n0, a.r, a.t, a.B, a.hd, a.sx, a.sw);
 
   // Wave wid fills rows [wid * BM/4, (wid + 1) * BM/4) of A and the same
   // share of B; one instruction covers 8 rows (8 lanes of 16 bytes per row).
@@ -162,11 +163,11 @@ void launch_shape(const I8Args& a, hipStream_t st) {
 
 void launch_gemm_fwd_w8(int dtype, int M, int N, int K, const int8_t* xq,
                         const int8_t* codes, const float* sx, const float* sw,
-                        const float* t, const float* B, int r, float s,
+                        const float* t, const float* B, int hd, int r, float s,
                         void* y, int32_t* acc_out, hipStream_t st) {
   I8Args a{};
   a.M = M; a.N = N; a.K = K; a.xq = xq; a.codes = codes; a.sx = sx; a.sw = sw;
-  a.t = t; a.B = B; a.r = r; a.s = s; a.y = y; a.acc_out = acc_out;
+  a.t = t; a.B = B; a.hd = hd; a.r = r; a.s = s; a.y = y; a.acc_out = acc_out;
   if (acc_out != nullptr) launch_shape<float, true>(a, st);
   else if (dtype == 0) launch_shape<float, false>(a, st);
   else launch_shape<uint16_t, false>(a, st);

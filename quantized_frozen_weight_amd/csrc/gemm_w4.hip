@@ -37,7 +37,8 @@ struct W4Args {
   const uint8_t* packed;    // [N, K / 2], low nibble = even k
   const _Float16* scales;   // [N, K / 128]
   const float* t;           // [M, r]
-  const float* B;           // [r, N]
+  const float* B;           // [r, N], or [heads, r, hd]
+  int hd;                   // head width (N: one head)
   int r;
   float s;
   uint16_t* y;              // [M, N] bf16
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(256) void fwd_w4_kernel(W4Args a) {
   const int nk = ngrp;
 
   EpiOps<BM, BN, R, false> ep;
-  ep.load(M, N, m0, n0, a.r, a.t, a.B, N, 1, nullptr, nullptr);
+  ep.load(M, N, m0, n0, a.r, a.t, a.B, a.hd, nullptr, nullptr);
 
   // the block's scale slab: rows n0 .. n0 + BN of [N][ngrp], contiguous
   {
@@ -211,11 +212,11 @@ void launch_groups(const W4Args& a, hipStream_t st) {
 
 void launch_gemm_fwd_w4(int M, int N, int K, const uint16_t* x,
                         const uint8_t* packed, const _Float16* scales,
-                        const float* t, const float* B, int r, float s,
+                        const float* t, const float* B, int hd, int r, float s,
                         uint16_t* y, hipStream_t st) {
   W4Args a{};
   a.M = M; a.N = N; a.K = K; a.x = x; a.packed = packed; a.scales = scales;
-  a.t = t; a.B = B; a.r = r; a.s = s; a.y = y;
+  a.t = t; a.B = B; a.hd = hd; a.r = r; a.s = s; a.y = y;
   const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
   if (t128 >= kCUs) launch_groups<128, 2>(a, st);
   else launch_groups<64, 2>(a, st);

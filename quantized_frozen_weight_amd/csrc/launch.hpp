@@ -11,14 +11,16 @@ namespace qlora {
 
 // dtype: 0 = float32, 1 = bfloat16 (matches qlora_dtype)
 
-void launch_quantize_w8(const float* W, int K, int N, int8_t* codes,
+// hd: head width of W's storage ([heads, K, hd]; N for a plain [K, N]), and
+// of B's ([heads, r, hd]) in the launches below
+void launch_quantize_w8(const float* W, int K, int N, int hd, int8_t* codes,
                         float* scales, hipStream_t st);
-void launch_quantize_w4(const float* W, int K, int N, uint8_t* packed,
+void launch_quantize_w4(const float* W, int K, int N, int hd, uint8_t* packed,
                         _Float16* scales, hipStream_t st);
 // int8 weight with the adapter merged in, re-quantized (r <= 32); the
 // outputs must not overlap the inputs.
 void launch_merge_w8(const int8_t* codes, const float* sw, const float* A,
-                     const float* B, int K, int N, int r, float s,
+                     const float* B, int hd, int K, int N, int r, float s,
                      int8_t* codes_out, float* scales_out, hipStream_t st);
 
 void launch_rowquant(int dtype, const void* x, int M, int K, const float* A,
@@ -29,7 +31,7 @@ void launch_lora_down(int dtype, const void* x, int M, int K, const float* A,
 // y = acc * sx[m] * sw[n] + s * t B   (acc_out != nullptr: write int32 acc)
 void launch_gemm_fwd_w8(int dtype, int M, int N, int K, const int8_t* xq,
                         const int8_t* codes, const float* sx, const float* sw,
-                        const float* t, const float* B, int r, float s,
+                        const float* t, const float* B, int hd, int r, float s,
                         void* y, int32_t* acc_out, hipStream_t st);
 // 4-bit weights: the products hold the scales of up to this many 128-wide k
 // groups per block in LDS (K <= 16384).
@@ -40,15 +42,15 @@ constexpr int kW4MaxGroups = 128;
 // group, weighted by the group's fp16 scale, times sx[m], plus s t B (bf16 y)
 void launch_gemm_fwd_a8w4(int M, int N, int K, const int8_t* xq, const float* sx,
                           const uint8_t* packed, const _Float16* scales,
-                          const float* t, const float* B, int r, float s,
+                          const float* t, const float* B, int hd, int r, float s,
                           uint16_t* y, hipStream_t st);
 void launch_gemm_fwd_w4(int M, int N, int K, const uint16_t* x,
                         const uint8_t* packed, const _Float16* scales,
-                        const float* t, const float* B, int r, float s,
+                        const float* t, const float* B, int hd, int r, float s,
                         uint16_t* y, hipStream_t st);
 
 // u = dy B^T (float32 [M, r]); if dys != nullptr also dys = bf16(dy * sw[n]).
-void launch_bwd_rows(int dtype, const void* dy, int M, int N, const float* B,
+void launch_bwd_rows(int dtype, const void* dy, int M, int N, const float* B, int hd,
                      int r, const float* sw, uint16_t* dys, float* u,
                      hipStream_t st);
 
@@ -70,7 +72,7 @@ void launch_skinny_stage2(const SkinnyJobs& p, hipStream_t st);
 // (partB [blocks, r, N]); blocks = ceil(M / bwd_row_block(fmt, M, K, r)).
 int bwd_row_block(int fmt, int M, int K, int r);
 void launch_bwd_fused(int fmt, int M, int K, int N, const uint16_t* dy,
-                      const void* codes, const void* scales, const float* B,
+                      const void* codes, const void* scales, const float* B, int hd,
                       const float* A, const float* t, const uint16_t* x, int r,
                       float s, uint16_t* dx, float* partA, float* partB,
                       hipStream_t st);

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void skinny_stage2_kernel(SkinnyJobs p) {
   }
   const float out = p.s * sum;
   if (p.transpose[job]) p.out[job][(long)c * p.r + j] = out;
-  else p.out[job][(long)j * C + c] = out;
+  else p.out[job][head_index(j, c, p.r, job == 0 ? p.hd0 : C)] = out;
 }
 
 template <typename T>
@@ -65,7 +65,7 @@ SkinnyJobs make_adapter_grad_jobs(int M, int r, float s, const float* t,
   const int rps = (M + p.nsplit - 1) / p.nsplit;
   p.rows_per_split = (rps + 3) / 4 * 4;
   p.P[0] = t; p.Q[0] = dy; p.C[0] = N; p.out[0] = dB; p.transpose[0] = 0;
-  p.partial[0] = partB; p.ncb[0] = (N + kSkCols - 1) / kSkCols;
+  p.partial[0] = partB; p.ncb[0] = (N + kSkCols - 1) / kSkCols; p.hd0 = N;
   p.P[1] = u; p.Q[1] = x; p.C[1] = K; p.out[1] = dA; p.transpose[1] = 1;
   p.partial[1] = partA; p.ncb[1] = (K + kSkCols - 1) / kSkCols;
   return p;

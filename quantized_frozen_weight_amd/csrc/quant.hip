@@ -16,7 +16,8 @@ __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, long n) {
 }
 
 // ---------------------------------------------------------------------------
-// int8 weights, per output channel n (a column of W [K, N]).
+// int8 weights, per output channel n (a column of W [K, N]; element (k, n)
+// at head_index(k, n, K, hd) when W is stored per head [heads, K, hd]).
 // Pass 1: column abs-max as ordered bits, combined across K-slices with an
 // integer atomic max (order-independent, hence deterministic). A thread
 // covers 4 adjacent columns (N % 16 == 0) of an 8-row slice, all 8 row loads
@@ -25,7 +26,7 @@ __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, long n) {
 constexpr int kColmaxRows = 8;
 
 __global__ __launch_bounds__(256) void w8_colmax_kernel(
-    const float* __restrict__ W, int K, int N, uint32_t* __restrict__ amax) {
+    const float* __restrict__ W, int K, int N, int hd, uint32_t* __restrict__ amax) {
   const int n = 4 * (blockIdx.x * 256 + threadIdx.x);
   if (n >= N) return;
   const int k0 = blockIdx.y * kColmaxRows;
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(256) void w8_colmax_kernel(
 #pragma unroll
   for (int i = 0; i < kColmaxRows; ++i) {
     const int k = k0 + i < K ? k0 + i : K - 1;     // repeats of a real row do not change a max
-    v[i] = *reinterpret_cast<const f32x4*>(W + (long)k * N + n);
+    v[i] = *reinterpret_cast<const f32x4*>(W + head_index(k, n, K, hd));   // 4 n in one head
   }
   uint32_t m[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(256) void w8_colmax_kernel(
 // Pass 2: codes for a 64(k) x 64(n) tile, transposed through LDS so that the
 // [N, K] code rows are written 16 bytes at a time.
 __global__ __launch_bounds__(256) void w8_codes_kernel(
-    const float* __restrict__ W, int K, int N,
+    const float* __restrict__ W, int K, int N, int hd,
     const uint32_t* __restrict__ amax, int8_t* __restrict__ codes) {
   __shared__ int8_t tile[64][64 + 16];
   const int n0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(256) void w8_codes_kernel(
   for (int i = 0; i < 16; ++i) {
     int kl = tk + 4 * i, k = k0 + kl;
     int q = 0;
-    if (n < N && k < K && p.live) q = quant_code(W[(long)k * N + n], p.inv, 127.f);
+    if (n < N && k < K && p.live) q = quant_code(W[head_index(k, n, K, hd)], p.inv, 127.f);
     tile[tn][kl] = (int8_t)q;
   }
   __syncthreads();
@@ -102,7 +103,8 @@ struct MergeSrc {
   const int8_t* codes;   // [N, K]
   const float* sw;       // [N]
   const float* A;        // [K, r]
-  const float* B;        // [r, N]
+  const float* B;        // [r, N], or [heads, r, hd]
+  int hd;                // head width of B (N: one head)
   int K, N, r;
   double s;
 };
@@ -138,7 +140,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeSrc p, uint32_t* __rest
   }
   for (int e = tid; e < 64 * r; e += 256) {
     const int j = e / 64, nl = e % 64, n = n0 + nl;
-    Bs[j][nl] = n < N ? p.B[(long)j * N + n] : 0.f;
+    Bs[j][nl] = n < N ? p.B[head_index(j, n, r, p.hd)] : 0.f;
   }
   __syncthreads();
   const int nl = tid >> 2, kl0 = (tid & 3) * 16;
@@ -182,9 +184,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeSrc p, uint32_t* __rest
 }
 
 void launch_merge_w8(const int8_t* codes, const float* sw, const float* A,
-                     const float* B, int K, int N, int r, float s,
+                     const float* B, int hd, int K, int N, int r, float s,
                      int8_t* codes_out, float* scales_out, hipStream_t st) {
-  MergeSrc p{codes, sw, A, B, K, N, r, (double)s};
+  MergeSrc p{codes, sw, A, B, hd, K, N, r, (double)s};
   uint32_t* amax = reinterpret_cast<uint32_t*>(scales_out);
   fill_u32_kernel<<<dim3((N + 255) / 256), 256, 0, st>>>(amax, 0u, N);
   const dim3 grid((N + 63) / 64, (K + 63) / 64);
@@ -193,14 +195,14 @@ void launch_merge_w8(const int8_t* codes, const float* sw, const float* A,
   w8_scales_kernel<<<dim3((N + 255) / 256), 256, 0, st>>>(amax, N);
 }
 
-void launch_quantize_w8(const float* W, int K, int N, int8_t* codes,
+void launch_quantize_w8(const float* W, int K, int N, int hd, int8_t* codes,
                         float* scales, hipStream_t st) {
   uint32_t* amax = reinterpret_cast<uint32_t*>(scales);
   fill_u32_kernel<<<dim3((N + 255) / 256), 256, 0, st>>>(amax, 0u, N);
   w8_colmax_kernel<<<dim3((N + 1023) / 1024, (K + kColmaxRows - 1) / kColmaxRows),
-                     256, 0, st>>>(W, K, N, amax);
+                     256, 0, st>>>(W, K, N, hd, amax);
   w8_codes_kernel<<<dim3((N + 63) / 64, (K + 63) / 64), 256, 0, st>>>(
-      W, K, N, amax, codes);
+      W, K, N, hd, amax, codes);
   w8_scales_kernel<<<dim3((N + 255) / 256), 256, 0, st>>>(amax, N);
 }
 
@@ -208,7 +210,7 @@ void launch_quantize_w8(const float* W, int K, int N, int8_t* codes,
 // 4-bit weights: one block per (64 output channels, one 128-input group).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void w4_quant_kernel(
-    const float* __restrict__ W, int K, int N, uint8_t* __restrict__ packed,
+    const float* __restrict__ W, int K, int N, int hd, uint8_t* __restrict__ packed,
     _Float16* __restrict__ scales) {
   __shared__ int8_t tile[64][128 + 16];
   __shared__ uint32_t part[4][64];
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(256) void w4_quant_kernel(
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     int k = k0 + tk + 4 * i;
-    v[i] = (n < N) ? W[(long)k * N + n] : 0.f;
+    v[i] = (n < N) ? W[head_index(k, n, K, hd)] : 0.f;
     uint32_t b = abs_bits(v[i]);
     m = b > m ? b : m;
   }
@@ -262,9 +264,9 @@ __global__ __launch_bounds__(256) void w4_quant_kernel(
   }
 }
 
-void launch_quantize_w4(const float* W, int K, int N, uint8_t* packed,
+void launch_quantize_w4(const float* W, int K, int N, int hd, uint8_t* packed,
                         _Float16* scales, hipStream_t st) {
-  w4_quant_kernel<<<dim3((N + 63) / 64, K / 128), 256, 0, st>>>(W, K, N, packed,
+  w4_quant_kernel<<<dim3((N + 63) / 64, K / 128), 256, 0, st>>>(W, K, N, hd, packed,
                                                                scales);
 }
 

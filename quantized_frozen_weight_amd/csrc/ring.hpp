@@ -90,13 +90,14 @@ template <int BM, int BN, int R, bool SCALED> struct EpiOps {
   static constexpr int NQ = (BN * R + 255) / 256;
   float t[NT], q[NQ], rs, cs;
 
-  // P float32 [M, r]; Q(j, n) = Q[j * ldj + n * ldn]; rsrc [M] / csrc [N]
+  // P float32 [M, r]; Q(j, n) = Q[head_index(j, n, r, hd)] ([r][N], or
+  // [heads][r][hd]); rsrc [M] / csrc [N]
   // read when SCALED (csrc NULL: column scale 1). Nothing here consumes the
   // loaded values: a use would make the wave wait for these loads before the
   // main loop starts. The masks are applied by store().
   __device__ __forceinline__ void load(int M, int N, int m0, int n0, int r,
                                        const float* __restrict__ P,
-                                       const float* __restrict__ Q, long ldj, long ldn,
+                                       const float* __restrict__ Q, int hd,
                                        const float* __restrict__ rsrc,
                                        const float* __restrict__ csrc) {
     const int tid = threadIdx.x;
@@ -110,7 +111,7 @@ template <int BM, int BN, int R, bool SCALED> struct EpiOps {
     for (int i = 0; i < NQ; ++i) {
       const int e = tid + 256 * i;
       const int j = e / BN, col = e % BN, gn = n0 + col;
-      q[i] = Q[(long)(j < r ? j : r - 1) * ldj + (long)(gn < N ? gn : N - 1) * ldn];
+      q[i] = Q[head_index(j < r ? j : r - 1, gn < N ? gn : N - 1, r, hd)];
     }
     if constexpr (SCALED) {
       const int im = m0 + (tid < BM ? tid : BM - 1), in = n0 + (tid < BN ? tid : BN - 1);

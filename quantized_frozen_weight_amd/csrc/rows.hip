@@ -79,10 +79,11 @@ __device__ __forceinline__ int ws_index(int k, int j, int sld) {
 }
 
 // Copy the slice [s0, s0 + len) of the adapter matrix into LDS.
-// MODE < kBwd: A [L, r] row-major; kBwd: B [r, L] row-major.
+// MODE < kBwd: A [L, r] row-major; kBwd: B [r, L] row-major, or per head
+// [heads, r, hd] (4-float units never straddle a head: hd % 4 == 0).
 template <int R, int MODE>
 __device__ __forceinline__ void stage_slice(float* Ws, const float* __restrict__ W,
-                                            int L, int r, int s0, int len, int sld) {
+                                            int L, int r, int s0, int len, int sld, int hd) {
   constexpr int SL = Slice<R>::len;
   constexpr int PER = (R * SL / 4 + 255) / 256;     // 16-byte units per thread
   if constexpr (MODE == kBwd) {
@@ -94,7 +95,7 @@ __device__ __forceinline__ void stage_slice(float* Ws, const float* __restrict__
     for (int q = 0; q < PER; ++q) {
       const int u = threadIdx.x + 256 * q;
       const int uc = u < n ? u : n - 1;
-      v[q] = *reinterpret_cast<const f32x4*>(W + (long)(uc / upr) * L + s0 + 4 * (uc % upr));
+      v[q] = *reinterpret_cast<const f32x4*>(W + head_index(uc / upr, s0 + 4 * (uc % upr), r, hd));
     }
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
@@ -133,7 +134,7 @@ __device__ __forceinline__ void stage_slice(float* Ws, const float* __restrict__
 template <typename T, int R, int MODE, bool HOLD>
 __global__ __launch_bounds__(256) void row_kernel(
     const typename Elem<T>::type* __restrict__ rows, int M, int L,
-    const float* __restrict__ W, int r, float* __restrict__ out_r,
+    const float* __restrict__ W, int hd, int r, float* __restrict__ out_r,
     int8_t* __restrict__ xq, float* __restrict__ sx,
     const float* __restrict__ sw, uint16_t* __restrict__ dys) {
   constexpr int SL = Slice<R>::len;
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(256) void row_kernel(
   for (int s0 = 0; s0 < L; s0 += SL) {
     const int len = min(SL, L - s0);
     if (s0 > 0) __syncthreads();
-    if (lowrank) stage_slice<R, MODE>(Ws, W, L, r, s0, len, sld);
+    if (lowrank) stage_slice<R, MODE>(Ws, W, L, r, s0, len, sld, hd);
     if (MODE == kFwdQuant && s0 == 0 && live) {
       uint32_t m = 0;
       if constexpr (HOLD) {
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(256) void row_kernel(
 }
 
 template <typename T, int R, int MODE>
-void row_launch(const void* rows, int M, int L, const float* W, int r,
+void row_launch(const void* rows, int M, int L, const float* W, int hd, int r,
                 float* out_r, int8_t* xq, float* sx, const float* sw,
                 uint16_t* dys, hipStream_t st) {
   dim3 grid((M + kRowsPerBlock - 1) / kRowsPerBlock);
@@ -285,23 +286,23 @@ void row_launch(const void* rows, int M, int L, const float* W, int r,
   if (out_r != nullptr)
     lds = (MODE == kBwd ? (size_t)R * sld : (size_t)(sld / 8) * (8 * R + 4)) * sizeof(float);
   if (L <= kHoldChunks * 512)
-    row_kernel<T, R, MODE, true><<<grid, 256, lds, st>>>(p, M, L, W, r, out_r, xq, sx,
+    row_kernel<T, R, MODE, true><<<grid, 256, lds, st>>>(p, M, L, W, hd, r, out_r, xq, sx,
                                                          sw, dys);
   else
-    row_kernel<T, R, MODE, false><<<grid, 256, lds, st>>>(p, M, L, W, r, out_r, xq, sx,
+    row_kernel<T, R, MODE, false><<<grid, 256, lds, st>>>(p, M, L, W, hd, r, out_r, xq, sx,
                                                           sw, dys);
 }
 
 template <typename T, int MODE>
-void row_dispatch_r(int r, const void* rows, int M, int L, const float* W,
+void row_dispatch_r(int r, const void* rows, int M, int L, const float* W, int hd,
                     float* out_r, int8_t* xq, float* sx, const float* sw,
                     uint16_t* dys, hipStream_t st) {
-  if (r <= 1) row_launch<T, 1, MODE>(rows, M, L, W, r, out_r, xq, sx, sw, dys, st);
-  else if (r <= 2) row_launch<T, 2, MODE>(rows, M, L, W, r, out_r, xq, sx, sw, dys, st);
-  else if (r <= 4) row_launch<T, 4, MODE>(rows, M, L, W, r, out_r, xq, sx, sw, dys, st);
-  else if (r <= 8) row_launch<T, 8, MODE>(rows, M, L, W, r, out_r, xq, sx, sw, dys, st);
-  else if (r <= 16) row_launch<T, 16, MODE>(rows, M, L, W, r, out_r, xq, sx, sw, dys, st);
-  else row_launch<T, 32, MODE>(rows, M, L, W, r, out_r, xq, sx, sw, dys, st);
+  if (r <= 1) row_launch<T, 1, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, sw, dys, st);
+  else if (r <= 2) row_launch<T, 2, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, sw, dys, st);
+  else if (r <= 4) row_launch<T, 4, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, sw, dys, st);
+  else if (r <= 8) row_launch<T, 8, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, sw, dys, st);
+  else if (r <= 16) row_launch<T, 16, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, sw, dys, st);
+  else row_launch<T, 32, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, sw, dys, st);
 }
 
 }  // namespace
@@ -310,26 +311,26 @@ void launch_rowquant(int dtype, const void* x, int M, int K, const float* A,
                      int r, int8_t* xq, float* sx, float* t, hipStream_t st) {
   const int rr = t == nullptr ? 1 : r;
   if (dtype == 0)
-    row_dispatch_r<F32, kFwdQuant>(rr, x, M, K, A, t, xq, sx, nullptr, nullptr, st);
+    row_dispatch_r<F32, kFwdQuant>(rr, x, M, K, A, K, t, xq, sx, nullptr, nullptr, st);
   else
-    row_dispatch_r<BF16, kFwdQuant>(rr, x, M, K, A, t, xq, sx, nullptr, nullptr, st);
+    row_dispatch_r<BF16, kFwdQuant>(rr, x, M, K, A, K, t, xq, sx, nullptr, nullptr, st);
 }
 
 void launch_lora_down(int dtype, const void* x, int M, int K, const float* A,
                       int r, float* t, hipStream_t st) {
   if (dtype == 0)
-    row_dispatch_r<F32, kFwdT>(r, x, M, K, A, t, nullptr, nullptr, nullptr, nullptr, st);
+    row_dispatch_r<F32, kFwdT>(r, x, M, K, A, K, t, nullptr, nullptr, nullptr, nullptr, st);
   else
-    row_dispatch_r<BF16, kFwdT>(r, x, M, K, A, t, nullptr, nullptr, nullptr, nullptr, st);
+    row_dispatch_r<BF16, kFwdT>(r, x, M, K, A, K, t, nullptr, nullptr, nullptr, nullptr, st);
 }
 
-void launch_bwd_rows(int dtype, const void* dy, int M, int N, const float* B,
+void launch_bwd_rows(int dtype, const void* dy, int M, int N, const float* B, int hd,
                      int r, const float* sw, uint16_t* dys, float* u,
                      hipStream_t st) {
   if (dtype == 0)
-    row_dispatch_r<F32, kBwd>(r, dy, M, N, B, u, nullptr, nullptr, sw, nullptr, st);
+    row_dispatch_r<F32, kBwd>(r, dy, M, N, B, hd, u, nullptr, nullptr, sw, nullptr, st);
   else
-    row_dispatch_r<BF16, kBwd>(r, dy, M, N, B, u, nullptr, nullptr, sw, dys, st);
+    row_dispatch_r<BF16, kBwd>(r, dy, M, N, B, hd, u, nullptr, nullptr, sw, dys, st);
 }
 
 }  // namespace qlora

@@ -30,6 +30,7 @@ struct SkinnyJobs {
   int C[2];
   int ncb[2];          // column blocks per job
   int transpose[2];
+  int hd0;             // job 0's output (dB): head width ([heads, r, hd]; C[0]: [r, C])
   int njobs, M, r, nsplit, rows_per_split;
   float s;
   int blocks() const { return (ncb[0] + (njobs > 1 ? ncb[1] : 0)) * nsplit; }

@@ -174,6 +174,17 @@ def test_calls_fail_before_launch(lib):
                               need4, None) == Q.QLORA_EUNSUPPORTED
     assert lib.qlora_fwd_a8w4(ctypes.byref(lin4), 64, Q.QLORA_BF16, None, FAKE, None, FAKE,
                               need4, None) == Q.QLORA_EINVAL
+    # multi-head layers: heads must divide N into multiples of 64
+    for heads, want in [(-1, Q.QLORA_EINVAL), (3, Q.QLORA_EINVAL), (8, Q.QLORA_EUNSUPPORTED)]:
+        lh = Q.qlora_linear(256, 256, 4, 8.0, Q.QLORA_W8, FAKE, FAKE, FAKE, FAKE, heads)
+        assert lib.qlora_fwd(ctypes.byref(lh), 64, Q.QLORA_BF16, FAKE, FAKE, None, FAKE,
+                             need, None) == want
+    lh = Q.qlora_linear(256, 256, 4, 8.0, Q.QLORA_W8, FAKE, FAKE, FAKE, FAKE, 4)
+    assert lib.qlora_fwd(ctypes.byref(lh), 64, Q.QLORA_BF16, FAKE, FAKE, None, FAKE,
+                         need - 1, None) == Q.QLORA_EWORKSPACE      # valid layout, small ws
+    assert lib.qlora_quantize_heads(FAKE, 3, 128, 256, Q.QLORA_W8, FAKE, FAKE, None) == Q.QLORA_EINVAL
+    assert lib.qlora_quantize_heads(FAKE, 0, 128, 256, Q.QLORA_W8, FAKE, FAKE, None) == Q.QLORA_EINVAL
+    assert lib.qlora_quantize_heads(FAKE, 8, 128, 256, Q.QLORA_W8, FAKE, FAKE, None) == Q.QLORA_EUNSUPPORTED
     # the two halves of the backward validate their own arguments
     assert lib.qlora_bwd_partial(ctypes.byref(lin), 64, Q.QLORA_BF16, None, FAKE, None, FAKE,
                                  FAKE, n.value, None) == Q.QLORA_EINVAL

@@ -397,6 +397,68 @@ def test_a8w4_exact_on_the_integer_grid(M, N):
     assert same_bits_f32(to_numpy(y), oy), "y differs from the exact result"
 
 
+HEADS = [
+    # (M, K, heads, hd, r, dtype, wfmt)
+    (512, 2048, 8, 256, 4, "bf16", "w8"),    # Gemma query projection, B [8, 4, 256]
+    (4096, 768, 12, 64, 4, "bf16", "w8"),    # GPT-2 heads (128 x 128 backward tiles)
+    (257, 1024, 4, 128, 8, "bf16", "w4g128"),
+    (64, 256, 2, 128, 4, "f32", "w8"),       # the float32 path
+]
+
+
+@pytest.mark.parametrize("M,K,H,hd,r,dtype,wfmt", HEADS)
+def test_multi_head_layer(M, K, H, hd, r, dtype, wfmt):
+    """A layer whose outputs are heads x hd: W [heads, K, hd] and B, dB
+    [heads, r, hd]; the oracle runs the plain layer on the mapped tensors."""
+    N = H * hd
+    say(f"multi-head: M={M} K={K} heads={H} hd={hd} r={r} {dtype} {wfmt}")
+    rng = np.random.default_rng(4242 + M + K)
+    Wh = (rng.standard_normal((H, K, hd)) * 0.02).astype(np.float32)
+    A = (rng.standard_normal((K, r)) * 0.01).astype(np.float32)
+    Bh = (rng.standard_normal((H, r, hd)) * 0.01).astype(np.float32)
+    x32 = rng.standard_normal((M, K)).astype(np.float32)
+    dy32 = rng.standard_normal((M, N)).astype(np.float32)
+    x_t, x = WL.as_compute_dtype(x32, dtype)
+    dy_t, dy = WL.as_compute_dtype(dy32, dtype)
+    x_t, dy_t = x_t.cuda(), dy_t.cuda()
+    alpha = 16.0
+    codes, scales = Q.qlora_quantize(dev(Wh), wfmt)
+    lin = Q.QLinear(K, N, r, alpha, wfmt, codes, scales, dev(A), dev(Bh), heads=H)
+    W, B = O.heads_to_plain(Wh), O.heads_to_plain(Bh)
+    if wfmt == "w8":
+        c, sc = O.quantize_w8(W)
+        deq = O.dequant_w8(c, sc)
+        assert np.array_equal(to_numpy(codes), c) and same_bits_f32(to_numpy(scales), sc)
+        oy, ot = O.fwd_w8(x, c, sc, A, B, alpha, dtype)
+    else:
+        c, sc = O.quantize_w4(W)
+        deq = O.dequant_w4(c, sc)
+        assert np.array_equal(to_numpy(codes), c) and same_bits_f16(to_numpy(scales), sc)
+        oy, ot = O.fwd_w4(x, c, sc, A, B, alpha, dtype)
+    rt = RTOL[dtype]
+    y, t = Q.qlora_fwd(lin, x_t)
+    torch.cuda.synchronize()
+    assert_close(to_numpy(y), oy, rt, "y")
+    assert_close(to_numpy(t), ot, rt, "t")
+    dx, dA, dB = Q.qlora_bwd(lin, x_t, dy_t, t=t)
+    torch.cuda.synchronize()
+    odx, odA, odB = O.bwd(x, dy, deq, A, B, alpha, dtype)
+    assert tuple(dB.shape) == (H, r, hd)
+    assert_close(to_numpy(dx), odx, rt, "dx")
+    assert_close(to_numpy(dA), odA, rt, "dA")
+    assert_close(to_numpy(dB), O.plain_to_heads(odB, H), rt, "dB")
+    if wfmt == "w4g128":
+        ya, _ = Q.qlora_fwd_a8w4(lin, x_t)
+        torch.cuda.synchronize()
+        oya, _ = O.fwd_a8w4(x, c, sc, A, B, alpha, dtype)
+        assert_close(to_numpy(ya), oya, rt, "y (int8 activations)")
+    if wfmt == "w8":
+        mc, ms = Q.qlora_merge(lin)
+        torch.cuda.synchronize()
+        oc, os_ = O.merge_w8(c, sc, A, B, alpha)
+        assert np.array_equal(to_numpy(mc), oc) and same_bits_f32(to_numpy(ms), os_)
+
+
 def test_mlp_stack_all_layers():
     """The 32-layer MLP workload exactly as the benchmark runs it: forward
     0..31, then backward 31..0, one stream, per-layer parity."""
