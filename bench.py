@@ -169,6 +169,13 @@ def main():
             else:
                 fwd_a8w4_ms = e0.elapsed_time(e1) / 20
 
+    # Gemma workload: its attention query projection as the multi-head layer
+    # the pages list (kernel [8, 2048, 256], B [8, 4, 256]), forward + backward,
+    # next to the same tensors taken as a one-head layer
+    heads_leg = None
+    if w.name == "gemma":
+        heads_leg = multi_head_leg(torch, dev, lib, check, M)
+
     def step(ev_b=None, repeats=1):
         st = torch.cuda.current_stream().cuda_stream
         for i, l in enumerate(layers):
@@ -261,6 +268,7 @@ def main():
         "merge_ms": None if merge_ms is None else round(merge_ms, 4),
         "fwd_ms": None if fwd_ms is None else round(fwd_ms, 4),
         "fwd_a8w4_ms": None if fwd_a8w4_ms is None else round(fwd_a8w4_ms, 4),
+        "attention_query_ms": heads_leg,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
@@ -285,8 +293,8 @@ def describe(w):
 TRAFFIC = {
     "workload": 2,
     "sources": ["gemm_bwd.hip", "ring.hpp", "common.hpp"],
-    "sha256": "c4a7bf8667353e2e323767aa9cf6fb34b2742426651b072c50e10af9f4d53aad",
-    "bytes_per_launch": 25010441,
+    "sha256": "1257ca38069c0abf19eca31df24988f54e417c13948f716e193d988db12795cf",
+    "bytes_per_launch": 25025647,
 }
 
 
@@ -310,6 +318,50 @@ def copy_calibration(torch, dev):
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
+
+
+def multi_head_leg(torch, dev, lib, check, M, K=2048, heads=8, hd=256, r=4, reps=20):
+    """fwd + bwd time (ms) of a [heads, K, hd] int8 layer with B [heads, r, hd],
+    and of the same tensors as a one-head layer."""
+    from quantized_frozen_weight_amd import binding as Q
+    N = heads * hd
+    g = torch.Generator().manual_seed(4000)
+    W = (torch.randn((heads, K, hd), generator=g) * 0.02).to(dev)
+    A = (torch.randn((K, r), generator=g) * 0.01).to(dev)
+    B = (torch.randn((heads, r, hd), generator=g) * 0.01).to(dev)
+    x = torch.randn((M, K), generator=g).to(torch.bfloat16).to(dev)
+    dy = torch.randn((M, N), generator=g).to(torch.bfloat16).to(dev)
+    codes, scales = Q.qlora_quantize(W, "w8")
+    out = {}
+    for name, h in (("heads", heads), ("plain", 1)):
+        lin = Q.QLinear(K, N, r, 16.0, "w8", codes, scales, A, B, heads=h)
+        ws = torch.empty((max(Q.qlora_fwd_workspace(lin, M, Q.QLORA_BF16),
+                              Q.qlora_bwd_workspace(lin, M, Q.QLORA_BF16)),),
+                         dtype=torch.uint8, device=dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        t = torch.empty((M, r), dtype=torch.float32, device=dev)
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        dA = torch.empty((K, r), dtype=torch.float32, device=dev)
+        dB = torch.empty((r * N,), dtype=torch.float32, device=dev)
+        cs = lin.cstruct()
+        st = torch.cuda.current_stream().cuda_stream
+
+        def once():
+            check(lib.qlora_fwd(ctypes.byref(cs), M, Q.QLORA_BF16, x.data_ptr(), y.data_ptr(),
+                                t.data_ptr(), ws.data_ptr(), ws.numel(), st), "fwd")
+            check(lib.qlora_bwd(ctypes.byref(cs), M, Q.QLORA_BF16, x.data_ptr(), dy.data_ptr(),
+                                t.data_ptr(), dx.data_ptr(), dA.data_ptr(), dB.data_ptr(),
+                                ws.data_ptr(), ws.numel(), st), "bwd")
+        once()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            once()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(e0.elapsed_time(e1) / reps, 4)
+    return out
 
 
 def dominant_kernel_roofline(w, layers, step, torch):
@@ -338,7 +390,12 @@ def dominant_kernel_roofline(w, layers, step, torch):
     avg_ms = tot_ms / launches
     if w.dtype == "bf16":   # fused backward: dx, u, dB, dA, s u A^T
         flops = sum(2.0 * w.M * l.K * l.N + 4.0 * w.M * w.r * (l.N + l.K) for l in layers) / n
-        kernel = ("bwd_kernel (fused backward: dx, u, dA and dB partial sums, "
+        # the library's tile choice: 64-row producer/consumer blocks while
+        # they make at most two per compute unit, else 128 x 128 blocks
+        bn = 64 if w.wfmt == "w8" else 128
+        names = sorted({"bwd_pc_kernel" if ((w.M + 63) // 64) * ((l.K + bn - 1) // bn) <= 512
+                        else "bwd_wide_kernel" for l in layers})
+        kernel = (" + ".join(names) + " (fused backward: dx, u, dA and dB partial sums, "
                   f"bf16 MFMA, {w.wfmt} weights)")
     else:                   # float32 input gradient: dy deq(W)^T + s u A^T
         flops = sum(2.0 * w.M * l.K * l.N + 2.0 * w.M * w.r * l.K for l in layers) / n
