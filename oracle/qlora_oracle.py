@@ -24,7 +24,9 @@ Sources (page title, then section):
   layer is frozen), "Why does LoRA reduce memory footprint?" (gradients only
   for the trainable adapter), "Merge weights and generate text!" (W = W0 + BA).
 * [llm-light]  keras-llm-light README: "Weights quantization" (LoRA weights kept
-  in fp32), "Simplified Int4Variable quantization" (two int4 values per int8).
+  in fp32), "Simplified Int4Variable quantization" (two int4 values per int8),
+  "Simplified Int8Variable quantization" (percentile cut, affine codes, fp16
+  outliers restored by position).
 * [4-bit issue]  GPTQ-for-LLaMa issue "How to fine-tune the 4-bit model?": the
   comments on 4-bit frozen weights under an fp32 adapter, the transposed
   product needed for gradients, dequantize-add-requantize to merge.
@@ -50,6 +52,12 @@ Readings taken where the pages are silent (each listed in the design doc):
 * 4-bit integer forward (the alternative): activations quantized per row as
   above, exact int8 x int4 sums per 128-wide group, each weighted by its fp16
   scale, the total by the row scale; adapter term as in the float forward.
+* outlier-compensated int8 weights ([llm-light] "Simplified Int8Variable
+  quantization"): one nearest-rank cut per tensor at the 0.1th and 99.9th
+  percentiles, an affine 255-step grid between the cuts (bias = lower cut),
+  the elements outside the cut kept as fp16 values at their positions; the
+  layer quantizes its activations per row as the int8 layer does (details
+  in that section below).
 
 Layouts: W [K, N] float32 (the pages' kernel orientation); int8 codes [N, K]
 (one output channel per row, K contiguous) with scales [N]; 4-bit codes
@@ -423,3 +431,102 @@ def merge_w8(codes, sw, A, B, alpha: float):
     are W' rounded to its own channel grid ([QLoRA-like] results-table
     footnote: merging LoRA into int8 kernels changes the outputs)."""
     return quantize_w8(merged_weight_w8(codes, sw, A, B, alpha))
+
+# ---------------------------------------------------------------------------
+# Outlier-compensated int8 weights ([llm-light] "Simplified Int8Variable
+# quantization"): the weight is cut at its 0.1th and 99.9th percentiles, the
+# clipped weight is stored as 8-bit codes of an affine grid (a bias and a
+# step, reconstructed as bias + value * scale in float32), and the elements
+# outside the cut are kept exactly, as fp16 values at their (row, column),
+# written over the reconstruction before the layer is used.
+#
+# Readings (the section gives the three steps and the reconstruction code but
+# no formulas for the cut or the grid):
+# * one cut, one bias and one scale per weight tensor (the section's memory
+#   table shows each 2048 x 16384 kernel barely above its size in bytes, and
+#   same-shaped kernels of different sizes, i.e. data-dependent outlier
+#   counts rather than per-channel arrays);
+# * "99.9 percentile cutoff" as two nearest-rank percentiles of all K*N
+#   elements, lo = P(0.1) and hi = P(99.9): P(q) is the smallest element x
+#   with at least q percent of the elements <= x, i.e. the element of 1-based
+#   rank ceil(q n / 100) in ascending order;
+# * outliers are the elements < lo ("min") and > hi ("max");
+# * the grid spans [lo, hi] in 255 steps: bias = lo, scale = fl32(d / 255)
+#   with d = fl32(hi - lo), value = clamp(rint(fl32(fl32(clip(w) - lo) *
+#   fl32(255 / d))), 0, 255) -- the same multiply-by-inverse form as the int8
+#   rule; if d is 0 or not finite, or 255 / d overflows, scale is 0 and every
+#   value 0;
+# * the layer itself is the int8 layer's: activations quantized per row, the
+#   base product sx[m] * sum_k xq[m, k] Wr[k, n] with Wr the reconstructed
+#   weight; the gradient passes the quantizers (dx = dy Wr^T + s u A^T).
+# W must be finite (no rule is stated for NaN or infinite weights).
+# ---------------------------------------------------------------------------
+
+OUTLIER_TAIL = (1, 1000)   # each tail holds 1/1000 of the elements (0.1 %)
+
+
+def nearest_rank_index(n: int, num: int, den: int) -> int:
+    """0-based ascending position of the nearest-rank percentile 100 num/den
+    of n elements: rank ceil(num n / den), at least 1, in exact integers."""
+    rank = -(-num * n // den)
+    return max(rank, 1) - 1
+
+
+def quantize_w8o(W) -> dict:
+    """W [K, N] float32 -> the outlier-compensated int8 weight:
+
+      lo, hi, scale   float32 scalars (bias = lo)
+      value           uint8 [K, N], the clipped weight's grid index
+      rows, cols      int64 [nnz], outlier positions in row-major (k, n) order
+      vals            float16 [nnz], the outliers' values
+    """
+    W = np.asarray(W, dtype=F32)
+    n = W.size
+    num, den = OUTLIER_TAIL
+    v = np.sort(W.ravel())
+    lo = F32(v[nearest_rank_index(n, num, den)])
+    hi = F32(v[nearest_rank_index(n, den - num, den)])
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        d = F32(hi - lo)
+        inv = F32(255) / d
+        scale = d / F32(255)
+    if not (d > 0 and np.isfinite(d) and np.isfinite(inv)):
+        inv, scale = F32(0), F32(0)
+    clipped = np.minimum(np.maximum(W, lo), hi)
+    value = np.clip(np.rint((clipped - lo) * inv), 0, 255).astype(np.uint8)
+    rows, cols = np.nonzero((W < lo) | (W > hi))
+    return dict(lo=lo, hi=hi, scale=F32(scale), value=value, rows=rows, cols=cols,
+                vals=W[rows, cols].astype(np.float16))
+
+
+def dequant_w8o(q) -> np.ndarray:
+    """The reconstructed weight Wr [K, N] float32, as the section's code does
+    it: bias + float(value) * scale in float32 (a multiply, then an add),
+    then every outlier position overwritten with its fp16 value."""
+    Wr = q["lo"] + q["value"].astype(F32) * q["scale"]
+    Wr = np.asarray(Wr, dtype=F32).copy()
+    Wr[q["rows"], q["cols"]] = q["vals"].astype(F32)
+    return Wr
+
+
+def w8o_device_codes(q) -> np.ndarray:
+    """The codes as the library stores them: int8 [N, K] = value - 128
+    (the same grid index, offset to the signed range of the int8 products)."""
+    return np.ascontiguousarray((q["value"].astype(np.int16) - 128).astype(np.int8).T)
+
+
+def fwd_w8o_f64(x, q, A, B, alpha: float):
+    """Unrounded forward of the outlier-compensated layer. Returns
+    (y64, t64, xq, sx): y = sx[m] sum_k xq[m, k] Wr[k, n] + s (x A) B."""
+    x32 = np.asarray(x, F32)
+    xq, sx = quantize_rows(x32)
+    Wr = dequant_w8o(q).astype(F64)
+    base = np.asarray(sx, F64)[:, None] * (xq.astype(F64) @ Wr)
+    t = lora_down(x32.astype(F64), A)
+    s = lora_scale(alpha, np.asarray(A).shape[1])
+    return base + s * (t @ np.asarray(B, F64)), t, xq, sx
+
+
+def fwd_w8o(x, q, A, B, alpha: float, dtype: str):
+    y, t, _, _ = fwd_w8o_f64(x, q, A, B, alpha)
+    return round_to(y, dtype), round_f32(t)
