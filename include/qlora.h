@@ -29,6 +29,20 @@
  * 4-bit format QLORA_W4G128: one fp16 scale per 128 consecutive inputs of an
  *   output channel, sc = f16(absmax / 7), codes round-half-even(W * (1/sc)) in
  *   [-7, 7]; the forward multiplies x (not quantized) by the dequantized weight.
+ * Outlier-compensated int8 format QLORA_W8O (keras-llm-light README,
+ *   "Simplified Int8Variable quantization": the weight is cut at its 0.1th and
+ *   99.9th percentiles, the clipped weight stored as 8-bit codes of an affine
+ *   grid reconstructed as bias + value * scale, and the elements outside the
+ *   cut kept as fp16 values at their positions): one cut, bias and scale per
+ *   weight tensor; lo and hi are the nearest-rank percentiles (the elements
+ *   of ascending rank ceil(n / 1000) and ceil(999 n / 1000) among n = K N);
+ *   d = fl32(hi - lo), scale = fl32(d / 255), bias = lo, grid index
+ *   v = clamp(round-half-even(fl32(fl32(clip(W, lo, hi) - lo) * fl32(255 / d))),
+ *   0, 255) (scale 0 and v = 0 if d is 0 or not finite or 255 / d
+ *   overflows); outliers are the elements < lo or > hi, kept as fp16
+ *   (round-half-even). The layer is reconstructed as Wr = lo + v * scale with
+ *   the outliers written over it; the forward quantizes x per row as for
+ *   QLORA_W8 and adds the product of the quantized rows with Wr.
  * Backward: the activation quantizer is passed straight through,
  *   dx = dy . deq(W)^T + s (dy B^T) A^T,  dA = s x^T (dy B^T),  dB = s (x A)^T dy,
  *   and the frozen weight receives no gradient (there is no dW argument).
@@ -39,8 +53,14 @@
  *          QLORA_W4G128: uint8 [N, K/2]   (byte j holds k = 2j in the low
  *                                          nibble, 2j+1 in the high nibble,
  *                                          two's complement)
+ *          QLORA_W8O:    int8  [N, K]     (v - 128)
  *   scales QLORA_W8:     float32 [N]
  *          QLORA_W4G128: float16 [N, K/128]
+ *          QLORA_W8O:    a side buffer of qlora_weight_bytes' scale_bytes:
+ *                        a qlora_outlier_header at offset 0, then the
+ *                        outlier list at the offsets that
+ *                        qlora_outlier_layout gives, then arrays the library
+ *                        uses internally
  *   x, dx  [M, K] in the compute dtype;  y, dy  [M, N] in the compute dtype
  *   A, dA  float32 [K, r];               B, dB  float32 [r, N]
  *   t      float32 [M, r]  (t = x A, unscaled; saved by the forward)
@@ -68,7 +88,9 @@
  *     1 <= r <= 32, all pointers 16-byte aligned; QLORA_W4G128 needs
  *     K % 128 == 0 and the bf16 compute dtype (EINVAL / EUNSUPPORTED
  *     otherwise), and qlora_fwd / qlora_bwd take K <= 16384 for it (the
- *     products keep one block's fp16 scales in LDS; EUNSUPPORTED above).
+ *     products keep one block's fp16 scales in LDS; EUNSUPPORTED above);
+ *     QLORA_W8O needs the bf16 compute dtype and N < 2^24
+ *     (EUNSUPPORTED otherwise).
  *   - Outputs (y, t, dx, dA, dB) are overwritten, never accumulated into.
  *     codes, scales, A and B are only read by qlora_fwd / qlora_bwd.
  *   - Non-finite x or dy propagate into the outputs; nothing is checked on
@@ -98,7 +120,7 @@ typedef enum {
 } qlora_status;
 
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
-typedef enum { QLORA_W8 = 0, QLORA_W4G128 = 1 } qlora_wfmt;
+typedef enum { QLORA_W8 = 0, QLORA_W4G128 = 1, QLORA_W8O = 2 } qlora_wfmt;
 
 /* One frozen layer with its adapter. All pointers are device memory owned by
  * the caller and only read by the library. */
@@ -114,6 +136,14 @@ typedef struct {
                              multiple of 64 (EUNSUPPORTED otherwise) */
 } qlora_linear;
 
+/* The public head of a QLORA_W8O side buffer (device memory, offset 0),
+ * written by qlora_quantize. */
+typedef struct {
+  float lo, hi;           /* the cut: lower and upper nearest-rank percentile */
+  float scale;            /* grid step; the grid's bias is lo */
+  int32_t nnz;            /* outliers stored */
+} qlora_outlier_header;
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* qlora_status_str(int status);
 
@@ -122,20 +152,36 @@ const char* qlora_status_str(int status);
 int qlora_weight_bytes(int K, int N, int fmt, size_t* codes_bytes,
                        size_t* scale_bytes);
 
+/* Where a QLORA_W8O side buffer keeps its outlier list (byte offsets from
+ * the buffer's start), in compressed-row form over W [K, N]: the outliers of
+ * weight row k are entries [rowptr[k], rowptr[k + 1]) in increasing n, with
+ *   rowptr int32 [K + 1] at *rowptr_off,
+ *   col    int32 [nnz]   at *col_off   (the output index n),
+ *   val    fp16  [nnz]   at *val_off   (the kept value),
+ * nnz <= *capacity = 2 floor(K N / 1000) + 2. Host-only arithmetic; the
+ * shape rules of qlora_weight_bytes apply. */
+int qlora_outlier_layout(int K, int N, size_t* rowptr_off, size_t* col_off,
+                         size_t* val_off, int32_t* capacity);
+
 /* Quantize a float32 weight W [K, N] into codes and scales (format above).
  * One-time preparation of the frozen weight ("Introduce QLoRA-like
  * technique", benchmark.py: model.quantize("int8")). Channels (W8) or groups
  * (W4G128) whose abs-max is 0 -- or so small that the inverse scale
  * overflows (W8) -- get scale 0 and zero codes; a non-finite abs-max, or an
  * fp16 scale overflow (W4G128), stores a NaN scale and zero codes so that
- * the NaN reaches every output that uses it. W is only read. */
+ * the NaN reaches every output that uses it. QLORA_W8O: W must be finite
+ * (with a NaN or infinite element the cut and codes are unspecified; no
+ * write leaves the side buffer); scales is the side buffer, and its whole
+ * size is written (the part past the outlier lists is scratch of this
+ * call). W is only read. */
 int qlora_quantize(const float* W, int K, int N, int fmt, void* codes,
                    void* scales, void* stream);
 
 /* qlora_quantize for a multi-head weight W [heads, K, N / heads] (see
  * Layouts): the same codes and scales as qlora_quantize of the equivalent
  * [K, N] matrix. heads must divide N and N / heads be a multiple of 64
- * (EINVAL / EUNSUPPORTED otherwise); heads = 1 is qlora_quantize. */
+ * (EINVAL / EUNSUPPORTED otherwise); heads = 1 is qlora_quantize. QLORA_W8O
+ * takes heads = 1 only (EUNSUPPORTED otherwise). */
 int qlora_quantize_heads(const float* W, int heads, int K, int N, int fmt,
                          void* codes, void* scales, void* stream);
 

@@ -20,9 +20,9 @@ LIB_PATH = os.environ.get("QLORA_LIB") or os.path.join(HERE, "libqlora.so")
 
 QLORA_OK, QLORA_EINVAL, QLORA_EUNSUPPORTED, QLORA_EWORKSPACE, QLORA_ERANGE, QLORA_EHIP = range(6)
 QLORA_F32, QLORA_BF16 = 0, 1
-QLORA_W8, QLORA_W4G128 = 0, 1
+QLORA_W8, QLORA_W4G128, QLORA_W8O = 0, 1, 2
 
-_FMT = {"w8": QLORA_W8, "w4g128": QLORA_W4G128}
+_FMT = {"w8": QLORA_W8, "w4g128": QLORA_W4G128, "w8o": QLORA_W8O}
 
 
 class QloraError(RuntimeError):
@@ -53,7 +53,7 @@ EXPORTS = (
     "qlora_fwd_workspace", "qlora_fwd", "qlora_bwd_workspace", "qlora_bwd",
     "qlora_quantize_rows", "qlora_fwd_acc", "qlora_fwd_timed", "qlora_bwd_timed",
     "qlora_merge", "qlora_bwd_partial", "qlora_bwd_finish", "qlora_fwd_a8w4",
-    "qlora_quantize_heads",
+    "qlora_quantize_heads", "qlora_outlier_layout",
 )
 
 
@@ -87,6 +87,7 @@ def lib() -> ctypes.CDLL:
     L.qlora_bwd_finish.argtypes = [plin, i, i, vp, vp, vp, sz, vp]
     L.qlora_fwd_a8w4.argtypes = [plin, i, i, vp, vp, vp, vp, sz, vp]
     L.qlora_quantize_heads.argtypes = [vp, i, i, i, i, vp, vp, vp]
+    L.qlora_outlier_layout.argtypes = [i, i, psz, psz, psz, ctypes.POINTER(ctypes.c_int32)]
     for name in EXPORTS[1:]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -136,7 +137,7 @@ class QLinear:
     alpha: float
     fmt: str
     codes: object     # int8 [N, K]  or uint8 [N, K/2]
-    scales: object    # float32 [N] or float16 [N, K/128]
+    scales: object    # float32 [N], float16 [N, K/128], or the w8o side buffer (uint8)
     A: object         # float32 [K, r]
     B: object         # float32 [r, N], or [heads, r, N / heads]
     heads: int = 1
@@ -167,6 +168,9 @@ def qlora_quantize(W, fmt: str = "w8"):
     if fmt == "w8":
         codes = torch.empty((N, K), dtype=torch.int8, device=W.device)
         scales = torch.empty((N,), dtype=torch.float32, device=W.device)
+    elif fmt == "w8o":
+        codes = torch.empty((N, K), dtype=torch.int8, device=W.device)
+        scales = torch.empty((sb,), dtype=torch.uint8, device=W.device)
     else:
         codes = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
         scales = torch.empty((N, K // 128), dtype=torch.float16, device=W.device)
@@ -176,6 +180,31 @@ def qlora_quantize(W, fmt: str = "w8"):
     _check(lib().qlora_quantize_heads(_ptr(W), heads, K, N, _FMT[fmt], _ptr(codes),
                                       _ptr(scales), _stream()), "qlora_quantize_heads")
     return codes, scales
+
+
+def qlora_outlier_layout(K: int, N: int) -> Tuple[int, int, int, int]:
+    """(rowptr, col, val) byte offsets of a w8o side buffer's outlier list,
+    and its capacity."""
+    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    cap = ctypes.c_int32()
+    _check(lib().qlora_outlier_layout(K, N, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
+                                      ctypes.byref(cap)), "qlora_outlier_layout")
+    return a.value, b.value, c.value, cap.value
+
+
+def qlora_outliers(side, K: int, N: int):
+    """Read a w8o side buffer back (device -> host): (header dict with lo, hi,
+    scale, nnz; rowptr int32 [K + 1]; col int32 [nnz]; val float16 [nnz])."""
+    import numpy as np
+    ro, co, vo, _ = qlora_outlier_layout(K, N)
+    raw = side.cpu().numpy()
+    hdr = raw[:16].view(np.float32)
+    nnz = int(raw[12:16].view(np.int32)[0])
+    head = dict(lo=hdr[0], hi=hdr[1], scale=hdr[2], nnz=nnz)
+    rowptr = raw[ro:ro + 4 * (K + 1)].view(np.int32).copy()
+    col = raw[co:co + 4 * nnz].view(np.int32).copy()
+    val = raw[vo:vo + 2 * nnz].view(np.float16).copy()
+    return head, rowptr, col, val
 
 
 def qlora_merge(layer: QLinear):

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include "launch.hpp"
+#include "outlier.hpp"
 #include "qlora.h"
 
 namespace {
@@ -39,7 +40,11 @@ int check_linear(const qlora_linear* L, int M, int dtype) {
   if (st) return st;
   st = check_shape(M, L->K, L->N, L->r);
   if (st) return st;
-  if (L->fmt != QLORA_W8 && L->fmt != QLORA_W4G128) return QLORA_EINVAL;
+  if (L->fmt != QLORA_W8 && L->fmt != QLORA_W4G128 && L->fmt != QLORA_W8O) return QLORA_EINVAL;
+  if (L->fmt == QLORA_W8O) {
+    if (dtype != QLORA_BF16) return QLORA_EUNSUPPORTED;
+    if (L->N >= (1 << 24)) return QLORA_EUNSUPPORTED;
+  }
   if (L->fmt == QLORA_W4G128) {
     if (L->K % 128) return QLORA_EINVAL;
     if (dtype != QLORA_BF16) return QLORA_EUNSUPPORTED;
@@ -63,7 +68,7 @@ inline float lora_s(const qlora_linear* L) {
 }
 
 struct FwdLayout {
-  size_t xq, sx, t, total;
+  size_t xq, sx, t, asum, total;
 };
 FwdLayout fwd_layout(const qlora_linear* L, int M) {
   FwdLayout w{};
@@ -73,6 +78,8 @@ FwdLayout fwd_layout(const qlora_linear* L, int M) {
   w.xq = off; off = align_up(off + (size_t)M * L->K);
   w.sx = off; off = align_up(off + (size_t)M * 4);
   w.t = off; off = align_up(off + (size_t)M * L->r * 4);
+  // row sums of the activation codes (affine weights)
+  w.asum = off; off = align_up(off + (L->fmt == QLORA_W8O ? (size_t)M * 4 : 0));
   w.total = off;
   return w;
 }
@@ -114,7 +121,7 @@ int launch_status() {
 // backward's row tile; the other paths split the rows the same way so that
 // the combine needs nothing but (L, M, dtype).
 int bwd_splits(const qlora_linear* L, int M) {
-  const int bm = bwd_row_block(L->fmt == QLORA_W8 ? 0 : 1, M, L->K, L->r);
+  const int bm = bwd_row_block(L->fmt, M, L->K, L->r);
   return (M + bm - 1) / bm;
 }
 
@@ -157,7 +164,25 @@ int qlora_weight_bytes(int K, int N, int fmt, size_t* codes_bytes,
     *scale_bytes = (size_t)N * (K / 128) * 2;
     return QLORA_OK;
   }
+  if (fmt == QLORA_W8O) {
+    *codes_bytes = (size_t)K * N;
+    *scale_bytes = w8o_layout(K, N).total;
+    return QLORA_OK;
+  }
   return QLORA_EINVAL;
+}
+
+int qlora_outlier_layout(int K, int N, size_t* rowptr_off, size_t* col_off,
+                         size_t* val_off, int32_t* capacity) {
+  if (!rowptr_off || !col_off || !val_off || !capacity) return QLORA_EINVAL;
+  if (K < 16 || N < 16 || K % 16 || N % 16) return QLORA_EINVAL;
+  if (!fits_int(K, N)) return QLORA_ERANGE;
+  const W8OLayout L = w8o_layout(K, N);
+  *rowptr_off = L.rowptr;
+  *col_off = L.col;
+  *val_off = L.val;
+  *capacity = L.cap;
+  return QLORA_OK;
 }
 
 int qlora_quantize(const float* W, int K, int N, int fmt, void* codes,
@@ -172,6 +197,7 @@ int qlora_quantize_heads(const float* W, int heads, int K, int N, int fmt,
   if (st) return st;
   if (heads < 1 || N % heads) return QLORA_EINVAL;
   if (heads > 1 && (N / heads) % 64) return QLORA_EUNSUPPORTED;
+  if (fmt == QLORA_W8O && (heads > 1 || N >= (1 << 24))) return QLORA_EUNSUPPORTED;
   const int hd = N / heads;
   if (!W || !codes || !scales || !aligned16(W) || !aligned16(codes) || !aligned16(scales))
     return QLORA_EINVAL;
@@ -180,6 +206,8 @@ int qlora_quantize_heads(const float* W, int heads, int K, int N, int fmt,
   if (fmt == QLORA_W8)
     launch_quantize_w8(W, K, N, hd, static_cast<int8_t*>(codes),
                        static_cast<float*>(scales), s);
+  else if (fmt == QLORA_W8O)
+    launch_quantize_w8o(W, K, N, static_cast<int8_t*>(codes), scales, s);
   else
     launch_quantize_w4(W, K, N, hd, static_cast<uint8_t*>(codes),
                        static_cast<_Float16*>(scales), s);
@@ -217,6 +245,17 @@ int qlora_fwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
                          static_cast<const int8_t*>(L->codes), sx,
                          static_cast<const float*>(L->scales), t, L->B, head_width(L), L->r,
                          lora_s(L), y, nullptr, s);
+    mark(ev_stop, s);
+  } else if (L->fmt == QLORA_W8O) {
+    int8_t* xq = reinterpret_cast<int8_t*>(at(ws, w.xq));
+    float* sx = reinterpret_cast<float*>(at(ws, w.sx));
+    float* asum = reinterpret_cast<float*>(at(ws, w.asum));
+    launch_rowquant(dtype, x, M, L->K, L->A, L->r, xq, sx, t, s, asum);
+    mark(ev_start, s);
+    for (int rep = 0; rep < repeats; ++rep)
+      launch_gemm_fwd_w8o(M, L->N, L->K, xq, static_cast<const int8_t*>(L->codes), sx, asum,
+                          L->scales, t, L->B, head_width(L), L->r, lora_s(L),
+                          static_cast<uint16_t*>(y), s);
     mark(ev_stop, s);
   } else {
     launch_lora_down(dtype, x, M, L->K, L->A, L->r, t, s);
@@ -289,14 +328,13 @@ int qlora_bwd_partial_timed(const qlora_linear* L, int M, int dtype, const void*
     launch_lora_down(dtype, x, M, L->K, L->A, L->r, tw, s);
     t = tw;
   }
-  const bool w8 = L->fmt == QLORA_W8;
   float* partB = reinterpret_cast<float*>(at(ws, w.pB));
   float* partA = reinterpret_cast<float*>(at(ws, w.pA));
   if (dtype == QLORA_BF16 && dx != nullptr) {
     // one launch: dx, u, and the per-row-block partial sums of dA and dB
     mark(ev_start, s);
     for (int rep = 0; rep < repeats; ++rep)
-      launch_bwd_fused(w8 ? 0 : 1, M, L->K, L->N, static_cast<const uint16_t*>(dy),
+      launch_bwd_fused(L->fmt, M, L->K, L->N, static_cast<const uint16_t*>(dy),
                        L->codes, L->scales, L->B, head_width(L), L->A, t,
                        static_cast<const uint16_t*>(x), L->r, sc,
                        static_cast<uint16_t*>(dx), partA, partB, s);
@@ -414,7 +452,7 @@ int qlora_fwd_acc(const qlora_linear* L, int M, int dtype, const void* x,
                   int32_t* acc, void* ws, size_t ws_bytes, void* stream) {
   int st = check_linear(L, M, dtype);
   if (st) return st;
-  if (L->fmt != QLORA_W8) return QLORA_EUNSUPPORTED;
+  if (L->fmt != QLORA_W8 && L->fmt != QLORA_W8O) return QLORA_EUNSUPPORTED;
   if (!x || !acc || !aligned16(x) || !aligned16(acc)) return QLORA_EINVAL;
   const FwdLayout w = fwd_layout(L, M);
   if (ws_bytes < w.total || !ws || !aligned16(ws)) return QLORA_EWORKSPACE;
@@ -423,10 +461,10 @@ int qlora_fwd_acc(const qlora_linear* L, int M, int dtype, const void* x,
   float* sx = reinterpret_cast<float*>(at(ws, w.sx));
   (void)hipGetLastError();
   launch_rowquant(dtype, x, M, L->K, nullptr, 1, xq, sx, nullptr, s);
+  // the integer product alone: no scale is read
   launch_gemm_fwd_w8(dtype, M, L->N, L->K, xq,
-                     static_cast<const int8_t*>(L->codes), sx,
-                     static_cast<const float*>(L->scales), nullptr, L->B, head_width(L),
-                     L->r, 0.f, nullptr, acc, s);
+                     static_cast<const int8_t*>(L->codes), sx, nullptr, nullptr, L->B,
+                     head_width(L), L->r, 0.f, nullptr, acc, s);
   return launch_status();
 }
 

@@ -39,6 +39,16 @@
 // are added in row-block order by a small second launch. No atomics:
 // results are bitwise reproducible.
 //
+// Outlier-compensated int8 weights (keras-llm-light README, "Simplified
+// Int8Variable quantization"; format in outlier.hpp) take the 64-row tiles:
+// the producers widen each code v - 128 to bf16(c (v - 128) + b') with the
+// weight's one grid step c and code-0 value b', and then write every outlier
+// of the stage over its place in the converted tile as bf16(value) -- the
+// weight the pages reconstruct before the layer runs, built in LDS one stage
+// at a time. The outliers of a stage (its 64 n x the block's 64 k) are read
+// one stage ahead, one per lane, and each is written by the thread that
+// converted that position, after its own write.
+//
 // Two block shapes share this scheme:
 //   * 64-row tiles, 512 threads in two roles (producer waves load and
 //     convert stage kt + 1 while consumer waves multiply stage kt), for
@@ -47,6 +57,7 @@
 //     where sharing each loaded tile among more outputs matters more than
 //     overlapping the steps.
 #include "launch.hpp"
+#include "outlier.hpp"
 #include "ring.hpp"
 
 namespace qlora {
@@ -72,6 +83,11 @@ struct BwdArgs {
   uint16_t* dx;            // [M, K] bf16
   float* partA;            // [row blocks, r, K]
   float* partB;            // [row blocks, r, N]
+  // outlier-compensated weights
+  const W8OHeader* w8o;    // grid step and code-0 value
+  const int* bptr;         // backward cells, outlier.hpp
+  const u32x2* bent;
+  int kg;                  // 16-row k groups
   int tiles_x;
 };
 
@@ -143,14 +159,15 @@ __device__ __forceinline__ float tile_bf16(const int8_t* tile, int row, int e) {
 // kt + 1 into the other buffer, so a compute unit overlaps the matrix work
 // of one wave with the vector work of the other on each SIMD. One barrier
 // per stage hands the buffers over.
-template <bool W4, int BM, int BN, int S, int R>
+template <bool W4, int BM, int BN, int S, int R, bool AFF = false>
 __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
   constexpr int KC = 64;                              // n per stage
   constexpr int RB = W4 ? BN / 2 : BN;                // code bytes per row of n
+  static_assert(!AFF || (!W4 && BN == 64 && KC == kW8OBwdCellN), "affine: int8, 64 x 64 cells");
   // aux tile: a header with the stage's weight scales (int8: sw[n], 64
   // floats; 4-bit: for each n the 16-byte chunk of the scale array that holds
-  // sc[n][k0 / 128]), then the B columns [R][64] float
-  constexpr int HDR = W4 ? 1024 : 256;
+  // sc[n][k0 / 128]; affine weights: none), then the B columns [R][64] float
+  constexpr int HDR = AFF ? 0 : W4 ? 1024 : 256;
   constexpr int AUXI = (HDR + R * 256 + 4095) / 4096;  // aux DMA instructions per producer wave
   constexpr int ASZ = BM * 128, BSZ = KC * RB, XSZ = 4 * AUXI * 1024;
   constexpr int STG = ASZ + BSZ + XSZ;
@@ -317,7 +334,34 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
   //   (4-bit: bf16(q[n][k] sc[n][k0 / 128]) for the 4 n of nq and 8 k);
   //   BU[j][n] = bf16(B[j][n]), 2 n per entry.
   constexpr int NBU = (R * 32 + 255) / 256;
-  auto convert = [&](int slot, int buf) {
+  float cstep = 0.f, cbias = 0.f;
+  if constexpr (AFF) {
+    cstep = a.w8o->scale;
+    cbias = a.w8o->bias_q;
+  }
+  // affine weights: outliers (k, n, value) of a stage, one per lane from the
+  // stage's first entry, and the stage's entry range
+  struct Outl {
+    u32x2 e;
+    int lo, hi;
+  };
+  const int kg0 = k0 / kW8OBwdCellK;
+  const int kg1 = (k0 + BN) / kW8OBwdCellK < a.kg ? (k0 + BN) / kW8OBwdCellK : a.kg;
+  auto outl_range = [&](int st, Outl& o) {
+    o.lo = a.bptr[st * a.kg + kg0];
+    o.hi = a.bptr[st * a.kg + kg1];
+  };
+  auto outl_load = [&](Outl& o) { o.e = a.bent[o.lo + lane]; };
+  // write one outlier over the converted tile: the thread that converted
+  // (k, n) holds n quad n / 4 and k quad (k - k0) / 4
+  auto outl_put = [&](int8_t* CB, uint32_t kn, uint32_t vbits) {
+    const int kl = (int)(kn >> 6) - k0, nl = (int)(kn & 63);
+    const int nqo = nl >> 2, owner = nqo | (((kl >> 2) & 15) << 4);
+    if (ptid == owner && (unsigned)kl < (unsigned)BN)
+      *reinterpret_cast<uint16_t*>(CB + swz128(kl, nqo >> 1) + (nqo & 1) * 8 + 2 * (nl & 3)) =
+          (uint16_t)f32_to_bf16(__uint_as_float(vbits));
+  };
+  auto convert = [&](int slot, int buf, const Outl& ol) {
     const int8_t* Bs = ring + slot * STG + ASZ;
     const int8_t* Xb = Bs + BSZ;
     const float* Xa = reinterpret_cast<const float*>(Xb);
@@ -351,7 +395,8 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
             u32x2{pk_bf16(v0, v1), pk_bf16(v2, v3)};
       }
     } else {
-      const f32x4 swv = *reinterpret_cast<const f32x4*>(Xa + 4 * nq);
+      f32x4 swv = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (!AFF) swv = *reinterpret_cast<const f32x4*>(Xa + 4 * nq);
 #pragma unroll
       for (int h = 0; h < BN / 64; ++h) {
         const int kcol = 4 * (kq0 + 16 * h);
@@ -363,12 +408,30 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int kk2 = 0; kk2 < 4; ++kk2) {
-          const float v0 = (float)(int8_t)(raw[0] >> (8 * kk2)) * swv.x;
-          const float v1 = (float)(int8_t)(raw[1] >> (8 * kk2)) * swv.y;
-          const float v2 = (float)(int8_t)(raw[2] >> (8 * kk2)) * swv.z;
-          const float v3 = (float)(int8_t)(raw[3] >> (8 * kk2)) * swv.w;
+          float v0, v1, v2, v3;
+          if constexpr (AFF) {
+            v0 = __builtin_fmaf((float)(int8_t)(raw[0] >> (8 * kk2)), cstep, cbias);
+            v1 = __builtin_fmaf((float)(int8_t)(raw[1] >> (8 * kk2)), cstep, cbias);
+            v2 = __builtin_fmaf((float)(int8_t)(raw[2] >> (8 * kk2)), cstep, cbias);
+            v3 = __builtin_fmaf((float)(int8_t)(raw[3] >> (8 * kk2)), cstep, cbias);
+          } else {
+            v0 = (float)(int8_t)(raw[0] >> (8 * kk2)) * swv.x;
+            v1 = (float)(int8_t)(raw[1] >> (8 * kk2)) * swv.y;
+            v2 = (float)(int8_t)(raw[2] >> (8 * kk2)) * swv.z;
+            v3 = (float)(int8_t)(raw[3] >> (8 * kk2)) * swv.w;
+          }
           *reinterpret_cast<u32x2*>(CB + swz128(kcol + kk2, nq >> 1) + (nq & 1) * 8) =
               u32x2{pk_bf16(v0, v1), pk_bf16(v2, v3)};
+        }
+      }
+      if constexpr (AFF) {
+        const int cnt = ol.hi - ol.lo, c64 = cnt < 64 ? cnt : 64;
+        for (int e = 0; e < c64; ++e)
+          outl_put(CB, (uint32_t)__builtin_amdgcn_readlane((int)ol.e.x, e),
+                   (uint32_t)__builtin_amdgcn_readlane((int)ol.e.y, e));
+        for (int p = ol.lo + 64; p < ol.hi; ++p) {   // more than 64 in one stage
+          const u32x2 ev = a.bent[p];
+          outl_put(CB, ev.x, ev.y);
         }
       }
     }
@@ -391,7 +454,14 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < UCB; ++j) uacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // affine weights (producers): outliers of the stage converted next (ocur)
+  // and the range of the stage after it (onext)
+  Outl ocur{}, onext{};
   if (producer) {
+    if constexpr (AFF) {
+      outl_range(0, ocur);
+      outl_range(nk > 1 ? 1 : 0, onext);
+    }
     // the block's rows of A, contiguous in memory: (K - k0 or BN) * r floats
     {
       const int rows = K - k0 < BN ? K - k0 : BN;
@@ -424,7 +494,16 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
   __builtin_amdgcn_s_barrier();
-  if (producer) convert(0, 0);
+  if (producer) {
+    if constexpr (AFF) outl_load(ocur);
+    convert(0, 0, ocur);
+    if constexpr (AFF) {
+      // stage 1's outliers are read before the loop queues more loads
+      ocur = onext;
+      outl_load(ocur);
+      outl_range(nk > 2 ? 2 : nk - 1, onext);
+    }
+  }
 
   const int rows_here = M - m0 < BM ? M - m0 : BM;
   // dB operand: t as bf16, lane -> rank (lane % 16), rows 32 c + 8 (lane / 16) + e
@@ -442,8 +521,20 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
     const int pslot = slot == 0 ? S - 1 : slot - 1;  // slot of stage kt - 1 = kt + S - 1
     const int nslot = slot == S - 1 ? 0 : slot + 1;  // slot of stage kt + 1
     if (producer) {
+      // affine weights: read stage kt + 2's outliers ahead of this
+      // iteration's loads, and stage kt + 3's range
+      Outl o2 = onext, o3{};
+      if constexpr (AFF) {
+        if (kt + 2 >= nk) o2.lo = 0;
+        outl_load(o2);
+        outl_range(kt + 3 < nk ? kt + 3 : nk - 1, o3);
+      }
       if (kt + S - 1 < nk) issue(kt + S - 1, pslot);
-      if (kt + 1 < nk) convert(nslot, (kt + 1) & 1);
+      if (kt + 1 < nk) convert(nslot, (kt + 1) & 1, ocur);
+      if constexpr (AFF) {
+        ocur = o2;
+        onext = o3;
+      }
     } else {
       const int8_t* As = ring + slot * STG;
       const int8_t* CB = CB0 + (kt & 1) * CBSZ;
@@ -992,15 +1083,15 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
 }
 
 
-template <bool W4, int BN, int S>
+template <bool W4, int BN, int S, bool AFF = false>
 void launch_pc(BwdArgs a, hipStream_t st) {
   constexpr int BM = 64;
   a.tiles_x = (a.K + BN - 1) / BN;
   const dim3 grid((unsigned)(a.tiles_x * ((a.M + BM - 1) / BM)));
-  if (a.r <= 4) bwd_pc_kernel<W4, BM, BN, S, 4><<<grid, 512, 0, st>>>(a);
-  else if (a.r <= 8) bwd_pc_kernel<W4, BM, BN, S, 8><<<grid, 512, 0, st>>>(a);
-  else if (a.r <= 16) bwd_pc_kernel<W4, BM, BN, S, 16><<<grid, 512, 0, st>>>(a);
-  else bwd_pc_kernel<W4, BM, BN, S, 32><<<grid, 512, 0, st>>>(a);
+  if (a.r <= 4) bwd_pc_kernel<W4, BM, BN, S, 4, AFF><<<grid, 512, 0, st>>>(a);
+  else if (a.r <= 8) bwd_pc_kernel<W4, BM, BN, S, 8, AFF><<<grid, 512, 0, st>>>(a);
+  else if (a.r <= 16) bwd_pc_kernel<W4, BM, BN, S, 16, AFF><<<grid, 512, 0, st>>>(a);
+  else bwd_pc_kernel<W4, BM, BN, S, 32, AFF><<<grid, 512, 0, st>>>(a);
 }
 
 template <bool W4>
@@ -1018,6 +1109,7 @@ void launch_wide(BwdArgs a, hipStream_t st) {
 
 int bwd_row_block(int fmt, int M, int K, int r) {
   (void)r;
+  if (fmt == 2) return 64;                         // affine weights: 64-row tiles only
   const int bn = fmt == 0 ? 64 : 128;
   const long t64 = (long)((M + 63) / 64) * ((K + bn - 1) / bn);
   return t64 <= 512 ? 64 : 128;
@@ -1035,7 +1127,15 @@ void launch_bwd_fused(int fmt, int M, int K, int N, const uint16_t* dy,
   // 64-row tiles (producer/consumer) while they make at most two blocks per
   // compute unit, else the wide 128 x 128 tiles
   const bool small = bwd_row_block(fmt, M, K, r) == 64;
-  if (fmt == 0) {
+  if (fmt == 2) {
+    const W8OLayout L = w8o_layout(K, N);
+    const char* sb = static_cast<const char*>(scales);
+    a.w8o = reinterpret_cast<const W8OHeader*>(sb);
+    a.bptr = reinterpret_cast<const int*>(sb + L.bptr);
+    a.bent = reinterpret_cast<const u32x2*>(sb + L.bent);
+    a.kg = L.kg;
+    launch_pc<false, 64, 3, true>(a, st);
+  } else if (fmt == 0) {
     a.sw = static_cast<const float*>(scales);
     if (small) launch_pc<false, 64, 3>(a, st);
     else launch_wide<false>(a, st);

@@ -8,6 +8,22 @@
 // scaled by alpha / rank; "Introduce QLoRA-like technique", "Highlights": the
 // frozen kernel is int8 with one scale per output channel.)
 //
+// Outlier-compensated weights (keras-llm-light README, "Simplified
+// Int8Variable quantization"; the format is described in outlier.hpp) use the
+// same product with the codes v - 128 of one affine grid for the whole
+// weight, so the epilogue becomes
+//
+//   y[m, n] = sx[m] (c acc[m, n] + b' as[m] + corr[m, n]) + s (t B)[m, n]
+//
+// with c the grid step, b' = b + 128 c the value of code 0, as[m] the row sum
+// of xq (from the row pass), and corr[m, n] = sum over the outliers (k, n) of
+// xq[m, k] (value - grid value). The corrections are added while the
+// activation codes of their k are in LDS: each stage, every wave walks the
+// outliers of its 32-column cells in that 128-wide k block (read one stage
+// ahead, one entry per lane, broadcast with readlane), and its lanes, one
+// per row, add xq[m, k] times the entry's difference into a float32 tile
+// corr [BN][BM] in LDS that the epilogue reads.
+//
 // Both operands are K-contiguous int8 rows, so every tile moves straight from
 // global memory into the LDS stage ring (ring.hpp) with no conversion. A block
 // of 4 waves (2 x 2) owns a BM x BN output tile; a wave owns (BM/2) x (BN/2)
@@ -17,6 +33,7 @@
 // depth pays), 128 x 128 or 128 x 64 with two stages for large grids (LDS per
 // block then allows several blocks per compute unit).
 #include "launch.hpp"
+#include "outlier.hpp"
 #include "ring.hpp"
 
 namespace qlora {
@@ -38,19 +55,29 @@ struct I8Args {
   float s;
   void* y;               // [M, N] float32 or bfloat16
   int32_t* acc_out;      // [M, N] (test hook) or nullptr
+  // outlier-compensated weights
+  const W8OHeader* w8o;  // grid step and bias
+  const float* asum;     // [M] row sums of xq
+  const int* fptr;       // forward cells, outlier.hpp
+  const u32x2* fent;
+  int ng;                // 32-column cells per 128-wide k block
   int tiles_x;
 };
 
-template <int BM, int BN, int S, int R, typename OutT, bool ACC_OUT>
+template <int BM, int BN, int S, int R, typename OutT, bool ACC_OUT, bool AFF>
 __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
   constexpr int BK = 128, ASZ = BM * BK, STG = (BM + BN) * BK;
   constexpr int AI = BM / 32, BI = BN / 32, LPS = AI + BI;   // loads per wave per stage
   constexpr int FM = BM / 32, FN = BN / 32;
+  static_assert(!AFF || BK == kW8OFwdCellK, "a stage is one forward cell deep");
   // after the loop the ring holds the epilogue operands, then one output
   // staging strip per wave
-  constexpr int EPB = (EpiOps<BM, BN, R, true>::kFloats * 4 + 15) / 16 * 16;
+  constexpr int EPB = (EpiOps<BM, BN, R, true, AFF>::kFloats * 4 + 15) / 16 * 16;
   static_assert(EPB + 4 * epi_strip_bytes<OutT, FN>() <= S * STG, "epilogue fits in the ring");
-  __shared__ __attribute__((aligned(1024))) int8_t ring[S * STG];
+  constexpr int CP = corr_pitch<BM>();
+  constexpr int CSZ = AFF ? BN * CP * 4 : 0;          // corr [BN][CP] float
+  __shared__ __attribute__((aligned(1024))) int8_t ring[S * STG + CSZ];
+  float* corr = reinterpret_cast<float*>(ring + S * STG);
 
   const int tid = threadIdx.x, lane = tid & 63, wid = wave_id();
   const int wm = wid >> 1, wn = wid & 1;
@@ -58,8 +85,28 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
   const int M = a.M, N = a.N, K = a.K;
   const int nk = (K + BK - 1) / BK;
 
-  EpiOps<BM, BN, R, true> ep;
-  if constexpr (!ACC_OUT) ep.load(M, N, m0, n0, a.r, a.t, a.B, a.hd, a.sx, a.sw);
+  EpiOps<BM, BN, R, true, AFF> ep;
+  if constexpr (!ACC_OUT) ep.load(M, N, m0, n0, a.r, a.t, a.B, a.hd, a.sx, AFF ? nullptr : a.sw);
+  if constexpr (AFF) ep.load_rows(M, m0, a.asum);
+
+  // AFF: the wave's outlier cells and its rows (lane -> row wm BM/2 + lane)
+  constexpr int WCELLS = BN / 2 / kW8OFwdCellN;       // 32-column cells per wave
+  const int g0 = (n0 + wn * (BN / 2)) / kW8OFwdCellN;
+  const int g1 = g0 + WCELLS < a.ng ? g0 + WCELLS : a.ng;
+  const int crow = wm * (BM / 2) + lane;
+  const bool clive = lane < BM / 2;
+  // entry range of stage kt: [fptr[kt ng + g0], fptr[kt ng + g1]) (empty
+  // when the wave's columns are past N)
+  auto cell_lo = [&](int kt) { return g0 < a.ng ? a.fptr[kt * a.ng + g0] : 0; };
+  auto cell_hi = [&](int kt) { return g0 < a.ng ? a.fptr[kt * a.ng + g1] : 0; };
+  // one entry per lane from p0 (the list has spare entries past its end)
+  auto entries = [&](int p0) { return a.fent[p0 + lane]; };
+  if constexpr (AFF) {
+    if (clive) {
+#pragma unroll 4
+      for (int c = 0; c < BN / 2; ++c) corr[(wn * (BN / 2) + c) * CP + crow] = 0.f;
+    }
+  }
 
   // Wave wid fills rows [wid * BM/4, (wid + 1) * BM/4) of A and the same
   // share of B; one instruction covers 8 rows (8 lanes of 16 bytes per row).
@@ -92,10 +139,31 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
 #pragma unroll
   for (int st = 0; st < S - 1; ++st)
     if (st < nk) issue(st, st);
+  // AFF: entries of stage kt (cur) and the ranges of stages kt, kt + 1
+  int clo = 0, chi = 0, nlo = 0, nhi = 0;
+  u32x2 cur = u32x2{0u, 0u};
+  if constexpr (AFF) {
+    clo = cell_lo(0);
+    chi = cell_hi(0);
+    cur = entries(clo);
+    const int k1 = nk > 1 ? 1 : 0;
+    nlo = cell_lo(k1);
+    nhi = cell_hi(k1);
+  }
   int slot = 0;
   for (int kt = 0; kt < nk; ++kt) {
     wait_stages<LPS, 0, S - 2>(nk - 1 - kt);   // stage kt has landed (this wave)
     __builtin_amdgcn_s_barrier();               // ... for every wave; slot kt-1 is free
+    // AFF: read ahead (before this iteration's loads enter the queue): the
+    // entries of stage kt + 1 and the range of stage kt + 2
+    u32x2 nxt = u32x2{0u, 0u};
+    int n2lo = 0, n2hi = 0;
+    if constexpr (AFF) {
+      nxt = entries(kt + 1 < nk ? nlo : 0);
+      const int k2 = kt + 2 < nk ? kt + 2 : nk - 1;
+      n2lo = cell_lo(k2);
+      n2hi = cell_hi(k2);
+    }
     if (kt + S - 1 < nk) issue(kt + S - 1, slot == 0 ? S - 1 : slot - 1);
     const int8_t* As = ring + slot * STG;
     const int8_t* Bs = As + ASZ;
@@ -115,6 +183,32 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
+    if constexpr (AFF) {
+      // corr[n][m] += xq[m, k] d for the stage's outliers (k, n, d) of this
+      // wave's cells; a wave owns its rows and columns of corr
+      auto add = [&](uint32_t kn, float d) {
+        const int nl = (int)(kn >> 7) - n0, kl = (int)(kn & 127);
+        if (clive && (unsigned)nl < (unsigned)BN) {
+          const float xv = (float)As[swz128(crow, kl >> 4) + (kl & 15)];
+          float* cp = corr + nl * CP + crow;
+          *cp = __builtin_fmaf(xv, d, *cp);
+        }
+      };
+      const int cnt = chi - clo;
+      const int c64 = cnt < 64 ? cnt : 64;
+      for (int e = 0; e < c64; ++e)
+        add((uint32_t)__builtin_amdgcn_readlane((int)cur.x, e),
+            __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)cur.y, e)));
+      for (int p = clo + 64; p < chi; ++p) {          // more than 64 in one stage
+        const u32x2 ev = a.fent[p];
+        add(ev.x, __uint_as_float(ev.y));
+      }
+      cur = nxt;
+      clo = nlo;
+      chi = nhi;
+      nlo = n2lo;
+      nhi = n2hi;
+    }
     slot = slot == S - 1 ? 0 : slot + 1;
   }
 
@@ -133,21 +227,23 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
     float* E = reinterpret_cast<float*>(ring);
     __syncthreads();                 // every wave is done with the ring
     ep.store(E, M, N, m0, n0, a.r);
+    if constexpr (AFF) ep.store_rows(E, M, m0, a.w8o->bias_q);
     __syncthreads();
-    epilogue_lowrank<BM, BN, R, true>(acc, E, M, N, m0, n0, wm * (BM / 2), wn * (BN / 2),
-                                      a.s, reinterpret_cast<OutT*>(a.y),
-                                      ring + EPB + wid * epi_strip_bytes<OutT, FN>());
+    epilogue_lowrank<BM, BN, R, true, AFF>(acc, E, M, N, m0, n0, wm * (BM / 2), wn * (BN / 2),
+                                           a.s, reinterpret_cast<OutT*>(a.y),
+                                           ring + EPB + wid * epi_strip_bytes<OutT, FN>(), corr,
+                                           AFF ? a.w8o->scale : 1.f);
   }
 }
 
-template <int BM, int BN, int S, typename OutT, bool ACC>
+template <int BM, int BN, int S, typename OutT, bool ACC, bool AFF = false>
 void launch_tiles(I8Args a, hipStream_t st) {
   a.tiles_x = (a.N + BN - 1) / BN;
   const dim3 grid((unsigned)(a.tiles_x * ((a.M + BM - 1) / BM)));
-  if (a.r <= 4) fwd_i8_kernel<BM, BN, S, 4, OutT, ACC><<<grid, 256, 0, st>>>(a);
-  else if (a.r <= 8) fwd_i8_kernel<BM, BN, S, 8, OutT, ACC><<<grid, 256, 0, st>>>(a);
-  else if (a.r <= 16) fwd_i8_kernel<BM, BN, S, 16, OutT, ACC><<<grid, 256, 0, st>>>(a);
-  else fwd_i8_kernel<BM, BN, S, 32, OutT, ACC><<<grid, 256, 0, st>>>(a);
+  if (a.r <= 4) fwd_i8_kernel<BM, BN, S, 4, OutT, ACC, AFF><<<grid, 256, 0, st>>>(a);
+  else if (a.r <= 8) fwd_i8_kernel<BM, BN, S, 8, OutT, ACC, AFF><<<grid, 256, 0, st>>>(a);
+  else if (a.r <= 16) fwd_i8_kernel<BM, BN, S, 16, OutT, ACC, AFF><<<grid, 256, 0, st>>>(a);
+  else fwd_i8_kernel<BM, BN, S, 32, OutT, ACC, AFF><<<grid, 256, 0, st>>>(a);
 }
 
 template <typename OutT, bool ACC>
@@ -171,6 +267,26 @@ void launch_gemm_fwd_w8(int dtype, int M, int N, int K, const int8_t* xq,
   if (acc_out != nullptr) launch_shape<float, true>(a, st);
   else if (dtype == 0) launch_shape<float, false>(a, st);
   else launch_shape<uint16_t, false>(a, st);
+}
+
+void launch_gemm_fwd_w8o(int M, int N, int K, const int8_t* xq, const int8_t* codes,
+                         const float* sx, const float* asum, const void* side,
+                         const float* t, const float* B, int hd, int r, float s,
+                         uint16_t* y, hipStream_t st) {
+  const W8OLayout L = w8o_layout(K, N);
+  const char* sb = static_cast<const char*>(side);
+  I8Args a{};
+  a.M = M; a.N = N; a.K = K; a.xq = xq; a.codes = codes; a.sx = sx; a.sw = nullptr;
+  a.t = t; a.B = B; a.hd = hd; a.r = r; a.s = s; a.y = y; a.acc_out = nullptr;
+  a.w8o = reinterpret_cast<const W8OHeader*>(sb);
+  a.asum = asum;
+  a.fptr = reinterpret_cast<const int*>(sb + L.fptr);
+  a.fent = reinterpret_cast<const u32x2*>(sb + L.fent);
+  a.ng = L.ng;
+  // the correction tile takes LDS: 64 x 64 (three stages) or 128 x 64 (two)
+  const long t64 = (long)((M + 63) / 64) * ((N + 63) / 64);
+  if (t64 <= 2 * kCUs) launch_tiles<64, 64, 3, uint16_t, false, true>(a, st);
+  else launch_tiles<128, 64, 2, uint16_t, false, true>(a, st);
 }
 
 }  // namespace qlora

@@ -17,14 +17,20 @@ void launch_quantize_w8(const float* W, int K, int N, int hd, int8_t* codes,
                         float* scales, hipStream_t st);
 void launch_quantize_w4(const float* W, int K, int N, int hd, uint8_t* packed,
                         _Float16* scales, hipStream_t st);
+// Outlier-compensated int8 weight (outlier.hpp): codes int8 [N, K] and the
+// side buffer (w8o_layout(K, N).total bytes); W is a plain [K, N].
+void launch_quantize_w8o(const float* W, int K, int N, int8_t* codes, void* side,
+                         hipStream_t st);
 // int8 weight with the adapter merged in, re-quantized (r <= 32); the
 // outputs must not overlap the inputs.
 void launch_merge_w8(const int8_t* codes, const float* sw, const float* A,
                      const float* B, int hd, int K, int N, int r, float s,
                      int8_t* codes_out, float* scales_out, hipStream_t st);
 
+// asum (optional): float32 [M] row sums of xq
 void launch_rowquant(int dtype, const void* x, int M, int K, const float* A,
-                     int r, int8_t* xq, float* sx, float* t, hipStream_t st);
+                     int r, int8_t* xq, float* sx, float* t, hipStream_t st,
+                     float* asum = nullptr);
 void launch_lora_down(int dtype, const void* x, int M, int K, const float* A,
                       int r, float* t, hipStream_t st);
 
@@ -33,6 +39,12 @@ void launch_gemm_fwd_w8(int dtype, int M, int N, int K, const int8_t* xq,
                         const int8_t* codes, const float* sx, const float* sw,
                         const float* t, const float* B, int hd, int r, float s,
                         void* y, int32_t* acc_out, hipStream_t st);
+// Outlier-compensated int8 weight (outlier.hpp) with int8 activations:
+// y = sx[m] (c acc + b' asum[m] + corr) + s t B (bf16 y)
+void launch_gemm_fwd_w8o(int M, int N, int K, const int8_t* xq, const int8_t* codes,
+                         const float* sx, const float* asum, const void* side,
+                         const float* t, const float* B, int hd, int r, float s,
+                         uint16_t* y, hipStream_t st);
 // 4-bit weights: the products hold the scales of up to this many 128-wide k
 // groups per block in LDS (K <= 16384).
 constexpr int kW4MaxGroups = 128;

@@ -1,0 +1,93 @@
+// Side buffer of the outlier-compensated int8 weight (keras-llm-light README,
+// "Simplified Int8Variable quantization": the weight is cut at its 0.1th and
+// 99.9th percentiles, stored as 8-bit codes of an affine grid, and the
+// elements outside the cut are kept as fp16 values at their positions).
+//
+// The codes live in the layer's `codes` array, int8 [N, K] = grid index - 128.
+// Everything else lives in one side buffer (the layer's `scales` pointer),
+// sections 256-byte aligned:
+//
+//   header      W8OHeader (the public part first)
+//   rowptr      int32 [K + 1]     outliers of weight row k (input k):
+//   col         int32 [cap]         [rowptr[k], rowptr[k + 1]) in n order
+//   val         fp16  [cap]
+//   fptr, fent  the same outliers for the forward product, grouped by cell
+//               (k / 128, n / 32) in cell order, (k, n) order inside a cell:
+//               fptr int32 [NKB * NG + 1], fent {(n << 7) | k % 128,
+//               correction} [cap + 64]; correction = value - the grid's
+//               reconstruction at that position
+//   bptr, bent  grouped by cell (n / 64, k / 16), (k, n) order inside:
+//               bptr int32 [NNB * KG + 1], bent {(k << 6) | n % 64, value}
+//               [cap + 64]
+//   scratch     used while quantizing only: per-(64-column tile, k) row
+//               counts, per-(64-row tile, 32-column group) counts, the
+//               16-row group counts, the select histograms
+//
+// cap bounds the outlier count: with nearest-rank cuts at ranks
+// ceil(n / 1000) and ceil(999 n / 1000) of n = K N elements, at most
+// floor(n / 1000) elements lie on each side. The entry arrays have 64 spare
+// entries so that a wave may read 64 entries from any start inside the list.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qlora {
+
+struct W8OHeader {
+  // public (qlora_outlier_header in include/qlora.h)
+  float lo, hi, scale;       // cut and grid step; bias = lo
+  int32_t nnz;               // outliers stored
+  // library-internal
+  float inv;                 // 255 / (hi - lo), or 0
+  float bias_q;              // lo + 128 scale: the reconstruction of code 0
+  int32_t cap;
+  uint32_t key[2];           // order keys found by the selection
+  int32_t rem[2];            // ranks still to resolve inside the key prefix
+};
+
+constexpr int kW8OFwdCellK = 128;   // k per forward cell (the forward's stage)
+constexpr int kW8OFwdCellN = 32;    // n per forward cell (a wave's columns)
+constexpr int kW8OBwdCellN = 64;    // n per backward cell (the backward's stage)
+constexpr int kW8OBwdCellK = 16;    // k per backward cell
+constexpr int kW8OPad = 64;         // spare entries after each entry list
+constexpr int kSelBins = 2048;      // histogram bins of one selection pass
+
+struct W8OLayout {
+  int K, N, cap, nkb, ng, nnb, kg, nkt;
+  size_t rowptr, col, val, fptr, fent, bptr, bent;   // byte offsets
+  size_t cnt_r, fcnt, bcell, rowtot, fcell, hist;     // scratch
+  size_t total;
+};
+
+inline size_t w8o_align(size_t v) { return (v + 255) / 256 * 256; }
+
+inline W8OLayout w8o_layout(int K, int N) {
+  W8OLayout L{};
+  L.K = K; L.N = N;
+  const long long n = (long long)K * N;
+  L.cap = (int)(2 * (n / 1000) + 2);
+  L.nkb = (K + kW8OFwdCellK - 1) / kW8OFwdCellK;
+  L.ng = (N + kW8OFwdCellN - 1) / kW8OFwdCellN;
+  L.nnb = (N + kW8OBwdCellN - 1) / kW8OBwdCellN;
+  L.kg = K / kW8OBwdCellK;
+  L.nkt = (K + 63) / 64;
+  size_t off = w8o_align(sizeof(W8OHeader));
+  L.rowptr = off; off = w8o_align(off + 4 * ((size_t)K + 1));
+  L.col = off;    off = w8o_align(off + 4 * (size_t)L.cap);
+  L.val = off;    off = w8o_align(off + 2 * (size_t)L.cap);
+  L.fptr = off;   off = w8o_align(off + 4 * ((size_t)L.nkb * L.ng + 1));
+  L.fent = off;   off = w8o_align(off + 8 * ((size_t)L.cap + kW8OPad));
+  L.bptr = off;   off = w8o_align(off + 4 * ((size_t)L.nnb * L.kg + 1));
+  L.bent = off;   off = w8o_align(off + 8 * ((size_t)L.cap + kW8OPad));
+  L.cnt_r = off;  off = w8o_align(off + 4 * (size_t)L.nnb * K);
+  L.fcnt = off;   off = w8o_align(off + 4 * (size_t)L.nkt * L.ng);
+  L.bcell = off;  off = w8o_align(off + 4 * (size_t)L.nnb * L.kg);
+  L.rowtot = off; off = w8o_align(off + 4 * (size_t)K);
+  L.fcell = off;  off = w8o_align(off + 4 * (size_t)L.nkb * L.ng);
+  L.hist = off;   off = w8o_align(off + 4 * 2 * (size_t)kSelBins);
+  L.total = off;
+  return L;
+}
+
+}  // namespace qlora

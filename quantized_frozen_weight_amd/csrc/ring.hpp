@@ -73,7 +73,11 @@ __device__ __forceinline__ int swz128(int row, int c) {
 
 // ---------------------------------------------------------------------------
 // Low-rank epilogue: out[m, n] = fma(s, sum_j P[m, j] Q(j, n), base[m, n])
-// with base = float(acc) * (rs[m] * cs[n]) or the float accumulator itself.
+// with base = float(acc) * (rs[m] * cs[n]) or the float accumulator itself,
+// or (affine weights, AFF) base = rs[m] * (c * acc + ra[m] + corr[n][m]) with
+// one grid step c for the whole weight, a per-row term ra[m] = b * as[m]
+// (b the grid's bias, as[m] a row sum of the activation codes) and a
+// per-output correction kept in LDS.
 // The rank-R product runs on v_mfma_f32_16x16x4_f32 (float32 operands and
 // accumulation), R / 4 instructions per 16 x 16 block, and lands in the same
 // lane layout as the main accumulator. The block's operands are fetched into
@@ -82,13 +86,14 @@ __device__ __forceinline__ int swz128(int row, int c) {
 // loop has released the ring:
 //   ts [BM][R]   P rows of the tile, ranks past r zero
 //   qs [R][BN]   Q of the tile's columns, ranks past r zero
-//   rsv [BM], csv [BN]
+//   rsv [BM], csv [BN]             (SCALED)
+//   rav [BM]                       (AFF)
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int R, bool SCALED> struct EpiOps {
-  static constexpr int kFloats = (BM + BN) * R + BM + BN;
+template <int BM, int BN, int R, bool SCALED, bool AFF = false> struct EpiOps {
+  static constexpr int kFloats = (BM + BN) * R + BM + BN + (AFF ? BM : 0);
   static constexpr int NT = (BM * R + 255) / 256;
   static constexpr int NQ = (BN * R + 255) / 256;
-  float t[NT], q[NQ], rs, cs;
+  float t[NT], q[NQ], rs, cs, ra;
 
   // P float32 [M, r]; Q(j, n) = Q[head_index(j, n, r, hd)] ([r][N], or
   // [heads][r][hd]); rsrc [M] / csrc [N]
@@ -120,6 +125,14 @@ template <int BM, int BN, int R, bool SCALED> struct EpiOps {
     }
   }
 
+  // AFF: the row sums as[M] of the activation codes (the grid's bias times
+  // them is the per-row term); read like the scales above.
+  __device__ __forceinline__ void load_rows(int M, int m0, const float* __restrict__ asrc) {
+    const int tid = threadIdx.x;
+    const int im = m0 + (tid < BM ? tid : BM - 1);
+    ra = asrc[im < M ? im : M - 1];
+  }
+
   __device__ __forceinline__ void store(float* E, int M, int N, int m0, int n0, int r) const {
     const int tid = threadIdx.x;
 #pragma unroll
@@ -139,7 +152,17 @@ template <int BM, int BN, int R, bool SCALED> struct EpiOps {
       if (tid < BN) E[(BM + BN) * R + BM + tid] = n0 + tid < N ? cs : 0.f;
     }
   }
+
+  // AFF: rav[m] = bias * as[m]
+  __device__ __forceinline__ void store_rows(float* E, int M, int m0, float bias) const {
+    const int tid = threadIdx.x;
+    if (tid < BM) E[(BM + BN) * R + BM + BN + tid] = m0 + tid < M ? bias * ra : 0.f;
+  }
 };
+
+// Row pitch (floats) of the AFF correction tile corr [BN][BM + 4]: the pad
+// spreads the 16 columns that one epilogue read touches over all banks.
+template <int BM> constexpr int corr_pitch() { return BM + 4; }
 
 // LDS bytes of one wave's output staging strip in epilogue_lowrank: 16 rows
 // of FN * 16 outputs, each row padded by 16 bytes (so that the four row
@@ -156,16 +179,20 @@ constexpr int epi_strip_bytes() {
 // one 16-row strip at a time is written there in the accumulator layout and
 // read back as 16-byte pieces of rows, so each global store instruction
 // writes whole 16-byte runs of a row instead of one element per lane.
-template <int BM, int BN, int R, bool SCALED, typename OutT, typename AccT, int FM, int FN>
+template <int BM, int BN, int R, bool SCALED, bool AFF = false, typename OutT, typename AccT,
+          int FM, int FN>
 __device__ __forceinline__ void epilogue_lowrank(const AccT (&acc)[FM][FN], const float* E,
                                                  int M, int N, int m0, int n0, int wr0,
                                                  int wc0, float s, OutT* __restrict__ out,
-                                                 int8_t* strip) {
+                                                 int8_t* strip, const float* corr = nullptr,
+                                                 float cstep = 1.f) {
+  static_assert(!AFF || SCALED, "the affine form uses the row scales");
   const int lane = threadIdx.x & 63;
   const float* ts = E;
   const float* qs = E + BM * R;
   const float* rsv = E + (BM + BN) * R;
   const float* csv = rsv + BM;
+  const float* rav = csv + BN;
   f32x4 low[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -198,11 +225,18 @@ __device__ __forceinline__ void epilogue_lowrank(const AccT (&acc)[FM][FN], cons
     for (int jn = 0; jn < FN; ++jn) {
       const int nl = wc0 + jn * 16 + (lane & 15);
       const float csn = SCALED ? csv[nl] : 1.f;
+      f32x4 cv = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (AFF)
+        cv = *reinterpret_cast<const f32x4*>(corr + nl * corr_pitch<BM>() + wr0 + i * 16 + (lane >> 4) * 4);
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int rl = (lane >> 4) * 4 + ii;             // row inside the strip
-        const float base = SCALED ? (float)acc[i][jn][ii] * (rsv[wr0 + i * 16 + rl] * csn)
-                                  : (float)acc[i][jn][ii];
+        const int ml = wr0 + i * 16 + rl;
+        float base;
+        if constexpr (AFF)
+          base = rsv[ml] * __builtin_fmaf(cstep, (float)acc[i][jn][ii], rav[ml] + cv[ii]);
+        else
+          base = SCALED ? (float)acc[i][jn][ii] * (rsv[ml] * csn) : (float)acc[i][jn][ii];
         store_out(reinterpret_cast<OutT*>(strip + rl * PITCH) + jn * 16 + (lane & 15),
                   __builtin_fmaf(s, low[i][jn][ii], base));
       }

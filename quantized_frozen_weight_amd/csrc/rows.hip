@@ -3,6 +3,8 @@
 //
 //   forward:  t[m, :] = x[m, :] A            (adapter down projection, float32)
 //             xq, sx  = abs-max int8 codes and scale of row m (int8 weights)
+//             as[m]   = sum_k xq[m, k] (optional: the affine weights' bias
+//                       term, outlier.hpp)
 //   backward: u[m, :] = dy[m, :] B^T         (gradient reaching the adapter)
 //             dys     = bf16(dy[m, n] * sw[n])   (int8 weights, bf16 compute:
 //                       the channel scale folded into the gradient rows that
@@ -135,7 +137,7 @@ template <typename T, int R, int MODE, bool HOLD>
 __global__ __launch_bounds__(256) void row_kernel(
     const typename Elem<T>::type* __restrict__ rows, int M, int L,
     const float* __restrict__ W, int hd, int r, float* __restrict__ out_r,
-    int8_t* __restrict__ xq, float* __restrict__ sx,
+    int8_t* __restrict__ xq, float* __restrict__ sx, float* __restrict__ asum,
     const float* __restrict__ sw, uint16_t* __restrict__ dys) {
   constexpr int SL = Slice<R>::len;
   extern __shared__ __attribute__((aligned(16))) float Ws[];
@@ -166,6 +168,7 @@ __global__ __launch_bounds__(256) void row_kernel(
   }
 
   QuantParams qp{0.f, 0.f, false};
+  int csum = 0;                      // sum of this lane's codes (asum)
   float acc[R];
 #pragma unroll
   for (int j = 0; j < R; ++j) acc[j] = 0.f;
@@ -204,8 +207,10 @@ __global__ __launch_bounds__(256) void row_kernel(
         if (qp.live) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            lo |= (uint32_t)(quant_code(v[e], qp.inv, 127.f) & 0xff) << (8 * e);
-            hi |= (uint32_t)(quant_code(v[e + 4], qp.inv, 127.f) & 0xff) << (8 * e);
+            const int q0 = quant_code(v[e], qp.inv, 127.f), q1 = quant_code(v[e + 4], qp.inv, 127.f);
+            lo |= (uint32_t)(q0 & 0xff) << (8 * e);
+            hi |= (uint32_t)(q1 & 0xff) << (8 * e);
+            csum += q0 + q1;
           }
         }
         *reinterpret_cast<u32x2*>(xq + (long)row * L + 8 * c) = u32x2{lo, hi};
@@ -272,11 +277,16 @@ __global__ __launch_bounds__(256) void row_kernel(
     if (lane < r) out_r[(long)row * r + lane] = mine;
   }
   if (MODE == kFwdQuant && lane == 0) sx[row] = qp.scale;
+  if (MODE == kFwdQuant && asum != nullptr) {
+    // |sum| <= 127 K < 2^24 for the shapes the library takes: exact in float
+    const float tot = wave_sum((float)csum);
+    if (lane == 0) asum[row] = tot;
+  }
 }
 
 template <typename T, int R, int MODE>
 void row_launch(const void* rows, int M, int L, const float* W, int hd, int r,
-                float* out_r, int8_t* xq, float* sx, const float* sw,
+                float* out_r, int8_t* xq, float* sx, float* asum, const float* sw,
                 uint16_t* dys, hipStream_t st) {
   dim3 grid((M + kRowsPerBlock - 1) / kRowsPerBlock);
   const auto* p = reinterpret_cast<const typename Elem<T>::type*>(rows);
@@ -287,50 +297,51 @@ void row_launch(const void* rows, int M, int L, const float* W, int hd, int r,
     lds = (MODE == kBwd ? (size_t)R * sld : (size_t)(sld / 8) * (8 * R + 4)) * sizeof(float);
   if (L <= kHoldChunks * 512)
     row_kernel<T, R, MODE, true><<<grid, 256, lds, st>>>(p, M, L, W, hd, r, out_r, xq, sx,
-                                                         sw, dys);
+                                                         asum, sw, dys);
   else
     row_kernel<T, R, MODE, false><<<grid, 256, lds, st>>>(p, M, L, W, hd, r, out_r, xq, sx,
-                                                          sw, dys);
+                                                          asum, sw, dys);
 }
 
 template <typename T, int MODE>
 void row_dispatch_r(int r, const void* rows, int M, int L, const float* W, int hd,
-                    float* out_r, int8_t* xq, float* sx, const float* sw,
+                    float* out_r, int8_t* xq, float* sx, float* asum, const float* sw,
                     uint16_t* dys, hipStream_t st) {
-  if (r <= 1) row_launch<T, 1, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, sw, dys, st);
-  else if (r <= 2) row_launch<T, 2, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, sw, dys, st);
-  else if (r <= 4) row_launch<T, 4, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, sw, dys, st);
-  else if (r <= 8) row_launch<T, 8, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, sw, dys, st);
-  else if (r <= 16) row_launch<T, 16, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, sw, dys, st);
-  else row_launch<T, 32, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, sw, dys, st);
+  if (r <= 1) row_launch<T, 1, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, asum, sw, dys, st);
+  else if (r <= 2) row_launch<T, 2, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, asum, sw, dys, st);
+  else if (r <= 4) row_launch<T, 4, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, asum, sw, dys, st);
+  else if (r <= 8) row_launch<T, 8, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, asum, sw, dys, st);
+  else if (r <= 16) row_launch<T, 16, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, asum, sw, dys, st);
+  else row_launch<T, 32, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, asum, sw, dys, st);
 }
 
 }  // namespace
 
 void launch_rowquant(int dtype, const void* x, int M, int K, const float* A,
-                     int r, int8_t* xq, float* sx, float* t, hipStream_t st) {
+                     int r, int8_t* xq, float* sx, float* t, hipStream_t st,
+                     float* asum) {
   const int rr = t == nullptr ? 1 : r;
   if (dtype == 0)
-    row_dispatch_r<F32, kFwdQuant>(rr, x, M, K, A, K, t, xq, sx, nullptr, nullptr, st);
+    row_dispatch_r<F32, kFwdQuant>(rr, x, M, K, A, K, t, xq, sx, asum, nullptr, nullptr, st);
   else
-    row_dispatch_r<BF16, kFwdQuant>(rr, x, M, K, A, K, t, xq, sx, nullptr, nullptr, st);
+    row_dispatch_r<BF16, kFwdQuant>(rr, x, M, K, A, K, t, xq, sx, asum, nullptr, nullptr, st);
 }
 
 void launch_lora_down(int dtype, const void* x, int M, int K, const float* A,
                       int r, float* t, hipStream_t st) {
   if (dtype == 0)
-    row_dispatch_r<F32, kFwdT>(r, x, M, K, A, K, t, nullptr, nullptr, nullptr, nullptr, st);
+    row_dispatch_r<F32, kFwdT>(r, x, M, K, A, K, t, nullptr, nullptr, nullptr, nullptr, nullptr, st);
   else
-    row_dispatch_r<BF16, kFwdT>(r, x, M, K, A, K, t, nullptr, nullptr, nullptr, nullptr, st);
+    row_dispatch_r<BF16, kFwdT>(r, x, M, K, A, K, t, nullptr, nullptr, nullptr, nullptr, nullptr, st);
 }
 
 void launch_bwd_rows(int dtype, const void* dy, int M, int N, const float* B, int hd,
                      int r, const float* sw, uint16_t* dys, float* u,
                      hipStream_t st) {
   if (dtype == 0)
-    row_dispatch_r<F32, kBwd>(r, dy, M, N, B, hd, u, nullptr, nullptr, sw, nullptr, st);
+    row_dispatch_r<F32, kBwd>(r, dy, M, N, B, hd, u, nullptr, nullptr, nullptr, sw, nullptr, st);
   else
-    row_dispatch_r<BF16, kBwd>(r, dy, M, N, B, hd, u, nullptr, nullptr, sw, dys, st);
+    row_dispatch_r<BF16, kBwd>(r, dy, M, N, B, hd, u, nullptr, nullptr, nullptr, sw, dys, st);
 }
 
 }  // namespace qlora

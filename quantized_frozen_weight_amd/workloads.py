@@ -29,7 +29,7 @@ its own.
 
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 from typing import List, Tuple
 
 import numpy as np
@@ -46,7 +46,7 @@ class Workload:
     r: int
     alpha: float
     dtype: str                     # "f32" or "bf16": x, y, dy, dx
-    wfmt: str                      # "w8" or "w4g128"
+    wfmt: str                      # "w8", "w4g128" or "w8o"
     w_dist: Tuple = ("normal", 0.02)
     x_sigma: float = 1.0
     lora_sigma: float = 0.01
@@ -139,6 +139,13 @@ def as_compute_dtype(a: np.ndarray, dtype: str):
     if dtype == "f32":
         return t.clone(), t.numpy().copy()
     raise ValueError(dtype)
+
+
+def with_format(w: Workload, wfmt: str) -> Workload:
+    """The same workload (same seeds, so the same tensors) stored in another
+    weight format, e.g. the Gemma kernels as outlier-compensated int8
+    ("w8o", keras-llm-light README, "Simplified Int8Variable quantization")."""
+    return replace(w, wfmt=wfmt, name=f"{w.name}_{wfmt}")
 
 
 def small(cid: int, M: int, K: int, N: int, r: int | None = None) -> Workload:

@@ -200,6 +200,42 @@ def test_calls_fail_before_launch(lib):
                                 n.value, None) == Q.QLORA_EINVAL
 
 
+@pytest.mark.parametrize("K,N", [(256, 256), (2048, 16384), (16384, 2048), (208, 80)])
+def test_outlier_format_sizes(lib, K, N):
+    # codes: one byte per weight; the side buffer holds the header, the
+    # outlier list (rowptr [K + 1], col [cap], val [cap]) and more, with
+    # cap = 2 floor(K N / 1000) + 2 (each tail of the nearest-rank cut holds
+    # at most floor(K N / 1000) elements)
+    cb, sb = Q.qlora_weight_bytes(K, N, "w8o")
+    ro, co, vo, cap = Q.qlora_outlier_layout(K, N)
+    assert cb == K * N
+    assert cap == 2 * (K * N // 1000) + 2
+    assert 16 <= ro and ro + 4 * (K + 1) <= co and co + 4 * cap <= vo
+    assert vo + 2 * cap <= sb
+    assert ro % 16 == 0 and co % 16 == 0 and vo % 16 == 0
+
+
+def test_outlier_format_validation(lib):
+    lo = _lin(fmt=Q.QLORA_W8O)
+    st, need = _fwd_ws(lib, lo)
+    assert st == Q.QLORA_OK
+    st_w8, need_w8 = _fwd_ws(lib, _lin())
+    assert need >= need_w8 + 64 * 4 - 256         # plus the row sums of xq
+    assert _fwd_ws(lib, lo, 64, Q.QLORA_F32)[0] == Q.QLORA_EUNSUPPORTED
+    assert _fwd_ws(lib, _lin(fmt=Q.QLORA_W8O, N=1 << 24, K=16))[0] == Q.QLORA_EUNSUPPORTED
+    # one head only at quantization; merge and the 4-bit forward do not apply
+    assert lib.qlora_quantize_heads(FAKE, 4, 128, 256, Q.QLORA_W8O, FAKE, FAKE,
+                                    None) == Q.QLORA_EUNSUPPORTED
+    assert lib.qlora_quantize(FAKE, 100, 64, Q.QLORA_W8O, FAKE, FAKE, None) == Q.QLORA_EINVAL
+    assert lib.qlora_merge(ctypes.byref(lo), FAKE + 4096, FAKE + 8192,
+                           None) == Q.QLORA_EUNSUPPORTED
+    assert lib.qlora_fwd_a8w4(ctypes.byref(lo), 64, Q.QLORA_BF16, FAKE, FAKE, None, FAKE,
+                              need, None) == Q.QLORA_EUNSUPPORTED
+    with pytest.raises(Q.QloraError) as e:
+        Q.qlora_outlier_layout(100, 64)
+    assert e.value.status == Q.QLORA_EINVAL
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(Q, "_lib", None)
     monkeypatch.setattr(Q, "LIB_PATH", str(tmp_path / "absent.so"))
