@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", type=int, default=2, help="1..5 (default: the 32-layer MLP)")
+    p.add_argument("--weights", choices=("w8", "w4g128", "w8o"), default=None,
+                   help="store the workload's weights in this format instead of its own "
+                        "(w8o: outlier-compensated int8, same tensors)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline (0: skip)")
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead")
@@ -70,6 +73,10 @@ class Layer:
         if w.wfmt == "w8":
             self.codes = torch.empty((self.N, self.K), dtype=torch.int8, device=dev)
             self.scales = torch.empty((self.N,), dtype=torch.float32, device=dev)
+        elif w.wfmt == "w8o":
+            # codes, and the side buffer with the cut, the grid and the outliers
+            self.codes = torch.empty((self.N, self.K), dtype=torch.int8, device=dev)
+            self.scales = torch.empty((sb,), dtype=torch.uint8, device=dev)
         else:
             self.codes = torch.empty((self.N, self.K // 2), dtype=torch.uint8, device=dev)
             self.scales = torch.empty((self.N, self.K // 128), dtype=torch.float16, device=dev)
@@ -81,7 +88,7 @@ class Layer:
         self.lin = Q.QLinear(self.K, self.N, w.r, w.alpha, w.wfmt, self.codes,
                              self.scales, self.A, self.B)
         self.cs = self.lin.cstruct()
-        self.fmt = Q.QLORA_W8 if w.wfmt == "w8" else Q.QLORA_W4G128
+        self.fmt = Q._FMT[w.wfmt]
         self.dt = Q.QLORA_BF16 if w.dtype == "bf16" else Q.QLORA_F32
         self.fwd_ws = Q.qlora_fwd_workspace(self.lin, M, self.dt)
         self.bwd_ws = Q.qlora_bwd_workspace(self.lin, M, self.dt)
@@ -104,6 +111,8 @@ def main():
     torch.cuda.set_device(dev)
     lib = Q.lib()
     w = WL.WORKLOADS[args.workload]
+    if args.weights is not None and args.weights != w.wfmt:
+        w = WL.with_format(w, args.weights)
     M = w.M
     layers = [Layer(w, i, dev) for i in range(len(w.layers))]
     ws_bytes = max(max(l.fwd_ws, l.bwd_ws) for l in layers)
@@ -173,7 +182,7 @@ def main():
     # the pages list (kernel [8, 2048, 256], B [8, 4, 256]), forward + backward,
     # next to the same tensors taken as a one-head layer
     heads_leg = None
-    if w.name == "gemma":
+    if w.cid == 4 and w.wfmt == "w8":
         heads_leg = multi_head_leg(torch, dev, lib, check, M)
 
     def step(ev_b=None, repeats=1):
@@ -392,7 +401,7 @@ def dominant_kernel_roofline(w, layers, step, torch):
         flops = sum(2.0 * w.M * l.K * l.N + 4.0 * w.M * w.r * (l.N + l.K) for l in layers) / n
         # the library's tile choice: 64-row producer/consumer blocks while
         # they make at most two per compute unit, else 128 x 128 blocks
-        bn = 64 if w.wfmt == "w8" else 128
+        bn = 128 if w.wfmt == "w4g128" else 64
         names = sorted({"bwd_pc_kernel" if ((w.M + 63) // 64) * ((l.K + bn - 1) // bn) <= 512
                         else "bwd_wide_kernel" for l in layers})
         kernel = (" + ".join(names) + " (fused backward: dx, u, dA and dB partial sums, "
@@ -437,12 +446,17 @@ def cpu_baseline(w, budget_s):
         _, dy = WL.as_compute_dtype(WL.out_grad(w, i), w.dtype)
         if w.wfmt == "w8":
             c, s = O.quantize_w8(W)
+        elif w.wfmt == "w8o":
+            q = O.quantize_w8o(W)
         else:
             c, s = O.quantize_w4(W)
         t0 = time.perf_counter()
         if w.wfmt == "w8":
             O.fwd_w8(x, c, s, A, B, w.alpha, w.dtype)
             O.bwd(x, dy, O.dequant_w8(c, s), A, B, w.alpha, w.dtype)
+        elif w.wfmt == "w8o":
+            O.fwd_w8o(x, q, A, B, w.alpha, w.dtype)
+            O.bwd(x, dy, O.dequant_w8o(q), A, B, w.alpha, w.dtype)
         else:
             O.fwd_w4(x, c, s, A, B, w.alpha, w.dtype)
             O.bwd(x, dy, O.dequant_w4(c, s), A, B, w.alpha, w.dtype)

@@ -45,9 +45,11 @@
 // weight's one grid step c and code-0 value b', and then write every outlier
 // of the stage over its place in the converted tile as bf16(value) -- the
 // weight the pages reconstruct before the layer runs, built in LDS one stage
-// at a time. The outliers of a stage (its 64 n x the block's 64 k) are read
-// one stage ahead, one per lane, and each is written by the thread that
-// converted that position, after its own write.
+// at a time. Producer wave w converts k in [k0 + 16 w, k0 + 16 w + 16), which
+// is one backward cell of the outlier lists (64 n x 16 k); it reads its
+// cell's outliers one stage ahead, one per lane, and each lane writes its
+// outlier after the wave's own conversion stores (in program order, so the
+// outlier wins).
 //
 // Two block shapes share this scheme:
 //   * 64-row tiles, 512 threads in two roles (producer waves load and
@@ -339,25 +341,22 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
     cstep = a.w8o->scale;
     cbias = a.w8o->bias_q;
   }
-  // affine weights: outliers (k, n, value) of a stage, one per lane from the
-  // stage's first entry, and the stage's entry range
+  // affine weights: outliers (k, n, value) of this producer wave's cell in a
+  // stage, one per lane from the cell's first entry, and the cell's range
+  // (past K the range is empty, lo == hi)
   struct Outl {
     u32x2 e;
     int lo, hi;
   };
-  const int kg0 = k0 / kW8OBwdCellK;
-  const int kg1 = (k0 + BN) / kW8OBwdCellK < a.kg ? (k0 + BN) / kW8OBwdCellK : a.kg;
-  auto outl_range = [&](int st, Outl& o) {
-    o.lo = a.bptr[st * a.kg + kg0];
-    o.hi = a.bptr[st * a.kg + kg1];
-  };
+  const int kgw = k0 / kW8OBwdCellK + (pw & 3);       // the wave's 16-row k group
+  const int kgl = kgw < a.kg ? kgw : a.kg, kgh = kgw + 1 < a.kg ? kgw + 1 : a.kg;
+  CellRanges cr;
+  auto outl_range = [&](int st, Outl& o) { cr.get(st, o.lo, o.hi); };
   auto outl_load = [&](Outl& o) { o.e = a.bent[o.lo + lane]; };
-  // write one outlier over the converted tile: the thread that converted
-  // (k, n) holds n quad n / 4 and k quad (k - k0) / 4
+  // write the lane's outlier over the converted tile
   auto outl_put = [&](int8_t* CB, uint32_t kn, uint32_t vbits) {
-    const int kl = (int)(kn >> 6) - k0, nl = (int)(kn & 63);
-    const int nqo = nl >> 2, owner = nqo | (((kl >> 2) & 15) << 4);
-    if (ptid == owner && (unsigned)kl < (unsigned)BN)
+    const int kl = (int)(kn >> 6) - k0, nl = (int)(kn & 63), nqo = nl >> 2;
+    if ((unsigned)kl < (unsigned)BN)
       *reinterpret_cast<uint16_t*>(CB + swz128(kl, nqo >> 1) + (nqo & 1) * 8 + 2 * (nl & 3)) =
           (uint16_t)f32_to_bf16(__uint_as_float(vbits));
   };
@@ -425,13 +424,11 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
         }
       }
       if constexpr (AFF) {
-        const int cnt = ol.hi - ol.lo, c64 = cnt < 64 ? cnt : 64;
-        for (int e = 0; e < c64; ++e)
-          outl_put(CB, (uint32_t)__builtin_amdgcn_readlane((int)ol.e.x, e),
-                   (uint32_t)__builtin_amdgcn_readlane((int)ol.e.y, e));
-        for (int p = ol.lo + 64; p < ol.hi; ++p) {   // more than 64 in one stage
-          const u32x2 ev = a.bent[p];
-          outl_put(CB, ev.x, ev.y);
+        const int cnt = ol.hi - ol.lo;
+        if (lane < cnt) outl_put(CB, ol.e.x, ol.e.y);
+        for (int b0 = 64; b0 < cnt; b0 += 64) {      // more than 64 in one cell
+          const u32x2 ev = a.bent[ol.lo + b0 + lane];
+          if (lane < cnt - b0) outl_put(CB, ev.x, ev.y);
         }
       }
     }
@@ -456,12 +453,9 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
 
   // affine weights (producers): outliers of the stage converted next (ocur)
   // and the range of the stage after it (onext)
-  Outl ocur{}, onext{};
+  Outl ocur{};
   if (producer) {
-    if constexpr (AFF) {
-      outl_range(0, ocur);
-      outl_range(nk > 1 ? 1 : 0, onext);
-    }
+    if constexpr (AFF) cr.init(a.bptr, a.kg, kgl, kgh, nk);
     // the block's rows of A, contiguous in memory: (K - k0 or BN) * r floats
     {
       const int rows = K - k0 < BN ? K - k0 : BN;
@@ -495,13 +489,15 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
   __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
   __builtin_amdgcn_s_barrier();
   if (producer) {
-    if constexpr (AFF) outl_load(ocur);
+    if constexpr (AFF) {
+      outl_range(0, ocur);
+      outl_load(ocur);
+    }
     convert(0, 0, ocur);
     if constexpr (AFF) {
       // stage 1's outliers are read before the loop queues more loads
-      ocur = onext;
+      outl_range(nk > 1 ? 1 : 0, ocur);
       outl_load(ocur);
-      outl_range(nk > 2 ? 2 : nk - 1, onext);
     }
   }
 
@@ -522,18 +518,23 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
     const int nslot = slot == S - 1 ? 0 : slot + 1;  // slot of stage kt + 1
     if (producer) {
       // affine weights: read stage kt + 2's outliers ahead of this
-      // iteration's loads, and stage kt + 3's range
-      Outl o2 = onext, o3{};
+      // iteration's loads
+      Outl o2{};
       if constexpr (AFF) {
-        if (kt + 2 >= nk) o2.lo = 0;
+        outl_range(kt + 2 < nk ? kt + 2 : nk - 1, o2);
         outl_load(o2);
-        outl_range(kt + 3 < nk ? kt + 3 : nk - 1, o3);
+        __builtin_amdgcn_sched_barrier(0);         // ahead of the stage loads
       }
-      if (kt + S - 1 < nk) issue(kt + S - 1, pslot);
+      // (affine weights: past the last stage the loads read the zero page into
+      // the free slot, so that every iteration queues the same loads and the
+      // read-ahead registers can be waited for by count)
+      if (AFF || kt + S - 1 < nk) issue(kt + S - 1, pslot);
       if (kt + 1 < nk) convert(nslot, (kt + 1) & 1, ocur);
       if constexpr (AFF) {
+        // the read-ahead outliers were queued before this iteration's stage
+        // loads: all but those loads are done
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS));
         ocur = o2;
-        onext = o3;
       }
     } else {
       const int8_t* As = ring + slot * STG;
@@ -697,7 +698,7 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
 // product, and the whole block's registers serve one role.
 // W4: 4-bit weights (two codes per byte, fp16 scale per 128 k, carried one
 // stage ahead in a register); else int8.
-template <bool W4, int BM, int BN, int S, int R>
+template <bool W4, int BM, int BN, int S, int R, bool AFF = false>
 __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
   constexpr int KC = 64;                              // n per stage
   constexpr int RB = W4 ? BN / 2 : BN;                // code bytes per row of n
@@ -711,6 +712,8 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
   static_assert(RB == 64 || RB == 128, "code rows of 64 or 128 bytes");
   static_assert(!W4 || (BN == 128 && S == 2),
                 "4-bit: one 128-wide k group per block; the scales ride one stage ahead in a register");
+  static_assert(!AFF || (!W4 && BN == 128 && S == 2 && KC == kW8OBwdCellN),
+                "affine: int8, the outliers of stage kt read during stage kt - 1");
   constexpr int UCB = (R + 15) / 16;                  // u column blocks of 16
   constexpr bool XPRE = BM * BN * 2 <= 8192;          // x tile kept outside the ring
   constexpr int CBSZ = BN * 128;                      // converted codes [BN][64] bf16
@@ -805,8 +808,8 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
     nX[i] = nn;
     isB[i] = j >= 0;
     okX[i] = j < r;
-    okX[i] = okX[i] && !(W4 && j < 0);                 // 4-bit: no channel scales
-    srcX[i] = j < 0 ? (W4 ? zero_chunk(lane) : reinterpret_cast<const int8_t*>(a.sw + nn))
+    okX[i] = okX[i] && !((W4 || AFF) && j < 0);        // 4-bit, affine: no channel scales
+    srcX[i] = j < 0 ? ((W4 || AFF) ? zero_chunk(lane) : reinterpret_cast<const int8_t*>(a.sw + nn))
                     : (j < r ? reinterpret_cast<const int8_t*>(a.B + (long)j * a.hd + nn) : zero_chunk(lane));
   }
   // 4-bit: lane l of wave w loads the scale of n = 16 w + l % 16 of the
@@ -842,6 +845,46 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
     }
   };
 
+  // affine weights: wave w converts k in [k0 + 16 w, +16) and
+  // [k0 + 64 + 16 w, +16), two backward cells of the outlier lists; their
+  // outliers in a stage, one per lane from each cell's first entry, and the
+  // cells' entry ranges
+  float cstep = 0.f, cbias = 0.f;
+  if constexpr (AFF) {
+    cstep = a.w8o->scale;
+    cbias = a.w8o->bias_q;
+  }
+  struct Outl2 {
+    u32x2 e[2];
+    int lo[2], hi[2];
+  };
+  const int kgw0 = k0 / kW8OBwdCellK + wid;
+  CellRanges cr2[2];
+  auto outl_range = [&](int st, Outl2& o) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) cr2[h].get(st, o.lo[h], o.hi[h]);
+  };
+  auto outl_load = [&](Outl2& o) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) o.e[h] = a.bent[o.lo[h] + lane];
+  };
+  auto outl_put = [&](uint32_t kn, uint32_t vbits) {
+    const int kl = (int)(kn >> 6) - k0, nl = (int)(kn & 63), nqo = nl >> 2;
+    if ((unsigned)kl < (unsigned)BN)
+      *reinterpret_cast<uint16_t*>(CB + swz128(kl, nqo >> 1) + (nqo & 1) * 8 + 2 * (nl & 3)) =
+          (uint16_t)f32_to_bf16(__uint_as_float(vbits));
+  };
+  // the first two stages' ranges are read before the stage loads, so that
+  // reading the first entries waits for them alone
+  Outl2 ocur{};
+  if constexpr (AFF) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kg = kgw0 + 4 * h;
+      cr2[h].init(a.bptr, a.kg, kg < a.kg ? kg : a.kg, kg + 1 < a.kg ? kg + 1 : a.kg, nk);
+    }
+  }
+
   f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -856,6 +899,10 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
 #pragma unroll
   for (int st = 0; st < S - 1; ++st)
     if (st < nk) issue(st, st);
+  if constexpr (AFF) {
+    outl_range(0, ocur);
+    outl_load(ocur);
+  }
 
   // t tile into LDS (pitch r); BU rows past the rank stay zero for good
 #pragma unroll
@@ -883,7 +930,17 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
       __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
     }
     __builtin_amdgcn_s_barrier();                    // stage kt landed; CB, BU free
-    if (kt + S - 1 < nk) issue(kt + S - 1, slot == 0 ? S - 1 : slot - 1);
+    // affine weights: read stage kt + 1's outliers ahead of this
+    // iteration's loads
+    Outl2 o1{};
+    if constexpr (AFF) {
+      outl_range(kt + 1 < nk ? kt + 1 : kt, o1);
+      outl_load(o1);
+      __builtin_amdgcn_sched_barrier(0);           // ahead of the stage loads
+    }
+    // (affine weights: every iteration queues the same loads; see the 64-row
+    // kernel)
+    if (AFF || kt + S - 1 < nk) issue(kt + S - 1, slot == 0 ? S - 1 : slot - 1);
     const int8_t* As = ring + slot * STG;
     const int8_t* Bs = As + ASZ;
     const float* Xa = reinterpret_cast<const float*>(Bs + BSZ);
@@ -909,7 +966,8 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
             u32x2{pk_bf16(v0, v1), pk_bf16(v2, v3)};
       }
     } else {
-      const f32x4 swv = *reinterpret_cast<const f32x4*>(Xa + 4 * nq);
+      f32x4 swv = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (!AFF) swv = *reinterpret_cast<const f32x4*>(Xa + 4 * nq);
 #pragma unroll
       for (int h = 0; h < BN / 64; ++h) {
         const int kcol = 4 * (kq0 + 16 * h);
@@ -921,13 +979,37 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int kk2 = 0; kk2 < 4; ++kk2) {
-          const float v0 = (float)(int8_t)(raw[0] >> (8 * kk2)) * swv.x;
-          const float v1 = (float)(int8_t)(raw[1] >> (8 * kk2)) * swv.y;
-          const float v2 = (float)(int8_t)(raw[2] >> (8 * kk2)) * swv.z;
-          const float v3 = (float)(int8_t)(raw[3] >> (8 * kk2)) * swv.w;
+          float v0, v1, v2, v3;
+          if constexpr (AFF) {
+            v0 = __builtin_fmaf((float)(int8_t)(raw[0] >> (8 * kk2)), cstep, cbias);
+            v1 = __builtin_fmaf((float)(int8_t)(raw[1] >> (8 * kk2)), cstep, cbias);
+            v2 = __builtin_fmaf((float)(int8_t)(raw[2] >> (8 * kk2)), cstep, cbias);
+            v3 = __builtin_fmaf((float)(int8_t)(raw[3] >> (8 * kk2)), cstep, cbias);
+          } else {
+            v0 = (float)(int8_t)(raw[0] >> (8 * kk2)) * swv.x;
+            v1 = (float)(int8_t)(raw[1] >> (8 * kk2)) * swv.y;
+            v2 = (float)(int8_t)(raw[2] >> (8 * kk2)) * swv.z;
+            v3 = (float)(int8_t)(raw[3] >> (8 * kk2)) * swv.w;
+          }
           *reinterpret_cast<u32x2*>(CB + swz128(kcol + kk2, nq >> 1) + (nq & 1) * 8) =
               u32x2{pk_bf16(v0, v1), pk_bf16(v2, v3)};
         }
+      }
+      if constexpr (AFF) {
+        // the wave's outliers over its own conversion stores
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int cnt = ocur.hi[h] - ocur.lo[h];
+          if (lane < cnt) outl_put(ocur.e[h].x, ocur.e[h].y);
+          for (int b0 = 64; b0 < cnt; b0 += 64) {    // more than 64 in one cell
+            const u32x2 ev = a.bent[ocur.lo[h] + b0 + lane];
+            if (lane < cnt - b0) outl_put(ev.x, ev.y);
+          }
+        }
+        // the read-ahead outliers were queued before this iteration's stage
+        // loads: all but those loads are done
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS));
+        ocur = o1;
       }
     }
     // BU[j][n] = bf16(B[j][n]), 2 n per entry
@@ -1094,23 +1176,22 @@ void launch_pc(BwdArgs a, hipStream_t st) {
   else bwd_pc_kernel<W4, BM, BN, S, 32, AFF><<<grid, 512, 0, st>>>(a);
 }
 
-template <bool W4>
+template <bool W4, bool AFF = false>
 void launch_wide(BwdArgs a, hipStream_t st) {
   constexpr int BM = 128, BN = 128, S = 2;
   a.tiles_x = (a.K + BN - 1) / BN;
   const dim3 grid((unsigned)(a.tiles_x * ((a.M + BM - 1) / BM)));
-  if (a.r <= 4) bwd_wide_kernel<W4, BM, BN, S, 4><<<grid, 256, 0, st>>>(a);
-  else if (a.r <= 8) bwd_wide_kernel<W4, BM, BN, S, 8><<<grid, 256, 0, st>>>(a);
-  else if (a.r <= 16) bwd_wide_kernel<W4, BM, BN, S, 16><<<grid, 256, 0, st>>>(a);
-  else bwd_wide_kernel<W4, BM, BN, S, 32><<<grid, 256, 0, st>>>(a);
+  if (a.r <= 4) bwd_wide_kernel<W4, BM, BN, S, 4, AFF><<<grid, 256, 0, st>>>(a);
+  else if (a.r <= 8) bwd_wide_kernel<W4, BM, BN, S, 8, AFF><<<grid, 256, 0, st>>>(a);
+  else if (a.r <= 16) bwd_wide_kernel<W4, BM, BN, S, 16, AFF><<<grid, 256, 0, st>>>(a);
+  else bwd_wide_kernel<W4, BM, BN, S, 32, AFF><<<grid, 256, 0, st>>>(a);
 }
 
 }  // namespace
 
 int bwd_row_block(int fmt, int M, int K, int r) {
   (void)r;
-  if (fmt == 2) return 64;                         // affine weights: 64-row tiles only
-  const int bn = fmt == 0 ? 64 : 128;
+  const int bn = fmt == 1 ? 128 : 64;             // k per 64-row tile
   const long t64 = (long)((M + 63) / 64) * ((K + bn - 1) / bn);
   return t64 <= 512 ? 64 : 128;
 }
@@ -1134,7 +1215,8 @@ void launch_bwd_fused(int fmt, int M, int K, int N, const uint16_t* dy,
     a.bptr = reinterpret_cast<const int*>(sb + L.bptr);
     a.bent = reinterpret_cast<const u32x2*>(sb + L.bent);
     a.kg = L.kg;
-    launch_pc<false, 64, 3, true>(a, st);
+    if (small) launch_pc<false, 64, 3, true>(a, st);
+    else launch_wide<false, true>(a, st);
   } else if (fmt == 0) {
     a.sw = static_cast<const float*>(scales);
     if (small) launch_pc<false, 64, 3>(a, st);

@@ -17,12 +17,19 @@
 //
 // with c the grid step, b' = b + 128 c the value of code 0, as[m] the row sum
 // of xq (from the row pass), and corr[m, n] = sum over the outliers (k, n) of
-// xq[m, k] (value - grid value). The corrections are added while the
-// activation codes of their k are in LDS: each stage, every wave walks the
-// outliers of its 32-column cells in that 128-wide k block (read one stage
-// ahead, one entry per lane, broadcast with readlane), and its lanes, one
-// per row, add xq[m, k] times the entry's difference into a float32 tile
-// corr [BN][BM] in LDS that the epilogue reads.
+// xq[m, k] d (d = value - grid value). The corrections are taken while the
+// activation codes of their k are in LDS: wave w owns the 16-column cell
+// [16 w, 16 w + 16) of the 64-wide tile over all its rows, one row per lane
+// (two for 128-row tiles), and holds the cell's outliers (k_e, n_e, d_e) in
+// the stage's 128-wide k block (read one stage ahead, one entry per lane).
+// Each entry is broadcast with readlane; every lane gathers xq[m, k_e] from
+// the stage's tile and adds xq[m, k_e] d_e into its register for column
+// n_e, addressed by the wave-uniform n_e (s_set_gpr_idx). The first eight
+// entries of a stage are straight-line code placed ahead of the stage's
+// products, so their latency hides behind the matrix work; the rest (rare)
+// follow in batches of four. After the loop the 16 columns of every
+// row go through LDS to the waves that own the accumulators and are folded
+// in: acc' = c acc + corr.
 //
 // Both operands are K-contiguous int8 rows, so every tile moves straight from
 // global memory into the LDS stage ring (ring.hpp) with no conversion. A block
@@ -60,7 +67,7 @@ struct I8Args {
   const float* asum;     // [M] row sums of xq
   const int* fptr;       // forward cells, outlier.hpp
   const u32x2* fent;
-  int ng;                // 32-column cells per 128-wide k block
+  int ng;                // 16-column cells per 128-wide k block
   int tiles_x;
 };
 
@@ -69,15 +76,13 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
   constexpr int BK = 128, ASZ = BM * BK, STG = (BM + BN) * BK;
   constexpr int AI = BM / 32, BI = BN / 32, LPS = AI + BI;   // loads per wave per stage
   constexpr int FM = BM / 32, FN = BN / 32;
-  static_assert(!AFF || BK == kW8OFwdCellK, "a stage is one forward cell deep");
+  static_assert(!AFF || (BK == kW8OFwdCellK && BN == 4 * kW8OFwdCellN),
+                "a stage is one forward cell deep; a wave owns one cell's columns");
   // after the loop the ring holds the epilogue operands, then one output
   // staging strip per wave
   constexpr int EPB = (EpiOps<BM, BN, R, true, AFF>::kFloats * 4 + 15) / 16 * 16;
   static_assert(EPB + 4 * epi_strip_bytes<OutT, FN>() <= S * STG, "epilogue fits in the ring");
-  constexpr int CP = corr_pitch<BM>();
-  constexpr int CSZ = AFF ? BN * CP * 4 : 0;          // corr [BN][CP] float
-  __shared__ __attribute__((aligned(1024))) int8_t ring[S * STG + CSZ];
-  float* corr = reinterpret_cast<float*>(ring + S * STG);
+  __shared__ __attribute__((aligned(1024))) int8_t ring[S * STG];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = wave_id();
   const int wm = wid >> 1, wn = wid & 1;
@@ -89,24 +94,20 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
   if constexpr (!ACC_OUT) ep.load(M, N, m0, n0, a.r, a.t, a.B, a.hd, a.sx, AFF ? nullptr : a.sw);
   if constexpr (AFF) ep.load_rows(M, m0, a.asum);
 
-  // AFF: the wave's outlier cells and its rows (lane -> row wm BM/2 + lane)
-  constexpr int WCELLS = BN / 2 / kW8OFwdCellN;       // 32-column cells per wave
-  const int g0 = (n0 + wn * (BN / 2)) / kW8OFwdCellN;
-  const int g1 = g0 + WCELLS < a.ng ? g0 + WCELLS : a.ng;
-  const int crow = wm * (BM / 2) + lane;
-  const bool clive = lane < BM / 2;
-  // entry range of stage kt: [fptr[kt ng + g0], fptr[kt ng + g1]) (empty
-  // when the wave's columns are past N)
-  auto cell_lo = [&](int kt) { return g0 < a.ng ? a.fptr[kt * a.ng + g0] : 0; };
-  auto cell_hi = [&](int kt) { return g0 < a.ng ? a.fptr[kt * a.ng + g1] : 0; };
+  // AFF: the wave's outlier cell, columns [16 wid, 16 wid + 16) of the tile;
+  // entry range of stage kt: [fptr[kt ng + g], fptr[kt ng + g + 1]), empty
+  // when the columns are past N
+  constexpr int CR = BM / 64;                          // correction rows per lane
+  const int g = n0 / kW8OFwdCellN + wid;
+  const int gl = g < a.ng ? g : a.ng, gh = g + 1 < a.ng ? g + 1 : a.ng;
+  CellRanges cr;
   // one entry per lane from p0 (the list has spare entries past its end)
   auto entries = [&](int p0) { return a.fent[p0 + lane]; };
-  if constexpr (AFF) {
-    if (clive) {
-#pragma unroll 4
-      for (int c = 0; c < BN / 2; ++c) corr[(wn * (BN / 2) + c) * CP + crow] = 0.f;
-    }
-  }
+  float corr[CR][kW8OFwdCellN];                      // [row lane + 64 r][column]
+#pragma unroll
+  for (int r = 0; r < CR; ++r)
+#pragma unroll
+    for (int c = 0; c < kW8OFwdCellN; ++c) corr[r][c] = 0.f;
 
   // Wave wid fills rows [wid * BM/4, (wid + 1) * BM/4) of A and the same
   // share of B; one instruction covers 8 rows (8 lanes of 16 bytes per row).
@@ -136,37 +137,67 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
+  // AFF: entries of stage kt (cur) and the ranges of stages kt, kt + 1; the
+  // ranges are read before the stage loads so that reading the first entries
+  // waits for them alone
+  int clo = 0, chi = 0;
+  u32x2 cur = u32x2{0u, 0u};
+  if constexpr (AFF) cr.init(a.fptr, a.ng, gl, gh, nk);
 #pragma unroll
   for (int st = 0; st < S - 1; ++st)
     if (st < nk) issue(st, st);
-  // AFF: entries of stage kt (cur) and the ranges of stages kt, kt + 1
-  int clo = 0, chi = 0, nlo = 0, nhi = 0;
-  u32x2 cur = u32x2{0u, 0u};
   if constexpr (AFF) {
-    clo = cell_lo(0);
-    chi = cell_hi(0);
+    cr.get(0, clo, chi);
     cur = entries(clo);
-    const int k1 = nk > 1 ? 1 : 0;
-    nlo = cell_lo(k1);
-    nhi = cell_hi(k1);
+    // (the first stage's entries, like its operands, have landed before the
+    // loop starts; the loop then never waits for a load it did not count)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
   int slot = 0;
   for (int kt = 0; kt < nk; ++kt) {
     wait_stages<LPS, 0, S - 2>(nk - 1 - kt);   // stage kt has landed (this wave)
     __builtin_amdgcn_s_barrier();               // ... for every wave; slot kt-1 is free
-    // AFF: read ahead (before this iteration's loads enter the queue): the
-    // entries of stage kt + 1 and the range of stage kt + 2
+    // AFF: read ahead (before this iteration's loads enter the queue) the
+    // entries of stage kt + 1
     u32x2 nxt = u32x2{0u, 0u};
-    int n2lo = 0, n2hi = 0;
+    int nlo = 0, nhi = 0;
     if constexpr (AFF) {
-      nxt = entries(kt + 1 < nk ? nlo : 0);
-      const int k2 = kt + 2 < nk ? kt + 2 : nk - 1;
-      n2lo = cell_lo(k2);
-      n2hi = cell_hi(k2);
+      cr.get(kt + 1 < nk ? kt + 1 : kt, nlo, nhi);
+      nxt = entries(nlo);
+      // keep this load ahead of the stage loads: it is then waited for by
+      // count when the next stage takes it over
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + S - 1 < nk) issue(kt + S - 1, slot == 0 ? S - 1 : slot - 1);
+    // (outlier-compensated weights: past the last stage the loads read the
+    // zero page into the free slot, so that every iteration queues the same
+    // loads and a read-ahead register can be waited for by count)
+    if (AFF || kt + S - 1 < nk) issue(kt + S - 1, slot == 0 ? S - 1 : slot - 1);
     const int8_t* As = ring + slot * STG;
     const int8_t* Bs = As + ASZ;
+    // AFF: the stage's first PEEL outliers as straight-line code ahead of the
+    // products, so that their gathers and adds hide behind the matrix work;
+    // entries past the stage's count add 0
+    constexpr int PEEL = 8;
+    const int c0 = n0 + 16 * wid;                    // the wave's first column
+    if constexpr (AFF) {
+      const int cnt = chi - clo;
+      uint32_t kn[PEEL];
+      float d[PEEL], xv[PEEL][CR];
+#pragma unroll
+      for (int u = 0; u < PEEL; ++u) {
+        kn[u] = (uint32_t)__builtin_amdgcn_readlane((int)cur.x, u);
+        d[u] = u < cnt ? __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)cur.y, u)) : 0.f;
+        const int kl = (int)(kn[u] & 127);
+#pragma unroll
+        for (int r = 0; r < CR; ++r) xv[u][r] = (float)As[swz128(64 * r + lane, kl >> 4) + (kl & 15)];
+      }
+#pragma unroll
+      for (int u = 0; u < PEEL; ++u) {
+        const int c = ((int)(kn[u] >> 7) - c0) & (kW8OFwdCellN - 1);
+#pragma unroll
+        for (int r = 0; r < CR; ++r) corr[r][c] = __builtin_fmaf(xv[u][r], d[u], corr[r][c]);
+      }
+    }
 #pragma unroll
     for (int kk = 0; kk < BK / 64; ++kk) {
       const int c = kk * 4 + (lane >> 4);
@@ -184,30 +215,41 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
           acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
     if constexpr (AFF) {
-      // corr[n][m] += xq[m, k] d for the stage's outliers (k, n, d) of this
-      // wave's cells; a wave owns its rows and columns of corr
-      auto add = [&](uint32_t kn, float d) {
-        const int nl = (int)(kn >> 7) - n0, kl = (int)(kn & 127);
-        if (clive && (unsigned)nl < (unsigned)BN) {
-          const float xv = (float)As[swz128(crow, kl >> 4) + (kl & 15)];
-          float* cp = corr + nl * CP + crow;
-          *cp = __builtin_fmaf(xv, d, *cp);
+      // corr[m][n_e - 16 w] += xq[m, k_e] d_e over the stage's outliers of
+      // this wave's cell, lane = row m (and m + 64)
+      const int cnt = chi - clo;
+      auto batch = [&](const u32x2 bat, int q0, int bc) {   // entries q0..bc of a batch
+        for (int q = q0; q < bc; q += 4) {
+          uint32_t kn[4];
+          float d[4], xv[4][CR];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int e = q + u < 64 ? q + u : 63;
+            kn[u] = (uint32_t)__builtin_amdgcn_readlane((int)bat.x, e);
+            d[u] = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)bat.y, e));
+            const int kl = (int)(kn[u] & 127);
+#pragma unroll
+            for (int r = 0; r < CR; ++r) xv[u][r] = (float)As[swz128(64 * r + lane, kl >> 4) + (kl & 15)];
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (q + u < bc) {                          // uniform
+              const int c = ((int)(kn[u] >> 7) - c0) & (kW8OFwdCellN - 1);
+#pragma unroll
+              for (int r = 0; r < CR; ++r) corr[r][c] = __builtin_fmaf(xv[u][r], d[u], corr[r][c]);
+            }
+          }
         }
       };
-      const int cnt = chi - clo;
-      const int c64 = cnt < 64 ? cnt : 64;
-      for (int e = 0; e < c64; ++e)
-        add((uint32_t)__builtin_amdgcn_readlane((int)cur.x, e),
-            __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)cur.y, e)));
-      for (int p = clo + 64; p < chi; ++p) {          // more than 64 in one stage
-        const u32x2 ev = a.fent[p];
-        add(ev.x, __uint_as_float(ev.y));
-      }
+      batch(cur, PEEL, cnt < 64 ? cnt : 64);           // past the peeled ones
+      for (int b0 = 64; b0 < cnt; b0 += 64)            // more than 64 in one stage
+        batch(a.fent[clo + b0 + lane], 0, cnt - b0 < 64 ? cnt - b0 : 64);
+      // the read-ahead entries were queued before this stage's operand loads:
+      // all but those loads are done
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS));
       cur = nxt;
       clo = nlo;
       chi = nhi;
-      nlo = n2lo;
-      nhi = n2hi;
     }
     slot = slot == S - 1 ? 0 : slot + 1;
   }
@@ -226,13 +268,42 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
   } else {
     float* E = reinterpret_cast<float*>(ring);
     __syncthreads();                 // every wave is done with the ring
-    ep.store(E, M, N, m0, n0, a.r);
-    if constexpr (AFF) ep.store_rows(E, M, m0, a.w8o->bias_q);
-    __syncthreads();
-    epilogue_lowrank<BM, BN, R, true, AFF>(acc, E, M, N, m0, n0, wm * (BM / 2), wn * (BN / 2),
-                                           a.s, reinterpret_cast<OutT*>(a.y),
-                                           ring + EPB + wid * epi_strip_bytes<OutT, FN>(), corr,
-                                           AFF ? a.w8o->scale : 1.f);
+    if constexpr (AFF) {
+      // corrections to the accumulators' owners through LDS ([BM][BN + 4]
+      // floats), folded in with the grid step: accf = c acc + corr
+      constexpr int CP = BN + 4;
+#pragma unroll
+      for (int r = 0; r < CR; ++r)
+#pragma unroll
+        for (int c = 0; c < kW8OFwdCellN; ++c)
+          E[(64 * r + lane) * CP + 16 * wid + c] = corr[r][c];
+      __syncthreads();
+      const float cstep = a.w8o->scale;
+      f32x4 accf[FM][FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int ml = wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + ii;
+            const int nl = wn * (BN / 2) + j * 16 + (lane & 15);
+            accf[i][j][ii] = __builtin_fmaf(cstep, (float)acc[i][j][ii], E[ml * CP + nl]);
+          }
+      __syncthreads();
+      ep.store(E, M, N, m0, n0, a.r);
+      ep.store_rows(E, M, m0, a.w8o->bias_q);
+      __syncthreads();
+      epilogue_lowrank<BM, BN, R, true, true>(accf, E, M, N, m0, n0, wm * (BM / 2), wn * (BN / 2),
+                                              a.s, reinterpret_cast<OutT*>(a.y),
+                                              ring + EPB + wid * epi_strip_bytes<OutT, FN>());
+    } else {
+      ep.store(E, M, N, m0, n0, a.r);
+      __syncthreads();
+      epilogue_lowrank<BM, BN, R, true>(acc, E, M, N, m0, n0, wm * (BM / 2), wn * (BN / 2),
+                                        a.s, reinterpret_cast<OutT*>(a.y),
+                                        ring + EPB + wid * epi_strip_bytes<OutT, FN>());
+    }
   }
 }
 
@@ -283,7 +354,8 @@ void launch_gemm_fwd_w8o(int M, int N, int K, const int8_t* xq, const int8_t* co
   a.fptr = reinterpret_cast<const int*>(sb + L.fptr);
   a.fent = reinterpret_cast<const u32x2*>(sb + L.fent);
   a.ng = L.ng;
-  // the correction tile takes LDS: 64 x 64 (three stages) or 128 x 64 (two)
+  // the correction accumulators take registers: 64 x 64 (three stages) or
+  // 128 x 64 (two)
   const long t64 = (long)((M + 63) / 64) * ((N + 63) / 64);
   if (t64 <= 2 * kCUs) launch_tiles<64, 64, 3, uint16_t, false, true>(a, st);
   else launch_tiles<128, 64, 2, uint16_t, false, true>(a, st);

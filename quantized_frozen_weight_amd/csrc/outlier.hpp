@@ -12,7 +12,7 @@
 //   col         int32 [cap]         [rowptr[k], rowptr[k + 1]) in n order
 //   val         fp16  [cap]
 //   fptr, fent  the same outliers for the forward product, grouped by cell
-//               (k / 128, n / 32) in cell order, (k, n) order inside a cell:
+//               (k / 128, n / 16) in cell order, (k, n) order inside a cell:
 //               fptr int32 [NKB * NG + 1], fent {(n << 7) | k % 128,
 //               correction} [cap + 64]; correction = value - the grid's
 //               reconstruction at that position
@@ -20,7 +20,7 @@
 //               bptr int32 [NNB * KG + 1], bent {(k << 6) | n % 64, value}
 //               [cap + 64]
 //   scratch     used while quantizing only: per-(64-column tile, k) row
-//               counts, per-(64-row tile, 32-column group) counts, the
+//               counts, per-(64-row tile, 16-column group) counts, the
 //               16-row group counts, the select histograms
 //
 // cap bounds the outlier count: with nearest-rank cuts at ranks
@@ -47,7 +47,7 @@ struct W8OHeader {
 };
 
 constexpr int kW8OFwdCellK = 128;   // k per forward cell (the forward's stage)
-constexpr int kW8OFwdCellN = 32;    // n per forward cell (a wave's columns)
+constexpr int kW8OFwdCellN = 16;    // n per forward cell (a wave's columns)
 constexpr int kW8OBwdCellN = 64;    // n per backward cell (the backward's stage)
 constexpr int kW8OBwdCellK = 16;    // k per backward cell
 constexpr int kW8OPad = 64;         // spare entries after each entry list
@@ -91,3 +91,45 @@ inline W8OLayout w8o_layout(int K, int N) {
 }
 
 }  // namespace qlora
+
+#ifdef __HIPCC__
+namespace qlora {
+
+// Entry ranges of one outlier cell for every stage of a product, read 64
+// stages at a time into registers: lane i of (lo, hi) holds stage 64 c + i of
+// chunk c, and the next chunk is read while this one is used. A stage's range
+// is then a readlane with a uniform index -- no load inside the stage loop
+// whose result the loop would have to wait for. p[st * stride + olo] and
+// p[st * stride + ohi] are the stage's first and one-past-last entries.
+struct CellRanges {
+  int lo, hi, nlo, nhi, chunk;
+  const int* p;
+  int stride, olo, ohi, nst;
+
+  __device__ __forceinline__ void read(int c, int& l, int& h) const {
+    int st = c * 64 + (int)(threadIdx.x & 63);
+    st = st < nst ? st : nst - 1;
+    l = p[(long)st * stride + olo];
+    h = p[(long)st * stride + ohi];
+  }
+  __device__ __forceinline__ void init(const int* p_, int stride_, int olo_, int ohi_, int nst_) {
+    p = p_; stride = stride_; olo = olo_; ohi = ohi_; nst = nst_;
+    chunk = 0;
+    read(0, lo, hi);
+    read(1, nlo, nhi);
+  }
+  // range of stage st; calls come with st non-decreasing, one chunk at a time
+  __device__ __forceinline__ void get(int st, int& l, int& h) {
+    if ((st >> 6) != chunk) {
+      lo = nlo;
+      hi = nhi;
+      ++chunk;
+      read(chunk + 1, nlo, nhi);
+    }
+    l = __builtin_amdgcn_readlane(lo, st & 63);
+    h = __builtin_amdgcn_readlane(hi, st & 63);
+  }
+};
+
+}  // namespace qlora
+#endif

@@ -13,7 +13,7 @@
 //    d = fl32(hi - lo).
 // 2. One wave per 64 x 64 tile of W [K, N] counts the outliers of every row
 //    (ballot over the tile's 64 columns), of every 16-row group and of every
-//    32-column half.
+//    16-column quarter.
 // 3. Prefix sums: per row over the column tiles, then three exclusive scans
 //    (rows, backward cells, forward cells), one block each.
 // 4. The same tiles again: each lane writes its column's 64 codes as four
@@ -189,7 +189,7 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 // Pass 2: outlier counts of one tile per wave.
 //   cnt_r[nt][k]   outliers of row k among the tile column's 64 n
 //   bcell[nt][kg]  the same summed over 16 rows
-//   fcnt[kt][g]    outliers of the tile's 32-column half g over its 64 rows
+//   fcnt[kt][g]    outliers of the tile's 16-column quarter g over its 64 rows
 __global__ __launch_bounds__(256) void outlier_count(const float* __restrict__ W,
                                                      const W8OHeader* __restrict__ h,
                                                      W8OLayout L, char* __restrict__ side) {
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256) void outlier_count(const float* __restrict__ W
   int* cnt_r = reinterpret_cast<int*>(side + L.cnt_r);
   int* bcell = reinterpret_cast<int*>(side + L.bcell);
   int* fcnt = reinterpret_cast<int*>(side + L.fcnt);
-  int mine = 0, grp = 0, g0 = 0, g1 = 0;
+  int mine = 0, grp = 0, gq[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int kk = 0; kk < 64; ++kk) {
     if (kk < rows) {
@@ -216,8 +216,8 @@ __global__ __launch_bounds__(256) void outlier_count(const float* __restrict__ W
       const int c = __popcll(mask);
       if (lane == kk) mine = c;
       grp += c;
-      g0 += __popc((uint32_t)mask);
-      g1 += __popc((uint32_t)(mask >> 32));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) gq[q] += __popc((uint32_t)(mask >> (16 * q)) & 0xffffu);
       if ((kk & 15) == 15) {
         if (lane == 0) bcell[nt * L.kg + kt * 4 + (kk >> 4)] = grp;
         grp = 0;
@@ -226,8 +226,9 @@ __global__ __launch_bounds__(256) void outlier_count(const float* __restrict__ W
   }
   if (lane < rows) cnt_r[(long)nt * K + k0 + lane] = mine;
   if (lane == 0) {
-    if (2 * nt < L.ng) fcnt[kt * L.ng + 2 * nt] = g0;
-    if (2 * nt + 1 < L.ng) fcnt[kt * L.ng + 2 * nt + 1] = g1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (4 * nt + q < L.ng) fcnt[kt * L.ng + 4 * nt + q] = gq[q];
   }
 }
 
@@ -321,20 +322,21 @@ __global__ __launch_bounds__(256) void outlier_fill(const float* __restrict__ W,
   u32x2* bent = reinterpret_cast<u32x2*>(side + L.bent);
 
   // list bases: lane j holds row j's CSR start; lanes 0..3 the backward
-  // cells of the tile's 16-row groups; lanes 0..1 the forward cells of its
-  // 32-column halves (plus the first 64-row tile of a 128-row cell)
+  // cells of the tile's 16-row groups, and the forward cells of its
+  // 16-column quarters (plus the first 64-row tile of a 128-row cell)
   const int rbase = lane < rows ? rowptr[k0 + lane] + rpre[(long)nt * K + k0 + lane] : 0;
   const int bbase = (lane < 4 && 16 * lane < rows) ? bptr[nt * L.kg + kt * 4 + lane] : 0;
   int fbase = 0;
-  if (lane < 2 && 2 * nt + lane < L.ng) {
-    const int g = 2 * nt + lane;
+  if (lane < 4 && 4 * nt + lane < L.ng) {
+    const int g = 4 * nt + lane;
     fbase = fptr[(kt >> 1) * L.ng + g] + ((kt & 1) ? fcnt[(kt - 1) * L.ng + g] : 0);
   }
+  const int quarter = lane >> 4;
 
   uint32_t cw[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) cw[i] = 0u;
-  int runB = 0, runF0 = 0, runF1 = 0;
+  int runB = 0, runF[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int kk = 0; kk < 64; ++kk) {
     if (kk < rows) {
@@ -348,7 +350,8 @@ __global__ __launch_bounds__(256) void outlier_fill(const float* __restrict__ W,
       const uint64_t mask = __ballot(o);
       if (mask != 0) {
         const int below = lanes_below(mask);
-        const int lower = __popc((uint32_t)mask);
+        // outliers of the lanes of lower quarters
+        const int lower = __popcll(mask & ((1ull << (16 * quarter)) - 1ull));
         if (o) {
           const int k = k0 + kk;
           const _Float16 v16 = (_Float16)w;
@@ -360,14 +363,20 @@ __global__ __launch_bounds__(256) void outlier_fill(const float* __restrict__ W,
           }
           const int posb = __builtin_amdgcn_readlane(bbase, kk >> 4) + runB + below;
           if (posb < cap) bent[posb] = u32x2{((uint32_t)k << 6) | (uint32_t)(n & 63), __float_as_uint(vf)};
-          const int posf = lane < 32 ? __builtin_amdgcn_readlane(fbase, 0) + runF0 + below
-                                     : __builtin_amdgcn_readlane(fbase, 1) + runF1 + (below - lower);
+          int fb = __builtin_amdgcn_readlane(fbase, 0), rf = runF[0];
+#pragma unroll
+          for (int q = 1; q < 4; ++q)
+            if (quarter == q) {
+              fb = __builtin_amdgcn_readlane(fbase, q);
+              rf = runF[q];
+            }
+          const int posf = fb + rf + (below - lower);
           const float d = vf - (bias_q + scale * (float)q);
           if (posf < cap) fent[posf] = u32x2{((uint32_t)n << 7) | (uint32_t)(k & 127), __float_as_uint(d)};
         }
         runB += __popcll(mask);
-        runF0 += lower;
-        runF1 += __popc((uint32_t)(mask >> 32));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) runF[q] += __popc((uint32_t)(mask >> (16 * q)) & 0xffffu);
       }
       if ((kk & 15) == 15) runB = 0;
     }

@@ -74,10 +74,10 @@ __device__ __forceinline__ int swz128(int row, int c) {
 // ---------------------------------------------------------------------------
 // Low-rank epilogue: out[m, n] = fma(s, sum_j P[m, j] Q(j, n), base[m, n])
 // with base = float(acc) * (rs[m] * cs[n]) or the float accumulator itself,
-// or (affine weights, AFF) base = rs[m] * (c * acc + ra[m] + corr[n][m]) with
-// one grid step c for the whole weight, a per-row term ra[m] = b * as[m]
-// (b the grid's bias, as[m] a row sum of the activation codes) and a
-// per-output correction kept in LDS.
+// or (affine weights, AFF) base = rs[m] * (acc + ra[m]) with acc already the
+// float c * (integer product) + correction of the affine grid, and a per-row
+// term ra[m] = b * as[m] (b the grid's value of code 0, as[m] a row sum of
+// the activation codes).
 // The rank-R product runs on v_mfma_f32_16x16x4_f32 (float32 operands and
 // accumulation), R / 4 instructions per 16 x 16 block, and lands in the same
 // lane layout as the main accumulator. The block's operands are fetched into
@@ -160,9 +160,6 @@ template <int BM, int BN, int R, bool SCALED, bool AFF = false> struct EpiOps {
   }
 };
 
-// Row pitch (floats) of the AFF correction tile corr [BN][BM + 4]: the pad
-// spreads the 16 columns that one epilogue read touches over all banks.
-template <int BM> constexpr int corr_pitch() { return BM + 4; }
 
 // LDS bytes of one wave's output staging strip in epilogue_lowrank: 16 rows
 // of FN * 16 outputs, each row padded by 16 bytes (so that the four row
@@ -184,8 +181,7 @@ template <int BM, int BN, int R, bool SCALED, bool AFF = false, typename OutT, t
 __device__ __forceinline__ void epilogue_lowrank(const AccT (&acc)[FM][FN], const float* E,
                                                  int M, int N, int m0, int n0, int wr0,
                                                  int wc0, float s, OutT* __restrict__ out,
-                                                 int8_t* strip, const float* corr = nullptr,
-                                                 float cstep = 1.f) {
+                                                 int8_t* strip) {
   static_assert(!AFF || SCALED, "the affine form uses the row scales");
   const int lane = threadIdx.x & 63;
   const float* ts = E;
@@ -225,16 +221,13 @@ __device__ __forceinline__ void epilogue_lowrank(const AccT (&acc)[FM][FN], cons
     for (int jn = 0; jn < FN; ++jn) {
       const int nl = wc0 + jn * 16 + (lane & 15);
       const float csn = SCALED ? csv[nl] : 1.f;
-      f32x4 cv = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (AFF)
-        cv = *reinterpret_cast<const f32x4*>(corr + nl * corr_pitch<BM>() + wr0 + i * 16 + (lane >> 4) * 4);
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int rl = (lane >> 4) * 4 + ii;             // row inside the strip
         const int ml = wr0 + i * 16 + rl;
         float base;
         if constexpr (AFF)
-          base = rsv[ml] * __builtin_fmaf(cstep, (float)acc[i][jn][ii], rav[ml] + cv[ii]);
+          base = rsv[ml] * ((float)acc[i][jn][ii] + rav[ml]);
         else
           base = SCALED ? (float)acc[i][jn][ii] * (rsv[ml] * csn) : (float)acc[i][jn][ii];
         store_out(reinterpret_cast<OutT*>(strip + rl * PITCH) + jn * 16 + (lane & 15),
