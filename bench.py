@@ -302,8 +302,8 @@ def describe(w):
 TRAFFIC = {
     "workload": 2,
     "sources": ["gemm_bwd.hip", "ring.hpp", "common.hpp"],
-    "sha256": "1257ca38069c0abf19eca31df24988f54e417c13948f716e193d988db12795cf",
-    "bytes_per_launch": 25025647,
+    "sha256": "68dd07152456fc40e129fc3d90f7f04c1982418d95733e8b5abe9041e3722d19",
+    "bytes_per_launch": 25011368,
 }
 
 
