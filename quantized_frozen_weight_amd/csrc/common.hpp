@@ -83,6 +83,86 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
+// Sums of R per-lane values over the 64 lanes in one butterfly: the first
+// log2 R levels pair lanes across bit 5, 4, 3, ... and each lane keeps half of
+// its values (those of its side of the pair) plus the partner's matching
+// half; the remaining levels are plain sums. Lane l ends with the total of
+// value rank_of_lane<R>(l). The cross-lane steps are v_permlane32_swap and
+// v_permlane16_swap (bits 5 and 4), then DPP within rows of 16: row_mirror
+// (bit 3), row_half_mirror (bit 2), quad_perm [3,2,1,0] (bit 1) and
+// [1,0,3,2] (bit 0) -- each pairs lanes that differ in that bit. Fixed order:
+// the same inputs give the same bits.
+template <int R>
+__device__ __forceinline__ int rank_of_lane(int lane) {
+  int j = 0;
+#pragma unroll
+  for (int b = 0, h = R / 2; h >= 1; ++b, h >>= 1) j += ((lane >> (5 - b)) & 1) ? h : 0;
+  return j;
+}
+
+__device__ __forceinline__ float dpp_pair(float v, int ctrl_id) {
+  // ctrl_id: 0 row_mirror, 1 row_half_mirror, 2 quad_perm [3,2,1,0], 3 quad_perm [1,0,3,2]
+  const int iv = __builtin_bit_cast(int, v);
+  int r;
+  if (ctrl_id == 0) r = __builtin_amdgcn_update_dpp(0, iv, 0x140, 0xf, 0xf, false);
+  else if (ctrl_id == 1) r = __builtin_amdgcn_update_dpp(0, iv, 0x141, 0xf, 0xf, false);
+  else if (ctrl_id == 2) r = __builtin_amdgcn_update_dpp(0, iv, 0x1b, 0xf, 0xf, false);
+  else r = __builtin_amdgcn_update_dpp(0, iv, 0xb1, 0xf, 0xf, false);
+  return __builtin_bit_cast(float, r);
+}
+
+template <int R>
+__device__ __forceinline__ float wave_sum_ranks(const float (&in)[R]) {
+  static_assert(R >= 1 && R <= 32 && (R & (R - 1)) == 0, "R a power of two up to 32");
+  const int lane = threadIdx.x & 63;
+  float v[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) v[i] = in[i];
+  int n = R;
+  // level 0: lanes l and l ^ 32
+  {
+    const int h = n > 1 ? n / 2 : 1;
+#pragma unroll
+    for (int i = 0; i < (R > 1 ? R / 2 : 1); ++i) {
+      const uint32_t a = __float_as_uint(v[i]), b = __float_as_uint(v[n > 1 ? i + h : i]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+      v[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    n = n > 1 ? n / 2 : 1;
+  }
+  // level 1: lanes l and l ^ 16
+  {
+    const int h = n > 1 ? n / 2 : 1;
+#pragma unroll
+    for (int i = 0; i < (R > 2 ? R / 4 : 1); ++i) {
+      const uint32_t a = __float_as_uint(v[i]), b = __float_as_uint(v[n > 1 ? i + h : i]);
+      const auto sw = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+      v[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    n = n > 1 ? n / 2 : 1;
+  }
+  // levels 2..5 inside rows of 16: bit 3, 2, 1, 0
+#pragma unroll
+  for (int lvl = 0; lvl < 4; ++lvl) {
+    const bool upper = (lane >> (3 - lvl)) & 1;
+    if (n > 1) {
+      const int h = n / 2;
+#pragma unroll
+      for (int i = 0; i < R / 8 + 1; ++i) {
+        if (i < h) {
+          const float keep = upper ? v[i + h] : v[i];
+          const float send = upper ? v[i] : v[i + h];
+          v[i] = keep + dpp_pair(send, lvl);
+        }
+      }
+      n = h;
+    } else {
+      v[0] = v[0] + dpp_pair(v[0], lvl);
+    }
+  }
+  return v[0];
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {

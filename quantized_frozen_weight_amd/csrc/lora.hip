@@ -15,7 +15,9 @@ __global__ __launch_bounds__(256) void skinny_stage1_kernel(SkinnyJobs p) {
 }
 
 // out = s * sum over splits (split order fixed); one thread per (job, j, c),
-// kSkMaxSplit loads in flight at a time.
+// NS loads in flight at a time (NS: the split count rounded up to 8, 16 or 32,
+// so no load is wasted on a clamped duplicate).
+template <int NS>
 __global__ __launch_bounds__(256) void skinny_stage2_kernel(SkinnyJobs p) {
   const long e0 = (long)blockIdx.x * 256 + threadIdx.x;
   const long n0 = (long)p.r * p.C[0];
@@ -27,13 +29,13 @@ __global__ __launch_bounds__(256) void skinny_stage2_kernel(SkinnyJobs p) {
   const float* __restrict__ base = p.partial[job] + (long)j * C + c;
   const long stride = (long)p.r * C;
   float sum = 0.f;
-  for (int k0 = 0; k0 < p.nsplit; k0 += kSkMaxSplit) {
-    float v[kSkMaxSplit];
+  for (int k0 = 0; k0 < p.nsplit; k0 += NS) {
+    float v[NS];
 #pragma unroll
-    for (int k = 0; k < kSkMaxSplit; ++k)
+    for (int k = 0; k < NS; ++k)
       v[k] = base[(k0 + k < p.nsplit ? k0 + k : k0) * stride];
 #pragma unroll
-    for (int k = 0; k < kSkMaxSplit; ++k)
+    for (int k = 0; k < NS; ++k)
       if (k0 + k < p.nsplit) sum += v[k];
   }
   const float out = p.s * sum;
@@ -78,7 +80,10 @@ void launch_skinny_stage1(int dtype, const SkinnyJobs& p, hipStream_t st) {
 
 void launch_skinny_stage2(const SkinnyJobs& p, hipStream_t st) {
   const long total = (long)p.r * p.C[0] + (p.njobs > 1 ? (long)p.r * p.C[1] : 0);
-  skinny_stage2_kernel<<<dim3((unsigned)((total + 255) / 256)), 256, 0, st>>>(p);
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (p.nsplit <= 8) skinny_stage2_kernel<8><<<grid, 256, 0, st>>>(p);
+  else if (p.nsplit <= 16) skinny_stage2_kernel<16><<<grid, 256, 0, st>>>(p);
+  else skinny_stage2_kernel<kSkMaxSplit><<<grid, 256, 0, st>>>(p);
 }
 
 }  // namespace qlora

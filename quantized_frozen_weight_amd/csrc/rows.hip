@@ -268,13 +268,11 @@ __global__ __launch_bounds__(256) void row_kernel(
   }
   if (!live) return;
   if (lowrank) {
-    float mine = 0.f;
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const float tot = wave_sum(acc[j]);
-      if (lane == j) mine = tot;
-    }
-    if (lane < r) out_r[(long)row * r + lane] = mine;
+    // one butterfly for all R sums; lane l holds rank rank_of_lane(l), and
+    // the first lane of each group of 64 / R writes it
+    const float tot = wave_sum_ranks<R>(acc);
+    const int j = rank_of_lane<R>(lane);
+    if ((lane & (64 / R - 1)) == 0 && j < r) out_r[(long)row * r + j] = tot;
   }
   if (MODE == kFwdQuant && lane == 0) sx[row] = qp.scale;
   if (MODE == kFwdQuant && asum != nullptr) {
