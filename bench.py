@@ -302,8 +302,8 @@ def describe(w):
 TRAFFIC = {
     "workload": 2,
     "sources": ["gemm_bwd.hip", "ring.hpp", "common.hpp"],
-    "sha256": "68dd07152456fc40e129fc3d90f7f04c1982418d95733e8b5abe9041e3722d19",
-    "bytes_per_launch": 25011368,
+    "sha256": "b1fe6eadcf0e55ca69bb359a34ce78f0aedf2d89f2833c04b3a930f5a75d3ee7",
+    "bytes_per_launch": 25011429,
 }
 
 
