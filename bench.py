@@ -399,11 +399,19 @@ def dominant_kernel_roofline(w, layers, step, torch):
     avg_ms = tot_ms / launches
     if w.dtype == "bf16":   # fused backward: dx, u, dB, dA, s u A^T
         flops = sum(2.0 * w.M * l.K * l.N + 4.0 * w.M * w.r * (l.N + l.K) for l in layers) / n
-        # the library's tile choice: 64-row producer/consumer blocks while
-        # they make at most two per compute unit, else 128 x 128 blocks
+        # the library's tile choice: 128 x 128 blocks over a split contraction
+        # (then a fixup launch) for at most 128 such tiles and N >= 2048;
+        # else 64-row producer/consumer blocks while they make at most two
+        # per compute unit, else 128 x 128 blocks
         bn = 128 if w.wfmt == "w4g128" else 64
-        names = sorted({"bwd_pc_kernel" if ((w.M + 63) // 64) * ((l.K + bn - 1) // bn) <= 512
-                        else "bwd_wide_kernel" for l in layers})
+
+        def bwd_name(l):
+            if ((w.M + 127) // 128) * ((l.K + 127) // 128) <= 128 and (l.N + 63) // 64 >= 32:
+                return "bwd_wide_kernel<SPLIT> + bwd_fixup_kernel"
+            if ((w.M + 63) // 64) * ((l.K + bn - 1) // bn) <= 512:
+                return "bwd_pc_kernel"
+            return "bwd_wide_kernel"
+        names = sorted({bwd_name(l) for l in layers})
         kernel = (" + ".join(names) + " (fused backward: dx, u, dA and dB partial sums, "
                   f"bf16 MFMA, {w.wfmt} weights)")
     else:                   # float32 input gradient: dy deq(W)^T + s u A^T

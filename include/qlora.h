@@ -213,7 +213,11 @@ int qlora_fwd_a8w4(const qlora_linear* L, int M, int dtype, const void* x,
                    void* y, float* t_save, void* ws, size_t ws_bytes,
                    void* stream);
 
-/* Workspace needed by qlora_bwd for M rows. */
+/* Workspace needed by qlora_bwd for M rows. In bf16, layers whose input
+ * gradient has few 128 x 128 output tiles (at most 128) over a long
+ * contraction (N of at least 2048) also keep there the per-split partial
+ * products of dx, 4 bytes per output per split (32 MiB for 512 rows of a
+ * 2048 -> 16384 layer). */
 int qlora_bwd_workspace(const qlora_linear* L, int M, int dtype,
                         size_t* bytes);
 

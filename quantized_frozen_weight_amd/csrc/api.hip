@@ -85,7 +85,7 @@ FwdLayout fwd_layout(const qlora_linear* L, int M) {
 }
 
 struct BwdLayout {
-  size_t t, u, pB, pA, total;
+  size_t t, u, pB, pA, pdx, pu, total;
 };
 // Partial sums of dA and dB: one per split of the rows. The fused int8
 // backward splits by row block (at least 64 rows), the other paths into at
@@ -94,13 +94,17 @@ inline size_t partial_floats(int M, int r, int C) {
   return (size_t)((M + 63) / 64) * (size_t)r * (size_t)C;
 }
 BwdLayout bwd_layout(const qlora_linear* L, int M, int dtype) {
-  (void)dtype;
   BwdLayout w{};
   size_t off = 0;
   w.t = off; off = align_up(off + (size_t)M * L->r * 4);
   w.u = off; off = align_up(off + (size_t)M * L->r * 4);
   w.pB = off; off = align_up(off + partial_floats(M, L->r, L->N) * 4);
   w.pA = off; off = align_up(off + partial_floats(M, L->r, L->K) * 4);
+  // split contraction of the bf16 input gradient (0 bytes when it does not split)
+  size_t fdx = 0, fu = 0;
+  if (dtype == QLORA_BF16) bwd_split_sizes(M, L->K, L->N, L->r, &fdx, &fu);
+  w.pdx = off; off = align_up(off + fdx * 4);
+  w.pu = off; off = align_up(off + fu * 4);
   w.total = off;
   return w;
 }
@@ -121,7 +125,7 @@ int launch_status() {
 // backward's row tile; the other paths split the rows the same way so that
 // the combine needs nothing but (L, M, dtype).
 int bwd_splits(const qlora_linear* L, int M) {
-  const int bm = bwd_row_block(L->fmt, M, L->K, L->r);
+  const int bm = bwd_row_block(L->fmt, M, L->K, L->N, L->r);
   return (M + bm - 1) / bm;
 }
 
@@ -337,7 +341,9 @@ int qlora_bwd_partial_timed(const qlora_linear* L, int M, int dtype, const void*
       launch_bwd_fused(L->fmt, M, L->K, L->N, static_cast<const uint16_t*>(dy),
                        L->codes, L->scales, L->B, head_width(L), L->A, t,
                        static_cast<const uint16_t*>(x), L->r, sc,
-                       static_cast<uint16_t*>(dx), partA, partB, s);
+                       static_cast<uint16_t*>(dx), partA, partB,
+                       reinterpret_cast<float*>(at(ws, w.pdx)),
+                       reinterpret_cast<float*>(at(ws, w.pu)), s);
     mark(ev_stop, s);
     return launch_status();
   }

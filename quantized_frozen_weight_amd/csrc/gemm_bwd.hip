@@ -69,6 +69,8 @@ namespace {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+constexpr int kMaxWideSplits = 8;   // contraction splits of the 128 x 128 backward
+
 struct BwdArgs {
   int M, K, N;
   const uint16_t* dy;      // [M, N] bf16
@@ -91,6 +93,11 @@ struct BwdArgs {
   const u32x2* bent;
   int kg;                  // 16-row k groups
   int tiles_x;
+  // split contraction (128 x 128 tiles): the partial products in the
+  // accumulator layout, the partial u, the split count and stages per split
+  float* pdx;              // [splits, tiles, 4 waves, 16 fragments, 64 lanes] float4
+  float* pu;               // [splits, M, r]
+  int splits, nks;
 };
 
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
@@ -698,7 +705,7 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
 // product, and the whole block's registers serve one role.
 // W4: 4-bit weights (two codes per byte, fp16 scale per 128 k, carried one
 // stage ahead in a register); else int8.
-template <bool W4, int BM, int BN, int S, int R, bool AFF = false>
+template <bool W4, int BM, int BN, int S, int R, bool AFF = false, bool SPLIT = false>
 __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
   constexpr int KC = 64;                              // n per stage
   constexpr int RB = W4 ? BN / 2 : BN;                // code bytes per row of n
@@ -735,10 +742,26 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wid = wave_id();
   const int wm = wid >> 1, wn = wid & 1;
-  const int mt = (int)blockIdx.x / a.tiles_x, kt_blk = (int)blockIdx.x % a.tiles_x;
-  const int m0 = mt * BM, k0 = kt_blk * BN;
   const int M = a.M, K = a.K, N = a.N, r = a.r;
   const int nk = (N + KC - 1) / KC;
+  // SPLIT: blocks (split, tile), split-major; the dispatcher deals blocks to
+  // the eight XCDs in turn, so block b runs as logical block
+  // (b % 8) * (blocks / 8) + b / 8 and the blocks of one XCD share one
+  // split's n range (its dy columns and code rows stay in that XCD's L2)
+  int bid = (int)blockIdx.x, split = 0;
+  const int tiles = a.tiles_x * ((M + BM - 1) / BM);
+  if constexpr (SPLIT) {
+    const int nb = (int)gridDim.x;
+    if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+    split = bid / tiles;
+    bid -= split * tiles;
+  }
+  const int mt = bid / a.tiles_x, kt_blk = bid % a.tiles_x;
+  const int m0 = mt * BM, k0 = kt_blk * BN;
+  // stages [kt0, kt1) of the contraction; nend bounds the n loaded
+  const int kt0 = SPLIT ? split * a.nks : 0;
+  const int kt1 = SPLIT ? (kt0 + a.nks < nk ? kt0 + a.nks : nk) : nk;
+  const int nend = kt1 * KC < N ? kt1 * KC : N;
 
   // t rows of the block (for dB), then A^T of the block's columns (for the
   // epilogue); masks are applied when stored
@@ -749,10 +772,12 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
     const int e = tid + 256 * i, row = e / R, j = e % R, gm = m0 + row;
     tv[i] = a.t[(long)(gm < M ? gm : M - 1) * r + (j < r ? j : r - 1)];
   }
+  if constexpr (!SPLIT) {
 #pragma unroll
-  for (int i = 0; i < NQ; ++i) {
-    const int e = tid + 256 * i, j = e / BN, col = e % BN, gk = k0 + col;
-    qv[i] = a.A[(long)(gk < K ? gk : K - 1) * r + (j < r ? j : r - 1)];
+    for (int i = 0; i < NQ; ++i) {
+      const int e = tid + 256 * i, j = e / BN, col = e % BN, gk = k0 + col;
+      qv[i] = a.A[(long)(gk < K ? gk : K - 1) * r + (j < r ? j : r - 1)];
+    }
   }
 
   // x tile [BM][BN] bf16 as swizzled 128-byte rows (64 columns per row half)
@@ -819,24 +844,24 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
   auto issue = [&](int kt, int slot) {
     int8_t* base = ring + slot * STG;
     const int nb = kt * KC;
-    const bool tail = nb + KC > N;
+    const bool tail = nb + KC > nend;
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       const int8_t* src = srcA[i] + 2L * nb;
-      if (tail && nb + nA[i] >= N) src = zero_chunk(lane);
+      if (tail && nb + nA[i] >= nend) src = zero_chunk(lane);
       lds_dma16(src, base + (wid * (BM / 4) + i * 8) * 128);
     }
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
       const int8_t* src = okB[i] ? srcB[i] + (long)nb * crs : srcB[i];
-      if (tail && nb + nB[i] >= N) src = zero_chunk(lane);
+      if (tail && nb + nB[i] >= nend) src = zero_chunk(lane);
       lds_dma16(src, base + ASZ + (wid * BI + i) * RPI * RB);
     }
     const long boff = 4 * head_index(0, nb, r, a.hd);   // bytes: B column nb, rank 0
 #pragma unroll
     for (int i = 0; i < AUXI; ++i) {
       const int8_t* src = okX[i] ? srcX[i] + (isB[i] ? boff : 4L * nb) : srcX[i];
-      if (tail && nb + nX[i] >= N) src = zero_chunk(lane);
+      if (tail && nb + nX[i] >= nend) src = zero_chunk(lane);
       lds_dma16(src, base + ASZ + BSZ + (wid * AUXI + i) * 1024);
     }
     if constexpr (W4) {
@@ -881,7 +906,7 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int kg = kgw0 + 4 * h;
-      cr2[h].init(a.bptr, a.kg, kg < a.kg ? kg : a.kg, kg + 1 < a.kg ? kg + 1 : a.kg, nk);
+      cr2[h].init(a.bptr, a.kg, kg < a.kg ? kg : a.kg, kg + 1 < a.kg ? kg + 1 : a.kg, nk, kt0);
     }
   }
 
@@ -898,9 +923,9 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
 
 #pragma unroll
   for (int st = 0; st < S - 1; ++st)
-    if (st < nk) issue(st, st);
+    if (kt0 + st < kt1) issue(kt0 + st, st);
   if constexpr (AFF) {
-    outl_range(0, ocur);
+    outl_range(kt0, ocur);
     outl_load(ocur);
   }
 
@@ -923,8 +948,8 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
   const int nq = tid & 15, kq0 = tid >> 4;
 
   int slot = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_stages<LPS, 0, S - 2>(nk - 1 - kt);
+  for (int kt = kt0; kt < kt1; ++kt) {
+    wait_stages<LPS, 0, S - 2>(kt1 - 1 - kt);
     if constexpr (W4) {                              // the stage's scales, as float
       if (lane < 16) SCs[scn] = (float)__builtin_bit_cast(_Float16, scr);
       __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
@@ -934,13 +959,13 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
     // iteration's loads
     Outl2 o1{};
     if constexpr (AFF) {
-      outl_range(kt + 1 < nk ? kt + 1 : kt, o1);
+      outl_range(kt + 1 < kt1 ? kt + 1 : kt, o1);
       outl_load(o1);
       __builtin_amdgcn_sched_barrier(0);           // ahead of the stage loads
     }
     // (affine weights: every iteration queues the same loads; see the 64-row
     // kernel)
-    if (AFF || kt + S - 1 < nk) issue(kt + S - 1, slot == 0 ? S - 1 : slot - 1);
+    if (AFF || kt + S - 1 < kt1) issue(kt + S - 1, slot == 0 ? S - 1 : slot - 1);
     const int8_t* As = ring + slot * STG;
     const int8_t* Bs = As + ASZ;
     const float* Xa = reinterpret_cast<const float*>(Bs + BSZ);
@@ -1110,6 +1135,36 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
     slot = slot == S - 1 ? 0 : slot + 1;
   }
 
+  if constexpr (SPLIT) {
+    // partial products, float4 unit ((split tiles + tile) 4 + wave) F + f)
+    // 64 + lane for fragment f = i FN + j of F = FM FN: each store writes
+    // 1 KB of consecutive bytes. The column-tile-0 block of each row block
+    // writes its split's partial u.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));        // ring loads done before the block ends
+    f32x4* P = reinterpret_cast<f32x4*>(a.pdx) +
+               ((long)(split * tiles + bid) * 4 + wid) * (FM * FN * 64) + lane;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) P[(i * FN + j) * 64] = acc[i][j];
+    if (kt_blk == 0) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        if ((i & 1) != wn) continue;
+#pragma unroll
+        for (int cb = 0; cb < UCB; ++cb) {
+          const int j = cb * 16 + (lane & 15);
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int gm = m0 + wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + ii;
+            if (j < r && gm < M) a.pu[((long)split * M + gm) * r + j] = uacc[i >> 1][cb][ii];
+          }
+        }
+      }
+    }
+    return;
+  }
+
   // ---- after the contraction: u to LDS, x tile, dA partial, dx epilogue ----
   float* E = reinterpret_cast<float*>(ring);             // U [BM][R] | A^T [R][BN]
   __syncthreads();                                        // ring released
@@ -1165,6 +1220,114 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
 }
 
 
+// Second launch of the split contraction, one block per 128-row x 64-column
+// half of a 128 x 128 tile (the same output ownership as the wide kernel's
+// epilogue): the partial products added in split order, u added in split
+// order from its partials, the dA partial of the 128-row block over these
+// 64 columns, and dx = bf16(sum + s u A^T) through the common epilogue.
+// Wave v takes rows [16 v, 16 v + 16): fragment row v % 4 of the wide
+// kernel's wave 2 (v / 4) + (column half). Every split's loads are issued
+// before the first add (NSPL: the split count's bound; splits past the
+// count read split 0 and are dropped by a select).
+template <int R, int NSPL>
+__global__ __launch_bounds__(512) void bwd_fixup_kernel(BwdArgs a) {
+  constexpr int BM = 128, HN = 64, FN = 4;
+  constexpr int EFL = (BM + HN) * R;                    // U [BM][R] | A^T [R][HN]
+  constexpr int XSZ = BM * HN * 2;                      // x [BM][HN] bf16, 128-byte rows
+  constexpr int STRIP = epi_strip_bytes<uint16_t, FN>();
+  __shared__ __attribute__((aligned(1024))) int8_t lds[XSZ + EFL * 4 + 8 * STRIP];
+  int8_t* Xs = lds;
+  float* E = reinterpret_cast<float*>(lds + XSZ);
+  int8_t* strips = lds + XSZ + EFL * 4;
+
+  const int tid = threadIdx.x, lane = tid & 63, v = wave_id();
+  const int M = a.M, K = a.K, r = a.r, nsp = a.splits;
+  const int tiles = a.tiles_x * ((M + BM - 1) / BM);
+  const int tile = (int)blockIdx.x >> 1, wn = (int)blockIdx.x & 1;
+  const int mt = tile / a.tiles_x;
+  const int m0 = mt * BM, k0 = (tile % a.tiles_x) * 128 + wn * HN;
+
+  // partial products of this wave's four fragments, all splits in flight
+  const int w = 2 * (v >> 2) + wn, fi = v & 3;
+  const f32x4* P = reinterpret_cast<const f32x4*>(a.pdx) + ((long)tile * 4 + w) * (16 * 64) +
+                   fi * 4 * 64 + lane;
+  const long pstride = (long)tiles * 4 * 16 * 64;       // float4 units per split
+  f32x4 pv[NSPL][FN];
+#pragma unroll
+  for (int sp = 0; sp < NSPL; ++sp)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) pv[sp][j] = P[(sp < nsp ? sp : 0) * pstride + j * 64];
+
+  // x tile by DMA: wave v moves rows 16 v .. + 16, 8 per instruction
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int rb = (2 * v + q) * 8, row = rb + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7), gm = m0 + row, gk = k0 + c * 8;
+    const void* src = gk < K ? (const void*)(a.x + (long)(gm < M ? gm : M - 1) * K + gk)
+                             : (const void*)zero_chunk(lane);
+    lds_dma16(src, Xs + rb * 128);
+  }
+
+  // U[m][j] = sum over splits of the partial u (rows past M and ranks past r: 0)
+  for (int e = tid; e < BM * R; e += 512) {
+    const int m = e / R, j = e % R, gm = m0 + m;
+    const bool ok = j < r && gm < M;
+    const float* pu = a.pu + ((long)(gm < M ? gm : M - 1)) * r + (j < r ? j : 0);
+    float uv[NSPL];
+#pragma unroll
+    for (int sp = 0; sp < NSPL; ++sp) uv[sp] = pu[(long)(sp < nsp ? sp : 0) * M * r];
+    float u = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < NSPL; ++sp) u += sp < nsp ? uv[sp] : 0.f;
+    E[e] = ok ? u : 0.f;
+  }
+  for (int e = tid; e < R * HN; e += 512) {
+    const int j = e / HN, col = e % HN, gk = k0 + col;
+    E[BM * R + e] = (j < r && gk < K) ? a.A[(long)gk * r + j] : 0.f;
+  }
+
+  f32x4 acc[1][FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    acc[0][j] = pv[0][j];
+#pragma unroll
+    for (int sp = 1; sp < NSPL; ++sp)
+      if (sp < nsp) acc[0][j] += pv[sp][j];
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+
+  // dA partial over the block's rows: thread -> column tid % 64, ranks
+  // tid / 64 + 8 jj
+  {
+    constexpr int JPT = (R + 7) / 8;
+    const int kl = tid % HN, jb = tid / HN;
+    const int rows_here = M - m0 < BM ? M - m0 : BM;
+    float da[JPT];
+#pragma unroll
+    for (int jj = 0; jj < JPT; ++jj) da[jj] = 0.f;
+    if (jb < R) {
+#pragma unroll 8
+      for (int m = 0; m < rows_here; ++m) {
+        const float xv = tile_bf16(Xs, m, kl);
+#pragma unroll
+        for (int jj = 0; jj < JPT; ++jj)
+          if (jb + 8 * jj < R) da[jj] = __builtin_fmaf(xv, E[m * R + jb + 8 * jj], da[jj]);
+      }
+    }
+    if (k0 + kl < K) {
+#pragma unroll
+      for (int jj = 0; jj < JPT; ++jj) {
+        const int j = jb + 8 * jj;
+        if (j < r) a.partA[((long)mt * r + j) * K + k0 + kl] = da[jj];
+      }
+    }
+  }
+
+  epilogue_lowrank<BM, HN, R, false>(acc, E, M, K, m0, k0, 16 * v, 0, a.s, a.dx,
+                                     strips + v * STRIP);
+}
+
 template <bool W4, int BN, int S, bool AFF = false>
 void launch_pc(BwdArgs a, hipStream_t st) {
   constexpr int BM = 64;
@@ -1176,21 +1339,66 @@ void launch_pc(BwdArgs a, hipStream_t st) {
   else bwd_pc_kernel<W4, BM, BN, S, 32, AFF><<<grid, 512, 0, st>>>(a);
 }
 
-template <bool W4, bool AFF = false>
+template <bool W4, bool AFF = false, bool SPLIT = false>
 void launch_wide(BwdArgs a, hipStream_t st) {
   constexpr int BM = 128, BN = 128, S = 2;
   a.tiles_x = (a.K + BN - 1) / BN;
-  const dim3 grid((unsigned)(a.tiles_x * ((a.M + BM - 1) / BM)));
-  if (a.r <= 4) bwd_wide_kernel<W4, BM, BN, S, 4, AFF><<<grid, 256, 0, st>>>(a);
-  else if (a.r <= 8) bwd_wide_kernel<W4, BM, BN, S, 8, AFF><<<grid, 256, 0, st>>>(a);
-  else if (a.r <= 16) bwd_wide_kernel<W4, BM, BN, S, 16, AFF><<<grid, 256, 0, st>>>(a);
-  else bwd_wide_kernel<W4, BM, BN, S, 32, AFF><<<grid, 256, 0, st>>>(a);
+  const dim3 grid((unsigned)(a.tiles_x * ((a.M + BM - 1) / BM) * (SPLIT ? a.splits : 1)));
+  if (a.r <= 4) bwd_wide_kernel<W4, BM, BN, S, 4, AFF, SPLIT><<<grid, 256, 0, st>>>(a);
+  else if (a.r <= 8) bwd_wide_kernel<W4, BM, BN, S, 8, AFF, SPLIT><<<grid, 256, 0, st>>>(a);
+  else if (a.r <= 16) bwd_wide_kernel<W4, BM, BN, S, 16, AFF, SPLIT><<<grid, 256, 0, st>>>(a);
+  else bwd_wide_kernel<W4, BM, BN, S, 32, AFF, SPLIT><<<grid, 256, 0, st>>>(a);
+  if constexpr (SPLIT) {
+    const dim3 fgrid((unsigned)(2 * a.tiles_x * ((a.M + BM - 1) / BM)));
+    if (a.splits <= 4) {
+      if (a.r <= 4) bwd_fixup_kernel<4, 4><<<fgrid, 512, 0, st>>>(a);
+      else if (a.r <= 8) bwd_fixup_kernel<8, 4><<<fgrid, 512, 0, st>>>(a);
+      else if (a.r <= 16) bwd_fixup_kernel<16, 4><<<fgrid, 512, 0, st>>>(a);
+      else bwd_fixup_kernel<32, 4><<<fgrid, 512, 0, st>>>(a);
+    } else {
+      if (a.r <= 4) bwd_fixup_kernel<4, kMaxWideSplits><<<fgrid, 512, 0, st>>>(a);
+      else if (a.r <= 8) bwd_fixup_kernel<8, kMaxWideSplits><<<fgrid, 512, 0, st>>>(a);
+      else if (a.r <= 16) bwd_fixup_kernel<16, kMaxWideSplits><<<fgrid, 512, 0, st>>>(a);
+      else bwd_fixup_kernel<32, kMaxWideSplits><<<fgrid, 512, 0, st>>>(a);
+    }
+  }
+}
+
+// Stages per split of the 128 x 128 contraction, and the split count: split
+// only while the tiles would leave most compute units idle (at most 128
+// tiles) and the contraction is long, doubling (up to 8) while the grid
+// stays within two blocks per compute unit and each split keeps at least 16
+// stages.
+void wide_split_plan(int M, int K, int N, int* splits, int* nks) {
+  const long tiles = (long)((M + 127) / 128) * ((K + 127) / 128);
+  const int nk = (N + 63) / 64;
+  int sp = 1;
+  if (tiles <= 128)
+    while (sp < kMaxWideSplits && tiles * sp * 2 <= 512 && nk / (sp * 2) >= 16) sp *= 2;
+  *nks = (nk + sp - 1) / sp;
+  *splits = (nk + *nks - 1) / *nks;
 }
 
 }  // namespace
 
-int bwd_row_block(int fmt, int M, int K, int r) {
+void bwd_split_sizes(int M, int K, int N, int r, size_t* pdx_floats, size_t* pu_floats) {
+  int sp, nks;
+  wide_split_plan(M, K, N, &sp, &nks);
+  if (sp == 1) {
+    *pdx_floats = 0;
+    *pu_floats = 0;
+    return;
+  }
+  const size_t tiles = (size_t)((M + 127) / 128) * (size_t)((K + 127) / 128);
+  *pdx_floats = (size_t)sp * tiles * 128 * 128;
+  *pu_floats = (size_t)sp * (size_t)M * (size_t)r;
+}
+
+int bwd_row_block(int fmt, int M, int K, int N, int r) {
   (void)r;
+  int sp, nks;
+  wide_split_plan(M, K, N, &sp, &nks);
+  if (sp > 1) return 128;                         // split 128 x 128 tiles
   const int bn = fmt == 1 ? 128 : 64;             // k per 64-row tile
   const long t64 = (long)((M + 63) / 64) * ((K + bn - 1) / bn);
   return t64 <= 512 ? 64 : 128;
@@ -1200,14 +1408,18 @@ void launch_bwd_fused(int fmt, int M, int K, int N, const uint16_t* dy,
                       const void* codes, const void* scales, const float* B, int hd,
                       const float* A, const float* t, const uint16_t* x, int r,
                       float s, uint16_t* dx, float* partA, float* partB,
-                      hipStream_t st) {
+                      float* pdx, float* pu, hipStream_t st) {
   BwdArgs a{};
   a.M = M; a.K = K; a.N = N; a.dy = dy; a.codes = static_cast<const int8_t*>(codes);
   a.B = B; a.hd = hd; a.A = A; a.t = t; a.x = x; a.r = r; a.s = s; a.dx = dx; a.partA = partA;
   a.partB = partB;
+  a.pdx = pdx; a.pu = pu;
+  wide_split_plan(M, K, N, &a.splits, &a.nks);
+  // split 128 x 128 tiles for few tiles over a long contraction; else
   // 64-row tiles (producer/consumer) while they make at most two blocks per
   // compute unit, else the wide 128 x 128 tiles
-  const bool small = bwd_row_block(fmt, M, K, r) == 64;
+  const bool split = a.splits > 1;
+  const bool small = !split && bwd_row_block(fmt, M, K, N, r) == 64;
   if (fmt == 2) {
     const W8OLayout L = w8o_layout(K, N);
     const char* sb = static_cast<const char*>(scales);
@@ -1215,15 +1427,18 @@ void launch_bwd_fused(int fmt, int M, int K, int N, const uint16_t* dy,
     a.bptr = reinterpret_cast<const int*>(sb + L.bptr);
     a.bent = reinterpret_cast<const u32x2*>(sb + L.bent);
     a.kg = L.kg;
-    if (small) launch_pc<false, 64, 3, true>(a, st);
+    if (split) launch_wide<false, true, true>(a, st);
+    else if (small) launch_pc<false, 64, 3, true>(a, st);
     else launch_wide<false, true>(a, st);
   } else if (fmt == 0) {
     a.sw = static_cast<const float*>(scales);
-    if (small) launch_pc<false, 64, 3>(a, st);
+    if (split) launch_wide<false, false, true>(a, st);
+    else if (small) launch_pc<false, 64, 3>(a, st);
     else launch_wide<false>(a, st);
   } else {
     a.sc4 = static_cast<const uint16_t*>(scales);
-    if (small) launch_pc<true, 128, 3>(a, st);
+    if (split) launch_wide<true, false, true>(a, st);
+    else if (small) launch_pc<true, 128, 3>(a, st);
     else launch_wide<true>(a, st);
   }
 }

@@ -77,17 +77,22 @@ SkinnyJobs make_adapter_grad_jobs(int M, int r, float s, const float* t,
 void launch_skinny_stage1(int dtype, const SkinnyJobs& p, hipStream_t st);
 void launch_skinny_stage2(const SkinnyJobs& p, hipStream_t st);
 
-// bf16 backward, int8 (fmt 0: codes [N, K], scales float [N]) or 4-bit
-// (fmt 1: packed [N, K/2], scales fp16 [N, K/128]) weights:
-// dx = dy deq(W)^T + s u A^T with u = dy B^T computed in the same launch,
-// plus per-row-block partial sums of dA (partA [blocks, r, K]) and dB
-// (partB [blocks, r, N]); blocks = ceil(M / bwd_row_block(fmt, M, K, r)).
-int bwd_row_block(int fmt, int M, int K, int r);
+// bf16 backward, int8 (fmt 0: codes [N, K], scales float [N]), 4-bit
+// (fmt 1: packed [N, K/2], scales fp16 [N, K/128]) or outlier-compensated
+// int8 (fmt 2) weights: dx = dy deq(W)^T + s u A^T with u = dy B^T computed
+// on the way, plus per-row-block partial sums of dA (partA [blocks, r, K])
+// and dB (partB [blocks, r, N]); blocks = ceil(M / bwd_row_block(...)).
+// Shapes with few output tiles and a long contraction split it: the partial
+// products go to pdx and the partial u to pu (sizes from bwd_split_sizes,
+// both 0 when the shape does not split; the pointers are then unused), and
+// a second launch adds them.
+int bwd_row_block(int fmt, int M, int K, int N, int r);
+void bwd_split_sizes(int M, int K, int N, int r, size_t* pdx_floats, size_t* pu_floats);
 void launch_bwd_fused(int fmt, int M, int K, int N, const uint16_t* dy,
                       const void* codes, const void* scales, const float* B, int hd,
                       const float* A, const float* t, const uint16_t* x, int r,
                       float s, uint16_t* dx, float* partA, float* partB,
-                      hipStream_t st);
+                      float* pdx, float* pu, hipStream_t st);
 // dx = dy (codes * sw)^T + s u A^T in float32
 void launch_gemm_dx_f32(int M, int K, int N, const float* dy,
                         const int8_t* codes, const float* sw, const float* u,

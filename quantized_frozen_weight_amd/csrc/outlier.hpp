@@ -112,13 +112,16 @@ struct CellRanges {
     l = p[(long)st * stride + olo];
     h = p[(long)st * stride + ohi];
   }
-  __device__ __forceinline__ void init(const int* p_, int stride_, int olo_, int ohi_, int nst_) {
+  // st0: the first stage that get() will be asked for
+  __device__ __forceinline__ void init(const int* p_, int stride_, int olo_, int ohi_, int nst_,
+                                       int st0 = 0) {
     p = p_; stride = stride_; olo = olo_; ohi = ohi_; nst = nst_;
-    chunk = 0;
-    read(0, lo, hi);
-    read(1, nlo, nhi);
+    chunk = st0 >> 6;
+    read(chunk, lo, hi);
+    read(chunk + 1, nlo, nhi);
   }
-  // range of stage st; calls come with st non-decreasing, one chunk at a time
+  // range of stage st; calls come with st non-decreasing from st0, one chunk
+  // at a time
   __device__ __forceinline__ void get(int st, int& l, int& h) {
     if ((st >> 6) != chunk) {
       lo = nlo;

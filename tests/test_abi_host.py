@@ -112,6 +112,26 @@ def test_workspace_queries(lib):
     assert n3.value >= 2 * 1000 * 4 * 4 + 16 * 4 * (256 + 256) * 4
 
 
+def _bwd_ws(lib, lin, M, dtype):
+    n = ctypes.c_size_t()
+    assert lib.qlora_bwd_workspace(ctypes.byref(lin), M, dtype, ctypes.byref(n)) == Q.QLORA_OK
+    return n.value
+
+
+def test_split_contraction_workspace(lib):
+    # 512 rows of a 2048 -> 16384 layer: 4 x 16 output tiles of 128 x 128 over
+    # 256 stages of 64 n split 8 ways -> 8 partial products of [512, 2048]
+    # float32 plus 8 partial u [512, 8] on top of t, u and the partial sums
+    lin = _lin(K=2048, N=16384, r=8)
+    bf = _bwd_ws(lib, lin, 512, Q.QLORA_BF16)
+    f32 = _bwd_ws(lib, lin, 512, Q.QLORA_F32)
+    assert bf - f32 >= 8 * 512 * 2048 * 4 + 8 * 512 * 8 * 4
+    assert bf - f32 <= 8 * 512 * 2048 * 4 + 8 * 512 * 8 * 4 + 2 * 256
+    # a short contraction does not split (the 1024 x 1024 layers)
+    lin = _lin(K=1024, N=1024, r=8)
+    assert _bwd_ws(lib, lin, 1024, Q.QLORA_BF16) == _bwd_ws(lib, lin, 1024, Q.QLORA_F32)
+
+
 @pytest.mark.parametrize("kw,M,dtype,want", [
     (dict(r=0), 64, Q.QLORA_BF16, Q.QLORA_EINVAL),
     (dict(r=33), 64, Q.QLORA_BF16, Q.QLORA_EINVAL),

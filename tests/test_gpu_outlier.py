@@ -137,6 +137,8 @@ LAYER_CASES = [
     (1, 512, 128, 16, 2),       # one row
     (257, 1024, 192, 32, 3),    # rank 32, a ragged row tile
     (64, 2048, 1024, 8, 4),     # several 128-wide k blocks
+    (70, 208, 2080, 4, 5),      # split contraction: 2 splits, ragged last stage
+    (40, 128, 8192, 8, 6),      # 8 splits; the later ones start past 64 stages
 ]
 
 

@@ -150,11 +150,14 @@ SMALL = [
     (2, 130, 128, 144, 16),
     (2, 257, 512, 1040, 32),
     (2, 64, 3072, 128, 8),      # more dx column tiles than 64-n stages
-    (2, 1000, 64, 2048, 4),     # one column tile walking 32 stages, 16 row blocks
+    (2, 1000, 64, 2048, 4),     # one 128-wide column tile, contraction split in 2
+    (2, 200, 320, 2240, 8),     # split contraction: 2 splits, ragged rows and k tile
+    (2, 130, 208, 8320, 4),     # 8 splits of 17 stages, the last one of 11
     (3, 200, 3072, 400, 4),
     (5, 1, 128, 16, 4),
     (5, 77, 256, 272, 8),
     (5, 130, 384, 144, 1),
+    (5, 77, 256, 4160, 8),      # 4-bit, contraction split in 4
 ]
 
 
@@ -325,6 +328,7 @@ SPLIT = [
     (3, 0, True),                         # 128 x 128 tiles (gpt2 qkv, full size)
     ((5, 512, 1024, 512, 4), None, True),  # 4-bit, 64-row tiles
     (5, 0, True),                         # 4-bit, 128 x 128 tiles (full size)
+    ((2, 200, 320, 2240, 8), None, True),  # split contraction
 ]
 
 
