@@ -83,10 +83,9 @@ __device__ __forceinline__ int ws_index(int k, int j, int sld) {
 // Copy the slice [s0, s0 + len) of the adapter matrix into LDS.
 // MODE < kBwd: A [L, r] row-major; kBwd: B [r, L] row-major, or per head
 // [heads, r, hd] (4-float units never straddle a head: hd % 4 == 0).
-template <int R, int MODE>
+template <int R, int MODE, int SL = Slice<R>::len>
 __device__ __forceinline__ void stage_slice(float* Ws, const float* __restrict__ W,
                                             int L, int r, int s0, int len, int sld, int hd) {
-  constexpr int SL = Slice<R>::len;
   constexpr int PER = (R * SL / 4 + 255) / 256;     // 16-byte units per thread
   if constexpr (MODE == kBwd) {
     // r rows of len floats
@@ -282,6 +281,184 @@ __global__ __launch_bounds__(256) void row_kernel(
   }
 }
 
+// ---- long rows (4096 < L <= 16384), forward modes, rank up to 8 ------------
+// Two rows per block. Wave w owns the 512-entry groups g = 4 i + w of both
+// rows (entries [512 g, 512 g + 512), one 8-entry chunk per lane), so every
+// adapter value read from LDS serves two rows, and the rows stay in
+// registers between the abs-max and the quantize pass (read once). The
+// adapter comes in slices of 2048 entries: slice i holds group i of every
+// wave. The row's abs-max, its code sum and its r sums of x A are combined
+// across the four waves through LDS in wave order.
+constexpr int kLongRows = 2;
+constexpr int kLongHold = 8;               // groups per wave: L <= 4 * 8 * 512
+constexpr int kLongMax = 4 * kLongHold * 512;
+constexpr int kLongSlice = 2048;
+constexpr int kLongMaxRank = 8;
+
+// |v| bits of the largest of a chunk's eight values, as float32 bits
+__device__ __forceinline__ uint32_t raw_absmax(const Raw<BF16>& r) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = r.v[i] & 0x7fffu, hi = (r.v[i] >> 16) & 0x7fffu;
+    m = lo > m ? lo : m;
+    m = hi > m ? hi : m;
+  }
+  return m << 16;
+}
+__device__ __forceinline__ uint32_t raw_absmax(const Raw<F32>& r) {
+  const float v[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { const uint32_t b = abs_bits(v[e]); m = b > m ? b : m; }
+  return m;
+}
+
+template <typename T, int R, int MODE>
+__global__ __launch_bounds__(256) void row_long_kernel(
+    const typename Elem<T>::type* __restrict__ rows, int M, int L,
+    const float* __restrict__ W, int r, float* __restrict__ out_r,
+    int8_t* __restrict__ xq, float* __restrict__ sx, float* __restrict__ asum) {
+  static_assert(MODE == kFwdQuant || MODE == kFwdT, "forward modes");
+  static_assert(R <= kLongMaxRank, "a 2048-entry slice fits the LDS budget");
+  constexpr int SL = kLongSlice, RB = kLongRows, NH = kLongHold;
+  extern __shared__ __attribute__((aligned(16))) float Ws[];
+  __shared__ uint32_t red_max[RB][4];
+  __shared__ float red_t[RB][4][R];
+  __shared__ float red_c[RB][4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int row0 = blockIdx.x * RB;
+  const int nchunk = L / 8;
+  const bool lowrank = out_r != nullptr;
+
+  // both rows' chunks, from clamped addresses: a chunk past the row repeats
+  // the row's last chunk and a row past M repeats row M - 1, which leaves
+  // the abs-max unchanged; neither is stored or summed
+  Raw<T> hold[RB][NH];
+#pragma unroll
+  for (int rr = 0; rr < RB; ++rr) {
+    const int row = row0 + rr;
+    const auto* xr = rows + (long)(row < M ? row : M - 1) * L;
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+      const int c = 64 * (4 * i + w) + lane;
+      raw_load(xr + 8 * (c < nchunk ? c : nchunk - 1), hold[rr][i]);
+    }
+  }
+  if (lowrank) stage_slice<R, MODE, SL>(Ws, W, L, r, 0, SL, SL, 0);
+
+  QuantParams qp[RB];
+  if constexpr (MODE == kFwdQuant) {
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < NH; ++i) {
+        const uint32_t b = raw_absmax(hold[rr][i]);
+        m = b > m ? b : m;
+      }
+      m = wave_max_u32(m);
+      if (lane == 0) red_max[rr][w] = m;
+    }
+  }
+  __syncthreads();                                  // slice 0 and the wave maxima
+  if constexpr (MODE == kFwdQuant) {
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      uint32_t m = red_max[rr][0];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) m = red_max[rr][q] > m ? red_max[rr][q] : m;
+      qp[rr] = absmax_params(m, 127.f);
+    }
+  }
+
+  int csum[RB];
+  float acc[RB][R];
+#pragma unroll
+  for (int rr = 0; rr < RB; ++rr) {
+    csum[rr] = 0;
+#pragma unroll
+    for (int j = 0; j < R; ++j) acc[rr][j] = 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < NH; ++i) {
+    if (SL * i >= L) break;
+    if (i > 0) {
+      __syncthreads();                              // slice i - 1 is used
+      if (lowrank) stage_slice<R, MODE, SL>(Ws, W, L, r, SL * i, min(SL, L - SL * i), SL, 0);
+      __syncthreads();
+    }
+    const int c = 64 * (4 * i + w) + lane;
+    if (c < nchunk) {
+      float v[RB][8];
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) raw_unpack(hold[rr][i], v[rr]);
+      if constexpr (MODE == kFwdQuant) {
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) {
+          const int row = row0 + rr;
+          uint32_t lo = 0, hi = 0;
+          if (qp[rr].live) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int q0 = quant_code(v[rr][e], qp[rr].inv, 127.f);
+              const int q1 = quant_code(v[rr][e + 4], qp[rr].inv, 127.f);
+              lo |= (uint32_t)(q0 & 0xff) << (8 * e);
+              hi |= (uint32_t)(q1 & 0xff) << (8 * e);
+              csum[rr] += q0 + q1;
+            }
+          }
+          if (row < M) *reinterpret_cast<u32x2*>(xq + (long)row * L + 8 * c) = u32x2{lo, hi};
+        }
+      }
+      if (lowrank) {
+        const float* gA = &Ws[(c - SL / 8 * i) * (8 * R + 4)];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+#pragma unroll
+          for (int j = 0; j < R; ++j) {
+            const float a = gA[e * R + j];
+#pragma unroll
+            for (int rr = 0; rr < RB; ++rr) acc[rr][j] = __builtin_fmaf(v[rr][e], a, acc[rr][j]);
+          }
+        }
+      }
+    }
+  }
+
+  // per-wave totals, then the four waves added in wave order
+#pragma unroll
+  for (int rr = 0; rr < RB; ++rr) {
+    if (lowrank) {
+      const float tot = wave_sum_ranks<R>(acc[rr]);
+      const int j = rank_of_lane<R>(lane);
+      if ((lane & (64 / R - 1)) == 0) red_t[rr][w][j] = tot;
+    }
+    if (MODE == kFwdQuant && asum != nullptr) {
+      // |sum| <= 127 L < 2^24: exact in float
+      const float cs = wave_sum((float)csum[rr]);
+      if (lane == 0) red_c[rr][w] = cs;
+    }
+  }
+  __syncthreads();
+  if (lowrank && tid < RB * R) {
+    const int rr = tid / R, j = tid % R, row = row0 + rr;
+    if (row < M && j < r)
+      out_r[(long)row * r + j] = ((red_t[rr][0][j] + red_t[rr][1][j]) + red_t[rr][2][j]) + red_t[rr][3][j];
+  }
+  if constexpr (MODE == kFwdQuant) {
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      const int row = row0 + rr;
+      if (tid == rr && row < M) {
+        sx[row] = qp[rr].scale;
+        if (asum != nullptr) asum[row] = ((red_c[rr][0] + red_c[rr][1]) + red_c[rr][2]) + red_c[rr][3];
+      }
+    }
+  }
+}
+
 template <typename T, int R, int MODE>
 void row_launch(const void* rows, int M, int L, const float* W, int hd, int r,
                 float* out_r, int8_t* xq, float* sx, float* asum, const float* sw,
@@ -293,6 +470,14 @@ void row_launch(const void* rows, int M, int L, const float* W, int hd, int r,
   size_t lds = 0;
   if (out_r != nullptr)
     lds = (MODE == kBwd ? (size_t)R * sld : (size_t)(sld / 8) * (8 * R + 4)) * sizeof(float);
+  if constexpr (MODE != kBwd && R <= kLongMaxRank) {
+    if (L > kHoldChunks * 512 && L <= kLongMax) {
+      const size_t ldsl = out_r != nullptr ? (size_t)(kLongSlice / 8) * (8 * R + 4) * sizeof(float) : 0;
+      const dim3 lgrid((M + kLongRows - 1) / kLongRows);
+      row_long_kernel<T, R, MODE><<<lgrid, 256, ldsl, st>>>(p, M, L, W, r, out_r, xq, sx, asum);
+      return;
+    }
+  }
   if (L <= kHoldChunks * 512)
     row_kernel<T, R, MODE, true><<<grid, 256, lds, st>>>(p, M, L, W, hd, r, out_r, xq, sx,
                                                          asum, sw, dys);

@@ -154,10 +154,16 @@ SMALL = [
     (2, 200, 320, 2240, 8),     # split contraction: 2 splits, ragged rows and k tile
     (2, 130, 208, 8320, 4),     # 8 splits of 17 stages, the last one of 11
     (3, 200, 3072, 400, 4),
+    (1, 3, 4608, 32, 2),        # float32 rows past 4096 entries (two rows per block)
+    (2, 5, 4112, 64, 8),        # long rows: odd row count, a 16-entry last slice
+    (2, 33, 16384, 48, 4),      # long rows at the longest length held in registers
+    (2, 4, 6144, 32, 16),       # long rows at rank 16 (streaming row pass)
+    (2, 3, 20480, 32, 8),       # rows past the held length (streaming row pass)
     (5, 1, 128, 16, 4),
     (5, 77, 256, 272, 8),
     (5, 130, 384, 144, 1),
     (5, 77, 256, 4160, 8),      # 4-bit, contraction split in 4
+    (5, 7, 8192, 64, 8),        # 4-bit: the adapter's down projection over long rows
 ]
 
 
