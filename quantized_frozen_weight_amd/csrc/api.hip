@@ -68,7 +68,7 @@ inline float lora_s(const qlora_linear* L) {
 }
 
 struct FwdLayout {
-  size_t xq, sx, t, asum, total;
+  size_t xq, sx, t, asum, pacc, total;
 };
 FwdLayout fwd_layout(const qlora_linear* L, int M) {
   FwdLayout w{};
@@ -80,6 +80,8 @@ FwdLayout fwd_layout(const qlora_linear* L, int M) {
   w.t = off; off = align_up(off + (size_t)M * L->r * 4);
   // row sums of the activation codes (affine weights)
   w.asum = off; off = align_up(off + (L->fmt == QLORA_W8O ? (size_t)M * 4 : 0));
+  // split contraction of the int8 product (0 bytes when it does not split)
+  w.pacc = off; off = align_up(off + (L->fmt == QLORA_W8 ? fwd_split_ints(M, L->N, L->K) * 4 : 0));
   w.total = off;
   return w;
 }
@@ -248,7 +250,7 @@ int qlora_fwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
       launch_gemm_fwd_w8(dtype, M, L->N, L->K, xq,
                          static_cast<const int8_t*>(L->codes), sx,
                          static_cast<const float*>(L->scales), t, L->B, head_width(L), L->r,
-                         lora_s(L), y, nullptr, s);
+                         lora_s(L), y, nullptr, reinterpret_cast<int32_t*>(at(ws, w.pacc)), s);
     mark(ev_stop, s);
   } else if (L->fmt == QLORA_W8O) {
     int8_t* xq = reinterpret_cast<int8_t*>(at(ws, w.xq));
@@ -470,7 +472,7 @@ int qlora_fwd_acc(const qlora_linear* L, int M, int dtype, const void* x,
   // the integer product alone: no scale is read
   launch_gemm_fwd_w8(dtype, M, L->N, L->K, xq,
                      static_cast<const int8_t*>(L->codes), sx, nullptr, nullptr, L->B,
-                     head_width(L), L->r, 0.f, nullptr, acc, s);
+                     head_width(L), L->r, 0.f, nullptr, acc, nullptr, s);
   return launch_status();
 }
 

@@ -69,10 +69,15 @@ struct I8Args {
   const u32x2* fent;
   int ng;                // 16-column cells per 128-wide k block
   int tiles_x;
+  // split contraction (128 x 128 tiles): the exact int32 partial sums in the
+  // accumulator layout, the split count and stages per split
+  int32_t* pacc;         // [splits, tiles, 4 waves, 16 fragments, 64 lanes] int4
+  int splits, nks;
 };
 
-template <int BM, int BN, int S, int R, typename OutT, bool ACC_OUT, bool AFF>
+template <int BM, int BN, int S, int R, typename OutT, bool ACC_OUT, bool AFF, bool SPLIT = false>
 __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
+  static_assert(!SPLIT || (!AFF && !ACC_OUT), "split: plain int8 products");
   constexpr int BK = 128, ASZ = BM * BK, STG = (BM + BN) * BK;
   constexpr int AI = BM / 32, BI = BN / 32, LPS = AI + BI;   // loads per wave per stage
   constexpr int FM = BM / 32, FN = BN / 32;
@@ -86,12 +91,25 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wid = wave_id();
   const int wm = wid >> 1, wn = wid & 1;
-  const int m0 = ((int)blockIdx.x / a.tiles_x) * BM, n0 = ((int)blockIdx.x % a.tiles_x) * BN;
   const int M = a.M, N = a.N, K = a.K;
   const int nk = (K + BK - 1) / BK;
+  // SPLIT: blocks (split, tile), split-major, renumbered so that the blocks
+  // the dispatcher deals to one XCD (every eighth) share one split's k range
+  int bid = (int)blockIdx.x, split = 0;
+  const int tiles = a.tiles_x * ((M + BM - 1) / BM);
+  if constexpr (SPLIT) {
+    const int nb = (int)gridDim.x;
+    if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+    split = bid / tiles;
+    bid -= split * tiles;
+  }
+  const int m0 = (bid / a.tiles_x) * BM, n0 = (bid % a.tiles_x) * BN;
+  // stages [kt0, kt1) of the contraction
+  const int kt0 = SPLIT ? split * a.nks : 0;
+  const int kt1 = SPLIT ? (kt0 + a.nks < nk ? kt0 + a.nks : nk) : nk;
 
   EpiOps<BM, BN, R, true, AFF> ep;
-  if constexpr (!ACC_OUT) ep.load(M, N, m0, n0, a.r, a.t, a.B, a.hd, a.sx, AFF ? nullptr : a.sw);
+  if constexpr (!ACC_OUT && !SPLIT) ep.load(M, N, m0, n0, a.r, a.t, a.B, a.hd, a.sx, AFF ? nullptr : a.sw);
   if constexpr (AFF) ep.load_rows(M, m0, a.asum);
 
   // AFF: the wave's outlier cell, columns [16 wid, 16 wid + 16) of the tile;
@@ -145,7 +163,7 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
   if constexpr (AFF) cr.init(a.fptr, a.ng, gl, gh, nk);
 #pragma unroll
   for (int st = 0; st < S - 1; ++st)
-    if (st < nk) issue(st, st);
+    if (kt0 + st < kt1) issue(kt0 + st, st);
   if constexpr (AFF) {
     cr.get(0, clo, chi);
     cur = entries(clo);
@@ -154,8 +172,8 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
   int slot = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_stages<LPS, 0, S - 2>(nk - 1 - kt);   // stage kt has landed (this wave)
+  for (int kt = kt0; kt < kt1; ++kt) {
+    wait_stages<LPS, 0, S - 2>(kt1 - 1 - kt);   // stage kt has landed (this wave)
     __builtin_amdgcn_s_barrier();               // ... for every wave; slot kt-1 is free
     // AFF: read ahead (before this iteration's loads enter the queue) the
     // entries of stage kt + 1
@@ -171,7 +189,7 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
     // (outlier-compensated weights: past the last stage the loads read the
     // zero page into the free slot, so that every iteration queues the same
     // loads and a read-ahead register can be waited for by count)
-    if (AFF || kt + S - 1 < nk) issue(kt + S - 1, slot == 0 ? S - 1 : slot - 1);
+    if (AFF || kt + S - 1 < kt1) issue(kt + S - 1, slot == 0 ? S - 1 : slot - 1);
     const int8_t* As = ring + slot * STG;
     const int8_t* Bs = As + ASZ;
     // AFF: the stage's first PEEL outliers as straight-line code ahead of the
@@ -254,7 +272,17 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
     slot = slot == S - 1 ? 0 : slot + 1;
   }
 
-  if constexpr (ACC_OUT) {
+  if constexpr (SPLIT) {
+    // int4 unit ((split tiles + tile) 4 + wave) F + f) 64 + lane for
+    // fragment f = i FN + j of F = FM FN: each store writes 1 KB of
+    // consecutive bytes
+    i32x4* P = reinterpret_cast<i32x4*>(a.pacc) +
+               ((long)(split * tiles + bid) * 4 + wid) * (FM * FN * 64) + lane;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) P[(i * FN + j) * 64] = acc[i][j];
+  } else if constexpr (ACC_OUT) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -307,6 +335,92 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
   }
 }
 
+// Second launch of the split int8 product, one 512-thread block per 128-row x
+// 64-column half of a 128 x 128 tile: the int32 partial sums added (exact, so
+// the result equals the one-pass product's bit for bit), then the scaled
+// low-rank epilogue. Wave v takes rows [16 v, 16 v + 16): fragment row v % 4
+// of the product kernel's wave 2 (v / 4) + (column half); all of a lane's
+// split loads are issued before the first add.
+template <int R, int NSPL, typename OutT>
+__global__ __launch_bounds__(512) void fwd_fixup_kernel(I8Args a) {
+  constexpr int BM = 128, HN = 64, FN = 4;
+  using Ep = EpiOps<BM, HN, R, true>;
+  constexpr int EPB = (Ep::kFloats * 4 + 15) / 16 * 16;
+  constexpr int STRIP = epi_strip_bytes<OutT, FN>();
+  __shared__ __attribute__((aligned(1024))) int8_t lds[EPB + 8 * STRIP];
+  float* E = reinterpret_cast<float*>(lds);
+
+  const int tid = threadIdx.x, lane = tid & 63, v = wave_id();
+  const int M = a.M, N = a.N, nsp = a.splits;
+  const int tiles = a.tiles_x * ((M + BM - 1) / BM);
+  const int tile = (int)blockIdx.x >> 1, wn = (int)blockIdx.x & 1;
+  const int m0 = (tile / a.tiles_x) * BM, n0 = (tile % a.tiles_x) * 128 + wn * HN;
+
+  const int w = 2 * (v >> 2) + wn, fi = v & 3;
+  const i32x4* P = reinterpret_cast<const i32x4*>(a.pacc) + ((long)tile * 4 + w) * (16 * 64) +
+                   fi * 4 * 64 + lane;
+  const long pstride = (long)tiles * 4 * 16 * 64;       // int4 units per split
+  i32x4 pv[NSPL][FN];
+#pragma unroll
+  for (int sp = 0; sp < NSPL; ++sp)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) pv[sp][j] = P[(sp < nsp ? sp : 0) * pstride + j * 64];
+
+  Ep ep;
+  if (tid < 256) ep.load(M, N, m0, n0, a.r, a.t, a.B, a.hd, a.sx, a.sw);
+  i32x4 acc[1][FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    acc[0][j] = pv[0][j];
+#pragma unroll
+    for (int sp = 1; sp < NSPL; ++sp)
+      if (sp < nsp) acc[0][j] += pv[sp][j];
+  }
+  if (tid < 256) ep.store(E, M, N, m0, n0, a.r);
+  __syncthreads();
+  epilogue_lowrank<BM, HN, R, true>(acc, E, M, N, m0, n0, 16 * v, 0, a.s,
+                                    reinterpret_cast<OutT*>(a.y), lds + EPB + v * STRIP);
+}
+
+constexpr int kMaxFwdSplits = 8;
+
+// Split count and stages per split of the 128 x 128 product: only for at
+// most 128 tiles over a long contraction, doubling (up to 8) while the grid
+// stays within two blocks per compute unit and each split keeps at least 16
+// stages of 128 k.
+void fwd_split_plan(int M, int N, int K, int* splits, int* nks) {
+  const long tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
+  const int nk = (K + 127) / 128;
+  int sp = 1;
+  if (tiles <= 128)
+    while (sp < kMaxFwdSplits && tiles * sp * 2 <= 2 * kCUs && nk / (sp * 2) >= 16) sp *= 2;
+  *nks = (nk + sp - 1) / sp;
+  *splits = (nk + *nks - 1) / *nks;
+}
+
+template <typename OutT>
+void launch_split(I8Args a, hipStream_t st) {
+  constexpr int BM = 128, BN = 128, S = 2;
+  a.tiles_x = (a.N + BN - 1) / BN;
+  const int tiles = a.tiles_x * ((a.M + BM - 1) / BM);
+  const dim3 grid((unsigned)(tiles * a.splits)), fgrid((unsigned)(2 * tiles));
+  if (a.r <= 4) fwd_i8_kernel<BM, BN, S, 4, OutT, false, false, true><<<grid, 256, 0, st>>>(a);
+  else if (a.r <= 8) fwd_i8_kernel<BM, BN, S, 8, OutT, false, false, true><<<grid, 256, 0, st>>>(a);
+  else if (a.r <= 16) fwd_i8_kernel<BM, BN, S, 16, OutT, false, false, true><<<grid, 256, 0, st>>>(a);
+  else fwd_i8_kernel<BM, BN, S, 32, OutT, false, false, true><<<grid, 256, 0, st>>>(a);
+  if (a.splits <= 4) {
+    if (a.r <= 4) fwd_fixup_kernel<4, 4, OutT><<<fgrid, 512, 0, st>>>(a);
+    else if (a.r <= 8) fwd_fixup_kernel<8, 4, OutT><<<fgrid, 512, 0, st>>>(a);
+    else if (a.r <= 16) fwd_fixup_kernel<16, 4, OutT><<<fgrid, 512, 0, st>>>(a);
+    else fwd_fixup_kernel<32, 4, OutT><<<fgrid, 512, 0, st>>>(a);
+  } else {
+    if (a.r <= 4) fwd_fixup_kernel<4, kMaxFwdSplits, OutT><<<fgrid, 512, 0, st>>>(a);
+    else if (a.r <= 8) fwd_fixup_kernel<8, kMaxFwdSplits, OutT><<<fgrid, 512, 0, st>>>(a);
+    else if (a.r <= 16) fwd_fixup_kernel<16, kMaxFwdSplits, OutT><<<fgrid, 512, 0, st>>>(a);
+    else fwd_fixup_kernel<32, kMaxFwdSplits, OutT><<<fgrid, 512, 0, st>>>(a);
+  }
+}
+
 template <int BM, int BN, int S, typename OutT, bool ACC, bool AFF = false>
 void launch_tiles(I8Args a, hipStream_t st) {
   a.tiles_x = (a.N + BN - 1) / BN;
@@ -318,7 +432,16 @@ void launch_tiles(I8Args a, hipStream_t st) {
 }
 
 template <typename OutT, bool ACC>
-void launch_shape(const I8Args& a, hipStream_t st) {
+void launch_shape(I8Args a, hipStream_t st) {
+  if constexpr (!ACC) {
+    if (a.pacc != nullptr) {
+      fwd_split_plan(a.M, a.N, a.K, &a.splits, &a.nks);
+      if (a.splits > 1) {
+        launch_split<OutT>(a, st);
+        return;
+      }
+    }
+  }
   const long t64 = (long)((a.M + 63) / 64) * ((a.N + 63) / 64);
   const long t128 = (long)((a.M + 127) / 128) * ((a.N + 127) / 128);
   if (t64 <= 2 * kCUs) launch_tiles<64, 64, 3, OutT, ACC>(a, st);
@@ -328,13 +451,22 @@ void launch_shape(const I8Args& a, hipStream_t st) {
 
 }  // namespace
 
+size_t fwd_split_ints(int M, int N, int K) {
+  int sp, nks;
+  fwd_split_plan(M, N, K, &sp, &nks);
+  if (sp == 1) return 0;
+  const size_t tiles = (size_t)((M + 127) / 128) * (size_t)((N + 127) / 128);
+  return (size_t)sp * tiles * 128 * 128;
+}
+
 void launch_gemm_fwd_w8(int dtype, int M, int N, int K, const int8_t* xq,
                         const int8_t* codes, const float* sx, const float* sw,
                         const float* t, const float* B, int hd, int r, float s,
-                        void* y, int32_t* acc_out, hipStream_t st) {
+                        void* y, int32_t* acc_out, int32_t* pacc, hipStream_t st) {
   I8Args a{};
   a.M = M; a.N = N; a.K = K; a.xq = xq; a.codes = codes; a.sx = sx; a.sw = sw;
   a.t = t; a.B = B; a.hd = hd; a.r = r; a.s = s; a.y = y; a.acc_out = acc_out;
+  a.pacc = pacc;
   if (acc_out != nullptr) launch_shape<float, true>(a, st);
   else if (dtype == 0) launch_shape<float, false>(a, st);
   else launch_shape<uint16_t, false>(a, st);

@@ -34,11 +34,15 @@ void launch_rowquant(int dtype, const void* x, int M, int K, const float* A,
 void launch_lora_down(int dtype, const void* x, int M, int K, const float* A,
                       int r, float* t, hipStream_t st);
 
-// y = acc * sx[m] * sw[n] + s * t B   (acc_out != nullptr: write int32 acc)
+// y = acc * sx[m] * sw[n] + s * t B   (acc_out != nullptr: write int32 acc).
+// Shapes with few output tiles and a long contraction split it when pacc is
+// given (fwd_split_ints(M, N, K) int32, 0 when the shape does not split):
+// the exact partial sums go there and a second launch adds them.
+size_t fwd_split_ints(int M, int N, int K);
 void launch_gemm_fwd_w8(int dtype, int M, int N, int K, const int8_t* xq,
                         const int8_t* codes, const float* sx, const float* sw,
                         const float* t, const float* B, int hd, int r, float s,
-                        void* y, int32_t* acc_out, hipStream_t st);
+                        void* y, int32_t* acc_out, int32_t* pacc, hipStream_t st);
 // Outlier-compensated int8 weight (outlier.hpp) with int8 activations:
 // y = sx[m] (c acc + b' asum[m] + corr) + s t B (bf16 y)
 void launch_gemm_fwd_w8o(int M, int N, int K, const int8_t* xq, const int8_t* codes,

@@ -132,6 +132,22 @@ def test_split_contraction_workspace(lib):
     assert _bwd_ws(lib, lin, 1024, Q.QLORA_BF16) == _bwd_ws(lib, lin, 1024, Q.QLORA_F32)
 
 
+def test_split_forward_workspace(lib):
+    # 512 rows of a 16384 -> 2048 int8 layer: 4 x 16 output tiles of 128 x 128
+    # over 128 stages of 128 k split 8 ways -> 8 int32 partial sums of
+    # [512, 2048]; the 4-bit layout of the same shape holds none
+    st, w8 = _fwd_ws(lib, _lin(K=16384, N=2048, r=8), M=512)
+    assert st == Q.QLORA_OK
+    base = 512 * 16384 + 512 * 4 + 512 * 8 * 4
+    assert w8 >= base + 8 * 512 * 2048 * 4
+    assert w8 <= base + 8 * 512 * 2048 * 4 + 4 * 256
+    st, w4 = _fwd_ws(lib, _lin(K=16384, N=2048, r=8, fmt=Q.QLORA_W4G128), M=512)
+    assert st == Q.QLORA_OK and w4 < base + 4 * 256
+    # a short contraction does not split
+    st, short = _fwd_ws(lib, _lin(K=1024, N=1024, r=8), M=1024)
+    assert short < 1024 * 1024 + 1024 * 4 + 1024 * 8 * 4 + 4 * 256
+
+
 @pytest.mark.parametrize("kw,M,dtype,want", [
     (dict(r=0), 64, Q.QLORA_BF16, Q.QLORA_EINVAL),
     (dict(r=33), 64, Q.QLORA_BF16, Q.QLORA_EINVAL),
