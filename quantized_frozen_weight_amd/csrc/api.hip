@@ -68,7 +68,7 @@ inline float lora_s(const qlora_linear* L) {
 }
 
 struct FwdLayout {
-  size_t xq, sx, t, asum, pacc, total;
+  size_t xq, sx, t, asum, pacc, pcorr, total;
 };
 FwdLayout fwd_layout(const qlora_linear* L, int M) {
   FwdLayout w{};
@@ -80,8 +80,12 @@ FwdLayout fwd_layout(const qlora_linear* L, int M) {
   w.t = off; off = align_up(off + (size_t)M * L->r * 4);
   // row sums of the activation codes (affine weights)
   w.asum = off; off = align_up(off + (L->fmt == QLORA_W8O ? (size_t)M * 4 : 0));
-  // split contraction of the int8 product (0 bytes when it does not split)
-  w.pacc = off; off = align_up(off + (L->fmt == QLORA_W8 ? fwd_split_ints(M, L->N, L->K) * 4 : 0));
+  // split contraction of the int8 product (0 bytes when it does not split):
+  // int32 partial sums, and the affine weights' partial corrections
+  const bool w8 = L->fmt == QLORA_W8, w8o = L->fmt == QLORA_W8O;
+  const size_t nsplit = (w8 || w8o) ? fwd_split_ints(M, L->N, L->K, w8o) : 0;
+  w.pacc = off; off = align_up(off + nsplit * 4);
+  w.pcorr = off; off = align_up(off + (w8o ? nsplit * 4 : 0));
   w.total = off;
   return w;
 }
@@ -261,7 +265,8 @@ int qlora_fwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
     for (int rep = 0; rep < repeats; ++rep)
       launch_gemm_fwd_w8o(M, L->N, L->K, xq, static_cast<const int8_t*>(L->codes), sx, asum,
                           L->scales, t, L->B, head_width(L), L->r, lora_s(L),
-                          static_cast<uint16_t*>(y), s);
+                          static_cast<uint16_t*>(y), reinterpret_cast<int32_t*>(at(ws, w.pacc)),
+                          reinterpret_cast<float*>(at(ws, w.pcorr)), s);
     mark(ev_stop, s);
   } else {
     launch_lora_down(dtype, x, M, L->K, L->A, L->r, t, s);

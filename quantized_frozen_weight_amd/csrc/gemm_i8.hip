@@ -71,13 +71,14 @@ struct I8Args {
   int tiles_x;
   // split contraction (128 x 128 tiles): the exact int32 partial sums in the
   // accumulator layout, the split count and stages per split
-  int32_t* pacc;         // [splits, tiles, 4 waves, 16 fragments, 64 lanes] int4
+  int32_t* pacc;         // [splits, tiles, 4 waves, FM FN fragments, 64 lanes] int4
+  float* pcorr;          // affine: [splits, tiles, 4 waves, CR rows, 16 columns, 64 lanes]
   int splits, nks;
 };
 
 template <int BM, int BN, int S, int R, typename OutT, bool ACC_OUT, bool AFF, bool SPLIT = false>
 __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
-  static_assert(!SPLIT || (!AFF && !ACC_OUT), "split: plain int8 products");
+  static_assert(!SPLIT || !ACC_OUT, "split: no integer test output");
   constexpr int BK = 128, ASZ = BM * BK, STG = (BM + BN) * BK;
   constexpr int AI = BM / 32, BI = BN / 32, LPS = AI + BI;   // loads per wave per stage
   constexpr int FM = BM / 32, FN = BN / 32;
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
 
   EpiOps<BM, BN, R, true, AFF> ep;
   if constexpr (!ACC_OUT && !SPLIT) ep.load(M, N, m0, n0, a.r, a.t, a.B, a.hd, a.sx, AFF ? nullptr : a.sw);
-  if constexpr (AFF) ep.load_rows(M, m0, a.asum);
+  if constexpr (AFF && !SPLIT) ep.load_rows(M, m0, a.asum);
 
   // AFF: the wave's outlier cell, columns [16 wid, 16 wid + 16) of the tile;
   // entry range of stage kt: [fptr[kt ng + g], fptr[kt ng + g + 1]), empty
@@ -160,12 +161,12 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
   // waits for them alone
   int clo = 0, chi = 0;
   u32x2 cur = u32x2{0u, 0u};
-  if constexpr (AFF) cr.init(a.fptr, a.ng, gl, gh, nk);
+  if constexpr (AFF) cr.init(a.fptr, a.ng, gl, gh, nk, kt0);
 #pragma unroll
   for (int st = 0; st < S - 1; ++st)
     if (kt0 + st < kt1) issue(kt0 + st, st);
   if constexpr (AFF) {
-    cr.get(0, clo, chi);
+    cr.get(kt0, clo, chi);
     cur = entries(clo);
     // (the first stage's entries, like its operands, have landed before the
     // loop starts; the loop then never waits for a load it did not count)
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
     u32x2 nxt = u32x2{0u, 0u};
     int nlo = 0, nhi = 0;
     if constexpr (AFF) {
-      cr.get(kt + 1 < nk ? kt + 1 : kt, nlo, nhi);
+      cr.get(kt + 1 < kt1 ? kt + 1 : kt, nlo, nhi);
       nxt = entries(nlo);
       // keep this load ahead of the stage loads: it is then waited for by
       // count when the next stage takes it over
@@ -282,6 +283,16 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) P[(i * FN + j) * 64] = acc[i][j];
+    if constexpr (AFF) {
+      // the wave's corrections, float unit ((((split tiles + tile) 4 +
+      // wave) CR + r) 16 + c) 64 + lane
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the zero-page stage loads past the range
+      float* Q = a.pcorr + ((long)(split * tiles + bid) * 4 + wid) * (CR * 16 * 64) + lane;
+#pragma unroll
+      for (int r = 0; r < CR; ++r)
+#pragma unroll
+        for (int c = 0; c < kW8OFwdCellN; ++c) Q[(r * 16 + c) * 64] = corr[r][c];
+    }
   } else if constexpr (ACC_OUT) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -382,18 +393,109 @@ __global__ __launch_bounds__(512) void fwd_fixup_kernel(I8Args a) {
                                     reinterpret_cast<OutT*>(a.y), lds + EPB + v * STRIP);
 }
 
+// The same for outlier-compensated weights on 128 x 64 tiles, one 512-thread
+// block per tile: the int32 partial sums added (exact), the corrections added
+// in split order into LDS ([128][64 + 4] floats, from the product kernel's
+// cell layout), then acc' = c acc + corr and the affine epilogue.
+template <int R, int NSPL>
+__global__ __launch_bounds__(512) void fwd_fixup_aff_kernel(I8Args a) {
+  constexpr int BM = 128, BN = 64, FN = 4, CR = 2, CP = BN + 4;
+  using Ep = EpiOps<BM, BN, R, true, true>;
+  constexpr int EPB = (Ep::kFloats * 4 + 15) / 16 * 16;
+  constexpr int CSZ = BM * CP * 4;
+  constexpr int STRIP = epi_strip_bytes<uint16_t, FN>();
+  __shared__ __attribute__((aligned(1024))) int8_t lds[CSZ + EPB + 8 * STRIP];
+  float* C = reinterpret_cast<float*>(lds);
+  float* E = reinterpret_cast<float*>(lds + CSZ);
+
+  const int tid = threadIdx.x, lane = tid & 63, v = wave_id();
+  const int M = a.M, N = a.N, nsp = a.splits;
+  const int tiles = a.tiles_x * ((M + BM - 1) / BM);
+  const int tile = (int)blockIdx.x;
+  const int m0 = (tile / a.tiles_x) * BM, n0 = (tile % a.tiles_x) * BN;
+
+  // wave v: rows [16 v, 16 v + 16) = fragment row v % 4 of the product
+  // kernel's waves 2 (v / 4) + {0, 1} (each 2 fragments of 16 columns)
+  const int fi = v & 3;
+  i32x4 pv[NSPL][FN];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int w = 2 * (v >> 2) + h;
+    const i32x4* P = reinterpret_cast<const i32x4*>(a.pacc) + ((long)tile * 4 + w) * (8 * 64) +
+                     fi * 2 * 64 + lane;
+    const long pstride = (long)tiles * 4 * 8 * 64;
+#pragma unroll
+    for (int sp = 0; sp < NSPL; ++sp)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) pv[sp][2 * h + j] = P[(sp < nsp ? sp : 0) * pstride + j * 64];
+  }
+  // corrections: element e = ((w CR + r) 16 + c) 64 + lane of the tile's
+  // cells -> row 64 r + lane, column 16 w + c
+  constexpr int CE = 4 * CR * 16 * 64 / 512;             // per thread
+  float cv[CE][NSPL];
+#pragma unroll
+  for (int q = 0; q < CE; ++q) {
+    const int e = tid + 512 * q;
+    const float* Qp = a.pcorr + (long)tile * (4 * CR * 16 * 64) + e;
+    const long qstride = (long)tiles * 4 * CR * 16 * 64;
+#pragma unroll
+    for (int sp = 0; sp < NSPL; ++sp) cv[q][sp] = Qp[(sp < nsp ? sp : 0) * qstride];
+  }
+  Ep ep;
+  if (tid < 256) {
+    ep.load(M, N, m0, n0, a.r, a.t, a.B, a.hd, a.sx, nullptr);
+    ep.load_rows(M, m0, a.asum);
+  }
+#pragma unroll
+  for (int q = 0; q < CE; ++q) {
+    const int e = tid + 512 * q;
+    const int ln = e & 63, c = (e >> 6) & 15, r = (e >> 10) & (CR - 1), w = e >> 11;
+    float sum = cv[q][0];
+#pragma unroll
+    for (int sp = 1; sp < NSPL; ++sp)
+      if (sp < nsp) sum += cv[q][sp];
+    C[(64 * r + ln) * CP + 16 * w + c] = sum;
+  }
+  i32x4 acc[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    acc[j] = pv[0][j];
+#pragma unroll
+    for (int sp = 1; sp < NSPL; ++sp)
+      if (sp < nsp) acc[j] += pv[sp][j];
+  }
+  if (tid < 256) {
+    ep.store(E, M, N, m0, n0, a.r);
+    ep.store_rows(E, M, m0, a.w8o->bias_q);
+  }
+  __syncthreads();
+  const float cstep = a.w8o->scale;
+  f32x4 accf[1][FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int ml = 16 * v + (lane >> 4) * 4 + ii, nl = j * 16 + (lane & 15);
+      accf[0][j][ii] = __builtin_fmaf(cstep, (float)acc[j][ii], C[ml * CP + nl]);
+    }
+  epilogue_lowrank<BM, BN, R, true, true>(accf, E, M, N, m0, n0, 16 * v, 0, a.s,
+                                          reinterpret_cast<uint16_t*>(a.y), lds + CSZ + EPB + v * STRIP);
+}
+
 constexpr int kMaxFwdSplits = 8;
 
-// Split count and stages per split of the 128 x 128 product: only for at
-// most 128 tiles over a long contraction, doubling (up to 8) while the grid
-// stays within two blocks per compute unit and each split keeps at least 16
-// stages of 128 k.
-void fwd_split_plan(int M, int N, int K, int* splits, int* nks) {
-  const long tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
+constexpr int kMaxAffSplits = 4;    // the affine fixup holds every split's loads
+
+// Split count and stages per split of the 128 x BN product: only for at
+// most 128 tiles over a long contraction, doubling (up to maxsp) while the
+// grid stays within two blocks per compute unit and each split keeps at
+// least 16 stages of 128 k.
+void fwd_split_plan(int M, int N, int K, int BN, int maxsp, int* splits, int* nks) {
+  const long tiles = (long)((M + 127) / 128) * ((N + BN - 1) / BN);
   const int nk = (K + 127) / 128;
   int sp = 1;
   if (tiles <= 128)
-    while (sp < kMaxFwdSplits && tiles * sp * 2 <= 2 * kCUs && nk / (sp * 2) >= 16) sp *= 2;
+    while (sp < maxsp && tiles * sp * 2 <= 2 * kCUs && nk / (sp * 2) >= 16) sp *= 2;
   *nks = (nk + sp - 1) / sp;
   *splits = (nk + *nks - 1) / *nks;
 }
@@ -435,7 +537,7 @@ template <typename OutT, bool ACC>
 void launch_shape(I8Args a, hipStream_t st) {
   if constexpr (!ACC) {
     if (a.pacc != nullptr) {
-      fwd_split_plan(a.M, a.N, a.K, &a.splits, &a.nks);
+      fwd_split_plan(a.M, a.N, a.K, 128, kMaxFwdSplits, &a.splits, &a.nks);
       if (a.splits > 1) {
         launch_split<OutT>(a, st);
         return;
@@ -451,12 +553,13 @@ void launch_shape(I8Args a, hipStream_t st) {
 
 }  // namespace
 
-size_t fwd_split_ints(int M, int N, int K) {
+size_t fwd_split_ints(int M, int N, int K, bool affine) {
+  const int bn = affine ? 64 : 128;
   int sp, nks;
-  fwd_split_plan(M, N, K, &sp, &nks);
+  fwd_split_plan(M, N, K, bn, affine ? kMaxAffSplits : kMaxFwdSplits, &sp, &nks);
   if (sp == 1) return 0;
-  const size_t tiles = (size_t)((M + 127) / 128) * (size_t)((N + 127) / 128);
-  return (size_t)sp * tiles * 128 * 128;
+  const size_t tiles = (size_t)((M + 127) / 128) * (size_t)((N + bn - 1) / bn);
+  return (size_t)sp * tiles * 128 * (size_t)bn;
 }
 
 void launch_gemm_fwd_w8(int dtype, int M, int N, int K, const int8_t* xq,
@@ -475,7 +578,7 @@ void launch_gemm_fwd_w8(int dtype, int M, int N, int K, const int8_t* xq,
 void launch_gemm_fwd_w8o(int M, int N, int K, const int8_t* xq, const int8_t* codes,
                          const float* sx, const float* asum, const void* side,
                          const float* t, const float* B, int hd, int r, float s,
-                         uint16_t* y, hipStream_t st) {
+                         uint16_t* y, int32_t* pacc, float* pcorr, hipStream_t st) {
   const W8OLayout L = w8o_layout(K, N);
   const char* sb = static_cast<const char*>(side);
   I8Args a{};
@@ -486,6 +589,27 @@ void launch_gemm_fwd_w8o(int M, int N, int K, const int8_t* xq, const int8_t* co
   a.fptr = reinterpret_cast<const int*>(sb + L.fptr);
   a.fent = reinterpret_cast<const u32x2*>(sb + L.fent);
   a.ng = L.ng;
+  a.pacc = pacc;
+  a.pcorr = pcorr;
+  if (pacc != nullptr && pcorr != nullptr) {
+    fwd_split_plan(M, N, K, 64, kMaxAffSplits, &a.splits, &a.nks);
+    if (a.splits > 1) {
+      // 128 x 64 tiles over the split contraction, then the fixup per tile
+      constexpr int BM = 128, BN = 64, S = 2;
+      a.tiles_x = (N + BN - 1) / BN;
+      const int tiles = a.tiles_x * ((M + BM - 1) / BM);
+      const dim3 grid((unsigned)(tiles * a.splits)), fgrid((unsigned)tiles);
+      if (r <= 4) fwd_i8_kernel<BM, BN, S, 4, uint16_t, false, true, true><<<grid, 256, 0, st>>>(a);
+      else if (r <= 8) fwd_i8_kernel<BM, BN, S, 8, uint16_t, false, true, true><<<grid, 256, 0, st>>>(a);
+      else if (r <= 16) fwd_i8_kernel<BM, BN, S, 16, uint16_t, false, true, true><<<grid, 256, 0, st>>>(a);
+      else fwd_i8_kernel<BM, BN, S, 32, uint16_t, false, true, true><<<grid, 256, 0, st>>>(a);
+      if (r <= 4) fwd_fixup_aff_kernel<4, kMaxAffSplits><<<fgrid, 512, 0, st>>>(a);
+      else if (r <= 8) fwd_fixup_aff_kernel<8, kMaxAffSplits><<<fgrid, 512, 0, st>>>(a);
+      else if (r <= 16) fwd_fixup_aff_kernel<16, kMaxAffSplits><<<fgrid, 512, 0, st>>>(a);
+      else fwd_fixup_aff_kernel<32, kMaxAffSplits><<<fgrid, 512, 0, st>>>(a);
+      return;
+    }
+  }
   // the correction accumulators take registers: 64 x 64 (three stages) or
   // 128 x 64 (two)
   const long t64 = (long)((M + 63) / 64) * ((N + 63) / 64);

@@ -36,19 +36,21 @@ void launch_lora_down(int dtype, const void* x, int M, int K, const float* A,
 
 // y = acc * sx[m] * sw[n] + s * t B   (acc_out != nullptr: write int32 acc).
 // Shapes with few output tiles and a long contraction split it when pacc is
-// given (fwd_split_ints(M, N, K) int32, 0 when the shape does not split):
-// the exact partial sums go there and a second launch adds them.
-size_t fwd_split_ints(int M, int N, int K);
+// given (fwd_split_ints(M, N, K, false) int32, 0 when the shape does not
+// split): the exact partial sums go there and a second launch adds them.
+size_t fwd_split_ints(int M, int N, int K, bool affine);
 void launch_gemm_fwd_w8(int dtype, int M, int N, int K, const int8_t* xq,
                         const int8_t* codes, const float* sx, const float* sw,
                         const float* t, const float* B, int hd, int r, float s,
                         void* y, int32_t* acc_out, int32_t* pacc, hipStream_t st);
 // Outlier-compensated int8 weight (outlier.hpp) with int8 activations:
-// y = sx[m] (c acc + b' asum[m] + corr) + s t B (bf16 y)
+// y = sx[m] (c acc + b' asum[m] + corr) + s t B (bf16 y). Split like the
+// int8 product when pacc and pcorr are given (fwd_split_ints(M, N, K, true)
+// int32 and as many floats).
 void launch_gemm_fwd_w8o(int M, int N, int K, const int8_t* xq, const int8_t* codes,
                          const float* sx, const float* asum, const void* side,
                          const float* t, const float* B, int hd, int r, float s,
-                         uint16_t* y, hipStream_t st);
+                         uint16_t* y, int32_t* pacc, float* pcorr, hipStream_t st);
 // 4-bit weights: the products hold the scales of up to this many 128-wide k
 // groups per block in LDS (K <= 16384).
 constexpr int kW4MaxGroups = 128;

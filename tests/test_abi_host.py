@@ -143,6 +143,12 @@ def test_split_forward_workspace(lib):
     assert w8 <= base + 8 * 512 * 2048 * 4 + 4 * 256
     st, w4 = _fwd_ws(lib, _lin(K=16384, N=2048, r=8, fmt=Q.QLORA_W4G128), M=512)
     assert st == Q.QLORA_OK and w4 < base + 4 * 256
+    # outlier-compensated weights: 4 x 32 tiles of 128 x 64 split 4 ways ->
+    # int32 partial sums and float partial corrections, 16 MiB each
+    st, w8o = _fwd_ws(lib, _lin(K=16384, N=2048, r=8, fmt=Q.QLORA_W8O), M=512)
+    assert st == Q.QLORA_OK
+    base_o = base + 512 * 4                            # and the code sums
+    assert base_o + 2 * 4 * 512 * 2048 * 4 <= w8o <= base_o + 2 * 4 * 512 * 2048 * 4 + 6 * 256
     # a short contraction does not split
     st, short = _fwd_ws(lib, _lin(K=1024, N=1024, r=8), M=1024)
     assert short < 1024 * 1024 + 1024 * 4 + 1024 * 8 * 4 + 4 * 256
