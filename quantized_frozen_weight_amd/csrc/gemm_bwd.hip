@@ -140,6 +140,16 @@ __device__ __forceinline__ void tr16_reads(const uint32_t (&addr)[NR], uint64_t 
   }
 }
 
+// a0 or a1 by a wave-uniform flag, as selects rather than a branch (the u
+// products take the odd or even row blocks of A by the wave's column half)
+__device__ __forceinline__ bf16x8 pick_frag(const bf16x8& a0, const bf16x8& a1, bool second) {
+  const u32x4 x = __builtin_bit_cast(u32x4, a0), y = __builtin_bit_cast(u32x4, a1);
+  u32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = second ? y[e] : x[e];
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // 32-bit LDS address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
@@ -183,6 +193,7 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
   // per producer wave and stage: dy rows, code rows, aux
   constexpr int AI = BM / 32, BI = RB / 64, LPS = AI + BI + AUXI;
   constexpr int FM = BM / 32, FN = BN / 32;
+  static_assert(FM % 2 == 0, "the u products pair the 16-row blocks by column half");
   constexpr int RPI = 1024 / RB, CPR = RB / 16;
   static_assert(RB == 64 || RB == 128, "code rows of 64 or 128 bytes");
   static_assert(S >= 3, "stage kt + 1 is resident while stage kt is used");
@@ -569,9 +580,9 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
 #pragma unroll
         for (int cb = 0; cb < UCB; ++cb)
 #pragma unroll
-          for (int i = 0; i < FM; ++i)
-            if ((i & 1) == wn)
-              uacc[i >> 1][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bu[cb], uacc[i >> 1][cb], 0, 0, 0);
+          for (int h = 0; h < FM / 2; ++h)
+            uacc[h][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pick_frag(af[2 * h], af[2 * h + 1], wn != 0),
+                                                                 bu[cb], uacc[h][cb], 0, 0, 0);
       }
       // dB partial for this stage's 64 n over the block's rows (one block
       // per row block and stage), on the matrix cores: consumer wave w takes
@@ -715,6 +726,7 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
   // per wave and stage: dy rows, code rows, aux, and (4-bit) one scale load
   constexpr int AI = BM / 32, BI = RB / 64, LPS = AI + BI + AUXI + (W4 ? 1 : 0);
   constexpr int FM = BM / 32, FN = BN / 32;
+  static_assert(FM % 2 == 0, "the u products pair the 16-row blocks by column half");
   constexpr int RPI = 1024 / RB, CPR = RB / 16;
   static_assert(RB == 64 || RB == 128, "code rows of 64 or 128 bytes");
   static_assert(!W4 || (BN == 128 && S == 2),
@@ -1066,9 +1078,9 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
       for (int cb = 0; cb < UCB; ++cb) {
         const bf16x8 bu = *reinterpret_cast<const bf16x8*>(BU + swz128(cb * 16 + (lane & 15), c));
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-          if ((i & 1) == wn)
-            uacc[i >> 1][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bu, uacc[i >> 1][cb], 0, 0, 0);
+        for (int h = 0; h < FM / 2; ++h)
+          uacc[h][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pick_frag(af[2 * h], af[2 * h + 1], wn != 0),
+                                                               bu, uacc[h][cb], 0, 0, 0);
       }
     }
     // dB partial for this stage's 64 n over the block's rows (one block per
