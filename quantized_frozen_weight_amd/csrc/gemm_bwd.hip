@@ -284,6 +284,23 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
     okB[i] = gk < crs;
     srcB[i] = okB[i] ? a.codes + (long)row * crs + gk : zero_chunk(lane);
   }
+  // the dy and code loads as 32-bit offsets from a base shared by the wave
+  // (the stage's first n), for every stage but a ragged last one; a code
+  // chunk past the row's K bytes reads the row's last chunk instead of
+  // zeros, which only reaches output columns past K (never stored)
+  uint32_t voA[AI], voB[BI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int row = pw * (BM / 4) + i * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7), gm = m0 + row;
+    voA[i] = (uint32_t)(((long)(gm < M ? gm : M - 1) * N + c * 8) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int row = (pw * BI + i) * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ code_swz<RB>(row), gk = (W4 ? k0 / 2 : k0) + c * 16;
+    voB[i] = (uint32_t)((long)row * crs + (gk < crs ? gk : crs - 16));
+  }
   // aux chunk ci of the tile: header chunks first, then B [j][64 n] in
   // 4-float chunks; a header source moves by adv bytes per n of the stage, a
   // B source (adv 0) by the stage's offset in B (a stage of 64 n lies inside
@@ -320,17 +337,28 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
     int8_t* base = ring + slot * STG;
     const int nb = kt * KC;
     const bool tail = nb + KC > N;
+    // (affine weights keep one branch-free form: their loop waits for loads
+    // by count, and a branch here makes the compiler wait for all of them)
+    if (!AFF && !tail) {
+      const int8_t* dyb = reinterpret_cast<const int8_t*>(a.dy) + 2L * nb;
+      const int8_t* cdb = a.codes + (long)nb * crs;
 #pragma unroll
-    for (int i = 0; i < AI; ++i) {
-      const int8_t* src = srcA[i] + 2L * nb;
-      if (tail && nb + nA[i] >= N) src = zero_chunk(lane);
-      lds_dma16(src, base + (pw * (BM / 4) + i * 8) * 128);
-    }
+      for (int i = 0; i < AI; ++i) lds_dma16(dyb + voA[i], base + (pw * (BM / 4) + i * 8) * 128);
 #pragma unroll
-    for (int i = 0; i < BI; ++i) {
-      const int8_t* src = okB[i] ? srcB[i] + (long)nb * crs : srcB[i];
-      if (tail && nb + nB[i] >= N) src = zero_chunk(lane);
-      lds_dma16(src, base + ASZ + (pw * BI + i) * RPI * RB);
+      for (int i = 0; i < BI; ++i) lds_dma16(cdb + voB[i], base + ASZ + (pw * BI + i) * RPI * RB);
+    } else {
+#pragma unroll
+      for (int i = 0; i < AI; ++i) {
+        const int8_t* src = srcA[i] + 2L * nb;
+        if (tail && nb + nA[i] >= N) src = zero_chunk(lane);
+        lds_dma16(src, base + (pw * (BM / 4) + i * 8) * 128);
+      }
+#pragma unroll
+      for (int i = 0; i < BI; ++i) {
+        const int8_t* src = okB[i] ? srcB[i] + (long)nb * crs : srcB[i];
+        if (tail && nb + nB[i] >= N) src = zero_chunk(lane);
+        lds_dma16(src, base + ASZ + (pw * BI + i) * RPI * RB);
+      }
     }
     const long boff = 4 * head_index(0, nb, r, a.hd);   // bytes: B column nb, rank 0
 #pragma unroll
@@ -824,6 +852,18 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
   const int8_t* srcB[BI];
   int nB[BI];
   bool okB[BI];
+  // the same loads as 32-bit offsets from a base shared by the wave (dy and
+  // the codes at the stage's first n), for every stage but a ragged last
+  // one; a code chunk past the row's K bytes reads the row's last chunk
+  // instead of zeros, which only reaches output columns past K (never
+  // stored)
+  uint32_t voA[AI], voB[BI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int row = wid * (BM / 4) + i * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7), gm = m0 + row;
+    voA[i] = (uint32_t)(((long)(gm < M ? gm : M - 1) * N + c * 8) * 2);
+  }
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
     const int row = (wid * BI + i) * RPI + lane / CPR;
@@ -831,6 +871,7 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
     nB[i] = row;
     okB[i] = gk < crs;
     srcB[i] = okB[i] ? a.codes + (long)row * crs + gk : zero_chunk(lane);
+    voB[i] = (uint32_t)((long)row * crs + (okB[i] ? gk : crs - 16));
   }
   // aux chunks: sw (row -1), then B [j][64 n]; sw moves by 4 bytes per n of
   // the stage, B by the stage's offset in B (a stage of 64 n lies inside one
@@ -857,17 +898,28 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
     int8_t* base = ring + slot * STG;
     const int nb = kt * KC;
     const bool tail = nb + KC > nend;
+    // (affine weights keep one branch-free form: their loop waits for loads
+    // by count, and a branch here makes the compiler wait for all of them)
+    if (!AFF && !tail) {
+      const int8_t* dyb = reinterpret_cast<const int8_t*>(a.dy) + 2L * nb;
+      const int8_t* cdb = a.codes + (long)nb * crs;
 #pragma unroll
-    for (int i = 0; i < AI; ++i) {
-      const int8_t* src = srcA[i] + 2L * nb;
-      if (tail && nb + nA[i] >= nend) src = zero_chunk(lane);
-      lds_dma16(src, base + (wid * (BM / 4) + i * 8) * 128);
-    }
+      for (int i = 0; i < AI; ++i) lds_dma16(dyb + voA[i], base + (wid * (BM / 4) + i * 8) * 128);
 #pragma unroll
-    for (int i = 0; i < BI; ++i) {
-      const int8_t* src = okB[i] ? srcB[i] + (long)nb * crs : srcB[i];
-      if (tail && nb + nB[i] >= nend) src = zero_chunk(lane);
-      lds_dma16(src, base + ASZ + (wid * BI + i) * RPI * RB);
+      for (int i = 0; i < BI; ++i) lds_dma16(cdb + voB[i], base + ASZ + (wid * BI + i) * RPI * RB);
+    } else {
+#pragma unroll
+      for (int i = 0; i < AI; ++i) {
+        const int8_t* src = srcA[i] + 2L * nb;
+        if (tail && nb + nA[i] >= nend) src = zero_chunk(lane);
+        lds_dma16(src, base + (wid * (BM / 4) + i * 8) * 128);
+      }
+#pragma unroll
+      for (int i = 0; i < BI; ++i) {
+        const int8_t* src = okB[i] ? srcB[i] + (long)nb * crs : srcB[i];
+        if (tail && nb + nB[i] >= nend) src = zero_chunk(lane);
+        lds_dma16(src, base + ASZ + (wid * BI + i) * RPI * RB);
+      }
     }
     const long boff = 4 * head_index(0, nb, r, a.hd);   // bytes: B column nb, rank 0
 #pragma unroll
