@@ -101,23 +101,30 @@ __global__ __launch_bounds__(256) void fwd_a8w4_kernel(A8W4Args a) {
       lds_dma16(src, lds + S * STG + o);
     }
   }
+  // Loads from a wave-wide base (the stage's first k) plus a fixed 32-bit
+  // lane offset. Rows past M repeat row M - 1 and weight rows past N repeat
+  // row N - 1: their products land only in outputs that are never stored.
+  uint32_t voA[AI], voB[BI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int rb = wid * (BM / 4) + i * 8, row = rb + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7), gm = m0 + row;
+    voA[i] = (uint32_t)((long)(gm < M ? gm : M - 1) * K + c * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int rb = (wid * BI + i) * 16, row = rb + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3), gn = n0 + row;
+    voB[i] = (uint32_t)((long)(gn < N ? gn : N - 1) * (K / 2) + c * 16);
+  }
   auto issue = [&](int kt, int slot) {
     int8_t* base = ring + slot * STG;
+    const int8_t* xb = a.xq + kt * BK;
+    const int8_t* pb = reinterpret_cast<const int8_t*>(a.packed) + kt * 64;
 #pragma unroll
-    for (int i = 0; i < AI; ++i) {
-      const int rb = wid * (BM / 4) + i * 8, row = rb + (lane >> 3);
-      const int c = (lane & 7) ^ ((row >> 1) & 7);
-      const int gm = m0 + row;
-      lds_dma16(a.xq + (long)(gm < M ? gm : M - 1) * K + kt * BK + c * 16, base + rb * 128);
-    }
+    for (int i = 0; i < AI; ++i) lds_dma16(xb + voA[i], base + (wid * (BM / 4) + i * 8) * 128);
 #pragma unroll
-    for (int i = 0; i < BI; ++i) {
-      const int rb = (wid * BI + i) * 16, row = rb + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 2) & 3), gn = n0 + row;
-      const uint8_t* src = gn < N ? a.packed + (long)gn * (K / 2) + kt * 64 + c * 16
-                                  : reinterpret_cast<const uint8_t*>(zero_chunk(lane));
-      lds_dma16(src, base + ASZ + rb * 64);
-    }
+    for (int i = 0; i < BI; ++i) lds_dma16(pb + voB[i], base + ASZ + (wid * BI + i) * 16 * 64);
   };
 
   f32x4 acc[FM][FN];

@@ -130,8 +130,34 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
 
   // Wave wid fills rows [wid * BM/4, (wid + 1) * BM/4) of A and the same
   // share of B; one instruction covers 8 rows (8 lanes of 16 bytes per row).
+  // Every stage but a ragged last one loads from a wave-wide base (the
+  // stage's first k) plus a fixed 32-bit lane offset; the ragged stage, and
+  // every stage of the affine form (whose loop waits for loads by count and
+  // must not branch here), compute each lane's address and zero page.
+  uint32_t voA[AI], voB[BI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int row = wid * (BM / 4) + i * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7), gm = m0 + row;
+    voA[i] = (uint32_t)((long)(gm < M ? gm : M - 1) * K + c * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int row = wid * (BN / 4) + i * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7), gn = n0 + row;
+    voB[i] = (uint32_t)((long)(gn < N ? gn : N - 1) * K + c * 16);
+  }
   auto issue = [&](int kt, int slot) {
     int8_t* base = ring + slot * STG;
+    if (!AFF && (kt + 1) * BK <= K) {
+      const int8_t* xb = a.xq + kt * BK;
+      const int8_t* cb = a.codes + kt * BK;
+#pragma unroll
+      for (int i = 0; i < AI; ++i) lds_dma16(xb + voA[i], base + (wid * (BM / 4) + i * 8) * BK);
+#pragma unroll
+      for (int i = 0; i < BI; ++i) lds_dma16(cb + voB[i], base + ASZ + (wid * (BN / 4) + i * 8) * BK);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       const int rb = wid * (BM / 4) + i * 8, row = rb + (lane >> 3);

@@ -100,23 +100,30 @@ __global__ __launch_bounds__(256) void fwd_w4_kernel(W4Args a) {
       lds_dma16(src, lds + S * STG + CBSZ + o);
     }
   }
+  // Loads from a wave-wide base (the stage's first k) plus a fixed 32-bit
+  // lane offset. Rows past M repeat row M - 1 and weight rows past N repeat
+  // row N - 1: their products land only in outputs that are never stored.
+  uint32_t voA[AI], voB[BI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int rb = (wid * AI + i) * 4, row = rb + (lane >> 4);
+    const int c = (lane & 15) ^ (row & 15), gm = m0 + row;
+    voA[i] = (uint32_t)(((long)(gm < M ? gm : M - 1) * K + c * 8) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int rb = (wid * BI + i) * 16, row = rb + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3), gn = n0 + row;
+    voB[i] = (uint32_t)((long)(gn < N ? gn : N - 1) * (K / 2) + c * 16);
+  }
   auto issue = [&](int kt, int slot) {
     int8_t* base = ring + slot * STG;
+    const int8_t* xb = reinterpret_cast<const int8_t*>(a.x) + 2L * kt * BK;
+    const int8_t* pb = reinterpret_cast<const int8_t*>(a.packed) + kt * 64;
 #pragma unroll
-    for (int i = 0; i < AI; ++i) {
-      const int rb = (wid * AI + i) * 4, row = rb + (lane >> 4);
-      const int c = (lane & 15) ^ (row & 15);
-      const int gm = m0 + row, gk = kt * BK + c * 8;
-      lds_dma16(a.x + (long)(gm < M ? gm : M - 1) * K + gk, base + rb * 256);
-    }
+    for (int i = 0; i < AI; ++i) lds_dma16(xb + voA[i], base + (wid * AI + i) * 4 * 256);
 #pragma unroll
-    for (int i = 0; i < BI; ++i) {
-      const int rb = (wid * BI + i) * 16, row = rb + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 2) & 3), gn = n0 + row;
-      const uint8_t* src = gn < N ? a.packed + (long)gn * (K / 2) + kt * 64 + c * 16
-                                  : reinterpret_cast<const uint8_t*>(zero_chunk(lane));
-      lds_dma16(src, base + ASZ + rb * 64);
-    }
+    for (int i = 0; i < BI; ++i) lds_dma16(pb + voB[i], base + ASZ + (wid * BI + i) * 16 * 64);
   };
 
   f32x4 acc[FM][FN];
