@@ -78,11 +78,6 @@ __device__ __forceinline__ long head_index(int row, int n, int rows, int hd) {
 }
 
 // ---- wave reductions ---------------------------------------------------------
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
 // Sums of R per-lane values over the 64 lanes in one butterfly: the first
 // log2 R levels pair lanes across bit 5, 4, 3, ... and each lane keeps half of
 // its values (those of its side of the pair) plus the partner's matching
@@ -163,12 +158,30 @@ __device__ __forceinline__ float wave_sum_ranks(const float (&in)[R]) {
   return v[0];
 }
 
+// All-lane max and sum over the 64 lanes by the same butterfly (every lane
+// ends with the result). The sum is used only on integer-valued floats below
+// 2^24, which add exactly in any order.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = s32[0] > s32[1] ? s32[0] : s32[1];
+  auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = s16[0] > s16[1] ? s16[0] : s16[1];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t w = __shfl_xor(v, o, kWave);
+  for (int lvl = 0; lvl < 4; ++lvl) {
+    const uint32_t w = __float_as_uint(dpp_pair(__uint_as_float(v), lvl));
     v = w > v ? w : v;
   }
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  const uint32_t b = __float_as_uint(v);
+  auto s32 = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  v = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+  const uint32_t c = __float_as_uint(v);
+  auto s16 = __builtin_amdgcn_permlane16_swap(c, c, false, false);
+  v = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+#pragma unroll
+  for (int lvl = 0; lvl < 4; ++lvl) v += dpp_pair(v, lvl);
   return v;
 }
 

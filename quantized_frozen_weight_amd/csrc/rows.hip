@@ -25,6 +25,8 @@
 // values it needs contiguous: A keeps its [k][j] order in groups of 8 rows
 // padded by 4 floats (so the 16 lanes of one LDS read land in distinct
 // banks); B is kept as [j][k].
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -459,6 +461,147 @@ __global__ __launch_bounds__(256) void row_long_kernel(
   }
 }
 
+// ---- many short rows, forward modes: RW rows per wave ---------------------
+// For grids of more than one block per compute unit, each wave takes RW
+// rows (L <= 512 NHC, held in registers) instead of one, so every adapter
+// value read from LDS serves RW rows and a block stages the adapter once for
+// 4 RW rows. Same chunk mapping, slices, abs-max and sums as row_kernel, per
+// row.
+template <typename T, int R, int MODE, int RW, int NHC>
+__global__ __launch_bounds__(256) void row_multi_kernel(
+    const typename Elem<T>::type* __restrict__ rows, int M, int L,
+    const float* __restrict__ W, int r, float* __restrict__ out_r,
+    int8_t* __restrict__ xq, float* __restrict__ sx, float* __restrict__ asum) {
+  static_assert(MODE == kFwdQuant || MODE == kFwdT, "forward modes");
+  constexpr int SL = Slice<R>::len;
+  extern __shared__ __attribute__((aligned(16))) float Ws[];
+  const int sld = min(SL, (L + 511) / 512 * 512);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int row0 = (blockIdx.x * kRowsPerBlock + w) * RW;
+  const int nchunk = L / 8;
+  const bool lowrank = out_r != nullptr;
+
+  // chunks from clamped addresses (a chunk past the row repeats its last
+  // chunk, a row past M repeats row M - 1: neither changes an abs-max, and
+  // neither is stored)
+  Raw<T> hold[RW][NHC];
+#pragma unroll
+  for (int q = 0; q < RW; ++q) {
+    const int row = row0 + q;
+    const auto* xr = rows + (long)(row < M ? row : M - 1) * L;
+#pragma unroll
+    for (int i = 0; i < NHC; ++i) {
+      const int c = lane + 64 * i;
+      raw_load(xr + 8 * (c < nchunk ? c : nchunk - 1), hold[q][i]);
+    }
+  }
+
+  QuantParams qp[RW];
+  int csum[RW];
+  float acc[RW][R];
+#pragma unroll
+  for (int q = 0; q < RW; ++q) {
+    csum[q] = 0;
+#pragma unroll
+    for (int j = 0; j < R; ++j) acc[q][j] = 0.f;
+  }
+  for (int s0 = 0; s0 < L; s0 += SL) {
+    const int len = min(SL, L - s0);
+    if (s0 > 0) __syncthreads();
+    if (lowrank) stage_slice<R, MODE>(Ws, W, L, r, s0, len, sld, 0);
+    if (MODE == kFwdQuant && s0 == 0) {
+#pragma unroll
+      for (int q = 0; q < RW; ++q) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < NHC; ++i) {
+          const uint32_t b = raw_absmax(hold[q][i]);
+          m = b > m ? b : m;
+        }
+        qp[q] = absmax_params(wave_max_u32(m), 127.f);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NHC; ++i) {
+      const int c = lane + 64 * i;
+      if (512 * i < s0 || 512 * i >= s0 + SL || c >= nchunk) continue;
+      float v[RW][8];
+#pragma unroll
+      for (int q = 0; q < RW; ++q) raw_unpack(hold[q][i], v[q]);
+      if constexpr (MODE == kFwdQuant) {
+#pragma unroll
+        for (int q = 0; q < RW; ++q) {
+          uint32_t lo = 0, hi = 0;
+          if (qp[q].live) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int q0 = quant_code(v[q][e], qp[q].inv, 127.f);
+              const int q1 = quant_code(v[q][e + 4], qp[q].inv, 127.f);
+              lo |= (uint32_t)(q0 & 0xff) << (8 * e);
+              hi |= (uint32_t)(q1 & 0xff) << (8 * e);
+              csum[q] += q0 + q1;
+            }
+          }
+          if (row0 + q < M) *reinterpret_cast<u32x2*>(xq + (long)(row0 + q) * L + 8 * c) = u32x2{lo, hi};
+        }
+      }
+      if (lowrank) {
+        const float* g = &Ws[(c - s0 / 8) * (8 * R + 4)];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+#pragma unroll
+          for (int j = 0; j < R; ++j) {
+            const float a = g[e * R + j];
+#pragma unroll
+            for (int q = 0; q < RW; ++q) acc[q][j] = __builtin_fmaf(v[q][e], a, acc[q][j]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < RW; ++q) {
+    const int row = row0 + q;
+    if (lowrank) {
+      const float tot = wave_sum_ranks<R>(acc[q]);
+      const int j = rank_of_lane<R>(lane);
+      if ((lane & (64 / R - 1)) == 0 && j < r && row < M) out_r[(long)row * r + j] = tot;
+    }
+    if constexpr (MODE == kFwdQuant) {
+      if (lane == 0 && row < M) sx[row] = qp[q].scale;
+      if (asum != nullptr) {
+        // |sum| <= 127 L < 2^24: exact in float
+        const float cs = wave_sum((float)csum[q]);
+        if (lane == 0 && row < M) asum[row] = cs;
+      }
+    }
+  }
+}
+
+// Rows per wave of the forward row pass for L <= 4096: doubled while the
+// grid keeps at least one block per compute unit, up to 4 (2 at rank 16 or
+// for float32 rows, 1 at rank 32), and to at most 16 held chunks per lane
+// (NHC chunks per row), so that the held rows and the sums fit in registers.
+template <typename T, int R>
+constexpr int row_multi_max() {
+  constexpr int byr = R <= 8 ? 4 : R <= 16 ? 2 : 1;
+  return std::is_same<T, F32>::value ? (byr > 1 ? byr / 2 : 1) : byr;
+}
+
+template <typename T, int R, int MODE, int RW>
+void row_multi_launch(int nhc, dim3 grid, size_t lds, const typename Elem<T>::type* p, int M,
+                      int L, const float* W, int r, float* out_r, int8_t* xq, float* sx,
+                      float* asum, hipStream_t st) {
+  if (nhc <= 2)
+    row_multi_kernel<T, R, MODE, RW, 2><<<grid, 256, lds, st>>>(p, M, L, W, r, out_r, xq, sx, asum);
+  else if (nhc <= 4)
+    row_multi_kernel<T, R, MODE, RW, 4><<<grid, 256, lds, st>>>(p, M, L, W, r, out_r, xq, sx, asum);
+  else if constexpr (RW <= 2)
+    row_multi_kernel<T, R, MODE, RW, 8><<<grid, 256, lds, st>>>(p, M, L, W, r, out_r, xq, sx, asum);
+}
+
 template <typename T, int R, int MODE>
 void row_launch(const void* rows, int M, int L, const float* W, int hd, int r,
                 float* out_r, int8_t* xq, float* sx, float* asum, const float* sw,
@@ -476,6 +619,24 @@ void row_launch(const void* rows, int M, int L, const float* W, int hd, int r,
       const dim3 lgrid((M + kLongRows - 1) / kLongRows);
       row_long_kernel<T, R, MODE><<<lgrid, 256, ldsl, st>>>(p, M, L, W, r, out_r, xq, sx, asum);
       return;
+    }
+  }
+  if constexpr (MODE != kBwd) {
+    if (L <= kHoldChunks * 512) {
+      constexpr int RWM = row_multi_max<T, R>();
+      const int nhc = L <= 1024 ? 2 : L <= 2048 ? 4 : 8;   // held chunks per row
+      int rw = 1;
+      while (rw < RWM && rw * 2 * nhc <= 16 && (M + 8 * rw - 1) / (8 * rw) >= 256) rw *= 2;
+      if (rw > 1) {
+        const dim3 mgrid((M + kRowsPerBlock * rw - 1) / (kRowsPerBlock * rw));
+        if constexpr (RWM >= 2)
+          if (rw == 2)
+            row_multi_launch<T, R, MODE, 2>(nhc, mgrid, lds, p, M, L, W, r, out_r, xq, sx, asum, st);
+        if constexpr (RWM >= 4)
+          if (rw == 4)
+            row_multi_launch<T, R, MODE, 4>(nhc, mgrid, lds, p, M, L, W, r, out_r, xq, sx, asum, st);
+        return;
+      }
     }
   }
   if (L <= kHoldChunks * 512)
