@@ -1403,9 +1403,10 @@ void launch_pc(BwdArgs a, hipStream_t st) {
   else bwd_pc_kernel<W4, BM, BN, S, 32, AFF><<<grid, 512, 0, st>>>(a);
 }
 
-template <bool W4, bool AFF = false, bool SPLIT = false>
+template <bool W4, bool AFF = false, bool SPLIT = false, int BN = 128>
 void launch_wide(BwdArgs a, hipStream_t st) {
-  constexpr int BM = 128, BN = 128, S = 2;
+  static_assert(BN == 128 || (!W4 && !AFF && !SPLIT), "64-wide tiles: plain int8, one pass");
+  constexpr int BM = 128, S = 2;
   a.tiles_x = (a.K + BN - 1) / BN;
   const dim3 grid((unsigned)(a.tiles_x * ((a.M + BM - 1) / BM) * (SPLIT ? a.splits : 1)));
   if (a.r <= 4) bwd_wide_kernel<W4, BM, BN, S, 4, AFF, SPLIT><<<grid, 256, 0, st>>>(a);
@@ -1496,8 +1497,11 @@ void launch_bwd_fused(int fmt, int M, int K, int N, const uint16_t* dy,
     else launch_wide<false, true>(a, st);
   } else if (fmt == 0) {
     a.sw = static_cast<const float*>(scales);
+    // 128 x 64 tiles while 128 x 128 ones would leave compute units idle
+    const long t128 = (long)((M + 127) / 128) * ((K + 127) / 128);
     if (split) launch_wide<false, false, true>(a, st);
     else if (small) launch_pc<false, 64, 3>(a, st);
+    else if (t128 < 256) launch_wide<false, false, false, 64>(a, st);
     else launch_wide<false>(a, st);
   } else {
     a.sc4 = static_cast<const uint16_t*>(scales);

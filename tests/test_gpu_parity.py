@@ -160,6 +160,7 @@ SMALL = [
     (2, 4, 6144, 32, 16),       # long rows at rank 16 (streaming row pass)
     (2, 3, 20480, 32, 8),       # rows past the held length (streaming row pass)
     (2, 4100, 96, 48, 8),       # four rows per wave in the row pass, ragged last block
+    (2, 2100, 1040, 336, 8),    # 128 x 64 backward tiles: ragged rows, k tile and last stage
     (2, 2050, 1552, 32, 16),    # two rows per wave at rank 16, three held chunks
     (1, 2052, 640, 32, 2),      # float32 rows, two per wave
     (3, 4098, 3072, 16, 4),     # two rows per wave over eight held chunks
