@@ -302,8 +302,8 @@ def describe(w):
 TRAFFIC = {
     "workload": 2,
     "sources": ["gemm_bwd.hip", "ring.hpp", "common.hpp"],
-    "sha256": "b1fe6eadcf0e55ca69bb359a34ce78f0aedf2d89f2833c04b3a930f5a75d3ee7",
-    "bytes_per_launch": 25011429,
+    "sha256": "978c44571867113cc0ba6b33485c2085aa7d9034e06b6a1aecb491949b0a3a16",
+    "bytes_per_launch": 25029601,
 }
 
 
