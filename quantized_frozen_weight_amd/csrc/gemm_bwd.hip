@@ -55,9 +55,15 @@
 //   * 64-row tiles, 512 threads in two roles (producer waves load and
 //     convert stage kt + 1 while consumer waves multiply stage kt), for
 //     shapes with at most two such tiles per compute unit;
-//   * 128 x 128 tiles, 256 threads that all do every step, for larger shapes,
-//     where sharing each loaded tile among more outputs matters more than
-//     overlapping the steps.
+//   * 128 x 128 (or, for int8 grids of fewer 128 x 128 tiles than compute
+//     units, 128 x 64) tiles, 256 threads that all do every step, for larger
+//     shapes, where sharing each loaded tile among more outputs matters more
+//     than overlapping the steps.
+// Few 128 x 128 tiles over a long contraction split it: up to 8 blocks per
+// tile each take a range of n and leave their float32 accumulators and
+// partial u in the workspace, and a second launch adds them in split order
+// and does what the one-pass kernel does after its loop (u, the dA partial,
+// the epilogue).
 #include "launch.hpp"
 #include "outlier.hpp"
 #include "ring.hpp"

@@ -38,7 +38,10 @@
 // rows of the current stage. Tile and depth are picked per shape: 64 x 64 with
 // three stages when the grid is about one wave of blocks (latency-bound, so
 // depth pays), 128 x 128 or 128 x 64 with two stages for large grids (LDS per
-// block then allows several blocks per compute unit).
+// block then allows several blocks per compute unit). Few tiles over a long
+// k axis split it (up to 8 ways, 4 for the affine form): each block leaves
+// its exact int32 sums (and the affine form its float corrections) in the
+// workspace, and a second launch adds them and applies the epilogue.
 #include "launch.hpp"
 #include "outlier.hpp"
 #include "ring.hpp"

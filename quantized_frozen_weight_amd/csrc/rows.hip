@@ -19,8 +19,11 @@
 // Latency, not bandwidth, decides these small passes, so every global load a
 // block needs is issued before anything waits: the row itself (rows of up
 // to 4096 entries stay in registers between the abs-max and the quantize
-// pass; longer rows are streamed twice) and the slice of the rank-r matrix
-// that the block's four rows share, copied to LDS with 16-byte loads. In LDS
+// pass; forward rows of up to 16384 too, two per block with each wave on a
+// quarter of them; longer rows are streamed twice) and the slice of the
+// rank-r matrix that the block's rows share, copied to LDS with 16-byte
+// loads (for many short rows each wave takes two or four of them, so one
+// LDS read of the adapter serves several rows). In LDS
 // a lane that holds 8 consecutive row entries k finds the 8 x R adapter
 // values it needs contiguous: A keeps its [k][j] order in groups of 8 rows
 // padded by 4 floats (so the 16 lanes of one LDS read land in distinct
