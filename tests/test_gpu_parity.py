@@ -229,9 +229,15 @@ def test_degenerate_rows_and_channels(cid):
     assert_close(to_numpy(y), oy, RTOL[w.dtype], "y (degenerate)")
 
 
-def test_deterministic_and_frozen():
-    w = WL.small(3, 300, 768, 400, 4)
-    say("determinism + frozen buffers")
+@pytest.mark.parametrize("spec", [
+    (3, 300, 768, 400, 4),
+    (2, 130, 2048, 8320, 4),    # input gradient split 8 ways
+    (2, 100, 16384, 256, 8),    # forward product split 8 ways, long-row pass
+    (5, 160, 2048, 8192, 4),    # 4-bit input gradient split 8 ways
+])
+def test_deterministic_and_frozen(spec):
+    w = WL.small(*spec)
+    say(f"determinism + frozen buffers: {w.name} M={spec[1]} K={spec[2]} N={spec[3]} r={spec[4]}")
     case = Case(w, 0)
     codes0 = case.lin.codes.clone()
     scales0 = case.lin.scales.clone()
@@ -293,12 +299,16 @@ def test_merge_zero_channel():
     assert to_numpy(ms)[5] == 0.0 and not to_numpy(mc)[5].any()
 
 
-def test_timed_repeats_are_identical():
+@pytest.mark.parametrize("spec", [
+    (2, 256, 1024, 1024, 8),
+    (2, 130, 4096, 4160, 8),    # both products split their contraction
+])
+def test_timed_repeats_are_identical(spec):
     """The timed entry points launch the product kernel several times; every
-    launch rewrites the same outputs, so results match the plain call bit for
-    bit."""
-    say("timed repeats: mlp layer 1 at 256 rows")
-    w = WL.small(2, 256, 1024, 1024, 8)
+    launch rewrites the same outputs (split products: the same partial sums
+    and fixups), so results match the plain call bit for bit."""
+    say(f"timed repeats: M={spec[1]} K={spec[2]} N={spec[3]} r={spec[4]}")
+    w = WL.small(*spec)
     case = Case(w, 0)
     y1, t1 = Q.qlora_fwd(case.lin, case.x_t)
     dx1, dA1, dB1 = Q.qlora_bwd(case.lin, case.x_t, case.dy_t, t=t1)
