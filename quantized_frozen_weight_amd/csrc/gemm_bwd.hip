@@ -146,6 +146,22 @@ __device__ __forceinline__ void tr16_reads(const uint32_t (&addr)[NR], uint64_t 
   }
 }
 
+// The eight codes of a packed 4-bit word (nibble e = k offset e, two's
+// complement) times sc: w ^ 0x88888888 turns each code q into q + 8 in
+// [0, 15], two masks spread the nibbles over bytes (v_cvt_f32_ubyte takes a
+// byte in one instruction), and fma(q + 8, sc, -8 sc) rounds q sc exactly
+// once, as q * sc would.
+__device__ __forceinline__ void nibble_vals(uint32_t w, float sc, float (&v)[8]) {
+  const uint32_t u = w ^ 0x88888888u;
+  const uint32_t lo = u & 0x0f0f0f0fu, hi = (u >> 4) & 0x0f0f0f0fu;   // even, odd e
+  const float nsc = -8.f * sc;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    v[2 * b] = __builtin_fmaf((float)((lo >> (8 * b)) & 0xffu), sc, nsc);
+    v[2 * b + 1] = __builtin_fmaf((float)((hi >> (8 * b)) & 0xffu), sc, nsc);
+  }
+}
+
 // a0 or a1 by a wave-uniform flag, as selects rather than a branch (the u
 // products take the odd or even row blocks of A by the wave's column half)
 __device__ __forceinline__ bf16x8 pick_frag(const bf16x8& a0, const bf16x8& a1, bool second) {
@@ -436,15 +452,13 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
         const int n = 4 * nq + i;
         raw[i] = *reinterpret_cast<const uint32_t*>(Bs + n * RB + (((kq8 >> 2) ^ code_swz<RB>(n)) << 4) + (kq8 & 3) * 4);
       }
+      float v[4][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v0 = (float)(((int)(raw[0] << (28 - 4 * e))) >> 28) * sc[0];
-        const float v1 = (float)(((int)(raw[1] << (28 - 4 * e))) >> 28) * sc[1];
-        const float v2 = (float)(((int)(raw[2] << (28 - 4 * e))) >> 28) * sc[2];
-        const float v3 = (float)(((int)(raw[3] << (28 - 4 * e))) >> 28) * sc[3];
+      for (int i = 0; i < 4; ++i) nibble_vals(raw[i], sc[i], v[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
         *reinterpret_cast<u32x2*>(CB + swz128(8 * kq8 + e, nq >> 1) + (nq & 1) * 8) =
-            u32x2{pk_bf16(v0, v1), pk_bf16(v2, v3)};
-      }
+            u32x2{pk_bf16(v[0][e], v[1][e]), pk_bf16(v[2][e], v[3][e])};
     } else {
       f32x4 swv = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (!AFF) swv = *reinterpret_cast<const f32x4*>(Xa + 4 * nq);
@@ -1051,15 +1065,15 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
         const int n = 4 * nq + i;
         raw[i] = *reinterpret_cast<const uint32_t*>(Bs + n * RB + (((kq8 >> 2) ^ code_swz<RB>(n)) << 4) + (kq8 & 3) * 4);
       }
+      float v[4][8];
+      nibble_vals(raw[0], scv.x, v[0]);
+      nibble_vals(raw[1], scv.y, v[1]);
+      nibble_vals(raw[2], scv.z, v[2]);
+      nibble_vals(raw[3], scv.w, v[3]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v0 = (float)(((int)(raw[0] << (28 - 4 * e))) >> 28) * scv.x;
-        const float v1 = (float)(((int)(raw[1] << (28 - 4 * e))) >> 28) * scv.y;
-        const float v2 = (float)(((int)(raw[2] << (28 - 4 * e))) >> 28) * scv.z;
-        const float v3 = (float)(((int)(raw[3] << (28 - 4 * e))) >> 28) * scv.w;
+      for (int e = 0; e < 8; ++e)
         *reinterpret_cast<u32x2*>(CB + swz128(8 * kq8 + e, nq >> 1) + (nq & 1) * 8) =
-            u32x2{pk_bf16(v0, v1), pk_bf16(v2, v3)};
-      }
+            u32x2{pk_bf16(v[0][e], v[1][e]), pk_bf16(v[2][e], v[3][e])};
     } else {
       f32x4 swv = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (!AFF) swv = *reinterpret_cast<const f32x4*>(Xa + 4 * nq);

@@ -54,9 +54,22 @@ __device__ __forceinline__ int swz256(int row, int c) {
   return row * 256 + ((c ^ (row & 15)) << 4);
 }
 
-// Two's-complement nibble e (0..7) of a packed word, as a float.
-__device__ __forceinline__ float nibble(uint32_t w, int e) {
-  return (float)(((int)(w << (28 - 4 * e))) >> 28);
+// The eight nibbles of a packed word (nibble e = the code of k offset e,
+// two's complement) times sc, as four bf16 pairs: w ^ 0x88888888 turns each
+// code q into q + 8 in [0, 15], two masks spread the nibbles over bytes
+// (v_cvt_f32_ubyte takes a byte in one instruction), and
+// fma(q + 8, sc, -8 sc) rounds q sc exactly once, as q * sc would.
+__device__ __forceinline__ u32x4 nibbles_bf16(uint32_t w, float sc) {
+  const uint32_t u = w ^ 0x88888888u;
+  const uint32_t lo = u & 0x0f0f0f0fu, hi = (u >> 4) & 0x0f0f0f0fu;   // even, odd e
+  const float nsc = -8.f * sc;
+  float v[8];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    v[2 * b] = __builtin_fmaf((float)((lo >> (8 * b)) & 0xffu), sc, nsc);
+    v[2 * b + 1] = __builtin_fmaf((float)((hi >> (8 * b)) & 0xffu), sc, nsc);
+  }
+  return u32x4{pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]), pk_bf16(v[4], v[5]), pk_bf16(v[6], v[7])};
 }
 
 // G: the largest number of 128-wide k groups the block's scale slab holds.
@@ -158,11 +171,7 @@ __global__ __launch_bounds__(256) void fwd_w4_kernel(W4Args a) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           const int kc = 4 * c + d;                  // 16-byte chunk of CB (8 k)
-          const u32x4 o = {pk_bf16(nibble(w[d], 0) * sc, nibble(w[d], 1) * sc),
-                           pk_bf16(nibble(w[d], 2) * sc, nibble(w[d], 3) * sc),
-                           pk_bf16(nibble(w[d], 4) * sc, nibble(w[d], 5) * sc),
-                           pk_bf16(nibble(w[d], 6) * sc, nibble(w[d], 7) * sc)};
-          *reinterpret_cast<u32x4*>(CB + swz256(crow, kc)) = o;
+          *reinterpret_cast<u32x4*>(CB + swz256(crow, kc)) = nibbles_bf16(w[d], sc);
         }
       }
     }
