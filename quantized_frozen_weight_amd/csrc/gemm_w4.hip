@@ -9,16 +9,17 @@
 // "LoRA equation" and "Create LoRA layer": the adapter term, scaled by
 // alpha / rank.)
 //
-// A stage covers one 128-wide group of k, so one fp16 scale per output
-// column applies to the whole stage. Three tiles move global -> LDS without
-// registers (ring.hpp): the x rows (bf16, 256-byte rows swizzled by 16-byte
-// chunk ^ (row % 16)), the packed codes [BN n][64 bytes] (chunk-swizzled),
-// and, once before the loop, the block's scales [BN][K / 128] (a contiguous
-// slab of the scale array). Once a stage has landed the block converts its
-// codes in one cooperative pass, every nibble once: CB [BN n][128 k] =
-// bf16(q sc), stored like the x rows. The MFMA loop then reads both operands
-// with plain 16-byte LDS reads. The adapter term runs in the epilogue on
-// v_mfma_f32_16x16x4_f32 (ring.hpp).
+// A stage covers half of one 128-wide group of k, so one fp16 scale per
+// output column applies to the whole stage, and a 128 x 128 block needs
+// 64 KB of LDS (two per compute unit). Three tiles move global -> LDS
+// without registers (ring.hpp): the x rows (bf16, 128-byte rows swizzled by
+// 16-byte chunk), the packed codes [BN n][32 bytes], and, once before the
+// loop, the block's scales [BN][K / 128] (a contiguous slab of the scale
+// array). Once a stage has landed the block converts its codes in one
+// cooperative pass, every nibble once: CB [BN n][64 k] = bf16(q sc), stored
+// like the x rows. The MFMA loop then reads both operands with plain 16-byte
+// LDS reads. The adapter term runs in the epilogue on v_mfma_f32_16x16x4_f32
+// (ring.hpp).
 #include "launch.hpp"
 #include "ring.hpp"
 
@@ -49,11 +50,6 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-// Byte offset of logical 16-byte chunk c of row `row` in a 256-byte-row tile.
-__device__ __forceinline__ int swz256(int row, int c) {
-  return row * 256 + ((c ^ (row & 15)) << 4);
-}
-
 // The eight nibbles of a packed word (nibble e = the code of k offset e,
 // two's complement) times sc, as four bf16 pairs: w ^ 0x88888888 turns each
 // code q into q + 8 in [0, 15], two masks spread the nibbles over bytes
@@ -75,18 +71,18 @@ __device__ __forceinline__ u32x4 nibbles_bf16(uint32_t w, float sc) {
 // G: the largest number of 128-wide k groups the block's scale slab holds.
 template <int BM, int BN, int S, int R, int G>
 __global__ __launch_bounds__(256) void fwd_w4_kernel(W4Args a) {
-  constexpr int BK = 128;                          // k per stage = one scale group
-  constexpr int ASZ = BM * 256, BSZ = BN * 64, STG = ASZ + BSZ;
-  constexpr int AI = BM / 16, BI = BN / 64, LPS = AI + BI;   // DMA per wave per stage
+  constexpr int BK = 64;                           // k per stage: half a scale group
+  constexpr int ASZ = BM * 128, BSZ = BN * 32, STG = ASZ + BSZ;
+  constexpr int AI = BM / 32, BI = BN / 128, LPS = AI + BI;   // DMA per wave per stage
   constexpr int FM = BM / 32, FN = BN / 32;
-  constexpr int CBSZ = BN * 256;
-  static_assert(BN == 128, "code rows of 64 bytes: 16 rows per DMA instruction, 2 threads per row");
-  // after the loop the ring holds the epilogue operands, then one output
-  // staging strip per wave
+  constexpr int CBSZ = BN * 128;
+  static_assert(BN == 128, "code rows of 32 bytes: 32 rows per DMA instruction, one per wave");
+  // after the loop the ring and the converted-code buffer hold the epilogue
+  // operands, then one output staging strip per wave
   constexpr int EPB = (EpiOps<BM, BN, R, false>::kFloats * 4 + 15) / 16 * 16;
-  static_assert(EPB + 4 * epi_strip_bytes<uint16_t, FN>() <= S * STG, "epilogue fits in the ring");
+  static_assert(EPB + 4 * epi_strip_bytes<uint16_t, FN>() <= S * STG + CBSZ, "epilogue fits");
   const int K = a.K, M = a.M, N = a.N;
-  const int ngrp = K / BK;
+  const int ngrp = K / 128;
   static_assert(BN * G * 2 % 1024 == 0, "the scale slab takes whole 1 KB DMA instructions");
   // scales of the block's columns: [BN][ngrp] fp16, ngrp <= G
   __shared__ __attribute__((aligned(1024))) int8_t lds[S * STG + CBSZ + BN * G * 2];
@@ -97,7 +93,7 @@ __global__ __launch_bounds__(256) void fwd_w4_kernel(W4Args a) {
   const int tid = threadIdx.x, lane = tid & 63, wid = wave_id();
   const int wm = wid >> 1, wn = wid & 1;
   const int m0 = ((int)blockIdx.x / a.tiles_x) * BM, n0 = ((int)blockIdx.x % a.tiles_x) * BN;
-  const int nk = ngrp;
+  const int nk = 2 * ngrp;
 
   EpiOps<BM, BN, R, false> ep;
   ep.load(M, N, m0, n0, a.r, a.t, a.B, a.hd, nullptr, nullptr);
@@ -114,29 +110,27 @@ __global__ __launch_bounds__(256) void fwd_w4_kernel(W4Args a) {
     }
   }
   // Loads from a wave-wide base (the stage's first k) plus a fixed 32-bit
-  // lane offset. Rows past M repeat row M - 1 and weight rows past N repeat
-  // row N - 1: their products land only in outputs that are never stored.
-  uint32_t voA[AI], voB[BI];
+  // lane offset: x as 128-byte rows swizzled by 16-byte chunk, 8 rows per
+  // instruction; the codes as 32-byte rows, 32 per instruction (lanes 2 i and
+  // 2 i + 1 take the two halves of row i, read back in that order). Rows past
+  // M repeat row M - 1 and weight rows past N repeat row N - 1: their products
+  // land only in outputs that are never stored.
+  uint32_t voA[AI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
-    const int rb = (wid * AI + i) * 4, row = rb + (lane >> 4);
-    const int c = (lane & 15) ^ (row & 15), gm = m0 + row;
+    const int row = wid * (BM / 4) + i * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7), gm = m0 + row;
     voA[i] = (uint32_t)(((long)(gm < M ? gm : M - 1) * K + c * 8) * 2);
   }
-#pragma unroll
-  for (int i = 0; i < BI; ++i) {
-    const int rb = (wid * BI + i) * 16, row = rb + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 2) & 3), gn = n0 + row;
-    voB[i] = (uint32_t)((long)(gn < N ? gn : N - 1) * (K / 2) + c * 16);
-  }
+  const int brow = wid * 32 + (lane >> 1), gn = n0 + brow;
+  const uint32_t voB = (uint32_t)((long)(gn < N ? gn : N - 1) * (K / 2) + (lane & 1) * 16);
   auto issue = [&](int kt, int slot) {
     int8_t* base = ring + slot * STG;
     const int8_t* xb = reinterpret_cast<const int8_t*>(a.x) + 2L * kt * BK;
-    const int8_t* pb = reinterpret_cast<const int8_t*>(a.packed) + kt * 64;
+    const int8_t* pb = reinterpret_cast<const int8_t*>(a.packed) + kt * (BK / 2);
 #pragma unroll
-    for (int i = 0; i < AI; ++i) lds_dma16(xb + voA[i], base + (wid * AI + i) * 4 * 256);
-#pragma unroll
-    for (int i = 0; i < BI; ++i) lds_dma16(pb + voB[i], base + ASZ + (wid * BI + i) * 16 * 64);
+    for (int i = 0; i < AI; ++i) lds_dma16(xb + voA[i], base + (wid * (BM / 4) + i * 8) * 128);
+    lds_dma16(pb + voB, base + ASZ + wid * 32 * 32);
   };
 
   f32x4 acc[FM][FN];
@@ -152,7 +146,7 @@ __global__ __launch_bounds__(256) void fwd_w4_kernel(W4Args a) {
   // may differ): loads complete in issue order, so every wave's share has
   // landed once its stage 0 has, and the first barrier covers all waves.
 
-  const int crow = tid >> 1, chalf = tid & 1;        // conversion: row n, 64 k half
+  const int crow = tid >> 1, chalf = tid & 1;        // conversion: row n, 32 k half
   int slot = 0;
   for (int kt = 0; kt < nk; ++kt) {
     wait_stages<LPS, 0, S - 2>(nk - 1 - kt);
@@ -161,19 +155,13 @@ __global__ __launch_bounds__(256) void fwd_w4_kernel(W4Args a) {
     const int8_t* As = ring + slot * STG;
     const int8_t* Bs = As + ASZ;
 
-    // CB[n][k] = bf16(q[n][k] sc[n][kt]) for row crow, k in [64 chalf, 64 chalf + 64)
+    // CB[n][k] = bf16(q[n][k] sc[n][kt / 2]) for row crow, k in [32 chalf, 32 chalf + 32)
     {
-      const float sc = (float)SC[crow * ngrp + kt];
+      const float sc = (float)SC[crow * ngrp + (kt >> 1)];
+      const u32x4 w = *reinterpret_cast<const u32x4*>(Bs + crow * 32 + chalf * 16);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int c = 2 * chalf + h;                 // 16-byte chunk of packed codes
-        const u32x4 w = *reinterpret_cast<const u32x4*>(Bs + crow * 64 + ((c ^ ((crow >> 2) & 3)) << 4));
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const int kc = 4 * c + d;                  // 16-byte chunk of CB (8 k)
-          *reinterpret_cast<u32x4*>(CB + swz256(crow, kc)) = nibbles_bf16(w[d], sc);
-        }
-      }
+      for (int d = 0; d < 4; ++d)
+        *reinterpret_cast<u32x4*>(CB + swz128(crow, 4 * chalf + d)) = nibbles_bf16(w[d], sc);
     }
     __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
     __builtin_amdgcn_s_barrier();                    // CB visible
@@ -184,10 +172,10 @@ __global__ __launch_bounds__(256) void fwd_w4_kernel(W4Args a) {
       bf16x8 af[FM], bf[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(As + swz256(wm * (BM / 2) + i * 16 + (lane & 15), c));
+        af[i] = *reinterpret_cast<const bf16x8*>(As + swz128(wm * (BM / 2) + i * 16 + (lane & 15), c));
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        bf[j] = *reinterpret_cast<const bf16x8*>(CB + swz256(wn * (BN / 2) + j * 16 + (lane & 15), c));
+        bf[j] = *reinterpret_cast<const bf16x8*>(CB + swz128(wn * (BN / 2) + j * 16 + (lane & 15), c));
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
