@@ -161,6 +161,8 @@ SMALL = [
     (2, 3, 20480, 32, 8),       # rows past the held length (streaming row pass)
     (2, 4100, 96, 48, 8),       # four rows per wave in the row pass, ragged last block
     (2, 2100, 1040, 336, 8),    # 128 x 64 backward tiles: ragged rows, k tile and last stage
+    (2, 1, 256, 4096, 8),       # one row: input gradient split 4 ways
+    (2, 1, 4112, 64, 4),        # one row: long-row pass, forward split 2 ways with a ragged k tail
     (2, 2050, 1552, 32, 16),    # two rows per wave at rank 16, three held chunks
     (1, 2052, 640, 32, 2),      # float32 rows, two per wave
     (3, 4098, 3072, 16, 4),     # two rows per wave over eight held chunks
