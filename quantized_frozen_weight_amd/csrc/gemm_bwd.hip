@@ -247,7 +247,8 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
   const int ptid = (int)threadIdx.x - 256;            // producer thread 0..255
   const int ctid = threadIdx.x;                       // consumer thread 0..255
   const int wm = (wid >> 1) & 1, wn = wid & 1;        // consumer wave position
-  const int mt = (int)blockIdx.x / a.tiles_x, kt_blk = (int)blockIdx.x % a.tiles_x;
+  int mt, kt_blk;
+  xcd_tile((int)blockIdx.x, (a.M + BM - 1) / BM, a.tiles_x, mt, kt_blk);
   const int m0 = mt * BM, k0 = kt_blk * BN;
   const int M = a.M, K = a.K, N = a.N, r = a.r;
   const int nk = (N + KC - 1) / KC;
@@ -816,7 +817,13 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
     split = bid / tiles;
     bid -= split * tiles;
   }
-  const int mt = bid / a.tiles_x, kt_blk = bid % a.tiles_x;
+  int mt, kt_blk;
+  if constexpr (SPLIT) {
+    mt = bid / a.tiles_x;
+    kt_blk = bid % a.tiles_x;
+  } else {
+    xcd_tile(bid, (M + BM - 1) / BM, a.tiles_x, mt, kt_blk);
+  }
   const int m0 = mt * BM, k0 = kt_blk * BN;
   // stages [kt0, kt1) of the contraction; nend bounds the n loaded
   const int kt0 = SPLIT ? split * a.nks : 0;

@@ -107,7 +107,14 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
     split = bid / tiles;
     bid -= split * tiles;
   }
-  const int m0 = (bid / a.tiles_x) * BM, n0 = (bid % a.tiles_x) * BN;
+  int mt, nt;
+  if constexpr (SPLIT) {
+    mt = bid / a.tiles_x;
+    nt = bid % a.tiles_x;
+  } else {
+    xcd_tile(bid, (M + BM - 1) / BM, a.tiles_x, mt, nt);
+  }
+  const int m0 = mt * BM, n0 = nt * BN;
   // stages [kt0, kt1) of the contraction
   const int kt0 = SPLIT ? split * a.nks : 0;
   const int kt1 = SPLIT ? (kt0 + a.nks < nk ? kt0 + a.nks : nk) : nk;

@@ -51,6 +51,27 @@ __device__ __forceinline__ void wait_stages(int n) {
   }
 }
 
+// Tile (row mt, column kt) of block b in a grid of tm x tx tiles. The
+// dispatcher deals blocks to the eight XCDs in turn, each XCD with its own
+// L2; numbering logical blocks L = (b % 8) (blocks / 8) + b / 8 and laying
+// them out in bands of gw tile columns, row-major inside a band, gives each
+// XCD a compact rectangle of tiles, so that its L2 fetches a few row and
+// column panels instead of a slice of all of them. Grids that do not divide
+// evenly keep the row-major order.
+__device__ __forceinline__ void xcd_tile(int b, int tm, int tx, int& mt, int& kt) {
+  const int nb = tm * tx;
+  const int gw = tx % 8 == 0 ? 8 : tx % 4 == 0 ? 4 : 0;
+  if ((nb & 7) == 0 && gw != 0) {
+    const int L = (b & 7) * (nb >> 3) + (b >> 3);
+    const int band = L / (tm * gw), r = L - band * (tm * gw);
+    mt = r / gw;
+    kt = band * gw + r % gw;
+  } else {
+    mt = b / tx;
+    kt = b % tx;
+  }
+}
+
 // Zero bytes: the source of direct-to-LDS lanes whose 16-byte chunk lies past
 // the end of the contraction axis (every shape keeps that axis a multiple of
 // 16, so a chunk is wholly inside or wholly outside).
