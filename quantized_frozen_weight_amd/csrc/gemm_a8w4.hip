@@ -82,7 +82,9 @@ __global__ __launch_bounds__(256) void fwd_a8w4_kernel(A8W4Args a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wid = wave_id();
   const int wm = wid >> 1, wn = wid & 1;
-  const int m0 = ((int)blockIdx.x / a.tiles_x) * BM, n0 = ((int)blockIdx.x % a.tiles_x) * BN;
+  int mt, nt;
+  xcd_tile((int)blockIdx.x, (a.M + BM - 1) / BM, a.tiles_x, mt, nt);
+  const int m0 = mt * BM, n0 = nt * BN;
   const int M = a.M, N = a.N, K = a.K;
   const int ngrp = K / BK;
 
