@@ -1311,20 +1311,21 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
 }
 
 
-// Second launch of the split contraction, one block per 128-row x 64-column
-// half of a 128 x 128 tile (the same output ownership as the wide kernel's
-// epilogue): the partial products added in split order, u added in split
-// order from its partials, the dA partial of the 128-row block over these
-// 64 columns, and dx = bf16(sum + s u A^T) through the common epilogue.
-// Wave v takes rows [16 v, 16 v + 16): fragment row v % 4 of the wide
-// kernel's wave 2 (v / 4) + (column half). Every split's loads are issued
-// before the first add (NSPL: the split count's bound; splits past the
-// count read split 0 and are dropped by a select).
+// Second launch of the split contraction, one block per 128-row x 32-column
+// quarter of a 128 x 128 tile (so that twice as many compute units read the
+// partial sums as with halves): the partial products added in split order,
+// u added in split order from its partials, the dA partial of the 128-row
+// block over these 32 columns, and dx = bf16(sum + s u A^T) through the
+// common epilogue. Wave v takes rows [16 v, 16 v + 16): fragment row v % 4,
+// fragment columns 2 (q % 2) + {0, 1} of the wide kernel's wave
+// 2 (v / 4) + q / 2 for quarter q. Every split's loads are issued before
+// the first add (NSPL: the split count's bound; splits past the count read
+// split 0 and are dropped by a select).
 template <int R, int NSPL>
 __global__ __launch_bounds__(512) void bwd_fixup_kernel(BwdArgs a) {
-  constexpr int BM = 128, HN = 64, FN = 4;
+  constexpr int BM = 128, HN = 32, FN = 2;
   constexpr int EFL = (BM + HN) * R;                    // U [BM][R] | A^T [R][HN]
-  constexpr int XSZ = BM * HN * 2;                      // x [BM][HN] bf16, 128-byte rows
+  constexpr int XSZ = BM * HN * 2;                      // x [BM][HN] bf16, 64-byte rows
   constexpr int STRIP = epi_strip_bytes<uint16_t, FN>();
   __shared__ __attribute__((aligned(1024))) int8_t lds[XSZ + EFL * 4 + 8 * STRIP];
   int8_t* Xs = lds;
@@ -1334,14 +1335,14 @@ __global__ __launch_bounds__(512) void bwd_fixup_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, v = wave_id();
   const int M = a.M, K = a.K, r = a.r, nsp = a.splits;
   const int tiles = a.tiles_x * ((M + BM - 1) / BM);
-  const int tile = (int)blockIdx.x >> 1, wn = (int)blockIdx.x & 1;
+  const int tile = (int)blockIdx.x >> 2, q = (int)blockIdx.x & 3;
   const int mt = tile / a.tiles_x;
-  const int m0 = mt * BM, k0 = (tile % a.tiles_x) * 128 + wn * HN;
+  const int m0 = mt * BM, k0 = (tile % a.tiles_x) * 128 + q * HN;
 
-  // partial products of this wave's four fragments, all splits in flight
-  const int w = 2 * (v >> 2) + wn, fi = v & 3;
+  // partial products of this wave's two fragments, all splits in flight
+  const int w = 2 * (v >> 2) + (q >> 1), fi = v & 3;
   const f32x4* P = reinterpret_cast<const f32x4*>(a.pdx) + ((long)tile * 4 + w) * (16 * 64) +
-                   fi * 4 * 64 + lane;
+                   (fi * 4 + 2 * (q & 1)) * 64 + lane;
   const long pstride = (long)tiles * 4 * 16 * 64;       // float4 units per split
   f32x4 pv[NSPL][FN];
 #pragma unroll
@@ -1349,14 +1350,15 @@ __global__ __launch_bounds__(512) void bwd_fixup_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) pv[sp][j] = P[(sp < nsp ? sp : 0) * pstride + j * 64];
 
-  // x tile by DMA: wave v moves rows 16 v .. + 16, 8 per instruction
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int rb = (2 * v + q) * 8, row = rb + (lane >> 3);
-    const int c = (lane & 7) ^ ((row >> 1) & 7), gm = m0 + row, gk = k0 + c * 8;
+  // x tile by DMA: [128 rows][32 columns] as 64-byte rows, 16 per
+  // instruction; wave v moves rows 16 v .. + 16 (chunk c of row r lands at
+  // 64 r + 16 (c ^ ((r >> 2) & 3)))
+  {
+    const int row = 16 * v + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3), gm = m0 + row, gk = k0 + c * 8;
     const void* src = gk < K ? (const void*)(a.x + (long)(gm < M ? gm : M - 1) * K + gk)
                              : (const void*)zero_chunk(lane);
-    lds_dma16(src, Xs + rb * 128);
+    lds_dma16(src, Xs + 16 * v * 64);
   }
 
   // U[m][j] = sum over splits of the partial u (rows past M and ranks past r: 0)
@@ -1388,10 +1390,10 @@ __global__ __launch_bounds__(512) void bwd_fixup_kernel(BwdArgs a) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
 
-  // dA partial over the block's rows: thread -> column tid % 64, ranks
-  // tid / 64 + 8 jj
+  // dA partial over the block's rows: thread -> column tid % 32, ranks
+  // tid / 32 + 16 jj
   {
-    constexpr int JPT = (R + 7) / 8;
+    constexpr int JPT = (R + 15) / 16;
     const int kl = tid % HN, jb = tid / HN;
     const int rows_here = M - m0 < BM ? M - m0 : BM;
     float da[JPT];
@@ -1400,16 +1402,18 @@ __global__ __launch_bounds__(512) void bwd_fixup_kernel(BwdArgs a) {
     if (jb < R) {
 #pragma unroll 8
       for (int m = 0; m < rows_here; ++m) {
-        const float xv = tile_bf16(Xs, m, kl);
+        const uint16_t xb = *reinterpret_cast<const uint16_t*>(
+            Xs + m * 64 + (((kl >> 3) ^ ((m >> 2) & 3)) << 4) + 2 * (kl & 7));
+        const float xv = __uint_as_float((uint32_t)xb << 16);
 #pragma unroll
         for (int jj = 0; jj < JPT; ++jj)
-          if (jb + 8 * jj < R) da[jj] = __builtin_fmaf(xv, E[m * R + jb + 8 * jj], da[jj]);
+          if (jb + 16 * jj < R) da[jj] = __builtin_fmaf(xv, E[m * R + jb + 16 * jj], da[jj]);
       }
     }
     if (k0 + kl < K) {
 #pragma unroll
       for (int jj = 0; jj < JPT; ++jj) {
-        const int j = jb + 8 * jj;
+        const int j = jb + 16 * jj;
         if (j < r) a.partA[((long)mt * r + j) * K + k0 + kl] = da[jj];
       }
     }
@@ -1441,7 +1445,7 @@ void launch_wide(BwdArgs a, hipStream_t st) {
   else if (a.r <= 16) bwd_wide_kernel<W4, BM, BN, S, 16, AFF, SPLIT><<<grid, 256, 0, st>>>(a);
   else bwd_wide_kernel<W4, BM, BN, S, 32, AFF, SPLIT><<<grid, 256, 0, st>>>(a);
   if constexpr (SPLIT) {
-    const dim3 fgrid((unsigned)(2 * a.tiles_x * ((a.M + BM - 1) / BM)));
+    const dim3 fgrid((unsigned)(4 * a.tiles_x * ((a.M + BM - 1) / BM)));
     if (a.splits <= 4) {
       if (a.r <= 4) bwd_fixup_kernel<4, 4><<<fgrid, 512, 0, st>>>(a);
       else if (a.r <= 8) bwd_fixup_kernel<8, 4><<<fgrid, 512, 0, st>>>(a);

@@ -383,14 +383,15 @@ __global__ __launch_bounds__(256) void fwd_i8_kernel(I8Args a) {
 }
 
 // Second launch of the split int8 product, one 512-thread block per 128-row x
-// 64-column half of a 128 x 128 tile: the int32 partial sums added (exact, so
-// the result equals the one-pass product's bit for bit), then the scaled
-// low-rank epilogue. Wave v takes rows [16 v, 16 v + 16): fragment row v % 4
-// of the product kernel's wave 2 (v / 4) + (column half); all of a lane's
-// split loads are issued before the first add.
+// 32-column quarter of a 128 x 128 tile: the int32 partial sums added (exact,
+// so the result equals the one-pass product's bit for bit), then the scaled
+// low-rank epilogue. Wave v takes rows [16 v, 16 v + 16): fragment row v % 4,
+// fragment columns 2 (q % 2) + {0, 1} of the product kernel's wave
+// 2 (v / 4) + q / 2 for quarter q; all of a lane's split loads are issued
+// before the first add.
 template <int R, int NSPL, typename OutT>
 __global__ __launch_bounds__(512) void fwd_fixup_kernel(I8Args a) {
-  constexpr int BM = 128, HN = 64, FN = 4;
+  constexpr int BM = 128, HN = 32, FN = 2;
   using Ep = EpiOps<BM, HN, R, true>;
   constexpr int EPB = (Ep::kFloats * 4 + 15) / 16 * 16;
   constexpr int STRIP = epi_strip_bytes<OutT, FN>();
@@ -400,12 +401,12 @@ __global__ __launch_bounds__(512) void fwd_fixup_kernel(I8Args a) {
   const int tid = threadIdx.x, lane = tid & 63, v = wave_id();
   const int M = a.M, N = a.N, nsp = a.splits;
   const int tiles = a.tiles_x * ((M + BM - 1) / BM);
-  const int tile = (int)blockIdx.x >> 1, wn = (int)blockIdx.x & 1;
-  const int m0 = (tile / a.tiles_x) * BM, n0 = (tile % a.tiles_x) * 128 + wn * HN;
+  const int tile = (int)blockIdx.x >> 2, q = (int)blockIdx.x & 3;
+  const int m0 = (tile / a.tiles_x) * BM, n0 = (tile % a.tiles_x) * 128 + q * HN;
 
-  const int w = 2 * (v >> 2) + wn, fi = v & 3;
+  const int w = 2 * (v >> 2) + (q >> 1), fi = v & 3;
   const i32x4* P = reinterpret_cast<const i32x4*>(a.pacc) + ((long)tile * 4 + w) * (16 * 64) +
-                   fi * 4 * 64 + lane;
+                   (fi * 4 + 2 * (q & 1)) * 64 + lane;
   const long pstride = (long)tiles * 4 * 16 * 64;       // int4 units per split
   i32x4 pv[NSPL][FN];
 #pragma unroll
@@ -541,7 +542,7 @@ void launch_split(I8Args a, hipStream_t st) {
   constexpr int BM = 128, BN = 128, S = 2;
   a.tiles_x = (a.N + BN - 1) / BN;
   const int tiles = a.tiles_x * ((a.M + BM - 1) / BM);
-  const dim3 grid((unsigned)(tiles * a.splits)), fgrid((unsigned)(2 * tiles));
+  const dim3 grid((unsigned)(tiles * a.splits)), fgrid((unsigned)(4 * tiles));
   if (a.r <= 4) fwd_i8_kernel<BM, BN, S, 4, OutT, false, false, true><<<grid, 256, 0, st>>>(a);
   else if (a.r <= 8) fwd_i8_kernel<BM, BN, S, 8, OutT, false, false, true><<<grid, 256, 0, st>>>(a);
   else if (a.r <= 16) fwd_i8_kernel<BM, BN, S, 16, OutT, false, false, true><<<grid, 256, 0, st>>>(a);
