@@ -302,8 +302,8 @@ def describe(w):
 TRAFFIC = {
     "workload": 2,
     "sources": ["gemm_bwd.hip", "ring.hpp", "common.hpp"],
-    "sha256": "978c44571867113cc0ba6b33485c2085aa7d9034e06b6a1aecb491949b0a3a16",
-    "bytes_per_launch": 25029601,
+    "sha256": "8133678b98566da0d06b65a24867ea3a24a5a79fc4dd5e7d9e138a33bd066289",
+    "bytes_per_launch": 14781660,
 }
 
 
