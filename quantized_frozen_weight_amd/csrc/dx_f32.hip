@@ -13,49 +13,61 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // 32 x 32 output tile per block (small layers still spread over many compute
-// units), contraction in slices of 32 n, each thread a 2 x 2 register tile.
-// The next slice is fetched into registers while the current one is used.
-// dy * sw is formed once per element (one float32 rounding), then multiplied
-// by the exact integer code.
+// units), contraction in slices of 128 n (small layers are latency-bound:
+// each slice is one round trip to memory), each thread a 2 x 2 register
+// tile. The next slice is fetched into registers while the current one is
+// used. dy * sw is formed once per element (one float32 rounding), then
+// multiplied by the exact integer code.
 // ---------------------------------------------------------------------------
-constexpr int kT = 32;
+constexpr int kT = 32, kS = 128;
 
 __global__ __launch_bounds__(256) void gemm_dx_f32_kernel(
     int M, int K, int N, const float* __restrict__ dy,
     const int8_t* __restrict__ codes, const float* __restrict__ sw,
     const float* __restrict__ u, const float* __restrict__ A, int r, float s,
     float* __restrict__ dx) {
-  __shared__ float Ds[kT][kT + 1];   // [n][m]
-  __shared__ float Ws[kT][kT + 1];   // [n][k]
+  __shared__ float Ds[kS][kT + 1];   // [n][m]
+  __shared__ float Ws[kS][kT + 1];   // [n][k]
   const int tid = threadIdx.x;
   const int m0 = blockIdx.y * kT, k0 = blockIdx.x * kT;
   const int tm = tid >> 4, tk = tid & 15;      // outputs rows 2 tm + i, cols 2 tk + j
-  // loader roles: dy element (ml, 4 n), codes (nl, 4 k)
-  const int lm = tid >> 3, ln = (tid & 7) * 4;
+  // loader roles per slice: dy rows tid / 32 + 8 p, 4 n from 4 (tid % 32);
+  // code rows (n) tid / 8 + 32 p, 4 k from 4 (tid % 8); p = 0..3
+  const int lm = tid >> 5, ln = (tid & 31) * 4;
   const int wn = tid >> 3, wk = (tid & 7) * 4;
-  float dv[4];
-  uint32_t wv;
+  float dv[4][4];
+  uint32_t wv[4];
   auto fetch = [&](int n0) {
-    const int gm = m0 + lm;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int gn = n0 + ln + i;
-      dv[i] = (gm < M && gn < N) ? dy[(long)gm * N + gn] * sw[gn] : 0.f;
+    for (int p = 0; p < 4; ++p) {
+      const int gm = m0 + lm + 8 * p;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int gn = n0 + ln + i;
+        dv[p][i] = (gm < M && gn < N) ? dy[(long)gm * N + gn] * sw[gn] : 0.f;
+      }
     }
-    const int gn = n0 + wn, gk = k0 + wk;
-    wv = (gn < N && gk < K) ? *reinterpret_cast<const uint32_t*>(codes + (long)gn * K + gk) : 0u;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int gn = n0 + wn + 32 * p, gk = k0 + wk;
+      wv[p] = (gn < N && gk < K) ? *reinterpret_cast<const uint32_t*>(codes + (long)gn * K + gk) : 0u;
+    }
   };
   float acc[2][2] = {};
   fetch(0);
-  for (int n0 = 0; n0 < N; n0 += kT) {
+  for (int n0 = 0; n0 < N; n0 += kS) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Ds[ln + i][lm] = dv[i];
+    for (int p = 0; p < 4; ++p)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Ws[wn][wk + i] = (float)(((int)(wv << (24 - 8 * i))) >> 24);
+      for (int i = 0; i < 4; ++i) Ds[ln + i][lm + 8 * p] = dv[p][i];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Ws[wn + 32 * p][wk + i] = (float)(((int)(wv[p] << (24 - 8 * i))) >> 24);
     __syncthreads();
-    if (n0 + kT < N) fetch(n0 + kT);
-#pragma unroll
-    for (int n = 0; n < kT; ++n) {
+    if (n0 + kS < N) fetch(n0 + kS);
+#pragma unroll 8
+    for (int n = 0; n < kS; ++n) {
       const float a0 = Ds[n][2 * tm], a1 = Ds[n][2 * tm + 1];
       const float b0 = Ws[n][2 * tk], b1 = Ws[n][2 * tk + 1];
       acc[0][0] = __builtin_fmaf(a0, b0, acc[0][0]);
