@@ -68,7 +68,7 @@ inline float lora_s(const qlora_linear* L) {
 }
 
 struct FwdLayout {
-  size_t xq, sx, t, asum, pacc, pcorr, total;
+  size_t xq, sx, t, asum, pacc, pcorr, rs, total;
 };
 FwdLayout fwd_layout(const qlora_linear* L, int M) {
   FwdLayout w{};
@@ -86,12 +86,14 @@ FwdLayout fwd_layout(const qlora_linear* L, int M) {
   const size_t nsplit = (w8 || w8o) ? fwd_split_ints(M, L->N, L->K, w8o) : 0;
   w.pacc = off; off = align_up(off + nsplit * 4);
   w.pcorr = off; off = align_up(off + (w8o ? nsplit * 4 : 0));
+  // the row pass of long rows split over k (0 bytes for other widths)
+  w.rs = off; off = align_up(off + row_split_floats(M, L->K, L->r) * 4);
   w.total = off;
   return w;
 }
 
 struct BwdLayout {
-  size_t t, u, pB, pA, pdx, pu, total;
+  size_t t, u, pB, pA, pdx, pu, rs, total;
 };
 // Partial sums of dA and dB: one per split of the rows. The fused int8
 // backward splits by row block (at least 64 rows), the other paths into at
@@ -111,6 +113,8 @@ BwdLayout bwd_layout(const qlora_linear* L, int M, int dtype) {
   if (dtype == QLORA_BF16) bwd_split_sizes(M, L->K, L->N, L->r, &fdx, &fu);
   w.pdx = off; off = align_up(off + fdx * 4);
   w.pu = off; off = align_up(off + fu * 4);
+  // recomputing t over long rows split over k (0 bytes for other widths)
+  w.rs = off; off = align_up(off + row_split_floats(M, L->K, L->r) * 4);
   w.total = off;
   return w;
 }
@@ -248,7 +252,8 @@ int qlora_fwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
   if (L->fmt == QLORA_W8) {
     int8_t* xq = reinterpret_cast<int8_t*>(at(ws, w.xq));
     float* sx = reinterpret_cast<float*>(at(ws, w.sx));
-    launch_rowquant(dtype, x, M, L->K, L->A, L->r, xq, sx, t, s);
+    launch_rowquant(dtype, x, M, L->K, L->A, L->r, xq, sx, t, s, nullptr,
+                    reinterpret_cast<float*>(at(ws, w.rs)));
     mark(ev_start, s);
     for (int rep = 0; rep < repeats; ++rep)
       launch_gemm_fwd_w8(dtype, M, L->N, L->K, xq,
@@ -260,7 +265,8 @@ int qlora_fwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
     int8_t* xq = reinterpret_cast<int8_t*>(at(ws, w.xq));
     float* sx = reinterpret_cast<float*>(at(ws, w.sx));
     float* asum = reinterpret_cast<float*>(at(ws, w.asum));
-    launch_rowquant(dtype, x, M, L->K, L->A, L->r, xq, sx, t, s, asum);
+    launch_rowquant(dtype, x, M, L->K, L->A, L->r, xq, sx, t, s, asum,
+                    reinterpret_cast<float*>(at(ws, w.rs)));
     mark(ev_start, s);
     for (int rep = 0; rep < repeats; ++rep)
       launch_gemm_fwd_w8o(M, L->N, L->K, xq, static_cast<const int8_t*>(L->codes), sx, asum,
@@ -269,7 +275,7 @@ int qlora_fwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
                           reinterpret_cast<float*>(at(ws, w.pcorr)), s);
     mark(ev_stop, s);
   } else {
-    launch_lora_down(dtype, x, M, L->K, L->A, L->r, t, s);
+    launch_lora_down(dtype, x, M, L->K, L->A, L->r, t, s, reinterpret_cast<float*>(at(ws, w.rs)));
     mark(ev_start, s);
     for (int rep = 0; rep < repeats; ++rep)
       launch_gemm_fwd_w4(M, L->N, L->K, static_cast<const uint16_t*>(x),
@@ -301,7 +307,8 @@ int qlora_fwd_a8w4(const qlora_linear* L, int M, int dtype, const void* x, void*
   int8_t* xq = reinterpret_cast<int8_t*>(at(ws, w.xq));
   float* sx = reinterpret_cast<float*>(at(ws, w.sx));
   (void)hipGetLastError();
-  launch_rowquant(dtype, x, M, L->K, L->A, L->r, xq, sx, t, s);
+  launch_rowquant(dtype, x, M, L->K, L->A, L->r, xq, sx, t, s, nullptr,
+                  reinterpret_cast<float*>(at(ws, w.rs)));
   launch_gemm_fwd_a8w4(M, L->N, L->K, xq, sx, static_cast<const uint8_t*>(L->codes),
                        static_cast<const _Float16*>(L->scales), t, L->B, head_width(L), L->r, lora_s(L),
                        static_cast<uint16_t*>(y), s);
@@ -336,7 +343,7 @@ int qlora_bwd_partial_timed(const qlora_linear* L, int M, int dtype, const void*
   const float* t = t_saved;
   if (t == nullptr) {
     float* tw = reinterpret_cast<float*>(at(ws, w.t));
-    launch_lora_down(dtype, x, M, L->K, L->A, L->r, tw, s);
+    launch_lora_down(dtype, x, M, L->K, L->A, L->r, tw, s, reinterpret_cast<float*>(at(ws, w.rs)));
     t = tw;
   }
   float* partB = reinterpret_cast<float*>(at(ws, w.pB));

@@ -28,11 +28,15 @@ void launch_merge_w8(const int8_t* codes, const float* sw, const float* A,
                      int8_t* codes_out, float* scales_out, hipStream_t st);
 
 // asum (optional): float32 [M] row sums of xq
+// scratch (optional): row_split_floats(M, K, r) floats; rows of 4097 to
+// 16384 entries with t wanted then take two launches split over k instead of
+// one that stages the whole adapter in every block
+size_t row_split_floats(int M, int K, int r);
 void launch_rowquant(int dtype, const void* x, int M, int K, const float* A,
                      int r, int8_t* xq, float* sx, float* t, hipStream_t st,
-                     float* asum = nullptr);
+                     float* asum = nullptr, float* scratch = nullptr);
 void launch_lora_down(int dtype, const void* x, int M, int K, const float* A,
-                      int r, float* t, hipStream_t st);
+                      int r, float* t, hipStream_t st, float* scratch = nullptr);
 
 // y = acc * sx[m] * sw[n] + s * t B   (acc_out != nullptr: write int32 acc).
 // Shapes with few output tiles and a long contraction split it when pacc is

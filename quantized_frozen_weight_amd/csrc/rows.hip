@@ -20,7 +20,8 @@
 // block needs is issued before anything waits: the row itself (rows of up
 // to 4096 entries stay in registers between the abs-max and the quantize
 // pass; forward rows of up to 16384 too, two per block with each wave on a
-// quarter of them; longer rows are streamed twice) and the slice of the
+// quarter of them, or -- with t wanted and scratch given -- split over k in
+// two launches; longer rows are streamed twice) and the slice of the
 // rank-r matrix that the block's rows share, copied to LDS with 16-byte
 // loads (for many short rows each wave takes two or four of them, so one
 // LDS read of the adapter serves several rows). In LDS
@@ -287,6 +288,7 @@ __global__ __launch_bounds__(256) void row_kernel(
 }
 
 // ---- long rows (4096 < L <= 16384), forward modes, rank up to 8 ------------
+// (with t wanted and scratch given, the split pass below takes these rows)
 // Two rows per block. Wave w owns the 512-entry groups g = 4 i + w of both
 // rows (entries [512 g, 512 g + 512), one 8-entry chunk per lane), so every
 // adapter value read from LDS serves two rows, and the rows stay in
@@ -464,6 +466,169 @@ __global__ __launch_bounds__(256) void row_long_kernel(
   }
 }
 
+// ---- long rows with the adapter product, split over k ---------------------
+// row_long_kernel stages the whole adapter through LDS in every block (512
+// KiB for 16384 x 8), one global round trip per 2048-entry slice, so its
+// blocks wait on those loads. With t wanted this path splits instead:
+//   part: block (g, s) takes rows [RB g, RB g + RB) and the 2048-entry slice
+//         s; thread i owns chunk 256 s + i (8 entries) of every row and holds
+//         that chunk's 8 x R adapter values in registers for all RB rows.
+//         It leaves per (row, slice) the abs-max bits and the r sums of the
+//         slice (the four waves' totals added in wave order);
+//   fin:  one block per row: the abs-max over the slices, the codes (the row
+//         read again), the code sum, and t as the slice sums added in slice
+//         order (the t-only mode: a small kernel that adds the slice sums).
+// Scratch: abs-max bits [M][S] then slice sums [M][S][R], S = ceil(L / 2048).
+constexpr int kSplitSlice = 2048;
+
+template <typename T> constexpr int split_rows() { return std::is_same<T, F32>::value ? 8 : 16; }
+
+template <typename T, int R, int MODE>
+__global__ __launch_bounds__(256) void row_split_part_kernel(
+    const typename Elem<T>::type* __restrict__ rows, int M, int L,
+    const float* __restrict__ W, int r, uint32_t* __restrict__ pmax, float* __restrict__ pt) {
+  constexpr int RB = split_rows<T>();
+  __shared__ uint32_t red_max[RB][4];
+  __shared__ float red_t[RB][4][R];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int row0 = blockIdx.x * RB, s = blockIdx.y, S = gridDim.y;
+  const int nchunk = L / 8;
+  const int c = s * (kSplitSlice / 8) + tid;
+  const int cc = c < nchunk ? c : nchunk - 1;
+
+  // every row's chunk from clamped addresses; a chunk past the row is zeroed
+  // (no abs-max, no sum), a row past M is computed and not stored
+  Raw<T> hold[RB];
+#pragma unroll
+  for (int rr = 0; rr < RB; ++rr) {
+    const int row = row0 + rr;
+    raw_load(rows + (long)(row < M ? row : M - 1) * L + 8 * cc, hold[rr]);
+  }
+  // the adapter rows k = 8 cc .. 8 cc + 7, ranks past r as zeros
+  float a[8][R];
+  if (r == R) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(W + (long)8 * cc * R);
+    f32x4 av[2 * R];
+#pragma unroll
+    for (int q = 0; q < 2 * R; ++q) av[q] = src[q];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int j = 0; j < R; ++j) a[e][j] = av[(e * R + j) / 4][(e * R + j) % 4];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int j = 0; j < R; ++j) a[e][j] = j < r ? W[(long)(8 * cc + e) * r + j] : 0.f;
+  }
+  if (c >= nchunk) {
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) raw_zero(hold[rr]);
+  }
+
+#pragma unroll
+  for (int rr = 0; rr < RB; ++rr) {
+    if constexpr (MODE == kFwdQuant) {
+      const uint32_t m = wave_max_u32(raw_absmax(hold[rr]));
+      if (lane == 0) red_max[rr][w] = m;
+    }
+    float v[8], acc[R];
+    raw_unpack(hold[rr], v);
+#pragma unroll
+    for (int j = 0; j < R; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int j = 0; j < R; ++j) acc[j] = __builtin_fmaf(v[e], a[e][j], acc[j]);
+    const float tot = wave_sum_ranks<R>(acc);
+    if ((lane & (64 / R - 1)) == 0) red_t[rr][w][rank_of_lane<R>(lane)] = tot;
+  }
+  __syncthreads();
+  if (tid < RB * R) {
+    const int rr = tid / R, j = tid % R, row = row0 + rr;
+    if (row < M)
+      pt[((long)row * S + s) * R + j] =
+          ((red_t[rr][0][j] + red_t[rr][1][j]) + red_t[rr][2][j]) + red_t[rr][3][j];
+  }
+  if (MODE == kFwdQuant && tid < RB) {
+    const int row = row0 + tid;
+    uint32_t m = red_max[tid][0];
+#pragma unroll
+    for (int q = 1; q < 4; ++q) m = red_max[tid][q] > m ? red_max[tid][q] : m;
+    if (row < M) pmax[(long)row * S + s] = m;
+  }
+}
+
+template <typename T, int R>
+__global__ __launch_bounds__(256) void row_split_fin_kernel(
+    const typename Elem<T>::type* __restrict__ rows, int M, int L, int r, int S,
+    const uint32_t* __restrict__ pmax, const float* __restrict__ pt, float* __restrict__ out_r,
+    int8_t* __restrict__ xq, float* __restrict__ sx, float* __restrict__ asum) {
+  constexpr int NH = kLongMax / 8 / 256;             // chunks per thread
+  __shared__ float red_c[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int row = blockIdx.x;
+  const int nchunk = L / 8;
+  const auto* xr = rows + (long)row * L;
+  Raw<T> hold[NH];
+#pragma unroll
+  for (int i = 0; i < NH; ++i) {
+    const int c = tid + 256 * i;
+    raw_load(xr + 8 * (c < nchunk ? c : nchunk - 1), hold[i]);
+  }
+  // the row's abs-max from its slices' (each wave reads them all)
+  const uint32_t m = wave_max_u32(lane < S ? pmax[(long)row * S + lane] : 0u);
+  const QuantParams qp = absmax_params(m, 127.f);
+  int csum = 0;
+#pragma unroll
+  for (int i = 0; i < NH; ++i) {
+    const int c = tid + 256 * i;
+    if (c < nchunk) {
+      float v[8];
+      raw_unpack(hold[i], v);
+      uint32_t lo = 0, hi = 0;
+      if (qp.live) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int q0 = quant_code(v[e], qp.inv, 127.f);
+          const int q1 = quant_code(v[e + 4], qp.inv, 127.f);
+          lo |= (uint32_t)(q0 & 0xff) << (8 * e);
+          hi |= (uint32_t)(q1 & 0xff) << (8 * e);
+          csum += q0 + q1;
+        }
+      }
+      *reinterpret_cast<u32x2*>(xq + (long)row * L + 8 * c) = u32x2{lo, hi};
+    }
+  }
+  if (tid < r) {
+    const float* p = pt + (long)row * S * R + tid;
+    float acc = p[0];
+    for (int s = 1; s < S; ++s) acc += p[s * R];
+    out_r[(long)row * r + tid] = acc;
+  }
+  if (tid == 0) sx[row] = qp.scale;
+  if (asum != nullptr) {
+    // |sum| <= 127 L < 2^24: exact in float
+    const float cs = wave_sum((float)csum);
+    if (lane == 0) red_c[w] = cs;
+    __syncthreads();
+    if (tid == 0) asum[row] = ((red_c[0] + red_c[1]) + red_c[2]) + red_c[3];
+  }
+}
+
+template <int R>
+__global__ __launch_bounds__(256) void row_split_tsum_kernel(int M, int r, int S,
+                                                              const float* __restrict__ pt,
+                                                              float* __restrict__ out_r) {
+  const long e = (long)blockIdx.x * 256 + threadIdx.x;
+  const int row = (int)(e / R), j = (int)(e % R);
+  if (row >= M || j >= r) return;
+  const float* p = pt + (long)row * S * R + j;
+  float acc = p[0];
+  for (int s = 1; s < S; ++s) acc += p[s * R];
+  out_r[(long)row * r + j] = acc;
+}
+
 // ---- many short rows, forward modes: RW rows per wave ---------------------
 // For grids of more than one block per compute unit, each wave takes RW
 // rows (L <= 512 NHC, held in registers) instead of one, so every adapter
@@ -608,7 +773,7 @@ void row_multi_launch(int nhc, dim3 grid, size_t lds, const typename Elem<T>::ty
 template <typename T, int R, int MODE>
 void row_launch(const void* rows, int M, int L, const float* W, int hd, int r,
                 float* out_r, int8_t* xq, float* sx, float* asum, const float* sw,
-                uint16_t* dys, hipStream_t st) {
+                uint16_t* dys, float* scratch, hipStream_t st) {
   dim3 grid((M + kRowsPerBlock - 1) / kRowsPerBlock);
   const auto* p = reinterpret_cast<const typename Elem<T>::type*>(rows);
   constexpr int SL = Slice<R>::len;
@@ -617,6 +782,18 @@ void row_launch(const void* rows, int M, int L, const float* W, int hd, int r,
   if (out_r != nullptr)
     lds = (MODE == kBwd ? (size_t)R * sld : (size_t)(sld / 8) * (8 * R + 4)) * sizeof(float);
   if constexpr (MODE != kBwd && R <= kLongMaxRank) {
+    if (L > kHoldChunks * 512 && L <= kLongMax && out_r != nullptr && scratch != nullptr) {
+      const int S = (L + kSplitSlice - 1) / kSplitSlice;
+      uint32_t* pmax = reinterpret_cast<uint32_t*>(scratch);
+      float* pt = scratch + (size_t)M * S;
+      constexpr int RB = split_rows<T>();
+      row_split_part_kernel<T, R, MODE><<<dim3((M + RB - 1) / RB, S), 256, 0, st>>>(p, M, L, W, r, pmax, pt);
+      if constexpr (MODE == kFwdQuant)
+        row_split_fin_kernel<T, R><<<M, 256, 0, st>>>(p, M, L, r, S, pmax, pt, out_r, xq, sx, asum);
+      else
+        row_split_tsum_kernel<R><<<(unsigned)(((long)M * R + 255) / 256), 256, 0, st>>>(M, r, S, pt, out_r);
+      return;
+    }
     if (L > kHoldChunks * 512 && L <= kLongMax) {
       const size_t ldsl = out_r != nullptr ? (size_t)(kLongSlice / 8) * (8 * R + 4) * sizeof(float) : 0;
       const dim3 lgrid((M + kLongRows - 1) / kLongRows);
@@ -653,33 +830,40 @@ void row_launch(const void* rows, int M, int L, const float* W, int hd, int r,
 template <typename T, int MODE>
 void row_dispatch_r(int r, const void* rows, int M, int L, const float* W, int hd,
                     float* out_r, int8_t* xq, float* sx, float* asum, const float* sw,
-                    uint16_t* dys, hipStream_t st) {
-  if (r <= 1) row_launch<T, 1, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, asum, sw, dys, st);
-  else if (r <= 2) row_launch<T, 2, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, asum, sw, dys, st);
-  else if (r <= 4) row_launch<T, 4, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, asum, sw, dys, st);
-  else if (r <= 8) row_launch<T, 8, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, asum, sw, dys, st);
-  else if (r <= 16) row_launch<T, 16, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, asum, sw, dys, st);
-  else row_launch<T, 32, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, asum, sw, dys, st);
+                    uint16_t* dys, hipStream_t st, float* scratch = nullptr) {
+  if (r <= 1) row_launch<T, 1, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, asum, sw, dys, scratch, st);
+  else if (r <= 2) row_launch<T, 2, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, asum, sw, dys, scratch, st);
+  else if (r <= 4) row_launch<T, 4, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, asum, sw, dys, scratch, st);
+  else if (r <= 8) row_launch<T, 8, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, asum, sw, dys, scratch, st);
+  else if (r <= 16) row_launch<T, 16, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, asum, sw, dys, scratch, st);
+  else row_launch<T, 32, MODE>(rows, M, L, W, hd, r, out_r, xq, sx, asum, sw, dys, scratch, st);
 }
 
 }  // namespace
 
+size_t row_split_floats(int M, int K, int r) {
+  if (K <= kHoldChunks * 512 || K > kLongMax || r > kLongMaxRank) return 0;
+  const int R = r <= 1 ? 1 : r <= 2 ? 2 : r <= 4 ? 4 : 8;   // row_dispatch_r's rank
+  const size_t S = (K + kSplitSlice - 1) / kSplitSlice;
+  return (size_t)M * S * (1 + R);
+}
+
 void launch_rowquant(int dtype, const void* x, int M, int K, const float* A,
                      int r, int8_t* xq, float* sx, float* t, hipStream_t st,
-                     float* asum) {
+                     float* asum, float* scratch) {
   const int rr = t == nullptr ? 1 : r;
   if (dtype == 0)
-    row_dispatch_r<F32, kFwdQuant>(rr, x, M, K, A, K, t, xq, sx, asum, nullptr, nullptr, st);
+    row_dispatch_r<F32, kFwdQuant>(rr, x, M, K, A, K, t, xq, sx, asum, nullptr, nullptr, st, scratch);
   else
-    row_dispatch_r<BF16, kFwdQuant>(rr, x, M, K, A, K, t, xq, sx, asum, nullptr, nullptr, st);
+    row_dispatch_r<BF16, kFwdQuant>(rr, x, M, K, A, K, t, xq, sx, asum, nullptr, nullptr, st, scratch);
 }
 
 void launch_lora_down(int dtype, const void* x, int M, int K, const float* A,
-                      int r, float* t, hipStream_t st) {
+                      int r, float* t, hipStream_t st, float* scratch) {
   if (dtype == 0)
-    row_dispatch_r<F32, kFwdT>(r, x, M, K, A, K, t, nullptr, nullptr, nullptr, nullptr, nullptr, st);
+    row_dispatch_r<F32, kFwdT>(r, x, M, K, A, K, t, nullptr, nullptr, nullptr, nullptr, nullptr, st, scratch);
   else
-    row_dispatch_r<BF16, kFwdT>(r, x, M, K, A, K, t, nullptr, nullptr, nullptr, nullptr, nullptr, st);
+    row_dispatch_r<BF16, kFwdT>(r, x, M, K, A, K, t, nullptr, nullptr, nullptr, nullptr, nullptr, st, scratch);
 }
 
 void launch_bwd_rows(int dtype, const void* dy, int M, int N, const float* B, int hd,

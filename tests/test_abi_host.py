@@ -138,20 +138,40 @@ def test_split_forward_workspace(lib):
     # [512, 2048]; the 4-bit layout of the same shape holds none
     st, w8 = _fwd_ws(lib, _lin(K=16384, N=2048, r=8), M=512)
     assert st == Q.QLORA_OK
-    base = 512 * 16384 + 512 * 4 + 512 * 8 * 4
+    # codes, scales, t, and the row pass split over 2048-entry slices of k:
+    # per row and slice the abs-max bits and r sums, 512 x 8 x (1 + 8) floats
+    base = 512 * 16384 + 512 * 4 + 512 * 8 * 4 + 512 * 8 * 9 * 4
     assert w8 >= base + 8 * 512 * 2048 * 4
-    assert w8 <= base + 8 * 512 * 2048 * 4 + 4 * 256
+    assert w8 <= base + 8 * 512 * 2048 * 4 + 5 * 256
     st, w4 = _fwd_ws(lib, _lin(K=16384, N=2048, r=8, fmt=Q.QLORA_W4G128), M=512)
-    assert st == Q.QLORA_OK and w4 < base + 4 * 256
+    assert st == Q.QLORA_OK and w4 < base + 5 * 256
     # outlier-compensated weights: 4 x 32 tiles of 128 x 64 split 4 ways ->
     # int32 partial sums and float partial corrections, 16 MiB each
     st, w8o = _fwd_ws(lib, _lin(K=16384, N=2048, r=8, fmt=Q.QLORA_W8O), M=512)
     assert st == Q.QLORA_OK
     base_o = base + 512 * 4                            # and the code sums
-    assert base_o + 2 * 4 * 512 * 2048 * 4 <= w8o <= base_o + 2 * 4 * 512 * 2048 * 4 + 6 * 256
+    assert base_o + 2 * 4 * 512 * 2048 * 4 <= w8o <= base_o + 2 * 4 * 512 * 2048 * 4 + 7 * 256
     # a short contraction does not split
     st, short = _fwd_ws(lib, _lin(K=1024, N=1024, r=8), M=1024)
     assert short < 1024 * 1024 + 1024 * 4 + 1024 * 8 * 4 + 4 * 256
+
+
+@pytest.mark.parametrize("K,r,slices,R", [(4096, 8, 0, 0), (4224, 8, 3, 8), (8192, 3, 4, 4),
+                                          (16384, 1, 8, 1), (16384, 9, 0, 0)])
+def test_row_split_workspace(lib, K, r, slices, R):
+    # rows of 4097..16384 entries with rank up to 8 add the split row pass's
+    # scratch (abs-max bits and R sums per row and 2048-entry slice, R the
+    # rank rounded up to a power of two) to the forward workspace and to the
+    # backward one (t recomputed from x); other widths add nothing
+    M = 100
+    extra = M * slices * (1 + R) * 4
+    st, f = _fwd_ws(lib, _lin(K=K, N=256, r=r, fmt=Q.QLORA_W4G128), M=M)
+    assert st == Q.QLORA_OK
+    base = M * K + M * 4 + M * r * 4
+    assert base + extra <= f <= base + extra + 6 * 256
+    b = _bwd_ws(lib, _lin(K=K, N=256, r=r), M, Q.QLORA_F32)
+    b0 = 2 * M * r * 4 + ((M + 63) // 64) * r * (K + 256) * 4
+    assert b0 + extra <= b <= b0 + extra + 7 * 256
 
 
 @pytest.mark.parametrize("kw,M,dtype,want", [

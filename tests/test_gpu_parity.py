@@ -159,6 +159,8 @@ SMALL = [
     (2, 33, 16384, 48, 4),      # long rows at the longest length held in registers
     (2, 4, 6144, 32, 16),       # long rows at rank 16 (streaming row pass)
     (2, 3, 20480, 32, 8),       # rows past the held length (streaming row pass)
+    (2, 17, 6160, 32, 3),       # long rows split over k: rank 3 of 4, 17 rows of 16-row blocks, 16-entry last slice
+    (1, 9, 8208, 32, 5),        # float32 long rows split over k, rank 5 of 8
     (2, 4100, 96, 48, 8),       # four rows per wave in the row pass, ragged last block
     (2, 2100, 1040, 336, 8),    # 128 x 64 backward tiles: ragged rows, k tile and last stage
     (2, 1, 256, 4096, 8),       # one row: input gradient split 4 ways
