@@ -6,6 +6,11 @@ A step is one training pass of the workload's layer stack through libqlora:
 the forward of every layer (per-row activation quantization + x A, int8
 MFMA product with the fused dequant + LoRA epilogue), then the backward of
 every layer in reverse (dy B^T, dB, dA, and the bf16 MFMA input gradient).
+For stacks of at least 4 layers (``--finish``) each layer's backward leaves
+its adapter-gradient partial sums in a workspace of its own and one batched
+call adds them into every layer's dA and dB after the last layer; otherwise
+each layer's ``qlora_bwd`` combines its own. Both steps are timed and
+reported (``batched_finish_ms_per_step``, ``layerwise_finish_ms_per_step``).
 The one-time weight quantization is timed separately (``quantize_ms``).
 Inputs are seeded synthetic tensors already resident in HBM. Steps are
 captured once in a HIP graph and replayed; ``value`` is the workload's
@@ -48,6 +53,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline (0: skip)")
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    p.add_argument("--finish", choices=("auto", "batched", "layerwise"), default="auto",
+                   help="adapter-gradient combine of the timed step: one batched call after "
+                        "the last layer, or one per layer (auto: batched for stacks of at "
+                        "least 4 layers)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 256 MiB device copy (for scaling HBM counters)")
     return p.parse_args()
@@ -199,38 +208,67 @@ def main():
                                       l.dA.data_ptr(), l.dB.data_ptr(), wsp, ws_bytes, st,
                                       repeats if ev_b else 1, a, b), "bwd")
 
+    # The timed step runs each layer's backward as qlora_bwd_partial (dx and
+    # the adapter-gradient partial sums, into a workspace of its own) and
+    # takes every layer's dA and dB at the end with qlora_bwd_finish_batch
+    # (one launch per 16 layers) instead of one combine launch per layer.
+    bws = [torch.empty((max(l.bwd_ws, 256),), dtype=torch.uint8, device=dev) for l in layers]
+    items = (Q.qlora_finish_item * len(layers))()
+    for i, l in enumerate(layers):
+        items[i] = Q.qlora_finish_item(ctypes.cast(ctypes.pointer(l.cs), ctypes.c_void_p), M,
+                                       l.dt, l.dA.data_ptr(), l.dB.data_ptr(),
+                                       bws[i].data_ptr(), bws[i].numel())
+
+    def step_batched():
+        st = torch.cuda.current_stream().cuda_stream
+        for l in layers:
+            check(lib.qlora_fwd(ctypes.byref(l.cs), M, l.dt, l.x.data_ptr(), l.y.data_ptr(),
+                                l.t.data_ptr(), wsp, ws_bytes, st), "fwd")
+        for i in reversed(range(len(layers))):
+            l = layers[i]
+            check(lib.qlora_bwd_partial(ctypes.byref(l.cs), M, l.dt, l.x.data_ptr(),
+                                        l.dy.data_ptr(), l.t.data_ptr(), l.dx.data_ptr(),
+                                        bws[i].data_ptr(), bws[i].numel(), st), "bwd_partial")
+        check(lib.qlora_bwd_finish_batch(items, len(layers), st), "finish_batch")
+
     # eager warm-up (also loads every kernel)
     for _ in range(3):
         step()
+        step_batched()
     torch.cuda.synchronize()
 
     use_graph = not args.no_graph
-    if use_graph:
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            step()
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            step()
-        torch.cuda.synchronize()
-        run = g.replay
-    else:
-        run = step
 
-    for _ in range(args.warmup):
-        run()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        run()
-    e1.record()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    ms = e0.elapsed_time(e1) / args.steps
+    def timed(fn):
+        if use_graph:
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                fn()
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                fn()
+            torch.cuda.synchronize()
+            run = g.replay
+        else:
+            run = fn
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(args.steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps, (time.perf_counter() - t0) * 1e3 / args.steps
+
+    batched = args.finish == "batched" or (args.finish == "auto" and len(layers) >= 4)
+    ms_b, wall_b = timed(step_batched)
+    ms_l, wall_l = timed(step)
+    ms, wall_ms = (ms_b, wall_b) if batched else (ms_l, wall_l)
     ops = w.total_ops()
     value = ops / (ms * 1e-3) / 1e12
 
@@ -238,7 +276,7 @@ def main():
     torch.cuda.synchronize()
     e0.record()
     for _ in range(10):
-        step()
+        (step_batched if batched else step)()
     e1.record()
     torch.cuda.synchronize()
     eager_ms = e0.elapsed_time(e1) / 10
@@ -272,6 +310,9 @@ def main():
             "hip_graph": use_graph,
         },
         "wall_ms_per_step": round(wall_ms, 5),
+        "finish": "batched" if batched else "layerwise",
+        "batched_finish_ms_per_step": round(ms_b, 5),
+        "layerwise_finish_ms_per_step": round(ms_l, 5),
         "eager_ms_per_step": round(eager_ms, 5),
         "quantize_ms": round(quantize_ms, 4),
         "merge_ms": None if merge_ms is None else round(merge_ms, 4),

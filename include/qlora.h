@@ -251,6 +251,31 @@ int qlora_bwd_partial(const qlora_linear* L, int M, int dtype, const void* x,
 int qlora_bwd_finish(const qlora_linear* L, int M, int dtype, float* dA,
                      float* dB, void* ws, size_t ws_bytes, void* stream);
 
+/* One layer of qlora_bwd_finish_batch: the arguments of qlora_bwd_finish. */
+typedef struct {
+  const qlora_linear* L;
+  int M;
+  int dtype;
+  float* dA;          /* [K, r] float32, overwritten */
+  float* dB;          /* [r, N] (or per head [heads, r, hd]) float32, overwritten */
+  void* ws;           /* that layer's qlora_bwd_partial workspace */
+  size_t ws_bytes;
+} qlora_finish_item;
+
+/* qlora_bwd_finish for `count` layers (count >= 1) in one launch per 16
+ * layers, for a backward pass that runs qlora_bwd_partial layer by layer and
+ * takes every adapter gradient ("Why does LoRA reduce memory footprint?":
+ * only the adapter's A and B get gradients) at the end. Each layer's dA and
+ * dB are bitwise those of its own qlora_bwd_finish (or qlora_bwd): the same
+ * sums in the same order. The items' workspaces must be distinct and each
+ * must hold its layer's qlora_bwd_partial results, ordered before this call
+ * on `stream`; items[] is read during the call only (host memory). Every
+ * item is validated as by qlora_bwd_finish before anything is enqueued; the
+ * first failing item's status is returned (EINVAL also for items == NULL
+ * or count < 1). */
+int qlora_bwd_finish_batch(const qlora_finish_item* items, int count,
+                           void* stream);
+
 /* qlora_fwd / qlora_bwd with timing marks, for timing the call's main
  * product kernel live: the int8 or 4-bit forward product; the fused int8
  * backward (dx, u and the adapter-gradient partial sums) or, on the other

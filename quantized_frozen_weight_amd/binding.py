@@ -53,8 +53,20 @@ EXPORTS = (
     "qlora_fwd_workspace", "qlora_fwd", "qlora_bwd_workspace", "qlora_bwd",
     "qlora_quantize_rows", "qlora_fwd_acc", "qlora_fwd_timed", "qlora_bwd_timed",
     "qlora_merge", "qlora_bwd_partial", "qlora_bwd_finish", "qlora_fwd_a8w4",
-    "qlora_quantize_heads", "qlora_outlier_layout",
+    "qlora_quantize_heads", "qlora_outlier_layout", "qlora_bwd_finish_batch",
 )
+
+
+class qlora_finish_item(ctypes.Structure):
+    _fields_ = [
+        ("L", ctypes.c_void_p),
+        ("M", ctypes.c_int),
+        ("dtype", ctypes.c_int),
+        ("dA", ctypes.c_void_p),
+        ("dB", ctypes.c_void_p),
+        ("ws", ctypes.c_void_p),
+        ("ws_bytes", ctypes.c_size_t),
+    ]
 
 
 def lib() -> ctypes.CDLL:
@@ -85,6 +97,7 @@ def lib() -> ctypes.CDLL:
     L.qlora_merge.argtypes = [plin, vp, vp, vp]
     L.qlora_bwd_partial.argtypes = [plin, i, i, vp, vp, vp, vp, vp, sz, vp]
     L.qlora_bwd_finish.argtypes = [plin, i, i, vp, vp, vp, sz, vp]
+    L.qlora_bwd_finish_batch.argtypes = [ctypes.POINTER(qlora_finish_item), i, vp]
     L.qlora_fwd_a8w4.argtypes = [plin, i, i, vp, vp, vp, vp, sz, vp]
     L.qlora_quantize_heads.argtypes = [vp, i, i, i, i, vp, vp, vp]
     L.qlora_outlier_layout.argtypes = [i, i, psz, psz, psz, ctypes.POINTER(ctypes.c_int32)]
@@ -317,6 +330,34 @@ def qlora_bwd_partial(layer: QLinear, x, dy, t=None, need_dx: bool = True, dx=No
                                    _stream() if stream is None else stream.cuda_stream),
            "qlora_bwd_partial")
     return (dx if need_dx else None), ws
+
+
+def qlora_bwd_finish_batch(items, stream=None):
+    """qlora_bwd_finish for several layers in one launch (per 16 layers).
+    items: (layer, M, dtype, ws) or (layer, M, dtype, ws, dA, dB) tuples, each
+    ws holding that layer's qlora_bwd_partial results (distinct workspaces).
+    Returns the list of (dA, dB)."""
+    import torch
+    arr = (qlora_finish_item * len(items))()
+    keep, out = [], []
+    for n, it in enumerate(items):
+        layer, M, dtype, ws = it[:4]
+        dA = it[4] if len(it) > 4 else None
+        dB = it[5] if len(it) > 5 else None
+        if dA is None:
+            dA = torch.empty((layer.K, layer.r), dtype=torch.float32, device=ws.device)
+        if dB is None:
+            dB = torch.empty(_b_shape(layer), dtype=torch.float32, device=ws.device)
+        s = layer.cstruct()
+        keep.append(s)
+        arr[n] = qlora_finish_item(ctypes.cast(ctypes.pointer(s), ctypes.c_void_p), M,
+                                   QLORA_F32 if dtype == torch.float32 else QLORA_BF16,
+                                   _ptr(dA), _ptr(dB), _ptr(ws), ws.numel() * ws.element_size())
+        out.append((dA, dB))
+    _check(lib().qlora_bwd_finish_batch(arr, len(items),
+                                        _stream() if stream is None else stream.cuda_stream),
+           "qlora_bwd_finish_batch")
+    return out
 
 
 def qlora_bwd_finish(layer: QLinear, M: int, dtype, ws, dA=None, dB=None, stream=None):

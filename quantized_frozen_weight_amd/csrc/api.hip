@@ -388,15 +388,19 @@ int qlora_bwd_partial(const qlora_linear* L, int M, int dtype, const void* x,
                                  1, nullptr, nullptr);
 }
 
-int qlora_bwd_finish(const qlora_linear* L, int M, int dtype, float* dA, float* dB,
-                     void* ws, size_t ws_bytes, void* stream) {
+namespace {
+int finish_check(const qlora_linear* L, int M, int dtype, float* dA, float* dB, void* ws,
+                 size_t ws_bytes) {
   int st = check_linear(L, M, dtype);
   if (st) return st;
   if (!dA || !dB || !aligned16(dA) || !aligned16(dB)) return QLORA_EINVAL;
-  st = bwd_check_ws(L, M, dtype, ws, ws_bytes);
-  if (st) return st;
+  return bwd_check_ws(L, M, dtype, ws, ws_bytes);
+}
+
+// The combine of one layer's partial sums (left in ws by qlora_bwd_partial).
+SkinnyJobs finish_jobs(const qlora_linear* L, int M, int dtype, float* dA, float* dB,
+                       void* ws) {
   const BwdLayout w = bwd_layout(L, M, dtype);
-  (void)hipGetLastError();
   SkinnyJobs sk{};
   sk.njobs = 2; sk.M = M; sk.r = L->r; sk.s = lora_s(L);
   sk.nsplit = bwd_splits(L, M);
@@ -404,7 +408,36 @@ int qlora_bwd_finish(const qlora_linear* L, int M, int dtype, float* dA, float* 
   sk.out[0] = dB; sk.transpose[0] = 0; sk.hd0 = head_width(L);
   sk.partial[1] = reinterpret_cast<float*>(at(ws, w.pA)); sk.C[1] = L->K;
   sk.out[1] = dA; sk.transpose[1] = 1;
-  launch_skinny_stage2(sk, static_cast<hipStream_t>(stream));
+  return sk;
+}
+}  // namespace
+
+int qlora_bwd_finish(const qlora_linear* L, int M, int dtype, float* dA, float* dB,
+                     void* ws, size_t ws_bytes, void* stream) {
+  const int st = finish_check(L, M, dtype, dA, dB, ws, ws_bytes);
+  if (st) return st;
+  (void)hipGetLastError();
+  launch_skinny_stage2(finish_jobs(L, M, dtype, dA, dB, ws), static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int qlora_bwd_finish_batch(const qlora_finish_item* items, int count, void* stream) {
+  if (!items || count < 1) return QLORA_EINVAL;
+  for (int i = 0; i < count; ++i) {
+    const qlora_finish_item& it = items[i];
+    const int st = finish_check(it.L, it.M, it.dtype, it.dA, it.dB, it.ws, it.ws_bytes);
+    if (st) return st;
+  }
+  (void)hipGetLastError();
+  SkinnyJobs sk[kFinishBatch];
+  for (int i0 = 0; i0 < count; i0 += kFinishBatch) {
+    const int n = count - i0 < kFinishBatch ? count - i0 : kFinishBatch;
+    for (int i = 0; i < n; ++i) {
+      const qlora_finish_item& it = items[i0 + i];
+      sk[i] = finish_jobs(it.L, it.M, it.dtype, it.dA, it.dB, it.ws);
+    }
+    launch_finish_batch(sk, n, static_cast<hipStream_t>(stream));
+  }
   return launch_status();
 }
 

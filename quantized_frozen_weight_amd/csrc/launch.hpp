@@ -86,6 +86,9 @@ SkinnyJobs make_adapter_grad_jobs(int M, int r, float s, const float* t,
                                   float* partA);
 void launch_skinny_stage1(int dtype, const SkinnyJobs& p, hipStream_t st);
 void launch_skinny_stage2(const SkinnyJobs& p, hipStream_t st);
+// stage 2 of n layers, kFinishBatch per launch; each output bitwise as
+// launch_skinny_stage2 of its own job
+void launch_finish_batch(const SkinnyJobs* jobs, int n, hipStream_t st);
 
 // bf16 backward, int8 (fmt 0: codes [N, K], scales float [N]), 4-bit
 // (fmt 1: packed [N, K/2], scales fp16 [N, K/128]) or outlier-compensated

@@ -18,8 +18,7 @@ __global__ __launch_bounds__(256) void skinny_stage1_kernel(SkinnyJobs p) {
 // NS loads in flight at a time (NS: the split count rounded up to 8, 16 or 32,
 // so no load is wasted on a clamped duplicate).
 template <int NS>
-__global__ __launch_bounds__(256) void skinny_stage2_kernel(SkinnyJobs p) {
-  const long e0 = (long)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void stage2_elem(const SkinnyJobs& p, long e0) {
   const long n0 = (long)p.r * p.C[0];
   const int job = e0 < n0 ? 0 : 1;
   const long e = job ? e0 - n0 : e0;
@@ -41,6 +40,29 @@ __global__ __launch_bounds__(256) void skinny_stage2_kernel(SkinnyJobs p) {
   const float out = p.s * sum;
   if (p.transpose[job]) p.out[job][(long)c * p.r + j] = out;
   else p.out[job][head_index(j, c, p.r, job == 0 ? p.hd0 : C)] = out;
+}
+
+template <int NS>
+__global__ __launch_bounds__(256) void skinny_stage2_kernel(SkinnyJobs p) {
+  stage2_elem<NS>(p, (long)blockIdx.x * 256 + threadIdx.x);
+}
+
+// Stage 2 of several layers in one launch. Block b belongs to item i with
+// bstart[i] <= b < bstart[i + 1] and is block b - bstart[i] of that item's
+// own stage-2 grid, so every output is the same sum in the same order as in
+// a launch of its own.
+struct FinishBatch {
+  SkinnyJobs job[kFinishBatch];
+  int bstart[kFinishBatch + 1];
+  int n;
+};
+
+template <int NS>
+__global__ __launch_bounds__(256) void finish_batch_kernel(FinishBatch fb) {
+  const int b = blockIdx.x;
+  int i = 0;
+  while (i + 1 < fb.n && b >= fb.bstart[i + 1]) ++i;   // block-uniform
+  stage2_elem<NS>(fb.job[i], (long)(b - fb.bstart[i]) * 256 + threadIdx.x);
 }
 
 template <typename T>
@@ -78,12 +100,36 @@ void launch_skinny_stage1(int dtype, const SkinnyJobs& p, hipStream_t st) {
   else stage1_dispatch<BF16>(p, st);
 }
 
-void launch_skinny_stage2(const SkinnyJobs& p, hipStream_t st) {
+namespace {
+int stage2_blocks(const SkinnyJobs& p) {
   const long total = (long)p.r * p.C[0] + (p.njobs > 1 ? (long)p.r * p.C[1] : 0);
-  const dim3 grid((unsigned)((total + 255) / 256));
+  return (int)((total + 255) / 256);
+}
+}  // namespace
+
+void launch_skinny_stage2(const SkinnyJobs& p, hipStream_t st) {
+  const dim3 grid((unsigned)stage2_blocks(p));
   if (p.nsplit <= 8) skinny_stage2_kernel<8><<<grid, 256, 0, st>>>(p);
   else if (p.nsplit <= 16) skinny_stage2_kernel<16><<<grid, 256, 0, st>>>(p);
   else skinny_stage2_kernel<kSkMaxSplit><<<grid, 256, 0, st>>>(p);
+}
+
+void launch_finish_batch(const SkinnyJobs* jobs, int n, hipStream_t st) {
+  for (int i0 = 0; i0 < n; i0 += kFinishBatch) {
+    FinishBatch fb{};
+    fb.n = n - i0 < kFinishBatch ? n - i0 : kFinishBatch;
+    int maxsplit = 1;
+    fb.bstart[0] = 0;
+    for (int i = 0; i < fb.n; ++i) {
+      fb.job[i] = jobs[i0 + i];
+      fb.bstart[i + 1] = fb.bstart[i] + stage2_blocks(jobs[i0 + i]);
+      maxsplit = jobs[i0 + i].nsplit > maxsplit ? jobs[i0 + i].nsplit : maxsplit;
+    }
+    const dim3 grid((unsigned)fb.bstart[fb.n]);
+    if (maxsplit <= 8) finish_batch_kernel<8><<<grid, 256, 0, st>>>(fb);
+    else if (maxsplit <= 16) finish_batch_kernel<16><<<grid, 256, 0, st>>>(fb);
+    else finish_batch_kernel<kSkMaxSplit><<<grid, 256, 0, st>>>(fb);
+  }
 }
 
 }  // namespace qlora

@@ -303,3 +303,30 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(Q, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="missing"):
         Q.lib()
+
+
+def test_finish_batch_fails_before_launch(lib):
+    # every item is validated before anything is enqueued: an error in the
+    # last item launches nothing for the first ones (no GPU is needed here)
+    lin, bad = _lin(), _lin(r=0)
+    n = ctypes.c_size_t()
+    lib.qlora_bwd_workspace(ctypes.byref(lin), 64, Q.QLORA_BF16, ctypes.byref(n))
+
+    def items(*specs):
+        arr = (Q.qlora_finish_item * len(specs))()
+        for i, (L, ws_bytes, dA) in enumerate(specs):
+            arr[i] = Q.qlora_finish_item(ctypes.cast(ctypes.pointer(L), ctypes.c_void_p), 64,
+                                         Q.QLORA_BF16, dA, FAKE, FAKE, ws_bytes)
+        return arr
+
+    good = (lin, n.value, FAKE)
+    assert lib.qlora_bwd_finish_batch(None, 1, None) == Q.QLORA_EINVAL
+    assert lib.qlora_bwd_finish_batch(items(good), 0, None) == Q.QLORA_EINVAL
+    assert lib.qlora_bwd_finish_batch(items(good, (lin, n.value - 1, FAKE)), 2,
+                                      None) == Q.QLORA_EWORKSPACE
+    assert lib.qlora_bwd_finish_batch(items(good, good, (bad, n.value, FAKE)), 3,
+                                      None) == Q.QLORA_EINVAL
+    assert lib.qlora_bwd_finish_batch(items(good, (lin, n.value, FAKE + 4)), 2,
+                                      None) == Q.QLORA_EINVAL
+    assert lib.qlora_bwd_finish_batch(items(good, (lin, n.value, None)), 2,
+                                      None) == Q.QLORA_EINVAL
