@@ -630,7 +630,9 @@ __global__ __launch_bounds__(256) void row_split_tsum_kernel(int M, int r, int S
 }
 
 // ---- many short rows, forward modes: RW rows per wave ---------------------
-// For grids of more than one block per compute unit, each wave takes RW
+// For grids of more than two blocks per compute unit (the multiple is kept
+// at 512 blocks or more: 768-wide rows of 4096 ran faster as 512 blocks of
+// two rows per wave than as 256 of four), each wave takes RW
 // rows (L <= 512 NHC, held in registers) instead of one, so every adapter
 // value read from LDS serves RW rows and a block stages the adapter once for
 // 4 RW rows. Same chunk mapping, slices, abs-max and sums as row_kernel, per
@@ -806,7 +808,7 @@ void row_launch(const void* rows, int M, int L, const float* W, int hd, int r,
       constexpr int RWM = row_multi_max<T, R>();
       const int nhc = L <= 1024 ? 2 : L <= 2048 ? 4 : 8;   // held chunks per row
       int rw = 1;
-      while (rw < RWM && rw * 2 * nhc <= 16 && (M + 8 * rw - 1) / (8 * rw) >= 256) rw *= 2;
+      while (rw < RWM && rw * 2 * nhc <= 16 && (M + 8 * rw - 1) / (8 * rw) >= 512) rw *= 2;
       if (rw > 1) {
         const dim3 mgrid((M + kRowsPerBlock * rw - 1) / (kRowsPerBlock * rw));
         if constexpr (RWM >= 2)

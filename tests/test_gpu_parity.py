@@ -161,12 +161,13 @@ SMALL = [
     (2, 3, 20480, 32, 8),       # rows past the held length (streaming row pass)
     (2, 17, 6160, 32, 3),       # long rows split over k: rank 3 of 4, 17 rows of 16-row blocks, 16-entry last slice
     (1, 9, 8208, 32, 5),        # float32 long rows split over k, rank 5 of 8
-    (2, 4100, 96, 48, 8),       # four rows per wave in the row pass, ragged last block
+    (2, 4100, 96, 48, 8),       # two rows per wave in the row pass, ragged last block
+    (2, 8200, 96, 48, 8),       # four rows per wave in the row pass, ragged last block
     (2, 2100, 1040, 336, 8),    # 128 x 64 backward tiles: ragged rows, k tile and last stage
     (2, 1, 256, 4096, 8),       # one row: input gradient split 4 ways
     (2, 1, 4112, 64, 4),        # one row: long-row pass, forward split 2 ways with a ragged k tail
-    (2, 2050, 1552, 32, 16),    # two rows per wave at rank 16, three held chunks
-    (1, 2052, 640, 32, 2),      # float32 rows, two per wave
+    (2, 4100, 1552, 32, 16),    # two rows per wave at rank 16, three held chunks
+    (1, 4100, 640, 32, 2),      # float32 rows, two per wave
     (3, 4098, 3072, 16, 4),     # two rows per wave over eight held chunks
     (5, 1, 128, 16, 4),
     (5, 77, 256, 272, 8),
