@@ -106,8 +106,9 @@ class Layer:
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(each GPU would run the same step on its own rows; see DESIGN.md)",
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(data-parallel, each GPU would run the same step on its own rows and "
+              "all-reduce the adapter gradients)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -31,7 +31,7 @@ Sources (page title, then section):
   comments on 4-bit frozen weights under an fp32 adapter, the transposed
   product needed for gradients, dequantize-add-requantize to merge.
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
 
 * int8 weight scale = abs-max of the output channel / 127 (a step size),
   codes = round-half-even(w * (127 / absmax)), symmetric range [-127, 127];
