@@ -212,7 +212,7 @@ def main():
     # The timed step runs each layer's backward as qlora_bwd_partial (dx and
     # the adapter-gradient partial sums, into a workspace of its own) and
     # takes every layer's dA and dB at the end with qlora_bwd_finish_batch
-    # (one launch per 16 layers) instead of one combine launch per layer.
+    # (one launch per 32 layers) instead of one combine launch per layer.
     bws = [torch.empty((max(l.bwd_ws, 256),), dtype=torch.uint8, device=dev) for l in layers]
     items = (Q.qlora_finish_item * len(layers))()
     for i, l in enumerate(layers):

@@ -262,7 +262,7 @@ typedef struct {
   size_t ws_bytes;
 } qlora_finish_item;
 
-/* qlora_bwd_finish for `count` layers (count >= 1) in one launch per 16
+/* qlora_bwd_finish for `count` layers (count >= 1) in one launch per 32
  * layers, for a backward pass that runs qlora_bwd_partial layer by layer and
  * takes every adapter gradient ("Why does LoRA reduce memory footprint?":
  * only the adapter's A and B get gradients) at the end. Each layer's dA and

@@ -333,7 +333,7 @@ def qlora_bwd_partial(layer: QLinear, x, dy, t=None, need_dx: bool = True, dx=No
 
 
 def qlora_bwd_finish_batch(items, stream=None):
-    """qlora_bwd_finish for several layers in one launch (per 16 layers).
+    """qlora_bwd_finish for several layers in one launch (per 32 layers).
     items: (layer, M, dtype, ws) or (layer, M, dtype, ws, dA, dB) tuples, each
     ws holding that layer's qlora_bwd_partial results (distinct workspaces).
     Returns the list of (dA, dB)."""

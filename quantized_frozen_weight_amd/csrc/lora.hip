@@ -17,8 +17,28 @@ __global__ __launch_bounds__(256) void skinny_stage1_kernel(SkinnyJobs p) {
 // out = s * sum over splits (split order fixed); one thread per (job, j, c),
 // NS loads in flight at a time (NS: the split count rounded up to 8, 16 or 32,
 // so no load is wasted on a clamped duplicate).
-template <int NS>
-__device__ __forceinline__ void stage2_elem(const SkinnyJobs& p, long e0) {
+// What stage 2 reads of a SkinnyJobs (the batched launch carries only this).
+struct Stage2Job {
+  float* partial[2];
+  float* out[2];
+  int C[2];
+  int transpose[2];
+  int hd0, njobs, r, nsplit;
+  float s;
+};
+
+inline Stage2Job stage2_job(const SkinnyJobs& p) {
+  Stage2Job q{};
+  for (int i = 0; i < 2; ++i) {
+    q.partial[i] = p.partial[i]; q.out[i] = p.out[i];
+    q.C[i] = p.C[i]; q.transpose[i] = p.transpose[i];
+  }
+  q.hd0 = p.hd0; q.njobs = p.njobs; q.r = p.r; q.nsplit = p.nsplit; q.s = p.s;
+  return q;
+}
+
+template <int NS, typename J>
+__device__ __forceinline__ void stage2_elem(const J& p, long e0) {
   const long n0 = (long)p.r * p.C[0];
   const int job = e0 < n0 ? 0 : 1;
   const long e = job ? e0 - n0 : e0;
@@ -44,25 +64,26 @@ __device__ __forceinline__ void stage2_elem(const SkinnyJobs& p, long e0) {
 
 template <int NS>
 __global__ __launch_bounds__(256) void skinny_stage2_kernel(SkinnyJobs p) {
-  stage2_elem<NS>(p, (long)blockIdx.x * 256 + threadIdx.x);
+  stage2_elem<NS, SkinnyJobs>(p, (long)blockIdx.x * 256 + threadIdx.x);
 }
 
 // Stage 2 of several layers in one launch. Block b belongs to item i with
 // bstart[i] <= b < bstart[i + 1] and is block b - bstart[i] of that item's
 // own stage-2 grid, so every output is the same sum in the same order as in
 // a launch of its own.
-struct FinishBatch {
-  SkinnyJobs job[kFinishBatch];
+struct FinishBatch {   // kernel arguments: kept under 4 KiB
+  Stage2Job job[kFinishBatch];
   int bstart[kFinishBatch + 1];
   int n;
 };
+static_assert(sizeof(FinishBatch) <= 4096, "kernel arguments");
 
 template <int NS>
 __global__ __launch_bounds__(256) void finish_batch_kernel(FinishBatch fb) {
   const int b = blockIdx.x;
   int i = 0;
   while (i + 1 < fb.n && b >= fb.bstart[i + 1]) ++i;   // block-uniform
-  stage2_elem<NS>(fb.job[i], (long)(b - fb.bstart[i]) * 256 + threadIdx.x);
+  stage2_elem<NS, Stage2Job>(fb.job[i], (long)(b - fb.bstart[i]) * 256 + threadIdx.x);
 }
 
 template <typename T>
@@ -121,7 +142,7 @@ void launch_finish_batch(const SkinnyJobs* jobs, int n, hipStream_t st) {
     int maxsplit = 1;
     fb.bstart[0] = 0;
     for (int i = 0; i < fb.n; ++i) {
-      fb.job[i] = jobs[i0 + i];
+      fb.job[i] = stage2_job(jobs[i0 + i]);
       fb.bstart[i + 1] = fb.bstart[i] + stage2_blocks(jobs[i0 + i]);
       maxsplit = jobs[i0 + i].nsplit > maxsplit ? jobs[i0 + i].nsplit : maxsplit;
     }

@@ -20,7 +20,7 @@ namespace qlora {
 
 constexpr int kSkCols = 256;       // columns per stage-1 block (64 lanes x 4)
 constexpr int kSkMaxSplit = 32;
-constexpr int kFinishBatch = 16;   // layers per launch of the batched stage 2
+constexpr int kFinishBatch = 32;   // layers per launch of the batched stage 2
 constexpr int kSkGroup = 8;        // rows whose loads are in flight together
 
 struct SkinnyJobs {

@@ -1,10 +1,10 @@
 """qlora_bwd_finish_batch: the adapter gradients of many layers in one launch
-per 16 layers, bitwise equal to each layer's own qlora_bwd.
+per 32 layers, bitwise equal to each layer's own qlora_bwd.
 
 The layers mix every backward path (64-row and 128-wide int8 tiles, the split
 contraction, 4-bit, float32) and split counts from 1 to 65, so one launch
 holds jobs of different split counts (each still summed in its own split
-order), and 21 layers take two launches.
+order), and 35 layers take two launches.
 """
 
 from __future__ import annotations
@@ -41,7 +41,7 @@ SPECS = [
     (5, 77, 256, 272, 8),       # 4-bit
     (1, 130, 128, 144, 16),     # float32
     (2, 4100, 96, 48, 8),       # 65 row blocks: more than one pass of loads
-] + [(2, 33 + 7 * i, 64, 48 + 16 * (i % 3), 1 + i % 8) for i in range(15)]
+] + [(2, 33 + 7 * i, 64, 48 + 16 * (i % 3), 1 + i % 8) for i in range(29)]
 
 
 def layer(spec):
