@@ -213,12 +213,22 @@ def main():
     # the adapter-gradient partial sums, into a workspace of its own) and
     # takes every layer's dA and dB at the end with qlora_bwd_finish_batch
     # (one launch per 32 layers) instead of one combine launch per layer.
-    bws = [torch.empty((max(l.bwd_ws, 256),), dtype=torch.uint8, device=dev) for l in layers]
+    # The workspaces are packed: the layer run k-th (the backward runs the
+    # layers in reverse) starts where the partial sums of the layers run
+    # before it end, so its scratch lies only over layers not yet run.
+    offs, o, total = {}, 0, 256
+    for i in reversed(range(len(layers))):
+        offs[i] = o
+        total = max(total, o + layers[i].bwd_ws)
+        o += Q.qlora_bwd_partials_bytes(layers[i].lin, M, layers[i].dt)
+    bpack = torch.empty((total,), dtype=torch.uint8, device=dev)
+    bws_ptr = [bpack.data_ptr() + offs[i] for i in range(len(layers))]
+    bws_n = [layers[i].bwd_ws for i in range(len(layers))]
     items = (Q.qlora_finish_item * len(layers))()
     for i, l in enumerate(layers):
         items[i] = Q.qlora_finish_item(ctypes.cast(ctypes.pointer(l.cs), ctypes.c_void_p), M,
                                        l.dt, l.dA.data_ptr(), l.dB.data_ptr(),
-                                       bws[i].data_ptr(), bws[i].numel())
+                                       bws_ptr[i], bws_n[i])
 
     def step_batched():
         st = torch.cuda.current_stream().cuda_stream
@@ -229,7 +239,7 @@ def main():
             l = layers[i]
             check(lib.qlora_bwd_partial(ctypes.byref(l.cs), M, l.dt, l.x.data_ptr(),
                                         l.dy.data_ptr(), l.t.data_ptr(), l.dx.data_ptr(),
-                                        bws[i].data_ptr(), bws[i].numel(), st), "bwd_partial")
+                                        bws_ptr[i], bws_n[i], st), "bwd_partial")
         check(lib.qlora_bwd_finish_batch(items, len(layers), st), "finish_batch")
 
     # eager warm-up (also loads every kernel)

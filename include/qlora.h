@@ -276,6 +276,17 @@ typedef struct {
 int qlora_bwd_finish_batch(const qlora_finish_item* items, int count,
                            void* stream);
 
+/* Bytes at the start of a qlora_bwd workspace (M rows) that hold the partial
+ * sums qlora_bwd_partial leaves for qlora_bwd_finish; the rest of the
+ * workspace is scratch only while a call runs. So for qlora_bwd_finish_batch
+ * a caller that runs the layers' qlora_bwd_partial in the order k = 0, 1, ...
+ * may put layer k's workspace at base + the sum of partials_bytes over the
+ * layers run before it (instead of a full workspace per layer): each call's
+ * scratch then lies only over bytes of layers that have not run yet. The
+ * value is a multiple of 256. */
+int qlora_bwd_partials_bytes(const qlora_linear* L, int M, int dtype,
+                             size_t* bytes);
+
 /* qlora_fwd / qlora_bwd with timing marks, for timing the call's main
  * product kernel live: the int8 or 4-bit forward product; the fused int8
  * backward (dx, u and the adapter-gradient partial sums) or, on the other

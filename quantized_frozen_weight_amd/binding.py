@@ -54,6 +54,7 @@ EXPORTS = (
     "qlora_quantize_rows", "qlora_fwd_acc", "qlora_fwd_timed", "qlora_bwd_timed",
     "qlora_merge", "qlora_bwd_partial", "qlora_bwd_finish", "qlora_fwd_a8w4",
     "qlora_quantize_heads", "qlora_outlier_layout", "qlora_bwd_finish_batch",
+    "qlora_bwd_partials_bytes",
 )
 
 
@@ -98,6 +99,7 @@ def lib() -> ctypes.CDLL:
     L.qlora_bwd_partial.argtypes = [plin, i, i, vp, vp, vp, vp, vp, sz, vp]
     L.qlora_bwd_finish.argtypes = [plin, i, i, vp, vp, vp, sz, vp]
     L.qlora_bwd_finish_batch.argtypes = [ctypes.POINTER(qlora_finish_item), i, vp]
+    L.qlora_bwd_partials_bytes.argtypes = [plin, i, i, psz]
     L.qlora_fwd_a8w4.argtypes = [plin, i, i, vp, vp, vp, vp, sz, vp]
     L.qlora_quantize_heads.argtypes = [vp, i, i, i, i, vp, vp, vp]
     L.qlora_outlier_layout.argtypes = [i, i, psz, psz, psz, ctypes.POINTER(ctypes.c_int32)]
@@ -330,6 +332,15 @@ def qlora_bwd_partial(layer: QLinear, x, dy, t=None, need_dx: bool = True, dx=No
                                    _stream() if stream is None else stream.cuda_stream),
            "qlora_bwd_partial")
     return (dx if need_dx else None), ws
+
+
+def qlora_bwd_partials_bytes(layer: QLinear, M: int, dtype: int) -> int:
+    """Leading bytes of a backward workspace that outlive qlora_bwd_partial."""
+    n = ctypes.c_size_t()
+    s = layer.cstruct()
+    _check(lib().qlora_bwd_partials_bytes(ctypes.byref(s), M, dtype, ctypes.byref(n)),
+           "qlora_bwd_partials_bytes")
+    return n.value
 
 
 def qlora_bwd_finish_batch(items, stream=None):

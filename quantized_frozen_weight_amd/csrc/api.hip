@@ -104,10 +104,12 @@ inline size_t partial_floats(int M, int r, int C) {
 BwdLayout bwd_layout(const qlora_linear* L, int M, int dtype) {
   BwdLayout w{};
   size_t off = 0;
-  w.t = off; off = align_up(off + (size_t)M * L->r * 4);
-  w.u = off; off = align_up(off + (size_t)M * L->r * 4);
+  // the partial sums first: they are the only bytes that outlive a call
+  // (qlora_bwd_partials_bytes), everything after them is scratch
   w.pB = off; off = align_up(off + partial_floats(M, L->r, L->N) * 4);
   w.pA = off; off = align_up(off + partial_floats(M, L->r, L->K) * 4);
+  w.t = off; off = align_up(off + (size_t)M * L->r * 4);
+  w.u = off; off = align_up(off + (size_t)M * L->r * 4);
   // split contraction of the bf16 input gradient (0 bytes when it does not split)
   size_t fdx = 0, fu = 0;
   if (dtype == QLORA_BF16) bwd_split_sizes(M, L->K, L->N, L->r, &fdx, &fu);
@@ -419,6 +421,14 @@ int qlora_bwd_finish(const qlora_linear* L, int M, int dtype, float* dA, float* 
   (void)hipGetLastError();
   launch_skinny_stage2(finish_jobs(L, M, dtype, dA, dB, ws), static_cast<hipStream_t>(stream));
   return launch_status();
+}
+
+int qlora_bwd_partials_bytes(const qlora_linear* L, int M, int dtype, size_t* bytes) {
+  if (!bytes) return QLORA_EINVAL;
+  const int st = check_linear(L, M, dtype);
+  if (st) return st;
+  *bytes = bwd_layout(L, M, dtype).t;
+  return QLORA_OK;
 }
 
 int qlora_bwd_finish_batch(const qlora_finish_item* items, int count, void* stream) {

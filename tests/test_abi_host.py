@@ -330,3 +330,21 @@ def test_finish_batch_fails_before_launch(lib):
                                       None) == Q.QLORA_EINVAL
     assert lib.qlora_bwd_finish_batch(items(good, (lin, n.value, None)), 2,
                                       None) == Q.QLORA_EINVAL
+
+
+def test_partials_bytes(lib):
+    # the partial sums of dB and dA lead the backward workspace: one per block
+    # of 64 rows, [r, N] and [r, K] float32, each rounded up to 256 bytes
+    n = ctypes.c_size_t()
+    for K, N, r, M in ((256, 256, 4, 64), (1024, 784, 8, 1000), (2048, 16384, 8, 512)):
+        lin = _lin(K=K, N=N, r=r)
+        assert lib.qlora_bwd_partials_bytes(ctypes.byref(lin), M, Q.QLORA_F32,
+                                            ctypes.byref(n)) == Q.QLORA_OK
+        up = lambda b: (b + 255) // 256 * 256
+        blocks = (M + 63) // 64
+        assert n.value == up(blocks * r * N * 4) + up(blocks * r * K * 4)
+        assert n.value < _bwd_ws(lib, lin, M, Q.QLORA_F32)
+    assert lib.qlora_bwd_partials_bytes(ctypes.byref(_lin(r=0)), 64, Q.QLORA_F32,
+                                        ctypes.byref(n)) == Q.QLORA_EINVAL
+    assert lib.qlora_bwd_partials_bytes(ctypes.byref(_lin()), 64, Q.QLORA_F32,
+                                        None) == Q.QLORA_EINVAL

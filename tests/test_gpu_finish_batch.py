@@ -55,15 +55,31 @@ def layer(spec):
     return lin, x, dy
 
 
-def test_finish_batch_matches_per_layer_backward():
-    print(f"[case] finish batch: {len(SPECS)} layers", file=sys.stderr, flush=True)
+@pytest.mark.parametrize("packed", [False, True], ids=["own workspaces", "packed workspaces"])
+def test_finish_batch_matches_per_layer_backward(packed):
+    print(f"[case] finish batch: {len(SPECS)} layers, packed={packed}", file=sys.stderr,
+          flush=True)
     layers = [layer(s) for s in SPECS]
-    refs, items = [], []
+    refs, items, ts = [], [], []
     for lin, x, dy in layers:
         _, t = Q.qlora_fwd(lin, x)
         _, dA, dB = Q.qlora_bwd(lin, x, dy, t=t)
         refs.append((dA, dB))
-        _, ws = Q.qlora_bwd_partial(lin, x, dy, t=t)   # a workspace per layer
+        ts.append(t)
+    # packed: layer k's workspace starts where the partial sums of layers
+    # 0..k-1 end (they run in that order), and the scratch of each call lies
+    # over the layers after it
+    views, o, total = [], 0, 0
+    for lin, x, _ in layers:
+        dt = Q.QLORA_F32 if x.dtype == torch.float32 else Q.QLORA_BF16
+        need = Q.qlora_bwd_workspace(lin, x.shape[0], dt)
+        views.append((o, need))
+        total = max(total, o + need)
+        o += Q.qlora_bwd_partials_bytes(lin, x.shape[0], dt)
+    pack = torch.empty((total,), dtype=torch.uint8, device="cuda")
+    for (lin, x, dy), t, (off, need) in zip(layers, ts, views):
+        ws = pack[off:off + need] if packed else None   # else a workspace per layer
+        _, ws = Q.qlora_bwd_partial(lin, x, dy, t=t, ws=ws)
         items.append((lin, x.shape[0], x.dtype, ws))
     got = Q.qlora_bwd_finish_batch(items)
     torch.cuda.synchronize()
