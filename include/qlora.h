@@ -82,8 +82,13 @@
  *     the matching *_workspace query; it may be reused between calls that are
  *     ordered on one stream.
  *   - Arguments are validated before anything is launched; a non-OK status
- *     means nothing was enqueued. Device faults surface at the caller's next
- *     synchronization.
+ *     means nothing was enqueued, except QLORA_EHIP from a launch the
+ *     runtime rejected (earlier launches of the same call may then be
+ *     queued). Device faults surface at the caller's next synchronization.
+ *   - A HIP error that earlier work on the calling thread left pending
+ *     (hipPeekAtLastError) is neither cleared nor blamed on the library: a
+ *     call that would launch returns QLORA_EHIP at once, enqueues nothing
+ *     and leaves the error for the caller to read with hipGetLastError.
  *   - Constraints: 1 <= M, 16 <= K, 16 <= N, K % 16 == 0, N % 16 == 0,
  *     1 <= r <= 32, all pointers 16-byte aligned; QLORA_W4G128 needs
  *     K % 128 == 0 and the bf16 compute dtype (EINVAL / EUNSUPPORTED
@@ -116,7 +121,8 @@ typedef enum {
   QLORA_EUNSUPPORTED = 2, /* valid but not implemented (e.g. W4 with f32) */
   QLORA_EWORKSPACE = 3,   /* ws smaller than the *_workspace query */
   QLORA_ERANGE = 4,       /* size products overflow the index range */
-  QLORA_EHIP = 5          /* a kernel launch was rejected by the runtime */
+  QLORA_EHIP = 5          /* a kernel launch was rejected by the runtime, or
+                             a HIP error was already pending (see below) */
 } qlora_status;
 
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
@@ -267,9 +273,13 @@ typedef struct {
  * takes every adapter gradient ("Why does LoRA reduce memory footprint?":
  * only the adapter's A and B get gradients) at the end. Each layer's dA and
  * dB are bitwise those of its own qlora_bwd_finish (or qlora_bwd): the same
- * sums in the same order. The items' workspaces must be distinct and each
- * must hold its layer's qlora_bwd_partial results, ordered before this call
- * on `stream`; items[] is read during the call only (host memory). Every
+ * sums in the same order. Each item's partial sums -- the first
+ * qlora_bwd_partials_bytes bytes of its workspace -- must not overlap any
+ * other item's, and must hold that layer's qlora_bwd_partial results,
+ * ordered before this call on `stream`; the rest of an item's workspace (its
+ * scratch, dead once that qlora_bwd_partial has completed) may overlap other
+ * items' partial sums, as the packing described at qlora_bwd_partials_bytes
+ * does; items[] is read during the call only (host memory). Every
  * item is validated as by qlora_bwd_finish before anything is enqueued; the
  * first failing item's status is returned (EINVAL also for items == NULL
  * or count < 1). */

@@ -14,9 +14,9 @@ from dataclasses import dataclass
 from typing import Optional, Tuple
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# QLORA_LIB may point at another build of the same library (e.g. a tuning
-# variant); by default the in-tree build next to this file is loaded.
-LIB_PATH = os.environ.get("QLORA_LIB") or os.path.join(HERE, "libqlora.so")
+# Always the in-tree build next to this file (python -m
+# quantized_frozen_weight_amd.build_lib); no other copy is ever loaded.
+LIB_PATH = os.path.join(HERE, "libqlora.so")
 
 QLORA_OK, QLORA_EINVAL, QLORA_EUNSUPPORTED, QLORA_EWORKSPACE, QLORA_ERANGE, QLORA_EHIP = range(6)
 QLORA_F32, QLORA_BF16 = 0, 1
@@ -346,7 +346,9 @@ def qlora_bwd_partials_bytes(layer: QLinear, M: int, dtype: int) -> int:
 def qlora_bwd_finish_batch(items, stream=None):
     """qlora_bwd_finish for several layers in one launch (per 32 layers).
     items: (layer, M, dtype, ws) or (layer, M, dtype, ws, dA, dB) tuples, each
-    ws holding that layer's qlora_bwd_partial results (distinct workspaces).
+    ws holding that layer's qlora_bwd_partial results. The items' partial
+    sums (the first qlora_bwd_partials_bytes of each ws) must not overlap;
+    the scratch past them may (packed workspaces).
     Returns the list of (dA, dB)."""
     import torch
     arr = (qlora_finish_item * len(items))()

@@ -128,6 +128,17 @@ void mark(void* ev, hipStream_t s) {
   if (ev != nullptr) (void)hipEventRecord(static_cast<hipEvent_t>(ev), s);
 }
 
+// Before a call enqueues anything: a HIP error that earlier work of the
+// caller left pending is not ours to clear, and launching on top of it would
+// blame it on this call. The call returns QLORA_EHIP, enqueues nothing and
+// leaves the error in place for the caller.
+int pending_error() {
+  return hipPeekAtLastError() == hipSuccess ? QLORA_OK : QLORA_EHIP;
+}
+
+// After a call's launches: nothing was pending before them (pending_error),
+// so an error now is one of this call's launches; it is reported and
+// cleared.
 int launch_status() {
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? QLORA_OK : QLORA_EHIP;
@@ -218,7 +229,7 @@ int qlora_quantize_heads(const float* W, int heads, int K, int N, int fmt,
   if (!W || !codes || !scales || !aligned16(W) || !aligned16(codes) || !aligned16(scales))
     return QLORA_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
+  if (pending_error()) return QLORA_EHIP;
   if (fmt == QLORA_W8)
     launch_quantize_w8(W, K, N, hd, static_cast<int8_t*>(codes),
                        static_cast<float*>(scales), s);
@@ -250,7 +261,7 @@ int qlora_fwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
   if (ws_bytes < w.total || (w.total && (!ws || !aligned16(ws)))) return QLORA_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* t = t_save ? t_save : reinterpret_cast<float*>(at(ws, w.t));
-  (void)hipGetLastError();
+  if (pending_error()) return QLORA_EHIP;
   if (L->fmt == QLORA_W8) {
     int8_t* xq = reinterpret_cast<int8_t*>(at(ws, w.xq));
     float* sx = reinterpret_cast<float*>(at(ws, w.sx));
@@ -308,7 +319,7 @@ int qlora_fwd_a8w4(const qlora_linear* L, int M, int dtype, const void* x, void*
   float* t = t_save ? t_save : reinterpret_cast<float*>(at(ws, w.t));
   int8_t* xq = reinterpret_cast<int8_t*>(at(ws, w.xq));
   float* sx = reinterpret_cast<float*>(at(ws, w.sx));
-  (void)hipGetLastError();
+  if (pending_error()) return QLORA_EHIP;
   launch_rowquant(dtype, x, M, L->K, L->A, L->r, xq, sx, t, s, nullptr,
                   reinterpret_cast<float*>(at(ws, w.rs)));
   launch_gemm_fwd_a8w4(M, L->N, L->K, xq, sx, static_cast<const uint8_t*>(L->codes),
@@ -341,7 +352,7 @@ int qlora_bwd_partial_timed(const qlora_linear* L, int M, int dtype, const void*
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float sc = lora_s(L);
   float* u = reinterpret_cast<float*>(at(ws, w.u));
-  (void)hipGetLastError();
+  if (pending_error()) return QLORA_EHIP;
   const float* t = t_saved;
   if (t == nullptr) {
     float* tw = reinterpret_cast<float*>(at(ws, w.t));
@@ -418,7 +429,7 @@ int qlora_bwd_finish(const qlora_linear* L, int M, int dtype, float* dA, float* 
                      void* ws, size_t ws_bytes, void* stream) {
   const int st = finish_check(L, M, dtype, dA, dB, ws, ws_bytes);
   if (st) return st;
-  (void)hipGetLastError();
+  if (pending_error()) return QLORA_EHIP;
   launch_skinny_stage2(finish_jobs(L, M, dtype, dA, dB, ws), static_cast<hipStream_t>(stream));
   return launch_status();
 }
@@ -438,7 +449,7 @@ int qlora_bwd_finish_batch(const qlora_finish_item* items, int count, void* stre
     const int st = finish_check(it.L, it.M, it.dtype, it.dA, it.dB, it.ws, it.ws_bytes);
     if (st) return st;
   }
-  (void)hipGetLastError();
+  if (pending_error()) return QLORA_EHIP;
   SkinnyJobs sk[kFinishBatch];
   for (int i0 = 0; i0 < count; i0 += kFinishBatch) {
     const int n = count - i0 < kFinishBatch ? count - i0 : kFinishBatch;
@@ -490,7 +501,7 @@ int qlora_merge(const qlora_linear* L, void* codes_out, void* scales_out,
       overlaps(codes_out, cb, scales_out, sb))
     return QLORA_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
+  if (pending_error()) return QLORA_EHIP;
   launch_merge_w8(static_cast<const int8_t*>(L->codes), static_cast<const float*>(L->scales),
                   L->A, L->B, head_width(L), L->K, L->N, L->r, lora_s(L),
                   static_cast<int8_t*>(codes_out), static_cast<float*>(scales_out), s);
@@ -505,7 +516,7 @@ int qlora_quantize_rows(const void* x, int M, int K, int dtype, int8_t* xq,
   if (!fits_int(M, K)) return QLORA_ERANGE;
   if (!x || !xq || !sx || !aligned16(x) || !aligned16(xq) || !aligned16(sx))
     return QLORA_EINVAL;
-  (void)hipGetLastError();
+  if (pending_error()) return QLORA_EHIP;
   launch_rowquant(dtype, x, M, K, nullptr, 1, xq, sx, nullptr,
                   static_cast<hipStream_t>(stream));
   return launch_status();
@@ -522,7 +533,7 @@ int qlora_fwd_acc(const qlora_linear* L, int M, int dtype, const void* x,
   hipStream_t s = static_cast<hipStream_t>(stream);
   int8_t* xq = reinterpret_cast<int8_t*>(at(ws, w.xq));
   float* sx = reinterpret_cast<float*>(at(ws, w.sx));
-  (void)hipGetLastError();
+  if (pending_error()) return QLORA_EHIP;
   launch_rowquant(dtype, x, M, L->K, nullptr, 1, xq, sx, nullptr, s);
   // the integer product alone: no scale is read
   launch_gemm_fwd_w8(dtype, M, L->N, L->K, xq,
