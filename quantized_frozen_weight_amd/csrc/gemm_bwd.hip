@@ -110,6 +110,48 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
+// Two float32 values each as a sum of three bf16 values, v = hi + mid + lo:
+// hi is the bf16 nearest to v, mid the bf16 nearest to the remainder
+// v - hi, lo the bf16 nearest to v - hi - mid (both remainders exact in
+// float32). Products with a bf16 operand on the matrix cores then carry v to
+// float32 precision (relative error at most 2^-24) instead of 8 significant
+// bits, which keeps the float32 adapter's gradients float32-accurate: B (for
+// u = dy B^T) and t (for dB = s t^T dy) enter their products as hi, mid and
+// lo columns of one operand. A non-finite hi (v infinite or NaN, or past the
+// bf16 range) takes mid = lo = 0, so hi alone carries the infinity or NaN.
+// Returns the packed hi pair; the mid and lo pairs go to mid2 and lo2.
+__device__ __forceinline__ uint32_t pk_bf16_split3(float a, float b, uint32_t& mid2, uint32_t& lo2) {
+  const uint32_t h = pk_bf16(a, b);
+  const bool fa = (h & 0x7f80u) != 0x7f80u, fb = (h & 0x7f800000u) != 0x7f800000u;
+  const float ra = fa ? a - __uint_as_float(h << 16) : 0.f;
+  const float rb = fb ? b - __uint_as_float(h & 0xffff0000u) : 0.f;
+  mid2 = pk_bf16(ra, rb);
+  lo2 = pk_bf16(ra - __uint_as_float(mid2 << 16), rb - __uint_as_float(mid2 & 0xffff0000u));
+  return h;
+}
+
+// The rank-r products u = dy B^T and dB^T = dy^T t run with 3R operand
+// columns: j in [0, R) the hi parts, [R, 2R) the mid parts, [2R, 3R) the lo
+// parts. The sum for rank j (j = cb * 16 + lane % 16 < R) of its columns j,
+// j + R, j + 2R of the accumulators (column c at block c / 16, lane c % 16 of
+// the 16-lane group): R = 4 and 8 put some of them in other lanes of the
+// group, read through a lane permute that every lane executes; for R >= 16
+// all three are the same lane of blocks cb, cb + R / 16, cb + R / 8.
+template <int R, int UCB>
+__device__ __forceinline__ float split3_sum(const f32x4 (&v)[UCB], int cb, int ii, int lane) {
+  if constexpr (R == 4) {
+    static_assert(UCB == 1, "12 columns in one block");
+    const int g = lane & ~15;
+    return v[0][ii] + __shfl(v[0][ii], g | ((lane + 4) & 15)) + __shfl(v[0][ii], g | ((lane + 8) & 15));
+  } else if constexpr (R == 8) {
+    static_assert(UCB == 2, "24 columns in two blocks");
+    return v[0][ii] + __shfl(v[0][ii], (lane & ~15) | ((lane + 8) & 15)) + v[1][ii];
+  } else {
+    static_assert(R % 16 == 0 && UCB == 3 * R / 16, "whole blocks per part");
+    return v[cb][ii] + v[cb + R / 16][ii] + v[cb + R / 8][ii];
+  }
+}
+
 // NR transposing LDS reads (ds_read_b64_tr_b16) issued together and completed
 // in the same asm block. Written as asm because the builtin form makes the
 // compiler wait for every direct-to-LDS load in flight (the ring's later
@@ -220,10 +262,11 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
   static_assert(RB == 64 || RB == 128, "code rows of 64 or 128 bytes");
   static_assert(S >= 3, "stage kt + 1 is resident while stage kt is used");
   static_assert(!W4 || BN == 128, "4-bit: one 128-wide k group per block");
-  constexpr int UCB = (R + 15) / 16;                  // u column blocks of 16
+  constexpr int UCB = (3 * R + 15) / 16;              // operand column blocks of 16: B (t) hi | mid | lo
+  constexpr int RCB = (R + 15) / 16;                  // column blocks of the ranks
   constexpr bool XPRE = BM * BN * 2 <= 8192;          // x tile kept outside the ring
   constexpr int CBSZ = BN * 128;                      // converted codes [BN][64] bf16
-  constexpr int BUSZ = UCB * 16 * 128;                // converted B [16 UCB][64] bf16
+  constexpr int BUSZ = UCB * 16 * 128;                // converted B [16 UCB][64] bf16: hi | mid | lo
   constexpr int TSZ = BM * R * 4;                     // t tile (pitch r)
   constexpr int XTSZ = BM * BN * 2;
   constexpr int AQSZ = BN * R * 4;                    // the block's rows of A [BN][r]
@@ -503,7 +546,13 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
     for (int q = 0; q < NBU; ++q) {
       const int e = ptid + 256 * q;
       const int j = e >> 5, p = e & 31;
-      if (e < R * 32) *reinterpret_cast<uint32_t*>(BU + swz128(j, p >> 2) + (p & 3) * 4) = pk_bf16(bq[q].x, bq[q].y);
+      if (e < R * 32) {
+        uint32_t mid2, lo2;
+        const uint32_t hi2 = pk_bf16_split3(bq[q].x, bq[q].y, mid2, lo2);
+        *reinterpret_cast<uint32_t*>(BU + swz128(j, p >> 2) + (p & 3) * 4) = hi2;
+        *reinterpret_cast<uint32_t*>(BU + swz128(R + j, p >> 2) + (p & 3) * 4) = mid2;
+        *reinterpret_cast<uint32_t*>(BU + swz128(2 * R + j, p >> 2) + (p & 3) * 4) = lo2;
+      }
     }
   };
 
@@ -538,7 +587,7 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
     for (int st = 0; st < S - 1; ++st)
       if (st < nk) issue(st, st);
     // BU rows past the rank stay zero for good
-    for (int e = R * 32 + ptid; e < UCB * 16 * 32; e += 256) {   // 4-byte pairs
+    for (int e = 3 * R * 32 + ptid; e < UCB * 16 * 32; e += 256) {   // 4-byte pairs
       const int off = swz128(e / 32, (e % 32) >> 2) + (e & 3) * 4;
       *reinterpret_cast<uint32_t*>(BU0 + off) = 0u;
       *reinterpret_cast<uint32_t*>(BU0 + BUSZ + off) = 0u;
@@ -569,10 +618,9 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
   }
 
   const int rows_here = M - m0 < BM ? M - m0 : BM;
-  // dB operand: t as bf16, lane -> rank (lane % 16), rows 32 c + 8 (lane / 16) + e
-  // (read back from LDS at the block's first dB stage)
-  bf16x8 tfr[UCB][BM / 32];
-  bool tfr_ready = false;
+  // dB operand: t split into bf16 hi, mid and lo columns, lane -> column
+  // (lane % 16), rows 32 c + 8 (lane / 16) + e; rebuilt from the t tile in
+  // LDS at each of the block's dB stages rather than held in registers
 
   int slot = 0;
   for (int kt = 0; kt < nk; ++kt) {
@@ -640,21 +688,29 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
       // 16-lane group, lanes 4 i + p fetch the 4 n at 16 w + 4 p of row i,
       // and lane q receives n = 16 w + q of rows 0..3.
       if (kt % a.tiles_x == kt_blk) {
-        if (!tfr_ready) {
-          tfr_ready = true;
+        bf16x8 tfr[UCB][BM / 32];
+        {
 #pragma unroll
           for (int cb = 0; cb < UCB; ++cb) {
-            const int j = cb * 16 + (lane & 15);
+            // column j: part j / R (hi, mid, lo) of t[., j % R]
+            const int j = cb * 16 + (lane & 15), part = j / R, jr = j - part * R;
 #pragma unroll
             for (int c = 0; c < BM / 32; ++c) {
               float v[8];
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
                 const int m = 32 * c + 8 * (lane >> 4) + e;
-                v[e] = j < r ? Ts[m * r + (j < r ? j : 0)] : 0.f;
+                v[e] = (jr < r && part < 3) ? Ts[m * r + (jr < r ? jr : 0)] : 0.f;
               }
-              tfr[cb][c] = __builtin_bit_cast(bf16x8, u32x4{pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]),
-                                                             pk_bf16(v[4], v[5]), pk_bf16(v[6], v[7])});
+              u32x4 hi, mid, lo;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                uint32_t me, le;
+                hi[e] = pk_bf16_split3(v[2 * e], v[2 * e + 1], me, le);
+                mid[e] = me;
+                lo[e] = le;
+              }
+              tfr[cb][c] = __builtin_bit_cast(bf16x8, part == 0 ? hi : part == 1 ? mid : lo);
             }
           }
         }
@@ -683,14 +739,13 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
             dbacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dyT, tfr[cb][c], dbacc[cb], 0, 0, 0);
         }
 #pragma unroll
-        for (int cb = 0; cb < UCB; ++cb) {
+        for (int cb = 0; cb < RCB; ++cb) {
           const int j = cb * 16 + (lane & 15);
-          if (j < r) {
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-              const int gn = kt * KC + 16 * wid + 4 * (lane >> 4) + ii;
-              if (gn < N) a.partB[((long)mt * r + j) * N + gn] = dbacc[cb][ii];
-            }
+          for (int ii = 0; ii < 4; ++ii) {
+            const float dbv = split3_sum<R, UCB>(dbacc, cb, ii, lane);
+            const int gn = kt * KC + 16 * wid + 4 * (lane >> 4) + ii;
+            if (j < r && gn < N) a.partB[((long)mt * r + j) * N + gn] = dbv;
           }
         }
       }
@@ -709,12 +764,13 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
     for (int i = 0; i < FM; ++i) {
       if ((i & 1) != wn) continue;
 #pragma unroll
-      for (int cb = 0; cb < UCB; ++cb) {
+      for (int cb = 0; cb < RCB; ++cb) {
         const int j = cb * 16 + (lane & 15);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
+          const float uv = split3_sum<R, UCB>(uacc[i >> 1], cb, ii, lane);
           const int ml = wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + ii;
-          if (j < R) E[ml * R + j] = j < r ? uacc[i >> 1][cb][ii] : 0.f;
+          if (j < R) E[ml * R + j] = j < r ? uv : 0.f;
         }
       }
     }
@@ -782,10 +838,11 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
                 "4-bit: one 128-wide k group per block; the scales ride one stage ahead in a register");
   static_assert(!AFF || (!W4 && BN == 128 && S == 2 && KC == kW8OBwdCellN),
                 "affine: int8, the outliers of stage kt read during stage kt - 1");
-  constexpr int UCB = (R + 15) / 16;                  // u column blocks of 16
+  constexpr int UCB = (3 * R + 15) / 16;              // operand column blocks of 16: B (t) hi | mid | lo
+  constexpr int RCB = (R + 15) / 16;                  // column blocks of the ranks
   constexpr bool XPRE = BM * BN * 2 <= 8192;          // x tile kept outside the ring
   constexpr int CBSZ = BN * 128;                      // converted codes [BN][64] bf16
-  constexpr int BUSZ = UCB * 16 * 128;                // converted B [16 UCB][64] bf16
+  constexpr int BUSZ = UCB * 16 * 128;                // converted B [16 UCB][64] bf16: hi | mid | lo
   constexpr int TSZ = BM * R * 4;                     // t tile (pitch r)
   constexpr int XTSZ = BM * BN * 2;
   constexpr int EFL = (BM + BN) * R;                  // epilogue floats: U [BM][R], A^T [R][BN]
@@ -1026,15 +1083,14 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
     const int e = tid + 256 * i, row = e / R, j = e % R;
     if (e < BM * R && j < r) Ts[row * r + j] = m0 + row < M ? tv[i] : 0.f;
   }
-  for (int e = R * 32 + tid; e < UCB * 16 * 32; e += 256)      // 4-byte pairs
+  for (int e = 3 * R * 32 + tid; e < UCB * 16 * 32; e += 256)      // 4-byte pairs
     *reinterpret_cast<uint32_t*>(BU + swz128(e / 32, (e % 32) >> 2) + (e & 3) * 4) = 0u;
   __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());    // stores land before the first barrier
 
   const int rows_here = M - m0 < BM ? M - m0 : BM;
-  // dB operand: t as bf16, lane -> rank (lane % 16), rows 32 c + 8 (lane / 16) + e
-  // (read back from LDS after the first barrier of the loop)
-  bf16x8 tfr[UCB][BM / 32];
-  bool tfr_ready = false;
+  // dB operand: t split into bf16 hi, mid and lo columns, lane -> column
+  // (lane % 16), rows 32 c + 8 (lane / 16) + e; rebuilt from the t tile in
+  // LDS at each of the block's dB stages rather than held in registers
   // cooperative conversion: thread -> n quad nq, k quads kq0 + 16 h
   const int nq = tid & 15, kq0 = tid >> 4;
 
@@ -1128,12 +1184,17 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
         ocur = o1;
       }
     }
-    // BU[j][n] = bf16(B[j][n]), 2 n per entry
+    // BU[j][n], BU[R + j][n], BU[2 R + j][n] = the bf16 hi, mid and lo parts of
+    // B[j][n], 2 n per entry
 #pragma unroll
     for (int e = tid; e < R * 32; e += 256) {
       const int j = e >> 5, p = e & 31;
       const f32x2 b = *reinterpret_cast<const f32x2*>(Xa + 64 * (1 + j) + 2 * p);
-      *reinterpret_cast<uint32_t*>(BU + swz128(j, p >> 2) + (p & 3) * 4) = pk_bf16(b.x, b.y);
+      uint32_t mid2, lo2;
+      const uint32_t hi2 = pk_bf16_split3(b.x, b.y, mid2, lo2);
+      *reinterpret_cast<uint32_t*>(BU + swz128(j, p >> 2) + (p & 3) * 4) = hi2;
+      *reinterpret_cast<uint32_t*>(BU + swz128(R + j, p >> 2) + (p & 3) * 4) = mid2;
+      *reinterpret_cast<uint32_t*>(BU + swz128(2 * R + j, p >> 2) + (p & 3) * 4) = lo2;
     }
     __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
     __builtin_amdgcn_s_barrier();                    // CB, BU visible
@@ -1169,21 +1230,29 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
     // lanes 4 i + p fetch the 4 n at 16 w + 4 p of row i, and lane q receives
     // n = 16 w + q of rows 0..3.
     if (kt % a.tiles_x == kt_blk) {
-      if (!tfr_ready) {
-        tfr_ready = true;
+      bf16x8 tfr[UCB][BM / 32];
+      {
 #pragma unroll
         for (int cb = 0; cb < UCB; ++cb) {
-          const int j = cb * 16 + (lane & 15);
+          // column j: part j / R (hi, mid, lo) of t[., j % R]
+          const int j = cb * 16 + (lane & 15), part = j / R, jr = j - part * R;
 #pragma unroll
           for (int c = 0; c < BM / 32; ++c) {
             float v[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int m = 32 * c + 8 * (lane >> 4) + e;
-              v[e] = j < r ? Ts[m * r + (j < r ? j : 0)] : 0.f;
+              v[e] = (jr < r && part < 3) ? Ts[m * r + (jr < r ? jr : 0)] : 0.f;
             }
-            tfr[cb][c] = __builtin_bit_cast(bf16x8, u32x4{pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]),
-                                                           pk_bf16(v[4], v[5]), pk_bf16(v[6], v[7])});
+            u32x4 hi, mid, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              uint32_t me, le;
+              hi[e] = pk_bf16_split3(v[2 * e], v[2 * e + 1], me, le);
+              mid[e] = me;
+              lo[e] = le;
+            }
+            tfr[cb][c] = __builtin_bit_cast(bf16x8, part == 0 ? hi : part == 1 ? mid : lo);
           }
         }
       }
@@ -1212,14 +1281,13 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
           dbacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dyT, tfr[cb][c], dbacc[cb], 0, 0, 0);
       }
 #pragma unroll
-      for (int cb = 0; cb < UCB; ++cb) {
+      for (int cb = 0; cb < RCB; ++cb) {
         const int j = cb * 16 + (lane & 15);
-        if (j < r) {
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            const int gn = kt * KC + 16 * wid + 4 * (lane >> 4) + ii;
-            if (gn < N) a.partB[((long)mt * r + j) * N + gn] = dbacc[cb][ii];
-          }
+        for (int ii = 0; ii < 4; ++ii) {
+          const float dbv = split3_sum<R, UCB>(dbacc, cb, ii, lane);
+          const int gn = kt * KC + 16 * wid + 4 * (lane >> 4) + ii;
+          if (j < r && gn < N) a.partB[((long)mt * r + j) * N + gn] = dbv;
         }
       }
     }
@@ -1243,12 +1311,13 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
       for (int i = 0; i < FM; ++i) {
         if ((i & 1) != wn) continue;
 #pragma unroll
-        for (int cb = 0; cb < UCB; ++cb) {
+        for (int cb = 0; cb < RCB; ++cb) {
           const int j = cb * 16 + (lane & 15);
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) {
+            const float uv = split3_sum<R, UCB>(uacc[i >> 1], cb, ii, lane);
             const int gm = m0 + wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + ii;
-            if (j < r && gm < M) a.pu[((long)split * M + gm) * r + j] = uacc[i >> 1][cb][ii];
+            if (j < r && gm < M) a.pu[((long)split * M + gm) * r + j] = uv;
           }
         }
       }
@@ -1264,12 +1333,13 @@ __global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
   for (int i = 0; i < FM; ++i) {
     if ((i & 1) != wn) continue;
 #pragma unroll
-    for (int cb = 0; cb < UCB; ++cb) {
+    for (int cb = 0; cb < RCB; ++cb) {
       const int j = cb * 16 + (lane & 15);
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
+        const float uv = split3_sum<R, UCB>(uacc[i >> 1], cb, ii, lane);
         const int ml = wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + ii;
-        if (j < R) E[ml * R + j] = j < r ? uacc[i >> 1][cb][ii] : 0.f;
+        if (j < R) E[ml * R + j] = j < r ? uv : 0.f;
       }
     }
   }

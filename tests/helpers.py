@@ -8,6 +8,9 @@ import numpy as np
 # 2e-2, relative per element against max(|oracle|, rms(oracle)) so that
 # entries near zero are judged on the tensor's scale.
 RTOL = {"f32": 1e-5, "bf16": 2e-2}
+# float32 outputs of every workload: t = x A (saved by the forward) and the
+# adapter gradients dA, dB (the adapter is float32 in every workload)
+RTOL_F32 = RTOL["f32"]
 
 
 def rel_errors(got, want):
@@ -22,11 +25,15 @@ def rel_errors(got, want):
 
 
 def assert_close(got, want, rtol, what=""):
+    """Per-element relative check; NaN and +-inf must sit at the same places
+    (an infinity must match exactly), the finite rest within rtol."""
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     assert got.shape == want.shape, (what, got.shape, want.shape)
     assert np.array_equal(np.isnan(got), np.isnan(want)), f"{what}: NaN pattern differs"
-    ok = ~np.isnan(want)
+    assert np.array_equal(np.isposinf(got), np.isposinf(want)), f"{what}: +inf pattern differs"
+    assert np.array_equal(np.isneginf(got), np.isneginf(want)), f"{what}: -inf pattern differs"
+    ok = np.isfinite(want)
     elem, nw = rel_errors(got[ok], want[ok])
     worst = float(elem.max()) if elem.size else 0.0
     assert worst <= rtol, f"{what}: max rel err {worst:.3e} > {rtol} (normwise {nw:.3e})"

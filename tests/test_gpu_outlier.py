@@ -124,11 +124,11 @@ def check_fwd_bwd(c: W8OCase, what):
     ye, te = O.fwd_w8o(c.x, c.q, c.A, c.B, c.alpha, "bf16")
     dxe, dAe, dBe = O.bwd(c.x, c.dy, O.dequant_w8o(c.q), c.A, c.B, c.alpha, "bf16")
     tol = RTOL["bf16"]
-    assert_close(t, te, RTOL["f32"] * 10, f"{what} t")
+    assert_close(t, te, RTOL["f32"], f"{what} t")
     assert_close(y, ye, tol, f"{what} y")
     assert_close(dx, dxe, tol, f"{what} dx")
-    assert_close(dA, dAe, tol, f"{what} dA")
-    assert_close(dB, dBe, tol, f"{what} dB")
+    assert_close(dA, dAe, RTOL["f32"], f"{what} dA")
+    assert_close(dB, dBe, RTOL["f32"], f"{what} dB")
 
 
 LAYER_CASES = [
