@@ -277,12 +277,16 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
   // direct-to-LDS loads still in flight, and waits for all of them.
   // Converted codes and B are double-buffered: buffer kt % 2 feeds the
   // products of stage kt while stage kt + 1 is converted into the other.
-  __shared__ __attribute__((aligned(1024))) int8_t ring[S * STG + 2 * CBSZ + 2 * BUSZ + TSZ + AQSZ + (XPRE ? XTSZ : 0)];
+  // the dB operand, t as bf16 hi, mid and lo columns in the MFMA operand
+  // layout [UCB][BM / 32][64 lanes][16 B], built once by the consumers
+  constexpr int TFSZ = UCB * (BM / 32) * 1024;
+  __shared__ __attribute__((aligned(1024))) int8_t ring[S * STG + 2 * CBSZ + 2 * BUSZ + TSZ + AQSZ + TFSZ + (XPRE ? XTSZ : 0)];
   int8_t* CB0 = ring + S * STG;
   int8_t* BU0 = CB0 + 2 * CBSZ;
   float* Ts = reinterpret_cast<float*>(BU0 + 2 * BUSZ);                        // [BM][r]
   const float* Aq = reinterpret_cast<const float*>(BU0 + 2 * BUSZ + TSZ);    // [BN][r]
-  int8_t* Xs = XPRE ? BU0 + 2 * BUSZ + TSZ + AQSZ : ring + EFL * 4;            // [BM][BN] bf16
+  int8_t* TF = BU0 + 2 * BUSZ + TSZ + AQSZ;                                    // t operand
+  int8_t* Xs = XPRE ? TF + TFSZ : ring + EFL * 4;                              // [BM][BN] bf16
 
   const int lane = threadIdx.x & 63, wid = wave_id();
   const bool producer = wid >= 4;
@@ -604,6 +608,31 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
   __builtin_amdgcn_s_barrier();
+  if (!producer) {
+    // the dB operand from the t tile, while the producers convert stage 0:
+    // consumer wave w builds fragments f = w, w + 4, ... of the UCB * BM / 32
+    // (fragment (cb, c): lane -> column cb * 16 + lane % 16, i.e. part
+    // j / R of rank j % R, rows 32 c + 8 (lane / 16) + e)
+    for (int f = wid; f < UCB * (BM / 32); f += 4) {
+      const int cb = f / (BM / 32), c = f % (BM / 32);
+      const int j = cb * 16 + (lane & 15), part = j / R, jr = j - part * R;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int m = 32 * c + 8 * (lane >> 4) + e;
+        v[e] = (jr < r && part < 3) ? Ts[m * r + (jr < r ? jr : 0)] : 0.f;
+      }
+      u32x4 hi, mid, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t me, le;
+        hi[e] = pk_bf16_split3(v[2 * e], v[2 * e + 1], me, le);
+        mid[e] = me;
+        lo[e] = le;
+      }
+      *reinterpret_cast<u32x4*>(TF + (f * 64 + lane) * 16) = part == 0 ? hi : part == 1 ? mid : lo;
+    }
+  }
   if (producer) {
     if constexpr (AFF) {
       outl_range(0, ocur);
@@ -689,31 +718,11 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
       // and lane q receives n = 16 w + q of rows 0..3.
       if (kt % a.tiles_x == kt_blk) {
         bf16x8 tfr[UCB][BM / 32];
-        {
 #pragma unroll
-          for (int cb = 0; cb < UCB; ++cb) {
-            // column j: part j / R (hi, mid, lo) of t[., j % R]
-            const int j = cb * 16 + (lane & 15), part = j / R, jr = j - part * R;
+        for (int cb = 0; cb < UCB; ++cb)
 #pragma unroll
-            for (int c = 0; c < BM / 32; ++c) {
-              float v[8];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const int m = 32 * c + 8 * (lane >> 4) + e;
-                v[e] = (jr < r && part < 3) ? Ts[m * r + (jr < r ? jr : 0)] : 0.f;
-              }
-              u32x4 hi, mid, lo;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                uint32_t me, le;
-                hi[e] = pk_bf16_split3(v[2 * e], v[2 * e + 1], me, le);
-                mid[e] = me;
-                lo[e] = le;
-              }
-              tfr[cb][c] = __builtin_bit_cast(bf16x8, part == 0 ? hi : part == 1 ? mid : lo);
-            }
-          }
-        }
+          for (int c = 0; c < BM / 32; ++c)
+            tfr[cb][c] = *reinterpret_cast<const bf16x8*>(TF + ((cb * (BM / 32) + c) * 64 + lane) * 16);
         constexpr int NRD = 2 * (BM / 32);
         uint32_t tra[NRD];
         uint64_t trv[NRD];
@@ -822,7 +831,7 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
 // W4: 4-bit weights (two codes per byte, fp16 scale per 128 k, carried one
 // stage ahead in a register); else int8.
 template <bool W4, int BM, int BN, int S, int R, bool AFF = false, bool SPLIT = false>
-__global__ __launch_bounds__(256) void bwd_wide_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_wide_kernel(BwdArgs a) {
   constexpr int KC = 64;                              // n per stage
   constexpr int RB = W4 ? BN / 2 : BN;                // code bytes per row of n
   constexpr int AUXI = ((1 + R) * 256 + 4095) / 4096;  // aux DMA instructions per wave
@@ -1501,7 +1510,8 @@ void launch_pc(BwdArgs a, hipStream_t st) {
   if (a.r <= 4) bwd_pc_kernel<W4, BM, BN, S, 4, AFF><<<grid, 512, 0, st>>>(a);
   else if (a.r <= 8) bwd_pc_kernel<W4, BM, BN, S, 8, AFF><<<grid, 512, 0, st>>>(a);
   else if (a.r <= 16) bwd_pc_kernel<W4, BM, BN, S, 16, AFF><<<grid, 512, 0, st>>>(a);
-  else bwd_pc_kernel<W4, BM, BN, S, 32, AFF><<<grid, 512, 0, st>>>(a);
+  else if constexpr (!W4) bwd_pc_kernel<W4, BM, BN, S, 32, AFF><<<grid, 512, 0, st>>>(a);
+  // (4-bit layers of rank above 16 take the 128 x 128 tiles: bwd_row_block)
 }
 
 template <bool W4, bool AFF = false, bool SPLIT = false, int BN = 128>
@@ -1561,10 +1571,10 @@ void bwd_split_sizes(int M, int K, int N, int r, size_t* pdx_floats, size_t* pu_
 }
 
 int bwd_row_block(int fmt, int M, int K, int N, int r) {
-  (void)r;
   int sp, nks;
   wide_split_plan(M, K, N, &sp, &nks);
   if (sp > 1) return 128;                         // split 128 x 128 tiles
+  if (fmt == 1 && r > 16) return 128;             // the 64-row 4-bit tile at rank 32 exceeds the LDS
   const int bn = fmt == 1 ? 128 : 64;             // k per 64-row tile
   const long t64 = (long)((M + 63) / 64) * ((K + bn - 1) / bn);
   return t64 <= 512 ? 64 : 128;

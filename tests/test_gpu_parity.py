@@ -175,6 +175,8 @@ SMALL = [
     (5, 130, 384, 144, 1),
     (5, 77, 256, 4160, 8),      # 4-bit, contraction split in 4
     (5, 7, 8192, 64, 8),        # 4-bit: the adapter's down projection over long rows
+    (5, 100, 256, 144, 32),     # 4-bit at rank 32: 128 x 128 backward tiles
+    (2, 90, 512, 272, 16),      # rank 16: three column blocks of the split operands
 ]
 
 
@@ -192,10 +194,18 @@ def test_ragged_shapes(cid, M, K, N, r):
     check_bwd(case, None, need_dx=False)
 
 
-@pytest.mark.parametrize("cid", [1, 2, 5])
-def test_zero_B_is_plain_quantized_product(cid):
-    w = WL.small(cid, 70, 256, 144, 4)
-    say(f"B=0: {w.name}")
+@pytest.mark.parametrize("cid,M,K,N,r", [
+    (1, 70, 256, 144, 4),
+    (2, 70, 256, 144, 4),
+    (5, 70, 256, 144, 4),
+    (2, 1024, 1024, 1024, 8),   # the MLP layer
+    (2, 257, 784, 1024, 8),     # ragged rows, a 16-wide last k step
+    (2, 64, 1040, 1024, 8),     # k not a multiple of 64
+    (2, 33, 512, 80, 16),       # rank 16, ragged columns
+])
+def test_zero_B_is_plain_quantized_product(cid, M, K, N, r):
+    w = WL.small(cid, M, K, N, r)
+    say(f"B=0: {w.name} M={M} K={K} N={N} r={r}")
     case = Case(w, 0, zero_B=True)
     y, t = check_fwd(case)
     _, dA, dB = Q.qlora_bwd(case.lin, case.x_t, case.dy_t, t=t)
