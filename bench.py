@@ -16,9 +16,23 @@ Inputs are seeded synthetic tensors already resident in HBM. Steps are
 captured once in a HIP graph and replayed; ``value`` is the workload's
 algorithmic operations divided by the measured time per step.
 
-Prints ONE JSON line (see the keys below), including the roofline of the
-dominant kernel, timed live with HIP events recorded by the library around
-each of its launches, and the CPU oracle timed on a bounded sample.
+Prints ONE JSON line. Besides the contract keys it carries:
+  * ``step_ms``: median, p10 and p90 over the timed steps, each replay
+    timed by its own pair of events (``ms_per_step`` is the total over the
+    timed steps divided by their number);
+  * ``cold``: the same step with a 512 MiB device write before each one
+    (outside the timed interval), so no input is left in the 256 MB
+    last-level cache;
+  * ``launch_floor``: the step graph's kernel count and the time of a
+    graph of as many empty kernels;
+  * ``peaks_measured``: dense bf16 and int8 MFMA throughput and HBM copy
+    and read bandwidth, re-measured on this GPU by the library's probes;
+  * ``roofline``: the dominant kernel (the fused backward) timed live with
+    HIP events on the stream it is launched on, against the roof its
+    algorithmic flops and bytes select (MFMA or HBM), and against the
+    measured peak as well;
+  * ``cpu_baseline``: the CPU oracle on a bounded sample of the workload,
+    median of 3 runs at the host's thread count and at one thread.
 """
 
 from __future__ import annotations
@@ -58,7 +72,11 @@ def parse():
                         "the last layer, or one per layer (auto: batched for stacks of at "
                         "least 4 layers)")
     p.add_argument("--copy-calibration", action="store_true",
-                   help="also run a plain 256 MiB device copy (for scaling HBM counters)")
+                   help="also run the library's copy (256 MiB) and read (1 GiB) probes, "
+                        "known byte counts for scaling HBM counters")
+    p.add_argument("--cold-steps", type=int, default=30,
+                   help="steps timed one by one after a 512 MiB flush (0: skip)")
+    p.add_argument("--no-peaks", action="store_true", help="skip re-measuring the peaks")
     return p.parse_args()
 
 
@@ -120,6 +138,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lib = Q.lib()
+    # the in-tree build, and nothing else, is what runs
+    loaded = Q.loaded_path()
+    assert os.path.realpath(loaded) == os.path.realpath(Q.LIB_PATH), loaded
     w = WL.WORKLOADS[args.workload]
     if args.weights is not None and args.weights != w.wfmt:
         w = WL.with_format(w, args.weights)
@@ -250,21 +271,30 @@ def main():
 
     use_graph = not args.no_graph
 
-    def timed(fn):
-        if use_graph:
+    def capture(fn):
+        """The step as a HIP graph (replay function, graph node count)."""
+        if not use_graph:
+            return fn, None
+        try:
+            g = torch.cuda.CUDAGraph(keep_graph=True)
+        except TypeError:  # pragma: no cover - older torch
             g = torch.cuda.CUDAGraph()
-            s = torch.cuda.Stream()
-            s.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(s):
-                fn()
-            torch.cuda.current_stream().wait_stream(s)
-            torch.cuda.synchronize()
-            with torch.cuda.graph(g):
-                fn()
-            torch.cuda.synchronize()
-            run = g.replay
-        else:
-            run = fn
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            fn()
+        nodes = graph_nodes(g)
+        if hasattr(g, "instantiate"):
+            g.instantiate()
+        torch.cuda.synchronize()
+        return g.replay, nodes
+
+    def timed(fn):
+        run, nodes = capture(fn)
         for _ in range(args.warmup):
             run()
         torch.cuda.synchronize()
@@ -274,7 +304,17 @@ def main():
             run()
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps, (time.perf_counter() - t0) * 1e3 / args.steps
+        ms = e0.elapsed_time(e1) / args.steps
+        wall = (time.perf_counter() - t0) * 1e3 / args.steps
+        # the same replays one by one, each between its own pair of events
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        ev[0].record()
+        for i in range(args.steps):
+            run()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+        return ms, wall, per, run, nodes
 
     batched = args.finish == "batched" or (args.finish == "auto" and len(layers) >= 4)
     # the other variant first: the first timed loop after capture runs a few
@@ -282,14 +322,36 @@ def main():
     # timed first, took about 8 us more), so it also warms the GPU for the
     # step that gives ``value``
     if batched:
-        ms_l, wall_l = timed(step)
-        ms_b, wall_b = timed(step_batched)
+        ms_l, wall_l, _, _, _ = timed(step)
+        ms_b, wall_b, per, run, nodes = timed(step_batched)
     else:
-        ms_b, wall_b = timed(step_batched)
-        ms_l, wall_l = timed(step)
+        ms_b, wall_b, _, _, _ = timed(step_batched)
+        ms_l, wall_l, per, run, nodes = timed(step)
     ms, wall_ms = (ms_b, wall_b) if batched else (ms_l, wall_l)
     ops = w.total_ops()
     value = ops / (ms * 1e-3) / 1e12
+    step_stats = stats(per)
+
+    # cold: a 512 MiB write before every step (outside its events), so that
+    # none of the step's inputs is left in the 256 MB last-level cache
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)
+        times = []
+        for i in range(args.cold_steps + 2):
+            flush.fill_(i & 0xff)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            run()
+            b.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                times.append(a.elapsed_time(b))
+        del flush
+        cold = dict(stats(times), flush_bytes=512 << 20)
+        cold["tflops_median"] = round(ops / (cold["median_ms"] * 1e-3) / 1e12, 3)
+
+    floor = launch_floor(torch, lib, check, nodes) if nodes else None
 
     # eager time per step, for reference (host launch cost included)
     torch.cuda.synchronize()
@@ -301,8 +363,9 @@ def main():
     eager_ms = e0.elapsed_time(e1) / 10
 
     if args.copy_calibration:
-        copy_calibration(torch, dev)
-    roof = dominant_kernel_roofline(w, layers, step, torch)
+        copy_calibration(torch, dev, lib, check)
+    peaks = None if args.no_peaks else measure_peaks(torch, dev, lib, check)
+    roof = dominant_kernel_roofline(w, layers, step, torch, Q, peaks)
     cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
 
     out = {
@@ -328,6 +391,10 @@ def main():
             "ops_per_step": ops,
             "hip_graph": use_graph,
         },
+        "library": os.path.relpath(loaded, ROOT),
+        "step_ms": step_stats,
+        "cold": cold,
+        "launch_floor": floor,
         "wall_ms_per_step": round(wall_ms, 5),
         "finish": "batched" if batched else "layerwise",
         "batched_finish_ms_per_step": round(ms_b, 5),
@@ -338,6 +405,7 @@ def main():
         "fwd_ms": None if fwd_ms is None else round(fwd_ms, 4),
         "fwd_a8w4_ms": None if fwd_a8w4_ms is None else round(fwd_a8w4_ms, 4),
         "attention_query_ms": heads_leg,
+        "peaks_measured": peaks,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
@@ -361,9 +429,10 @@ def describe(w):
 # and of the compiler flags; otherwise reported as null.
 TRAFFIC = {
     "workload": 2,
+    "weights": "w8",
     "sources": ["gemm_bwd.hip", "ring.hpp", "common.hpp"],
-    "sha256": "8133678b98566da0d06b65a24867ea3a24a5a79fc4dd5e7d9e138a33bd066289",
-    "bytes_per_launch": 14781660,
+    "sha256": None,
+    "bytes_per_launch": None,
 }
 
 
@@ -378,14 +447,117 @@ def kernel_sources_sha256(names):
     return h.hexdigest()
 
 
-def copy_calibration(torch, dev):
-    """A plain device-to-device copy of 256 MiB, three times (its counters
-    calibrate the HBM byte counters of the kernels in the same run)."""
+def stats(times_ms):
+    v = sorted(times_ms)
+    q = lambda f: v[min(len(v) - 1, max(0, int(round(f * (len(v) - 1)))))]  # noqa: E731
+    return {"median_ms": round(q(0.5), 5), "p10_ms": round(q(0.1), 5),
+            "p90_ms": round(q(0.9), 5), "samples": len(v)}
+
+
+def graph_nodes(g):
+    """Node count of a captured graph (kernel launches: the library records
+    nothing else), from the HIP runtime the process has mapped."""
+    try:
+        raw = g.raw_cuda_graph()
+        path = next((ln.split()[-1] for ln in open("/proc/self/maps")
+                     if ln.rstrip().endswith("libamdhip64.so") or "libamdhip64.so." in ln),
+                    "libamdhip64.so")
+        hip = ctypes.CDLL(path)
+        n = ctypes.c_size_t(0)
+        if hip.hipGraphGetNodes(ctypes.c_void_p(raw), None, ctypes.byref(n)) != 0:
+            return None
+        return int(n.value)
+    except Exception:  # pragma: no cover - API not available
+        return None
+
+
+def launch_floor(torch, lib, check, nodes, reps=20):
+    """Time of a graph of `nodes` empty kernels (256 blocks of 256 threads):
+    what the step's launches cost with no work in them."""
+    st = torch.cuda.current_stream().cuda_stream
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        check(lib.qlora_probe_empty(256, 256, s.cuda_stream), "probe_empty")
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream().cuda_stream
+        for _ in range(nodes):
+            check(lib.qlora_probe_empty(256, 256, cs), "probe_empty")
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del st
+    ms = e0.elapsed_time(e1) / reps
+    return {"kernels_per_step": nodes, "empty_kernel_us": round(ms * 1e3 / nodes, 3),
+            "floor_ms_per_step": round(ms, 5)}
+
+
+def measure_peaks(torch, dev, lib, check):
+    """Dense MFMA throughput (bf16, int8) and HBM copy / read bandwidth on
+    this GPU, from the library's probes (best of 5 launches each)."""
+    st = torch.cuda.current_stream().cuda_stream
+    out = torch.empty((4096 * 256,), dtype=torch.float32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(fn, n=5):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(n):
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1) * 1e-3)
+        return min(t)
+
+    res = {}
+    for kind, key in ((0, "bf16_mfma_tflops"), (1, "int8_mfma_tops")):
+        ops = ctypes.c_double()
+        blocks, iters = 2048, 1000
+        t = best(lambda: check(lib.qlora_probe_mfma(kind, blocks, iters, out.data_ptr(), st,
+                                                      ctypes.byref(ops)), "probe_mfma"))
+        res[key] = round(ops.value / t / 1e12, 1)
+    nbytes = 1 << 30
+    src = torch.empty((nbytes,), dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    t = best(lambda: check(lib.qlora_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, 4096, st),
+                           "probe_copy"))
+    res["hbm_copy_gbs"] = round(2 * nbytes / t / 1e9, 1)
+    del dst
+    big = torch.empty((4 * nbytes,), dtype=torch.uint8, device=dev).fill_(2)
+    red = torch.empty((4096 * 256 * 16,), dtype=torch.uint8, device=dev)
+    t = best(lambda: check(lib.qlora_probe_read(big.data_ptr(), 4 * nbytes, 4096, red.data_ptr(), st),
+                           "probe_read"))
+    res["hbm_read_gbs"] = round(4 * nbytes / t / 1e9, 1)
+    res["how"] = ("best of 5 launches: 2048 blocks x 4 waves x 1000 rounds of 8 independent "
+                  "MFMAs; 1 GiB copy (2 GiB moved); 4 GiB read")
+    return res
+
+
+def copy_calibration(torch, dev, lib, check):
+    """Kernels of known HBM traffic, for scaling the byte counters of a
+    counter pass: the copy probe over 256 MiB (256 MiB read, 256 MiB
+    written) three times, and the read probe over 1 GiB (1 GiB read, larger
+    than the last-level cache) three times."""
+    st = torch.cuda.current_stream().cuda_stream
     n = 256 << 20
     src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     for _ in range(3):
-        dst.copy_(src)
+        check(lib.qlora_probe_copy(src.data_ptr(), dst.data_ptr(), n, 4096, st), "probe_copy")
+    big = torch.empty(4 * n, dtype=torch.uint8, device=dev).fill_(2)
+    red = torch.empty((4096 * 256 * 16,), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        check(lib.qlora_probe_read(big.data_ptr(), 4 * n, 4096, red.data_ptr(), st), "probe_read")
     torch.cuda.synchronize()
 
 
@@ -433,17 +605,26 @@ def multi_head_leg(torch, dev, lib, check, M, K=2048, heads=8, hd=256, r=4, reps
     return out
 
 
-def dominant_kernel_roofline(w, layers, step, torch):
-    """Time the backward launch (the step's largest kernel) live.
+def dominant_kernel_roofline(w, layers, step, torch, Q, peaks):
+    """Time the backward launch (the step's largest kernel) live, and place
+    it on the roofline.
 
     In one eager step the library launches each layer's backward kernel 20
     times back to back (same inputs, same outputs) between two HIP events
     that it records on the stream it launches on; the average duration is
-    the summed intervals over all launches. Peak: dense bf16 MFMA (float32
-    vector peak for the float32 workload). Algorithmic work per launch of the fused int8
-    backward: 2 M K N for dx, 2 M N r each for u and dB, 2 M K r each for dA
-    and the rank-r term of dx, i.e. 2 M K N + 4 M r (N + K) flops; peak: dense
-    bf16 MFMA.
+    the summed intervals over all launches.
+
+    Algorithmic work per launch, averaged over the layers:
+      * flops of the fused bf16 backward: 2 M K N for dx, 2 M N r each for u
+        and dB, 2 M K r each for dA and the rank-r term of dx, i.e.
+        2 M K N + 4 M r (N + K); of the float32 input gradient 2 M K N +
+        2 M K r;
+      * bytes of a backward: dy, codes, scales, x, t, A, B read, dx, dA, dB
+        written, each once.
+    The roof is the one these select: MFMA (dense bf16, or the float32
+    matrix peak for float32 layers) when flops / peak exceeds bytes / HBM
+    bandwidth, else HBM; ``frac`` is the kernel's fraction of that roof,
+    ``frac_measured`` the same against the peak re-measured on this GPU.
     """
     n = len(layers)
     repeats = 20
@@ -456,90 +637,122 @@ def dominant_kernel_roofline(w, layers, step, torch):
     torch.cuda.synchronize()
     tot_ms = sum(a.elapsed_time(b) for a, b in pairs)
     launches = n * repeats
-    avg_ms = tot_ms / launches
-    if w.dtype == "bf16":   # fused backward: dx, u, dB, dA, s u A^T
-        flops = sum(2.0 * w.M * l.K * l.N + 4.0 * w.M * w.r * (l.N + l.K) for l in layers) / n
-        # the library's tile choice: 128 x 128 blocks over a split contraction
-        # (then a fixup launch) for at most 128 such tiles and N >= 2048;
-        # else 64-row producer/consumer blocks while they make at most two
-        # per compute unit, else 128 x 128 blocks
-        bn = 128 if w.wfmt == "w4g128" else 64
-
-        def bwd_name(l):
-            if ((w.M + 127) // 128) * ((l.K + 127) // 128) <= 128 and (l.N + 63) // 64 >= 32:
-                return "bwd_wide_kernel<SPLIT> + bwd_fixup_kernel"
-            if ((w.M + 63) // 64) * ((l.K + bn - 1) // bn) <= 512:
-                return "bwd_pc_kernel"
-            return "bwd_wide_kernel"
-        names = sorted({bwd_name(l) for l in layers})
-        kernel = (" + ".join(names) + " (fused backward: dx, u, dA and dB partial sums, "
-                  f"bf16 MFMA, {w.wfmt} weights)")
-    else:                   # float32 input gradient: dy deq(W)^T + s u A^T
-        flops = sum(2.0 * w.M * l.K * l.N + 2.0 * w.M * w.r * l.K for l in layers) / n
-        kernel = "dx_f32_kernel (float32 input gradient)"
-    achieved = flops / (avg_ms * 1e-3) / 1e12
-    peak = PEAK["bf16" if w.dtype == "bf16" else "f32"] / 1e12
+    avg_s = tot_ms / launches * 1e-3
+    M, r = w.M, w.r
+    xb = 2 if w.dtype == "bf16" else 4                 # bytes per activation
+    cb = {"w8": 1.0, "w8o": 1.0, "w4g128": 0.5}[w.wfmt]
+    flops = nbytes = 0.0
+    for l in layers:
+        K, N = l.K, l.N
+        if w.dtype == "bf16":
+            flops += 2.0 * M * K * N + 4.0 * M * r * (N + K)
+        else:
+            flops += 2.0 * M * K * N + 2.0 * M * K * r
+        scale_b = 4.0 * N if w.wfmt == "w8" else (2.0 * N * K / 128 if w.wfmt == "w4g128" else 0.0)
+        nbytes += (xb * M * N + cb * K * N + scale_b + xb * M * K + 4.0 * M * r + 4.0 * K * r
+                   + 4.0 * r * N + xb * M * K + 4.0 * K * r + 4.0 * r * N)
+    flops /= n
+    nbytes /= n
+    mfma_peak = PEAK["bf16" if w.dtype == "bf16" else "f32"]
+    t_mfma, t_hbm = flops / mfma_peak, nbytes / PEAK["hbm"]
+    bound = "mfma" if t_mfma >= t_hbm else "hbm"
+    names = sorted({Q.qlora_bwd_main_kernel(l.lin, M, l.dt) for l in layers})
+    kernel = " + ".join(names) + (f" ({w.wfmt} weights, {w.dtype})")
+    if bound == "mfma":
+        achieved, peak, unit = flops / avg_s / 1e12, mfma_peak / 1e12, "TFLOP/s"
+        mpeak = peaks.get("bf16_mfma_tflops") if (peaks and w.dtype == "bf16") else None
+    else:
+        achieved, peak, unit = nbytes / avg_s / 1e9, PEAK["hbm"] / 1e9, "GB/s"
+        mpeak = peaks.get("hbm_read_gbs") if peaks else None
     traffic = None
     if (TRAFFIC["sha256"] is not None and w.cid == TRAFFIC["workload"]
+            and w.wfmt == TRAFFIC["weights"]
             and kernel_sources_sha256(TRAFFIC["sources"]) == TRAFFIC["sha256"]):
         traffic = TRAFFIC["bytes_per_launch"]
     return {
         "kernel": kernel,
-        "bound": "mfma",
+        "bound": bound,
         "achieved": round(achieved, 2),
         "peak": peak,
-        "unit": "TFLOP/s",
+        "unit": unit,
         "frac": round(achieved / peak, 4),
         "traffic": traffic,
-        "avg_launch_us": round(avg_ms * 1e3, 3),
+        "avg_launch_us": round(avg_s * 1e6, 3),
         "launches_timed": launches,
         "flops_per_launch": flops,
+        "bytes_per_launch": nbytes,
+        "mfma_frac": round(flops / avg_s / mfma_peak, 4),
+        "hbm_frac": round(nbytes / avg_s / PEAK["hbm"], 4),
+        "roofline_us": round(max(t_mfma, t_hbm) * 1e6, 3),
+        "frac_measured": None if not mpeak else round(achieved / mpeak, 4),
+        "measured_peak": mpeak,
     }
 
 
 def cpu_baseline(w, budget_s):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    whole layers (all rows), forward + backward, until the budget is used."""
+    """The CPU oracle, as it stands, on a bounded sample of the same
+    workload: whole layers (all rows), forward + backward. The sample is
+    the first layers whose one run fits about budget_s / 6; it runs three
+    times at the host's thread count and (its first layer) three times at
+    one thread; medians are reported."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
     from oracle import qlora_oracle as O
     from quantized_frozen_weight_amd import workloads as WL
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
-    done_ops, spent, n = 0, 0.0, 0
-    for i in range(len(w.layers)):
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+
+    prepared = []
+
+    def layer_inputs(i):
         W, A, B = WL.weight(w, i), WL.lora_A(w, i), WL.lora_B(w, i)
         _, x = WL.as_compute_dtype(WL.activations(w, i), w.dtype)
         _, dy = WL.as_compute_dtype(WL.out_grad(w, i), w.dtype)
         if w.wfmt == "w8":
-            c, s = O.quantize_w8(W)
+            q = O.quantize_w8(W)
         elif w.wfmt == "w8o":
             q = O.quantize_w8o(W)
         else:
-            c, s = O.quantize_w4(W)
-        t0 = time.perf_counter()
+            q = O.quantize_w4(W)
+        return x, dy, q, A, B
+
+    def run_layer(x, dy, q, A, B):
         if w.wfmt == "w8":
-            O.fwd_w8(x, c, s, A, B, w.alpha, w.dtype)
-            O.bwd(x, dy, O.dequant_w8(c, s), A, B, w.alpha, w.dtype)
+            O.fwd_w8(x, q[0], q[1], A, B, w.alpha, w.dtype)
+            O.bwd(x, dy, O.dequant_w8(*q), A, B, w.alpha, w.dtype)
         elif w.wfmt == "w8o":
             O.fwd_w8o(x, q, A, B, w.alpha, w.dtype)
             O.bwd(x, dy, O.dequant_w8o(q), A, B, w.alpha, w.dtype)
         else:
-            O.fwd_w4(x, c, s, A, B, w.alpha, w.dtype)
-            O.bwd(x, dy, O.dequant_w4(c, s), A, B, w.alpha, w.dtype)
-        spent += time.perf_counter() - t0
-        done_ops += w.ops_per_layer(*w.layers[i])
-        n += 1
-        if spent >= budget_s:
+            O.fwd_w4(x, q[0], q[1], A, B, w.alpha, w.dtype)
+            O.bwd(x, dy, O.dequant_w4(*q), A, B, w.alpha, w.dtype)
+
+    def run(sample):
+        t0 = time.perf_counter()
+        for args in sample:
+            run_layer(*args)
+        return time.perf_counter() - t0
+
+    # the sample: layers until one pass takes about budget / 6
+    spent = 0.0
+    for i in range(len(w.layers)):
+        prepared.append(layer_inputs(i))
+        spent += run([prepared[-1]])
+        if spent >= budget_s / 6:
             break
+    ops = sum(w.ops_per_layer(*w.layers[i]) for i in range(len(prepared)))
+    full = sorted(run(prepared) for _ in range(3))[1]
+    with threadpool_limits(limits=1):
+        one = sorted(run(prepared[:1]) for _ in range(3))[1]
+    ops1 = w.ops_per_layer(*w.layers[0])
     return {
-        "value": round(done_ops / spent / 1e12, 5),
+        "value": round(ops / full / 1e12, 5),
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{n} of {len(w.layers)} layers, all {w.M} rows, fwd+bwd "
-                  f"(numpy float64 oracle), {spent:.1f} s",
+        "sample": f"{len(prepared)} of {len(w.layers)} layers, all {w.M} rows, fwd+bwd "
+                  f"(numpy float64 oracle), median of 3 runs of {full:.2f} s",
+        "value_1thread": round(ops1 / one / 1e12, 5),
+        "sample_1thread": f"layer 0, median of 3 runs of {one:.2f} s",
     }
 
 

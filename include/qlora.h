@@ -315,6 +315,13 @@ int qlora_bwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
                     float* dB, void* ws, size_t ws_bytes, void* stream,
                     int repeats, void* ev_start, void* ev_stop);
 
+/* Name of the kernel that qlora_bwd_timed times for this layer, M and
+ * dtype (with dx): the fused backward's block shape, or the float32 input
+ * gradient. A static string, for benchmarks and profiles to label their
+ * timings; NULL for invalid arguments (as qlora_bwd would reject). Host-only
+ * arithmetic; usable without a GPU. */
+const char* qlora_bwd_main_kernel(const qlora_linear* L, int M, int dtype);
+
 /* Merge the trained adapter into the frozen int8 weight ("Parameter-efficient
  * fine-tuning of GPT-2 with LoRA", "Merge weights and generate text!": the
  * merged kernel is the frozen kernel plus the adapter product; "Introduce

@@ -54,8 +54,11 @@ EXPORTS = (
     "qlora_quantize_rows", "qlora_fwd_acc", "qlora_fwd_timed", "qlora_bwd_timed",
     "qlora_merge", "qlora_bwd_partial", "qlora_bwd_finish", "qlora_fwd_a8w4",
     "qlora_quantize_heads", "qlora_outlier_layout", "qlora_bwd_finish_batch",
-    "qlora_bwd_partials_bytes",
+    "qlora_bwd_partials_bytes", "qlora_bwd_main_kernel",
 )
+# include/qlora_probe.h: measurement probes (not part of the layer)
+PROBE_EXPORTS = ("qlora_probe_mfma", "qlora_probe_copy", "qlora_probe_read", "qlora_probe_empty")
+QLORA_PROBE_BF16, QLORA_PROBE_I8 = 0, 1
 
 
 class qlora_finish_item(ctypes.Structure):
@@ -103,10 +106,38 @@ def lib() -> ctypes.CDLL:
     L.qlora_fwd_a8w4.argtypes = [plin, i, i, vp, vp, vp, vp, sz, vp]
     L.qlora_quantize_heads.argtypes = [vp, i, i, i, i, vp, vp, vp]
     L.qlora_outlier_layout.argtypes = [i, i, psz, psz, psz, ctypes.POINTER(ctypes.c_int32)]
+    L.qlora_bwd_main_kernel.argtypes = [plin, i, i]
     for name in EXPORTS[1:]:
+        getattr(L, name).restype = ctypes.c_int
+    L.qlora_bwd_main_kernel.restype = ctypes.c_char_p
+    L.qlora_probe_mfma.argtypes = [i, i, i, vp, vp, ctypes.POINTER(ctypes.c_double)]
+    L.qlora_probe_copy.argtypes = [vp, vp, sz, i, vp]
+    L.qlora_probe_read.argtypes = [vp, sz, i, vp, vp]
+    L.qlora_probe_empty.argtypes = [i, i, vp]
+    for name in PROBE_EXPORTS:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
+
+
+def loaded_path() -> str:
+    """Path of the libqlora.so this process has mapped (from
+    /proc/self/maps), after lib() has loaded it; '' if none is mapped."""
+    lib()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if line.rstrip().endswith("/libqlora.so"):
+                return line.split()[-1]
+    return ""
+
+
+def qlora_bwd_main_kernel(layer: "QLinear", M: int, dtype: int) -> str:
+    """Name of the kernel qlora_bwd_timed times for this layer (static)."""
+    s = layer.cstruct()
+    name = lib().qlora_bwd_main_kernel(ctypes.byref(s), M, dtype)
+    if name is None:
+        raise QloraError(QLORA_EINVAL, "qlora_bwd_main_kernel")
+    return name.decode()
 
 
 def _check(status: int, what: str) -> None:

@@ -483,6 +483,12 @@ int qlora_bwd(const qlora_linear* L, int M, int dtype, const void* x,
                          stream, 1, nullptr, nullptr);
 }
 
+const char* qlora_bwd_main_kernel(const qlora_linear* L, int M, int dtype) {
+  if (check_linear(L, M, dtype)) return nullptr;
+  if (dtype == QLORA_BF16) return bwd_fused_kernel_name(L->fmt, M, L->K, L->N, L->r);
+  return "gemm_dx_f32_kernel";
+}
+
 int qlora_merge(const qlora_linear* L, void* codes_out, void* scales_out,
                 void* stream) {
   int st = check_linear(L, 1, QLORA_BF16);

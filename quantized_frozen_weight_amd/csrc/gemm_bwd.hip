@@ -1580,6 +1580,33 @@ int bwd_row_block(int fmt, int M, int K, int N, int r) {
   return t64 <= 512 ? 64 : 128;
 }
 
+namespace {
+// The fused backward's block shape for a layer: split 128 x 128 tiles for
+// few tiles over a long contraction; else 64-row tiles (producer/consumer)
+// while they make at most two blocks per compute unit; else 128 x 64 tiles
+// (plain int8) while 128 x 128 ones would be fewer than the compute units;
+// else 128 x 128 tiles.
+enum class BwdKind { kSplit, kPC, kWide64, kWide128 };
+BwdKind bwd_kind(int fmt, int M, int K, int N, int r) {
+  int sp, nks;
+  wide_split_plan(M, K, N, &sp, &nks);
+  if (sp > 1) return BwdKind::kSplit;
+  if (bwd_row_block(fmt, M, K, N, r) == 64) return BwdKind::kPC;
+  const long t128 = (long)((M + 127) / 128) * ((K + 127) / 128);
+  if (fmt == 0 && t128 < 256) return BwdKind::kWide64;
+  return BwdKind::kWide128;
+}
+}  // namespace
+
+const char* bwd_fused_kernel_name(int fmt, int M, int K, int N, int r) {
+  switch (bwd_kind(fmt, M, K, N, r)) {
+    case BwdKind::kSplit: return "bwd_wide_kernel<SPLIT> + bwd_fixup_kernel";
+    case BwdKind::kPC: return "bwd_pc_kernel";
+    case BwdKind::kWide64: return "bwd_wide_kernel (128 x 64 tiles)";
+    default: return "bwd_wide_kernel";
+  }
+}
+
 void launch_bwd_fused(int fmt, int M, int K, int N, const uint16_t* dy,
                       const void* codes, const void* scales, const float* B, int hd,
                       const float* A, const float* t, const uint16_t* x, int r,
@@ -1591,11 +1618,7 @@ void launch_bwd_fused(int fmt, int M, int K, int N, const uint16_t* dy,
   a.partB = partB;
   a.pdx = pdx; a.pu = pu;
   wide_split_plan(M, K, N, &a.splits, &a.nks);
-  // split 128 x 128 tiles for few tiles over a long contraction; else
-  // 64-row tiles (producer/consumer) while they make at most two blocks per
-  // compute unit, else the wide 128 x 128 tiles
-  const bool split = a.splits > 1;
-  const bool small = !split && bwd_row_block(fmt, M, K, N, r) == 64;
+  const BwdKind kind = bwd_kind(fmt, M, K, N, r);
   if (fmt == 2) {
     const W8OLayout L = w8o_layout(K, N);
     const char* sb = static_cast<const char*>(scales);
@@ -1603,21 +1626,19 @@ void launch_bwd_fused(int fmt, int M, int K, int N, const uint16_t* dy,
     a.bptr = reinterpret_cast<const int*>(sb + L.bptr);
     a.bent = reinterpret_cast<const u32x2*>(sb + L.bent);
     a.kg = L.kg;
-    if (split) launch_wide<false, true, true>(a, st);
-    else if (small) launch_pc<false, 64, 3, true>(a, st);
+    if (kind == BwdKind::kSplit) launch_wide<false, true, true>(a, st);
+    else if (kind == BwdKind::kPC) launch_pc<false, 64, 3, true>(a, st);
     else launch_wide<false, true>(a, st);
   } else if (fmt == 0) {
     a.sw = static_cast<const float*>(scales);
-    // 128 x 64 tiles while 128 x 128 ones would leave compute units idle
-    const long t128 = (long)((M + 127) / 128) * ((K + 127) / 128);
-    if (split) launch_wide<false, false, true>(a, st);
-    else if (small) launch_pc<false, 64, 3>(a, st);
-    else if (t128 < 256) launch_wide<false, false, false, 64>(a, st);
+    if (kind == BwdKind::kSplit) launch_wide<false, false, true>(a, st);
+    else if (kind == BwdKind::kPC) launch_pc<false, 64, 3>(a, st);
+    else if (kind == BwdKind::kWide64) launch_wide<false, false, false, 64>(a, st);
     else launch_wide<false>(a, st);
   } else {
     a.sc4 = static_cast<const uint16_t*>(scales);
-    if (split) launch_wide<true, false, true>(a, st);
-    else if (small) launch_pc<true, 128, 3>(a, st);
+    if (kind == BwdKind::kSplit) launch_wide<true, false, true>(a, st);
+    else if (kind == BwdKind::kPC) launch_pc<true, 128, 3>(a, st);
     else launch_wide<true>(a, st);
   }
 }

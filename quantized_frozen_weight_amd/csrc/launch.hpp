@@ -100,6 +100,9 @@ void launch_finish_batch(const SkinnyJobs* jobs, int n, hipStream_t st);
 // both 0 when the shape does not split; the pointers are then unused), and
 // a second launch adds them.
 int bwd_row_block(int fmt, int M, int K, int N, int r);
+// Name of the fused backward kernel (or kernels) launch_bwd_fused uses for
+// this shape (static string).
+const char* bwd_fused_kernel_name(int fmt, int M, int K, int N, int r);
 void bwd_split_sizes(int M, int K, int N, int r, size_t* pdx_floats, size_t* pu_floats);
 void launch_bwd_fused(int fmt, int M, int K, int N, const uint16_t* dy,
                       const void* codes, const void* scales, const float* B, int hd,

@@ -17,6 +17,7 @@ from quantized_frozen_weight_amd import binding as Q
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qlora.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "qlora_probe.h")
 GOLDEN = os.path.join(ROOT, "tests", "golden", "page_sizes.txt")
 
 FAKE = 0x100000   # aligned, never dereferenced: every call below fails validation
@@ -27,8 +28,8 @@ def lib():
     return Q.lib()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(qlora_\w+)\s*\(", text, re.M)))
 
 
@@ -42,8 +43,31 @@ def test_header_declares_the_abi():
 
 
 def test_library_exports_every_declared_symbol(lib):
-    for n in declared_functions():
+    for n in declared_functions() + declared_functions(PROBE_HEADER):
         assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_probe_header_matches_the_binding():
+    assert set(declared_functions(PROBE_HEADER)) == set(Q.PROBE_EXPORTS)
+
+
+def test_loaded_library_is_the_in_tree_build(lib):
+    """The binding maps exactly the libqlora.so built next to it."""
+    assert os.path.realpath(Q.loaded_path()) == os.path.realpath(Q.LIB_PATH)
+
+
+def test_backward_kernel_names(lib):
+    """The kernel-name query follows the backward's dispatch (and rejects
+    what qlora_bwd would reject)."""
+    def name(K, N, r, M, dtype):
+        v = lib.qlora_bwd_main_kernel(ctypes.byref(_lin(K, N, r)), M, dtype)
+        return None if v is None else v.decode()
+    assert name(1024, 1024, 8, 1024, Q.QLORA_BF16) == "bwd_pc_kernel"
+    assert name(768, 2304, 4, 4096, Q.QLORA_BF16) == "bwd_wide_kernel (128 x 64 tiles)"
+    assert name(3072, 768, 4, 4096, Q.QLORA_BF16) == "bwd_wide_kernel"
+    assert name(2048, 16384, 8, 512, Q.QLORA_BF16).startswith("bwd_wide_kernel<SPLIT>")
+    assert name(256, 256, 4, 64, Q.QLORA_F32) == "gemm_dx_f32_kernel"
+    assert name(100, 256, 4, 64, Q.QLORA_BF16) is None      # K % 16 != 0
 
 
 def test_status_strings(lib):
