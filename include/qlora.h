@@ -239,6 +239,24 @@ int qlora_bwd(const qlora_linear* L, int M, int dtype, const void* x,
               const void* dy, const float* t_saved, void* dx, float* dA,
               float* dB, void* ws, size_t ws_bytes, void* stream);
 
+/* qlora_bwd for callers that cannot allocate device memory (code under
+ * stream capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * workspace argument; the kernels' scratch is a static device array of
+ * QLORA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends (the one piece of mutable global state of the
+ * library), its address looked up on the first call on each device. The
+ * call allocates and frees nothing. Layers whose backward needs more
+ * scratch than that (qlora_bwd_workspace) return QLORA_EWORKSPACE before
+ * anything is enqueued. All calls on one GPU share the array and it keeps
+ * the last call's contents (nothing in it needs to start at zero): calls
+ * that can overlap on one GPU -- other streams, other threads -- race, so
+ * order them on one stream. Otherwise the same arguments, results (bitwise
+ * those of qlora_bwd) and errors as qlora_bwd. */
+#define QLORA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int qlora_bwd_noalloc(const qlora_linear* L, int M, int dtype, const void* x,
+                      const void* dy, const float* t_saved, void* dx, float* dA,
+                      float* dB, void* stream);
+
 /* qlora_bwd in two calls, for callers that take the adapter gradients off the
  * path that carries dx to the next layer (for instance onto a second stream,
  * the way weight gradients are usually overlapped with the rest of a

@@ -54,8 +54,9 @@ EXPORTS = (
     "qlora_quantize_rows", "qlora_fwd_acc", "qlora_fwd_timed", "qlora_bwd_timed",
     "qlora_merge", "qlora_bwd_partial", "qlora_bwd_finish", "qlora_fwd_a8w4",
     "qlora_quantize_heads", "qlora_outlier_layout", "qlora_bwd_finish_batch",
-    "qlora_bwd_partials_bytes", "qlora_bwd_main_kernel",
+    "qlora_bwd_partials_bytes", "qlora_bwd_main_kernel", "qlora_bwd_noalloc",
 )
+QLORA_NOALLOC_SCRATCH_BYTES = 16 << 20
 # include/qlora_probe.h: measurement probes (not part of the layer)
 PROBE_EXPORTS = ("qlora_probe_mfma", "qlora_probe_copy", "qlora_probe_read", "qlora_probe_empty")
 QLORA_PROBE_BF16, QLORA_PROBE_I8 = 0, 1
@@ -107,6 +108,7 @@ def lib() -> ctypes.CDLL:
     L.qlora_quantize_heads.argtypes = [vp, i, i, i, i, vp, vp, vp]
     L.qlora_outlier_layout.argtypes = [i, i, psz, psz, psz, ctypes.POINTER(ctypes.c_int32)]
     L.qlora_bwd_main_kernel.argtypes = [plin, i, i]
+    L.qlora_bwd_noalloc.argtypes = [plin, i, i, vp, vp, vp, vp, vp, vp, vp]
     for name in EXPORTS[1:]:
         getattr(L, name).restype = ctypes.c_int
     L.qlora_bwd_main_kernel.restype = ctypes.c_char_p

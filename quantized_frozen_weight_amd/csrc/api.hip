@@ -2,6 +2,8 @@
 // sequence of each call. Contract and citations: include/qlora.h.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "launch.hpp"
 #include "outlier.hpp"
 #include "qlora.h"
@@ -122,6 +124,33 @@ BwdLayout bwd_layout(const qlora_linear* L, int M, int dtype) {
 }
 
 inline char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+// Scratch of qlora_bwd_noalloc: a static device array, one copy per GPU the
+// library runs on, held until the process ends. In host code `scratch`
+// names a host-side stand-in, not device memory: its device address is taken
+// once per device with hipGetSymbolAddress (that device current) and only
+// that address is passed to kernels.
+constexpr size_t kNoAllocScratch = QLORA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) int8_t scratch[kNoAllocScratch];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up on the first call
+// on that device.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QLORA_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return QLORA_EHIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return QLORA_OK;
+}
 
 // Optional timing marks around a call's main product kernel.
 void mark(void* ev, hipStream_t s) {
@@ -487,6 +516,19 @@ const char* qlora_bwd_main_kernel(const qlora_linear* L, int M, int dtype) {
   if (check_linear(L, M, dtype)) return nullptr;
   if (dtype == QLORA_BF16) return bwd_fused_kernel_name(L->fmt, M, L->K, L->N, L->r);
   return "gemm_dx_f32_kernel";
+}
+
+int qlora_bwd_noalloc(const qlora_linear* L, int M, int dtype, const void* x,
+                      const void* dy, const float* t_saved, void* dx, float* dA,
+                      float* dB, void* stream) {
+  int st = check_linear(L, M, dtype);
+  if (st) return st;
+  if (bwd_layout(L, M, dtype).total > kNoAllocScratch) return QLORA_EWORKSPACE;
+  if (pending_error()) return QLORA_EHIP;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st) return st;
+  return qlora_bwd(L, M, dtype, x, dy, t_saved, dx, dA, dB, ws, kNoAllocScratch, stream);
 }
 
 int qlora_merge(const qlora_linear* L, void* codes_out, void* scales_out,

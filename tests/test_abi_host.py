@@ -372,3 +372,16 @@ def test_partials_bytes(lib):
                                         ctypes.byref(n)) == Q.QLORA_EINVAL
     assert lib.qlora_bwd_partials_bytes(ctypes.byref(_lin()), 64, Q.QLORA_F32,
                                         None) == Q.QLORA_EINVAL
+
+
+def test_noalloc_backward_validates_before_any_launch(lib):
+    """qlora_bwd_noalloc checks its arguments and the static scratch's size
+    on the host, before touching the GPU."""
+    call = lambda L, M: lib.qlora_bwd_noalloc(ctypes.byref(L), M, Q.QLORA_BF16, FAKE, FAKE,  # noqa: E731
+                                              None, FAKE, FAKE, FAKE, None)
+    assert call(_lin(K=100), 64) == Q.QLORA_EINVAL                 # K % 16 != 0
+    assert call(_lin(K=2048, N=16384, r=8), 512) == Q.QLORA_EWORKSPACE   # 37 MiB of scratch
+    L = _lin(K=2048, N=16384, r=8)
+    need = ctypes.c_size_t()
+    assert lib.qlora_bwd_workspace(ctypes.byref(L), 512, Q.QLORA_BF16, ctypes.byref(need)) == 0
+    assert need.value > Q.QLORA_NOALLOC_SCRATCH_BYTES
