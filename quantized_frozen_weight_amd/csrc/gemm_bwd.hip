@@ -852,7 +852,13 @@ __global__ __launch_bounds__(256, 2) void bwd_wide_kernel(BwdArgs a) {
   constexpr bool XPRE = BM * BN * 2 <= 8192;          // x tile kept outside the ring
   constexpr int CBSZ = BN * 128;                      // converted codes [BN][64] bf16
   constexpr int BUSZ = UCB * 16 * 128;                // converted B [16 UCB][64] bf16: hi | mid | lo
-  constexpr int TSZ = BM * R * 4;                     // t tile (pitch r)
+  // The dB operand, t split into bf16 hi, mid and lo columns in the MFMA
+  // operand layout [UCB][BM / 32][64 lanes][16 B], built once per block in
+  // LDS where it fits beside two blocks per compute unit and the float32 t
+  // tile fits in the converted-code buffer it passes through (TFL); else
+  // each dB stage rebuilds it from the t tile.
+  constexpr bool TFL = R != 8 && BM * R * 4 <= CBSZ;
+  constexpr int TSZ = TFL ? UCB * (BM / 32) * 1024 : BM * R * 4;   // t operand, or t tile (pitch r)
   constexpr int XTSZ = BM * BN * 2;
   constexpr int EFL = (BM + BN) * R;                  // epilogue floats: U [BM][R], A^T [R][BN]
   static_assert(EFL * 4 + (XPRE ? 0 : XTSZ) <= S * STG, "epilogue and x tile fit in the ring");
@@ -863,7 +869,10 @@ __global__ __launch_bounds__(256, 2) void bwd_wide_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) int8_t ring[S * STG + CBSZ + BUSZ + TSZ + SCSZ + (XPRE ? XTSZ : 0)];
   int8_t* CB = ring + S * STG;
   int8_t* BU = CB + CBSZ;
-  float* Ts = reinterpret_cast<float*>(BU + BUSZ);                             // [BM][r]
+  // t tile [BM][r] float32: its own region, or (TFL) the converted-code
+  // buffer until the t operand is built from it
+  float* Ts = reinterpret_cast<float*>(TFL ? CB : BU + BUSZ);
+  int8_t* TF = BU + BUSZ;                                                      // t operand (TFL)
   float* SCs = reinterpret_cast<float*>(BU + BUSZ + TSZ);                      // [64] (4-bit)
   int8_t* Xs = XPRE ? BU + BUSZ + TSZ + SCSZ : ring + EFL * 4;                 // [BM][BN] bf16
 
@@ -1095,6 +1104,32 @@ __global__ __launch_bounds__(256, 2) void bwd_wide_kernel(BwdArgs a) {
   for (int e = 3 * R * 32 + tid; e < UCB * 16 * 32; e += 256)      // 4-byte pairs
     *reinterpret_cast<uint32_t*>(BU + swz128(e / 32, (e % 32) >> 2) + (e & 3) * 4) = 0u;
   __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());    // stores land before the first barrier
+  if constexpr (TFL) {
+    // the t operand from the t tile (which sits in the converted-code
+    // buffer: the loop's first barrier comes before the first conversion);
+    // wave w builds fragments f = w, w + 4, ... of the UCB * BM / 32
+    __syncthreads();
+    for (int f = wid; f < UCB * (BM / 32); f += 4) {
+      const int cb = f / (BM / 32), c = f % (BM / 32);
+      const int j = cb * 16 + (lane & 15), part = j / R, jr = j - part * R;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int m = 32 * c + 8 * (lane >> 4) + e;
+        v[e] = (jr < r && part < 3) ? Ts[m * r + (jr < r ? jr : 0)] : 0.f;
+      }
+      u32x4 hi, mid, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t me, le;
+        hi[e] = pk_bf16_split3(v[2 * e], v[2 * e + 1], me, le);
+        mid[e] = me;
+        lo[e] = le;
+      }
+      *reinterpret_cast<u32x4*>(TF + (f * 64 + lane) * 16) = part == 0 ? hi : part == 1 ? mid : lo;
+    }
+    __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+  }
 
   const int rows_here = M - m0 < BM ? M - m0 : BM;
   // dB operand: t split into bf16 hi, mid and lo columns, lane -> column
@@ -1240,7 +1275,13 @@ __global__ __launch_bounds__(256, 2) void bwd_wide_kernel(BwdArgs a) {
     // n = 16 w + q of rows 0..3.
     if (kt % a.tiles_x == kt_blk) {
       bf16x8 tfr[UCB][BM / 32];
-      {
+      if constexpr (TFL) {
+#pragma unroll
+        for (int cb = 0; cb < UCB; ++cb)
+#pragma unroll
+          for (int c = 0; c < BM / 32; ++c)
+            tfr[cb][c] = *reinterpret_cast<const bf16x8*>(TF + ((cb * (BM / 32) + c) * 64 + lane) * 16);
+      } else {
 #pragma unroll
         for (int cb = 0; cb < UCB; ++cb) {
           // column j: part j / R (hi, mid, lo) of t[., j % R]
