@@ -77,6 +77,10 @@ def parse():
     p.add_argument("--cold-steps", type=int, default=30,
                    help="steps timed one by one after a 512 MiB flush (0: skip)")
     p.add_argument("--no-peaks", action="store_true", help="skip re-measuring the peaks")
+    p.add_argument("--pmc-summary", metavar="DIR", default=None,
+                   help="no GPU work: print the per-dispatch mean of every counter, per "
+                        "kernel, from the counter_collection.csv files of a rocprofv3 "
+                        "--pmc run written under DIR")
     return p.parse_args()
 
 
@@ -123,6 +127,9 @@ class Layer:
 
 def main():
     args = parse()
+    if args.pmc_summary is not None:
+        pmc_summary(args.pmc_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(data-parallel, each GPU would run the same step on its own rows and "
@@ -754,6 +761,33 @@ def cpu_baseline(w, budget_s):
         "value_1thread": round(ops1 / one / 1e12, 5),
         "sample_1thread": f"layer 0, median of 3 runs of {one:.2f} s",
     }
+
+
+def pmc_summary(d):
+    """Per-kernel table of a rocprofv3 --pmc run: for each kernel (name, grid,
+    workgroup) the number of dispatches and, per counter, the mean and the
+    median over dispatches of the counter's value summed over its instances
+    (shader engines, channels) within a dispatch."""
+    import collections
+    import csv
+    import glob
+    import re
+    rows = collections.defaultdict(lambda: collections.defaultdict(lambda: collections.defaultdict(float)))
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                name = re.sub(r"\(.*", "", row.get("Kernel_Name", "")
+                              .replace("(anonymous namespace)::", "").replace("qlora::", ""))
+                key = (name, row.get("Grid_Size"), row.get("Workgroup_Size"))
+                rows[key][row["Counter_Name"]][row.get("Dispatch_Id")] += float(row["Counter_Value"])
+    print("| kernel | grid | wg | dispatches | counter | mean | median |")
+    print("|---|---|---|---|---|---|---|")
+    order = sorted(rows.items(), key=lambda kv: -max(len(v) for v in kv[1].values()))
+    for (name, grid, wg), counters in order:
+        for c, per in sorted(counters.items()):
+            v = sorted(per.values())
+            print(f"| {name} | {grid} | {wg} | {len(v)} | {c} | {sum(v) / len(v):.6g} "
+                  f"| {v[len(v) // 2]:.6g} |")
 
 
 if __name__ == "__main__":
