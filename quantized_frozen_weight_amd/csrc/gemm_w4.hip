@@ -10,16 +10,13 @@
 // alpha / rank.)
 //
 // A stage covers half of one 128-wide group of k, so one fp16 scale per
-// output column applies to the whole stage, and a 128 x 128 block needs
-// 64 KB of LDS (two per compute unit). Three tiles move global -> LDS
+// output column applies to the whole stage. Two tiles move global -> LDS
 // without registers (ring.hpp): the x rows (bf16, 128-byte rows swizzled by
-// 16-byte chunk), the packed codes [BN n][32 bytes], and, once before the
-// loop, the block's scales [BN][K / 128] (a contiguous slab of the scale
-// array). Once a stage has landed the block converts its codes in one
-// cooperative pass, every nibble once: CB [BN n][64 k] = bf16(q sc), stored
-// like the x rows. The MFMA loop then reads both operands with plain 16-byte
-// LDS reads. The adapter term runs in the epilogue on v_mfma_f32_16x16x4_f32
-// (ring.hpp).
+// 16-byte chunk) and the packed codes [BN n][32 bytes]; once before the loop
+// the block's scales [BN][K / 128] (a contiguous slab of the scale array)
+// follow the same path. Each wave widens the codes of its own columns from
+// LDS straight into MFMA operand registers (below). The adapter term runs in
+// the epilogue on v_mfma_f32_16x16x4_f32 (ring.hpp).
 #include "launch.hpp"
 #include "ring.hpp"
 
@@ -69,29 +66,34 @@ __device__ __forceinline__ u32x4 nibbles_bf16(uint32_t w, float sc) {
 }
 
 // G: the largest number of 128-wide k groups the block's scale slab holds.
-template <int BM, int BN, int S, int R, int G>
-__global__ __launch_bounds__(256) void fwd_w4_kernel(W4Args a) {
-  constexpr int BK = 64;                           // k per stage: half a scale group
+//
+// A block owns BM rows x 128 columns of y. Wave w owns columns
+// [32 w, 32 w + 32) and every row of the block, so the codes it multiplies
+// are its own: each lane reads the packed word holding the 8 codes of its
+// operand slot (column n, 8 consecutive k -- exactly one 32-bit word of the
+// [n][k / 2] layout) and widens it straight into the MFMA operand register,
+// with no converted copy in LDS and no second barrier per stage. The
+// widening of one operand then overlaps the matrix work of the previous one
+// inside the wave.
+template <int BM, int S, int R, int G>
+__global__ __launch_bounds__(256, 2) void fwd_w4_kernel(W4Args a) {
+  constexpr int BN = 128, BK = 64;                 // k per stage: half a scale group
   constexpr int ASZ = BM * 128, BSZ = BN * 32, STG = ASZ + BSZ;
-  constexpr int AI = BM / 32, BI = BN / 128, LPS = AI + BI;   // DMA per wave per stage
-  constexpr int FM = BM / 32, FN = BN / 32;
-  constexpr int CBSZ = BN * 128;
-  static_assert(BN == 128, "code rows of 32 bytes: 32 rows per DMA instruction, one per wave");
-  // after the loop the ring and the converted-code buffer hold the epilogue
-  // operands, then one output staging strip per wave
+  constexpr int AI = BM / 32, LPS = AI + 1;        // DMA per wave per stage: x rows, code rows
+  constexpr int FM = BM / 16, FN = 2;              // the wave's 16 x 16 blocks: all rows, 32 columns
+  // after the loop the ring holds the epilogue operands, then one output
+  // staging strip per wave
   constexpr int EPB = (EpiOps<BM, BN, R, false>::kFloats * 4 + 15) / 16 * 16;
-  static_assert(EPB + 4 * epi_strip_bytes<uint16_t, FN>() <= S * STG + CBSZ, "epilogue fits");
+  static_assert(EPB + 4 * epi_strip_bytes<uint16_t, FN>() <= S * STG, "epilogue fits");
   const int K = a.K, M = a.M, N = a.N;
   const int ngrp = K / 128;
   static_assert(BN * G * 2 % 1024 == 0, "the scale slab takes whole 1 KB DMA instructions");
   // scales of the block's columns: [BN][ngrp] fp16, ngrp <= G
-  __shared__ __attribute__((aligned(1024))) int8_t lds[S * STG + CBSZ + BN * G * 2];
+  __shared__ __attribute__((aligned(1024))) int8_t lds[S * STG + BN * G * 2];
   int8_t* ring = lds;
-  int8_t* CB = lds + S * STG;
-  const _Float16* SC = reinterpret_cast<const _Float16*>(lds + S * STG + CBSZ);
+  const _Float16* SC = reinterpret_cast<const _Float16*>(lds + S * STG);
 
   const int tid = threadIdx.x, lane = tid & 63, wid = wave_id();
-  const int wm = wid >> 1, wn = wid & 1;
   int mt, nt;
   xcd_tile((int)blockIdx.x, (a.M + BM - 1) / BM, a.tiles_x, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
@@ -108,15 +110,16 @@ __global__ __launch_bounds__(256) void fwd_w4_kernel(W4Args a) {
     for (int o = wid * 1024; o < bytes; o += 4096) {
       const int e = o + lane * 16;
       const int8_t* src = (e < bytes && e < valid) ? src0 + e : zero_chunk(lane);
-      lds_dma16(src, lds + S * STG + CBSZ + o);
+      lds_dma16(src, lds + S * STG + o);
     }
   }
   // Loads from a wave-wide base (the stage's first k) plus a fixed 32-bit
   // lane offset: x as 128-byte rows swizzled by 16-byte chunk, 8 rows per
-  // instruction; the codes as 32-byte rows, 32 per instruction (lanes 2 i and
-  // 2 i + 1 take the two halves of row i, read back in that order). Rows past
-  // M repeat row M - 1 and weight rows past N repeat row N - 1: their products
-  // land only in outputs that are never stored.
+  // instruction; the codes as 32-byte rows, 32 per instruction (lanes 2 i
+  // and 2 i + 1 take the two halves of row i), wave w loading the rows of
+  // its own columns. Rows past M repeat row M - 1 and weight rows past N
+  // repeat row N - 1: their products land only in outputs that are never
+  // stored.
   uint32_t voA[AI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
@@ -148,44 +151,40 @@ __global__ __launch_bounds__(256) void fwd_w4_kernel(W4Args a) {
   // may differ): loads complete in issue order, so every wave's share has
   // landed once its stage 0 has, and the first barrier covers all waves.
 
-  const int crow = tid >> 1, chalf = tid & 1;        // conversion: row n, 32 k half
+  // the lane's operand slots: column 32 wid + 16 jf + lane % 16 (code row
+  // in the tile), k 8 (lane / 16) .. + 8 of each 32-wide step
+  const int nl = 32 * wid + (lane & 15);
   int slot = 0;
   for (int kt = 0; kt < nk; ++kt) {
     wait_stages<LPS, 0, S - 2>(nk - 1 - kt);
-    __builtin_amdgcn_s_barrier();                    // stage kt landed; CB free
+    __builtin_amdgcn_s_barrier();                    // stage kt landed; slot of kt - 1 free
     const int8_t* As = ring + slot * STG;
     const int8_t* Bs = As + ASZ;
-
-    // CB[n][k] = bf16(q[n][k] sc[n][kt / 2]) for row crow, k in [32 chalf, 32 chalf + 32)
-    {
-      const float sc = (float)SC[crow * ngrp + (kt >> 1)];
-      const u32x4 w = *reinterpret_cast<const u32x4*>(Bs + crow * 32 + chalf * 16);
+    uint32_t raw[FN][BK / 32];
+    float sc[FN];
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
-        *reinterpret_cast<u32x4*>(CB + swz128(crow, 4 * chalf + d)) = nibbles_bf16(w[d], sc);
+    for (int jf = 0; jf < FN; ++jf) {
+      sc[jf] = (float)SC[(nl + 16 * jf) * ngrp + (kt >> 1)];
+#pragma unroll
+      for (int kk = 0; kk < BK / 32; ++kk)
+        raw[jf][kk] = *reinterpret_cast<const uint32_t*>(Bs + (nl + 16 * jf) * 32 + kk * 16 + (lane >> 4) * 4);
     }
-    __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
-    __builtin_amdgcn_s_barrier();                    // CB visible
-    // the next stage's loads, into the slot stage kt - 1 left: queued beside
-    // the products rather than ahead of the conversion, where the wave would
-    // wait for the memory pipeline to take them (measured: 4% faster)
+    // the next stage's loads, into the slot stage kt - 1 left, once this
+    // stage's codes are read
     if (kt + S - 1 < nk) issue(kt + S - 1, slot == 0 ? S - 1 : slot - 1);
-
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
       const int c = kk * 4 + (lane >> 4);
-      bf16x8 af[FM], bf[FN];
+      bf16x8 bf[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(As + swz128(wm * (BM / 2) + i * 16 + (lane & 15), c));
+      for (int jf = 0; jf < FN; ++jf) bf[jf] = __builtin_bit_cast(bf16x8, nibbles_bf16(raw[jf][kk], sc[jf]));
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bf[j] = *reinterpret_cast<const bf16x8*>(CB + swz128(wn * (BN / 2) + j * 16 + (lane & 15), c));
+      for (int i = 0; i < FM; ++i) {
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(As + swz128(i * 16 + (lane & 15), c));
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        for (int jf = 0; jf < FN; ++jf)
+          acc[i][jf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[jf], acc[i][jf], 0, 0, 0);
+      }
     }
     slot = slot == S - 1 ? 0 : slot + 1;
   }
@@ -194,7 +193,7 @@ __global__ __launch_bounds__(256) void fwd_w4_kernel(W4Args a) {
   __syncthreads();
   ep.store(E, M, N, m0, n0, a.r);
   __syncthreads();
-  epilogue_lowrank<BM, BN, R, false>(acc, E, M, N, m0, n0, wm * (BM / 2), wn * (BN / 2), a.s, a.y,
+  epilogue_lowrank<BM, BN, R, false>(acc, E, M, N, m0, n0, 0, 32 * wid, a.s, a.y,
                                      ring + EPB + wid * epi_strip_bytes<uint16_t, FN>());
 }
 
@@ -203,18 +202,20 @@ void launch_tiles(W4Args a, hipStream_t st) {
   constexpr int BN = 128;
   a.tiles_x = (a.N + BN - 1) / BN;
   const dim3 grid((unsigned)(a.tiles_x * ((a.M + BM - 1) / BM)));
-  if (a.r <= 4) fwd_w4_kernel<BM, BN, S, 4, G><<<grid, 256, 0, st>>>(a);
-  else if (a.r <= 8) fwd_w4_kernel<BM, BN, S, 8, G><<<grid, 256, 0, st>>>(a);
-  else if (a.r <= 16) fwd_w4_kernel<BM, BN, S, 16, G><<<grid, 256, 0, st>>>(a);
-  else fwd_w4_kernel<BM, BN, S, 32, G><<<grid, 256, 0, st>>>(a);
+  if (a.r <= 4) fwd_w4_kernel<BM, S, 4, G><<<grid, 256, 0, st>>>(a);
+  else if (a.r <= 8) fwd_w4_kernel<BM, S, 8, G><<<grid, 256, 0, st>>>(a);
+  else if (a.r <= 16) fwd_w4_kernel<BM, S, 16, G><<<grid, 256, 0, st>>>(a);
+  else fwd_w4_kernel<BM, S, 32, G><<<grid, 256, 0, st>>>(a);
 }
 
-template <int BM, int S>
+// Three ring slots where they fit beside the scale slab at two blocks per
+// compute unit (80 KB each), else two.
+template <int BM>
 void launch_groups(const W4Args& a, hipStream_t st) {
   const int ngrp = a.K / 128;                      // validated: <= kW4MaxGroups
-  if (ngrp <= 8) launch_tiles<BM, S, 8>(a, st);
-  else if (ngrp <= 32) launch_tiles<BM, S, 32>(a, st);
-  else launch_tiles<BM, S, kW4MaxGroups>(a, st);
+  if (ngrp <= 8) launch_tiles<BM, 3, 8>(a, st);
+  else if (ngrp <= 32) launch_tiles<BM, 3, 32>(a, st);
+  else launch_tiles<BM, BM == 128 ? 2 : 3, kW4MaxGroups>(a, st);
 }
 
 }  // namespace
@@ -227,8 +228,8 @@ void launch_gemm_fwd_w4(int M, int N, int K, const uint16_t* x,
   a.M = M; a.N = N; a.K = K; a.x = x; a.packed = packed; a.scales = scales;
   a.t = t; a.B = B; a.hd = hd; a.r = r; a.s = s; a.y = y;
   const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
-  if (t128 >= kCUs) launch_groups<128, 2>(a, st);
-  else launch_groups<64, 2>(a, st);
+  if (t128 >= kCUs) launch_groups<128>(a, st);
+  else launch_groups<64>(a, st);
 }
 
 }  // namespace qlora
