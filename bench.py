@@ -428,18 +428,21 @@ def describe(w):
            f"LoRA r={w.r} alpha={w.alpha:g}, {w.dtype} activations"
 
 
-# HBM traffic of the dominant kernel per launch on the benchmarked workload,
-# from two rocprofv3 counter passes (FETCH_SIZE, then WRITE_SIZE, KiB per
-# dispatch), each divided by what the same counter reads per KiB of a plain
-# 256 MiB device copy in the same run. Valid only for the kernel's device
-# code it was taken on: the SHA-256 of the sources that define that kernel
-# and of the compiler flags; otherwise reported as null.
+# HBM traffic of the dominant kernel per launch on the benchmarked workload
+# (the MLP's fused backward, bwd_pc_kernel), averaged over its 32 layers like
+# "achieved": 31 launches at 1024 -> 1024 (14.32 MB each) and one at
+# 784 -> 1024 (29.57 MB). From two rocprofv3 counter passes (FETCH_SIZE,
+# then WRITE_SIZE, KiB per dispatch), each divided by what the same counter
+# reads per KiB for the library's read probe (1 GiB, larger than the
+# last-level cache) and copy probe (256 MiB) in the same runs. Valid only for
+# the kernel's device code it was taken on: the SHA-256 of the sources that
+# define that kernel and of the compiler flags; otherwise reported as null.
 TRAFFIC = {
     "workload": 2,
     "weights": "w8",
     "sources": ["gemm_bwd.hip", "ring.hpp", "common.hpp"],
-    "sha256": None,
-    "bytes_per_launch": None,
+    "sha256": "7e733130757bab3989fa1036865eeefcc987e0332039ee0132208c9621c3fa04",
+    "bytes_per_launch": 14795848,
 }
 
 
