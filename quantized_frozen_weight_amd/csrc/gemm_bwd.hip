@@ -242,16 +242,24 @@ __device__ __forceinline__ float tile_bf16(const int8_t* tile, int row, int e) {
 // kt + 1 into the other buffer, so a compute unit overlaps the matrix work
 // of one wave with the vector work of the other on each SIMD. One barrier
 // per stage hands the buffers over.
-template <bool W4, int BM, int BN, int S, int R, bool AFF = false>
+// BRES (int8 weights of one head, N <= kBresN): the channel scales sw [N]
+// and B [R][N] stay in LDS for the whole kernel, loaded once before the
+// loop, so that a stage's loads are only its dy and code rows.
+constexpr int kBresN = 1024;
+
+template <bool W4, int BM, int BN, int S, int R, bool AFF = false, bool BRES = false>
 __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
   constexpr int KC = 64;                              // n per stage
   constexpr int RB = W4 ? BN / 2 : BN;                // code bytes per row of n
   static_assert(!AFF || (!W4 && BN == 64 && KC == kW8OBwdCellN), "affine: int8, 64 x 64 cells");
+  static_assert(!BRES || (!W4 && !AFF), "resident scales and B: plain int8 weights");
   // aux tile: a header with the stage's weight scales (int8: sw[n], 64
   // floats; 4-bit: for each n the 16-byte chunk of the scale array that holds
   // sc[n][k0 / 128]; affine weights: none), then the B columns [R][64] float
+  // (none with BRES)
   constexpr int HDR = AFF ? 0 : W4 ? 1024 : 256;
-  constexpr int AUXI = (HDR + R * 256 + 4095) / 4096;  // aux DMA instructions per producer wave
+  constexpr int AUXI = BRES ? 0 : (HDR + R * 256 + 4095) / 4096;  // aux DMA instructions per producer wave
+  constexpr int BRSZ = BRES ? (1 + R) * kBresN * 4 : 0;           // resident sw [kBresN] | B [R][kBresN]
   constexpr int ASZ = BM * 128, BSZ = KC * RB, XSZ = 4 * AUXI * 1024;
   constexpr int STG = ASZ + BSZ + XSZ;
   // per producer wave and stage: dy rows, code rows, aux
@@ -280,13 +288,14 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
   // the dB operand, t as bf16 hi, mid and lo columns in the MFMA operand
   // layout [UCB][BM / 32][64 lanes][16 B], built once by the consumers
   constexpr int TFSZ = UCB * (BM / 32) * 1024;
-  __shared__ __attribute__((aligned(1024))) int8_t ring[S * STG + 2 * CBSZ + 2 * BUSZ + TSZ + AQSZ + TFSZ + (XPRE ? XTSZ : 0)];
+  __shared__ __attribute__((aligned(1024))) int8_t ring[S * STG + 2 * CBSZ + 2 * BUSZ + TSZ + AQSZ + TFSZ + (XPRE ? XTSZ : 0) + BRSZ];
   int8_t* CB0 = ring + S * STG;
   int8_t* BU0 = CB0 + 2 * CBSZ;
   float* Ts = reinterpret_cast<float*>(BU0 + 2 * BUSZ);                        // [BM][r]
   const float* Aq = reinterpret_cast<const float*>(BU0 + 2 * BUSZ + TSZ);    // [BN][r]
   int8_t* TF = BU0 + 2 * BUSZ + TSZ + AQSZ;                                    // t operand
   int8_t* Xs = XPRE ? TF + TFSZ : ring + EFL * 4;                              // [BM][BN] bf16
+  float* BRs = reinterpret_cast<float*>(TF + TFSZ + (XPRE ? XTSZ : 0));        // BRES: sw | B
 
   const int lane = threadIdx.x & 63, wid = wave_id();
   const bool producer = wid >= 4;
@@ -375,9 +384,10 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
   // 4-float chunks; a header source moves by adv bytes per n of the stage, a
   // B source (adv 0) by the stage's offset in B (a stage of 64 n lies inside
   // one head: the head width is a multiple of 64)
-  const int8_t* srcX[AUXI];
-  int nX[AUXI], advX[AUXI];
-  bool okX[AUXI];
+  constexpr int AUXA = AUXI > 0 ? AUXI : 1;         // (array extent: none used when AUXI = 0)
+  const int8_t* srcX[AUXA];
+  int nX[AUXA], advX[AUXA];
+  bool okX[AUXA];
 #pragma unroll
   for (int i = 0; i < AUXI; ++i) {
     const int ci = (pw * AUXI + i) * 64 + lane;
@@ -476,10 +486,14 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
       *reinterpret_cast<uint16_t*>(CB + swz128(kl, nqo >> 1) + (nqo & 1) * 8 + 2 * (nl & 3)) =
           (uint16_t)f32_to_bf16(__uint_as_float(vbits));
   };
-  auto convert = [&](int slot, int buf, const Outl& ol, auto&& hook) {
+  auto convert = [&](int slot, int buf, const Outl& ol, int nb, auto&& hook) {
     const int8_t* Bs = ring + slot * STG + ASZ;
     const int8_t* Xb = Bs + BSZ;
-    const float* Xa = reinterpret_cast<const float*>(Xb);
+    // the stage's sw [64] and B [R] columns: the aux tile, or (BRES) the
+    // resident copies at the stage's first n
+    const float* Xa = BRES ? BRs + nb : reinterpret_cast<const float*>(Xb);
+    constexpr int BP = BRES ? kBresN : 64;           // pitch of B's rows
+    constexpr int BO = BRES ? kBresN : HDR / 4;      // offset of B's first row
     int8_t* CB = CB0 + buf * CBSZ;
     int8_t* BU = BU0 + buf * BUSZ;
     hook();
@@ -488,7 +502,7 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
     for (int q = 0; q < NBU; ++q) {
       const int e = ptid + 256 * q;
       const int j = e >> 5, p = e & 31;
-      if (e < R * 32) bq[q] = *reinterpret_cast<const f32x2*>(Xa + HDR / 4 + 64 * j + 2 * p);
+      if (e < R * 32) bq[q] = *reinterpret_cast<const f32x2*>(Xa + BO + BP * j + 2 * p);
     }
     if constexpr (W4) {
       float sc[4];
@@ -588,6 +602,18 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
       }
     }
     if constexpr (XPRE) issue_x();
+    if constexpr (BRES) {
+      // sw [N] and B [r][N] (rows up to R, columns up to kBresN; zeros past
+      // them), 16 bytes per lane, ahead of the stage loads (loads complete in
+      // issue order, so they have landed once stage 0 has)
+      for (int o = pw * 1024; o < BRSZ; o += 4096) {
+        const int e = (o + lane * 16) / 4;             // float index in sw | B
+        const int row = e / kBresN, n = e % kBresN;    // row 0: sw; row 1 + j: B[j]
+        const float* src = row == 0 ? a.sw + n : a.B + (long)(row - 1) * N + n;
+        const bool ok = n < N && (row == 0 || row - 1 < r);
+        lds_dma16(ok ? (const void*)src : (const void*)zero_chunk(lane), BRs + o / 4);
+      }
+    }
 #pragma unroll
     for (int st = 0; st < S - 1; ++st)
       if (st < nk) issue(st, st);
@@ -639,7 +665,7 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
       outl_range(0, ocur);
       outl_load(ocur);
     }
-    convert(0, 0, ocur, [] {});
+    convert(0, 0, ocur, 0, [] {});
     if constexpr (AFF) {
       // stage 1's outliers are read before the loop queues more loads
       outl_range(nk > 1 ? 1 : 0, ocur);
@@ -675,14 +701,14 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
       // read-ahead registers can be waited for by count)
       if constexpr (AFF) {
         issue(kt + S - 1, pslot);
-        if (kt + 1 < nk) convert(nslot, (kt + 1) & 1, ocur, [] {});
+        if (kt + 1 < nk) convert(nslot, (kt + 1) & 1, ocur, (kt + 1) * KC, [] {});
       } else if (kt + 1 < nk) {
         // the stage loads are queued from inside the conversion, ahead of
         // its first LDS read (measured: about 5% faster on 1024-wide layers
         // than queueing them before the call, the form the affine weights
         // keep)
         const bool more = kt + S - 1 < nk;
-        convert(nslot, (kt + 1) & 1, ocur, [&] {
+        convert(nslot, (kt + 1) & 1, ocur, (kt + 1) * KC, [&] {
           if (more) issue(kt + S - 1, pslot);
         });
       }
@@ -1570,6 +1596,17 @@ void launch_pc(BwdArgs a, hipStream_t st) {
   constexpr int BM = 64;
   a.tiles_x = (a.K + BN - 1) / BN;
   const dim3 grid((unsigned)(a.tiles_x * ((a.M + BM - 1) / BM)));
+  if constexpr (!W4 && !AFF) {
+    // plain int8 of one head and at most kBresN outputs, rank 5 to 8, at
+    // least 512 rows: scales and B resident in LDS (measured: 1-1.5 % faster
+    // on 1024-row layers; on short grids loading them up front costs more
+    // than it saves). The block takes 112 KB, one per compute unit as
+    // without them; at rank 4 they would cost the second block.
+    if (a.N <= kBresN && a.hd == a.N && a.r > 4 && a.r <= 8 && a.M >= 512) {
+      bwd_pc_kernel<false, BM, BN, S, 8, false, true><<<grid, 512, 0, st>>>(a);
+      return;
+    }
+  }
   if (a.r <= 4) bwd_pc_kernel<W4, BM, BN, S, 4, AFF><<<grid, 512, 0, st>>>(a);
   else if (a.r <= 8) bwd_pc_kernel<W4, BM, BN, S, 8, AFF><<<grid, 512, 0, st>>>(a);
   else if (a.r <= 16) bwd_pc_kernel<W4, BM, BN, S, 16, AFF><<<grid, 512, 0, st>>>(a);
