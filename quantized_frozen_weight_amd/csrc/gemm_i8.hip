@@ -583,7 +583,16 @@ void launch_shape(I8Args a, hipStream_t st) {
   }
   const long t64 = (long)((a.M + 63) / 64) * ((a.N + 63) / 64);
   const long t128 = (long)((a.M + 127) / 128) * ((a.N + 127) / 128);
+  const long t192 = (long)((a.M + 127) / 128) * ((a.N + 191) / 192);
+  // rounds of two blocks per compute unit, weighted by the work per block:
+  // 128 x 192 tiles (1.5 times a 128 x 128 tile's) where N is a multiple of
+  // 192 and they take fewer weighted rounds (GPT-2's 2304- and 3072-wide
+  // products: 576 and 768 blocks of 128 x 128 in two rounds, 384 and 512 of
+  // 128 x 192 in one)
+  const long rounds128 = (t128 + 2 * kCUs - 1) / (2 * kCUs), rounds192 = (t192 + 2 * kCUs - 1) / (2 * kCUs);
   if (t64 <= 2 * kCUs) launch_tiles<64, 64, 3, OutT, ACC>(a, st);
+  else if (t128 >= 2 * kCUs && a.N % 192 == 0 && 3 * rounds192 < 2 * rounds128)
+    launch_tiles<128, 192, 2, OutT, ACC>(a, st);
   else if (t128 >= 2 * kCUs) launch_tiles<128, 128, 2, OutT, ACC>(a, st);
   else launch_tiles<128, 64, 2, OutT, ACC>(a, st);
 }
