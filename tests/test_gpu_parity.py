@@ -178,6 +178,7 @@ SMALL = [
     (5, 100, 256, 144, 32),     # 4-bit at rank 32: 128 x 128 backward tiles
     (2, 90, 512, 272, 16),      # rank 16: three column blocks of the split operands
     (2, 2100, 320, 4608, 8),    # 128 x 192 forward tiles: ragged rows and last k stage
+    (2, 600, 256, 784, 6),      # 64-row backward with B and scales resident: ragged rows and last stage
 ]
 
 
