@@ -179,6 +179,8 @@ SMALL = [
     (2, 90, 512, 272, 16),      # rank 16: three column blocks of the split operands
     (2, 2100, 320, 4608, 8),    # 128 x 192 forward tiles: ragged rows and last k stage
     (2, 600, 256, 784, 6),      # 64-row backward with B and scales resident: ragged rows and last stage
+    (2, 2100, 2064, 208, 8),    # register-widening 128 x 128 backward: ragged rows, k tile and last stage
+    (2, 1100, 2048, 96, 3),     # the same at rank 3 of 4, two stages
 ]
 
 
