@@ -1322,38 +1322,6 @@ __global__ __launch_bounds__(256, 2) void bwd_wide_kernel(BwdArgs a) {
     // lanes 4 i + p fetch the 4 n at 16 w + 4 p of row i, and lane q receives
     // n = 16 w + q of rows 0..3.
     if (kt % a.tiles_x == kt_blk) {
-      bf16x8 tfr[UCB][BM / 32];
-      if constexpr (TFL) {
-#pragma unroll
-        for (int cb = 0; cb < UCB; ++cb)
-#pragma unroll
-          for (int c = 0; c < BM / 32; ++c)
-            tfr[cb][c] = *reinterpret_cast<const bf16x8*>(TF + ((cb * (BM / 32) + c) * 64 + lane) * 16);
-      } else {
-#pragma unroll
-        for (int cb = 0; cb < UCB; ++cb) {
-          // column j: part j / R (hi, mid, lo) of t[., j % R]
-          const int j = cb * 16 + (lane & 15), part = j / R, jr = j - part * R;
-#pragma unroll
-          for (int c = 0; c < BM / 32; ++c) {
-            float v[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int m = 32 * c + 8 * (lane >> 4) + e;
-              v[e] = (jr < r && part < 3) ? Ts[m * r + (jr < r ? jr : 0)] : 0.f;
-            }
-            u32x4 hi, mid, lo;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              uint32_t me, le;
-              hi[e] = pk_bf16_split3(v[2 * e], v[2 * e + 1], me, le);
-              mid[e] = me;
-              lo[e] = le;
-            }
-            tfr[cb][c] = __builtin_bit_cast(bf16x8, part == 0 ? hi : part == 1 ? mid : lo);
-          }
-        }
-      }
       constexpr int NRD = 2 * (BM / 32);
       uint32_t tra[NRD];
       uint64_t trv[NRD];
@@ -1375,8 +1343,33 @@ __global__ __launch_bounds__(256, 2) void bwd_wide_kernel(BwdArgs a) {
         const bf16x8 dyT = __builtin_bit_cast(bf16x8, u32x4{(uint32_t)trv[2 * c], (uint32_t)(trv[2 * c] >> 32),
                                                             (uint32_t)trv[2 * c + 1], (uint32_t)(trv[2 * c + 1] >> 32)});
 #pragma unroll
-        for (int cb = 0; cb < UCB; ++cb)
-          dbacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dyT, tfr[cb][c], dbacc[cb], 0, 0, 0);
+        for (int cb = 0; cb < UCB; ++cb) {
+          // the t operand's fragment (cb, c): from LDS, or (rank 8) rebuilt
+          // from the t tile here, one fragment at a time (fewer registers
+          // live): column j is part j / R (hi, mid, lo) of t[., j % R]
+          bf16x8 tf;
+          if constexpr (TFL) {
+            tf = *reinterpret_cast<const bf16x8*>(TF + ((cb * (BM / 32) + c) * 64 + lane) * 16);
+          } else {
+            const int j = cb * 16 + (lane & 15), part = j / R, jr = j - part * R;
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int m = 32 * c + 8 * (lane >> 4) + e;
+              v[e] = (jr < r && part < 3) ? Ts[m * r + (jr < r ? jr : 0)] : 0.f;
+            }
+            u32x4 hi, mid, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              uint32_t me, le;
+              hi[e] = pk_bf16_split3(v[2 * e], v[2 * e + 1], me, le);
+              mid[e] = me;
+              lo[e] = le;
+            }
+            tf = __builtin_bit_cast(bf16x8, part == 0 ? hi : part == 1 ? mid : lo);
+          }
+          dbacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dyT, tf, dbacc[cb], 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int cb = 0; cb < RCB; ++cb) {
