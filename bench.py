@@ -430,8 +430,8 @@ def describe(w):
 
 # HBM traffic of the dominant kernel per launch on the benchmarked workload
 # (the MLP's fused backward, bwd_pc_kernel), averaged over its 32 layers like
-# "achieved": 31 launches at 1024 -> 1024 (14.30 MB each) and one at
-# 784 -> 1024 (29.55 MB). From two rocprofv3 counter passes (FETCH_SIZE,
+# "achieved": 31 launches at 1024 -> 1024 (14.31 MB each) and one at
+# 784 -> 1024 (29.56 MB). From two rocprofv3 counter passes (FETCH_SIZE,
 # then WRITE_SIZE, KiB per dispatch), each divided by what the same counter
 # reads per KiB for the library's read probe (1 GiB, larger than the
 # last-level cache) and copy probe (256 MiB) in the same runs. Valid only for
@@ -441,8 +441,8 @@ TRAFFIC = {
     "workload": 2,
     "weights": "w8",
     "sources": ["gemm_bwd.hip", "ring.hpp", "common.hpp"],
-    "sha256": "a9b60595e8c7291d7e9c409859630cb87d8499b63a87e10fc56b1f5df2850c7d",
-    "bytes_per_launch": 14778505,
+    "sha256": "41e47c47a63611e758abe4e19b844d45db09b246e3469b1b5d0711cf7ff33c5b",
+    "bytes_per_launch": 14785673,
 }
 
 
