@@ -51,7 +51,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "fwd+bwd TFLOP/s of int8-weight+LoRA linear; % of MFMA/HBM roofline"
-# MI355X published dense peaks
+# MI355X published peaks: dense bf16 and int8 MFMA, float32 vector ALU, HBM
 PEAK = {"bf16": 2.5e15, "int8": 5.0e15, "f32": 157.3e12, "hbm": 8.0e12}
 
 
@@ -631,10 +631,15 @@ def dominant_kernel_roofline(w, layers, step, torch, Q, peaks):
         2 M K r;
       * bytes of a backward: dy, codes, scales, x, t, A, B read, dx, dA, dB
         written, each once.
-    The roof is the one these select: MFMA (dense bf16, or the float32
-    matrix peak for float32 layers) when flops / peak exceeds bytes / HBM
-    bandwidth, else HBM; ``frac`` is the kernel's fraction of that roof,
-    ``frac_measured`` the same against the peak re-measured on this GPU.
+    The roof is the one these select: compute when flops / peak exceeds
+    bytes / HBM bandwidth, else HBM. Compute is the dense bf16 MFMA peak for
+    the bf16 backward ("mfma"); the float32 input gradient is an FMA kernel
+    on the vector ALUs ("alu"), against the published float32 vector peak
+    (256 CUs x 4 SIMDs x 16 lanes x 2 (packed) x 2 (FMA) x 2.4 GHz = 157.3
+    TFLOP/s; code without packed float32 instructions, like this library's,
+    can reach half of it). ``frac`` is the kernel's fraction of that roof,
+    ``frac_measured`` the same against the peak re-measured on this GPU
+    (MFMA and HBM only).
     """
     n = len(layers)
     repeats = 20
@@ -665,10 +670,11 @@ def dominant_kernel_roofline(w, layers, step, torch, Q, peaks):
     nbytes /= n
     mfma_peak = PEAK["bf16" if w.dtype == "bf16" else "f32"]
     t_mfma, t_hbm = flops / mfma_peak, nbytes / PEAK["hbm"]
-    bound = "mfma" if t_mfma >= t_hbm else "hbm"
+    compute = "mfma" if w.dtype == "bf16" else "alu"
+    bound = compute if t_mfma >= t_hbm else "hbm"
     names = sorted({Q.qlora_bwd_main_kernel(l.lin, M, l.dt) for l in layers})
     kernel = " + ".join(names) + (f" ({w.wfmt} weights, {w.dtype})")
-    if bound == "mfma":
+    if bound != "hbm":
         achieved, peak, unit = flops / avg_s / 1e12, mfma_peak / 1e12, "TFLOP/s"
         mpeak = peaks.get("bf16_mfma_tflops") if (peaks and w.dtype == "bf16") else None
     else:
