@@ -441,8 +441,8 @@ TRAFFIC = {
     "workload": 2,
     "weights": "w8",
     "sources": ["gemm_bwd.hip", "ring.hpp", "common.hpp"],
-    "sha256": "41e47c47a63611e758abe4e19b844d45db09b246e3469b1b5d0711cf7ff33c5b",
-    "bytes_per_launch": 14785673,
+    "sha256": "fa83d2a6b841ffa317fb1f5651d459ee0b154165af0faf86a54647bc25a62451",
+    "bytes_per_launch": 14785679,
 }
 
 
