@@ -225,10 +225,42 @@ __device__ __forceinline__ int code_swz(int row) {
   return (row >> (RB == 64 ? 2 : 1)) & (RB / 16 - 1);
 }
 
-// bfloat16 element e of a swizzled 128-byte-row bf16 tile (64 per row).
-__device__ __forceinline__ float tile_bf16(const int8_t* tile, int row, int e) {
-  const uint16_t v = *reinterpret_cast<const uint16_t*>(tile + swz128(row, e >> 3) + 2 * (e & 7));
-  return __uint_as_float((uint32_t)v << 16);
+// dA partial over a block's rows, in row order:
+//   da[jj] = sum over m < rows of x[m][kl] U[m][jb + TPK jj]
+// with x the block's bf16 tile [BM][BN] (swizzled 128-byte row halves, as
+// the x tile loads lay it out) and U = E [BM][R]. The wave's 64 lanes hold
+// 64 consecutive columns of one row half (lane = kl % 64). The tile is read
+// four rows at a time through transposing reads: in each 16-lane group,
+// lane 4 i + p fetches the 4 columns at 16 g + 4 p of row i, and lane q
+// receives column 16 g + q of the four rows.
+template <int BM, int BN, int R, int TPK, int JPT>
+__device__ __forceinline__ void da_partial(const int8_t* Xs, const float* E, int kl, int jb,
+                                           int rows, float (&da)[JPT]) {
+  constexpr int RH = BN / 64;
+  const int lane = threadIdx.x & 63, g = lane >> 4, q = lane & 15, h = kl / 64;
+  auto batch = [&](int b0, bool check) {            // rows [b0, b0 + 16)
+    uint32_t ad[4];
+    uint64_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int hrow = (b0 + 4 * u + (q >> 2)) * RH + h;
+      ad[u] = lds_addr(Xs + swz128(hrow, 2 * g + ((q & 3) >> 1)) + 8 * (q & 1));
+    }
+    tr16_reads<4>(ad, v);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = b0 + 4 * u + i;
+        if (check && m >= rows) continue;            // uniform
+        const float xv = __uint_as_float((uint32_t)(v[u] >> (16 * i)) << 16);
+#pragma unroll
+        for (int jj = 0; jj < JPT; ++jj) da[jj] = __builtin_fmaf(xv, E[m * R + jb + TPK * jj], da[jj]);
+      }
+  };
+  int b0 = 0;
+  for (; b0 + 16 <= rows; b0 += 16) batch(b0, false);
+  if (b0 < rows) batch(b0, true);
 }
 
 // W4: 4-bit weights (two codes per byte, fp16 scale per 128 k); else int8.
@@ -837,13 +869,7 @@ __global__ __launch_bounds__(512) void bwd_pc_kernel(BwdArgs a) {
     float da[JPT];
 #pragma unroll
     for (int jj = 0; jj < JPT; ++jj) da[jj] = 0.f;
-#pragma unroll 8
-    for (int m = 0; m < rows_here; ++m) {
-      const int hrow = m * (BN / 64) + kl / 64;
-      const float xv = tile_bf16(Xs, hrow, kl % 64);
-#pragma unroll
-      for (int jj = 0; jj < JPT; ++jj) da[jj] = __builtin_fmaf(xv, E[m * R + jb + TPK * jj], da[jj]);
-    }
+    da_partial<BM, BN, R, TPK, JPT>(Xs, E, kl, jb, rows_here, da);
     if (k0 + kl < K) {
 #pragma unroll
       for (int jj = 0; jj < JPT; ++jj) {
@@ -1449,13 +1475,7 @@ __global__ __launch_bounds__(256, 2) void bwd_wide_kernel(BwdArgs a) {
     float da[JPT];
 #pragma unroll
     for (int jj = 0; jj < JPT; ++jj) da[jj] = 0.f;
-#pragma unroll 8
-    for (int m = 0; m < rows_here; ++m) {
-      const int hrow = m * (BN / 64) + kl / 64;
-      const float xv = tile_bf16(Xs, hrow, kl % 64);
-#pragma unroll
-      for (int jj = 0; jj < JPT; ++jj) da[jj] = __builtin_fmaf(xv, E[m * R + jb + TPK * jj], da[jj]);
-    }
+    da_partial<BM, BN, R, TPK, JPT>(Xs, E, kl, jb, rows_here, da);
     if (k0 + kl < K) {
 #pragma unroll
       for (int jj = 0; jj < JPT; ++jj) {
