@@ -33,9 +33,11 @@
 //     column-tile count adds t^T dy over its rows for the stage's 64 n
 //     (dy^T through transposing LDS reads, t rounded to bf16), giving one
 //     partial per row block.
-// After the loop u goes to LDS; the dA partial over the block's rows is a
-// float32 vector-ALU sum of x (a tile loaded into LDS) times u; the dx
-// epilogue adds s u A^T on v_mfma_f32_16x16x4_f32. The partials of dA and dB
+// After the loop u goes to LDS and the dA partial x^T u over the block's
+// rows is taken from an x tile loaded into LDS: on the 64-row tiles a
+// float32 vector-ALU sum in row order (beside the consumers' epilogue), on
+// the 128-row tiles bf16 MFMAs with u split into hi, mid and lo parts like
+// B and t; the dx epilogue adds s u A^T on v_mfma_f32_16x16x4_f32. The partials of dA and dB
 // are added in row-block order by a small second launch. No atomics:
 // results are bitwise reproducible.
 //
@@ -986,7 +988,8 @@ __global__ __launch_bounds__(256, 2) void bwd_wide_kernel(BwdArgs a) {
     }
   }
 
-  // x tile [BM][BN] bf16 as swizzled 128-byte rows (64 columns per row half)
+  // x tile [BM][BN] bf16 as swizzled 128-byte rows (64 columns per row
+  // half), zeros past M and K
   auto issue_x = [&]() {
     constexpr int RH = BN / 64;                        // 128-byte halves per row
 #pragma unroll
@@ -995,8 +998,8 @@ __global__ __launch_bounds__(256, 2) void bwd_wide_kernel(BwdArgs a) {
       const int row = hrow / RH, half = hrow % RH;
       const int c = (lane & 7) ^ ((hrow >> 1) & 7);
       const int gm = m0 + row, gk = k0 + half * 64 + c * 8;
-      const void* src = gk < K ? (const void*)(a.x + (long)(gm < M ? gm : M - 1) * K + gk)
-                               : (const void*)zero_chunk(lane);
+      const void* src = gk < K && gm < M ? (const void*)(a.x + (long)gm * K + gk)
+                                         : (const void*)zero_chunk(lane);
       lds_dma16(src, Xs + rb * 128);
     }
   };
@@ -1465,24 +1468,92 @@ __global__ __launch_bounds__(256, 2) void bwd_wide_kernel(BwdArgs a) {
     const int e = tid + 256 * i, j = e / BN, col = e % BN;
     if (e < BN * R) E[BM * R + e] = (j < r && k0 + col < K) ? qv[i] : 0.f;
   }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
 
-  // dA partial: thread -> column k = tid % BN, ranks jb + (256 / BN) jj
+  // dA partial on the matrix cores: dA^T[k][j] = sum_m x[m][k] u[m][j] over
+  // the block's rows, with u split like B and t into bf16 hi, mid and lo
+  // columns (the u operand, [UCB][BM / 32][64 lanes][16 B] in the B and t
+  // buffers the loop has released; wave w builds fragments w, w + 4, ...;
+  // rows past M are zero there and in the x tile) and x^T read from the x
+  // tile through transposing reads (in each 16-lane group lane 4 i + p
+  // fetches the 4 columns at c0 + 4 p of row i, and lane q receives column
+  // c0 + q of rows 0..3). Wave w takes the columns [BN / 4 w, BN / 4 (w + 1)).
+  int8_t* UF = BU;
+  static_assert(UCB * (BM / 32) * 1024 <= BUSZ + TSZ, "u operand fits in the B and t buffers");
+  for (int f = wid; f < UCB * (BM / 32); f += 4) {
+    const int cb = f / (BM / 32), c = f % (BM / 32);
+    const int j = cb * 16 + (lane & 15), part = j / R, jr = j - part * R;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int m = 32 * c + 8 * (lane >> 4) + e;
+      v[e] = (jr < r && part < 3 && m < rows_here) ? E[m * R + (jr < r ? jr : 0)] : 0.f;
+    }
+    u32x4 hi, mid, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t me, le;
+      hi[e] = pk_bf16_split3(v[2 * e], v[2 * e + 1], me, le);
+      mid[e] = me;
+      lo[e] = le;
+    }
+    *reinterpret_cast<u32x4*>(UF + (f * 64 + lane) * 16) = part == 0 ? hi : part == 1 ? mid : lo;
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));              // the x tile
+  __syncthreads();
   {
-    constexpr int TPK = 256 / BN, JPT = R / TPK;
-    const int kl = tid % BN, jb = tid / BN;
-    float da[JPT];
+    constexpr int KB = BN / 64, RH = BN / 64;          // 16-column blocks per wave
+    f32x4 dacc[KB][UCB];
 #pragma unroll
-    for (int jj = 0; jj < JPT; ++jj) da[jj] = 0.f;
-    da_partial<BM, BN, R, TPK, JPT>(Xs, E, kl, jb, rows_here, da);
-    if (k0 + kl < K) {
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int jj = 0; jj < JPT; ++jj) {
-        const int j = jb + TPK * jj;
-        if (j < r) a.partA[((long)mt * r + j) * K + k0 + kl] = da[jj];
+      for (int cb = 0; cb < UCB; ++cb) dacc[kb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int q = lane & 15, i4 = q >> 2, p4 = q & 3;
+#pragma unroll
+    for (int c0 = 0; c0 < BM / 32; c0 += 2) {
+      uint32_t tra[4 * KB];
+      uint64_t trv[4 * KB];
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int m = 32 * (c0 + cc) + 8 * (lane >> 4) + 4 * h + i4;
+            const int col = (BN / 4) * wid + 16 * kb + 4 * p4;
+            tra[(cc * KB + kb) * 2 + h] = lds_addr(Xs + swz128(m * RH + col / 64, (col % 64) >> 3) + (col & 7) * 2);
+          }
+      tr16_reads<4 * KB>(tra, trv);
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int c = c0 + cc;
+        bf16x8 uf[UCB];
+#pragma unroll
+        for (int cb = 0; cb < UCB; ++cb)
+          uf[cb] = *reinterpret_cast<const bf16x8*>(UF + ((cb * (BM / 32) + c) * 64 + lane) * 16);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int t0 = (cc * KB + kb) * 2;
+          const bf16x8 xT = __builtin_bit_cast(bf16x8, u32x4{(uint32_t)trv[t0], (uint32_t)(trv[t0] >> 32),
+                                                             (uint32_t)trv[t0 + 1], (uint32_t)(trv[t0 + 1] >> 32)});
+#pragma unroll
+          for (int cb = 0; cb < UCB; ++cb)
+            dacc[kb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xT, uf[cb], dacc[kb][cb], 0, 0, 0);
+        }
       }
     }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int cb = 0; cb < RCB; ++cb) {
+        const int j = cb * 16 + (lane & 15);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const float dav = split3_sum<R, UCB>(dacc[kb], cb, ii, lane);
+          const int kl = (BN / 4) * wid + 16 * kb + 4 * (lane >> 4) + ii;
+          if (j < r && k0 + kl < K) a.partA[((long)mt * r + j) * K + k0 + kl] = dav;
+        }
+      }
   }
 
   // output staging strips in the converted-code buffer, free after the loop
