@@ -1542,18 +1542,53 @@ __global__ __launch_bounds__(256, 2) void bwd_wide_kernel(BwdArgs a) {
         }
       }
     }
+    float dav[KB][RCB][4];
+    bool nan = false;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int cb = 0; cb < RCB; ++cb) {
-        const int j = cb * 16 + (lane & 15);
+      for (int cb = 0; cb < RCB; ++cb)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-          const float dav = split3_sum<R, UCB>(dacc[kb], cb, ii, lane);
-          const int kl = (BN / 4) * wid + 16 * kb + 4 * (lane >> 4) + ii;
-          if (j < r && k0 + kl < K) a.partA[((long)mt * r + j) * K + k0 + kl] = dav;
+          dav[kb][cb][ii] = split3_sum<R, UCB>(dacc[kb], cb, ii, lane);
+          nan |= dav[kb][cb][ii] != dav[kb][cb][ii];
         }
+    if (__builtin_amdgcn_ballot_w64(nan) == 0) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int cb = 0; cb < RCB; ++cb) {
+          const int j = cb * 16 + (lane & 15);
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int kl = (BN / 4) * wid + 16 * kb + 4 * (lane >> 4) + ii;
+            if (j < r && k0 + kl < K) a.partA[((long)mt * r + j) * K + k0 + kl] = dav[kb][cb][ii];
+          }
+        }
+    } else {
+      // A NaN in the wave's columns: an infinite x times the three parts of
+      // u can give inf - inf where the plain product is infinite, so the
+      // wave takes its columns again as float32 sums in row order (lane ->
+      // column (BN / 4) w + lane % (BN / 4), ranks jb + TPK jj).
+      constexpr int CPW = BN / 4, TPK = 64 / CPW, JPT = (R + TPK - 1) / TPK;
+      const int kl = CPW * wid + lane % CPW, jb = lane / CPW;
+      float da[JPT];
+#pragma unroll
+      for (int jj = 0; jj < JPT; ++jj) da[jj] = 0.f;
+      for (int m = 0; m < rows_here; ++m) {
+        const int e = kl % 64;
+        const uint16_t xb = *reinterpret_cast<const uint16_t*>(Xs + swz128(m * RH + kl / 64, e >> 3) + 2 * (e & 7));
+        const float xv = __uint_as_float((uint32_t)xb << 16);
+#pragma unroll
+        for (int jj = 0; jj < JPT; ++jj)
+          if (jb + TPK * jj < R) da[jj] = __builtin_fmaf(xv, E[m * R + jb + TPK * jj], da[jj]);
       }
+#pragma unroll
+      for (int jj = 0; jj < JPT; ++jj) {
+        const int j = jb + TPK * jj;
+        if (j < r && k0 + kl < K) a.partA[((long)mt * r + j) * K + k0 + kl] = da[jj];
+      }
+    }
   }
 
   // output staging strips in the converted-code buffer, free after the loop

@@ -18,7 +18,7 @@ import sys
 import numpy as np
 import pytest
 
-from helpers import RTOL, RTOL_F32, assert_close, same_bits_f16, same_bits_f32, to_numpy
+from helpers import RTOL, RTOL_F32, assert_close, rel_errors, same_bits_f16, same_bits_f32, to_numpy
 from oracle import qlora_oracle as O
 from quantized_frozen_weight_amd import binding as Q
 from quantized_frozen_weight_amd import workloads as WL
@@ -47,7 +47,7 @@ class Case:
     """One layer: synthetic inputs, device tensors and the oracle's answers."""
 
     def __init__(self, w: WL.Workload, layer: int, M=None, zero_B=False, W=None,
-                 x32=None):
+                 x32=None, dy32=None):
         self.w = w
         self.K, self.N = w.layers[layer]
         self.M = w.M if M is None else M
@@ -55,7 +55,7 @@ class Case:
         self.A = WL.lora_A(w, layer)
         self.B = np.zeros((w.r, self.N), np.float32) if zero_B else WL.lora_B(w, layer)
         x32 = WL.activations(w, layer, self.M) if x32 is None else x32
-        dy32 = WL.out_grad(w, layer, self.M)
+        dy32 = WL.out_grad(w, layer, self.M) if dy32 is None else dy32
         self.x_t, self.x = WL.as_compute_dtype(x32, w.dtype)
         self.dy_t, self.dy = WL.as_compute_dtype(dy32, w.dtype)
         self.x_t, self.dy_t = self.x_t.cuda(), self.dy_t.cuda()
@@ -227,10 +227,19 @@ def test_zero_B_is_plain_quantized_product(cid, M, K, N, r):
     assert same_bits_f32(to_numpy(y), want)
 
 
-@pytest.mark.parametrize("cid", [1, 2, 5])
-def test_degenerate_rows_and_channels(cid):
-    w = WL.small(cid, 40, 256, 160, 4)
-    say(f"degenerate: {w.name}")
+@pytest.mark.parametrize("spec", [
+    (1, 40, 256, 160, 4),
+    (2, 40, 256, 160, 4),
+    (5, 40, 256, 160, 4),
+    (2, 1100, 2048, 96, 4),     # 128 x 64 backward tiles, ragged last row tile
+    (2, 2100, 2048, 96, 8),     # 128 x 128 backward tiles, ragged last row tile
+    (5, 2100, 2048, 256, 4),    # 4-bit 128 x 128 backward tiles
+    (2, 130, 2048, 4160, 4),    # input gradient split 4 ways
+])
+def test_degenerate_rows_and_channels(spec):
+    w = WL.small(*spec)
+    M = spec[1]
+    say(f"degenerate: {w.name} M={M} K={spec[2]} N={spec[3]} r={spec[4]}")
     W = WL.weight(w, 0)
     W[:, 3] = 0.0                # zero output channel
     W[7, 5] = np.nan             # NaN channel
@@ -238,7 +247,9 @@ def test_degenerate_rows_and_channels(cid):
     x = WL.activations(w, 0)
     x[2] = 0.0                   # zero row
     if w.wfmt == "w8":
-        x[5, 11] = np.inf        # non-finite row: NaN row scale
+        # non-finite row (NaN row scale); in the last, ragged row tile of
+        # the larger shapes
+        x[5 if M < 64 else M - 1, 11] = np.inf
     case = Case(w, 0, W=W, x32=x)
     check_weights(case)
     if w.wfmt == "w8":
@@ -260,6 +271,39 @@ def test_degenerate_rows_and_channels(cid):
         assert_close(to_numpy(dx), odx, rt, "dx (degenerate)")
         assert_close(to_numpy(dA), odA, RTOL_F32, "dA (degenerate)")
         assert_close(to_numpy(dB), odB, RTOL_F32, "dB (degenerate)")
+
+
+@pytest.mark.parametrize("spec", [
+    (2, 40, 256, 160, 4),
+    (2, 1100, 2048, 96, 4),     # 128 x 64 backward tiles
+    (2, 2100, 2048, 96, 8),     # 128 x 128 backward tiles
+    (5, 2100, 2048, 256, 4),    # 4-bit 128 x 128 backward tiles
+    (2, 130, 2048, 4160, 4),    # input gradient split 4 ways
+])
+def test_nonfinite_output_gradient(spec):
+    """Infinite entries in dy: dx, dA and dB are non-finite exactly where the
+    oracle's are, and the finite rest is within tolerance. An infinity may
+    come out as NaN: times the three bf16 parts of B (for u) or of t (for dB)
+    it can cancel as inf - inf where the plain product stays infinite."""
+    w = WL.small(*spec)
+    M = spec[1]
+    say(f"non-finite dy: {w.name} M={M} K={spec[2]} N={spec[3]} r={spec[4]}")
+    dy = WL.out_grad(w, 0, M)
+    dy[M - 1, 5] = np.inf
+    dy[3, 7] = -np.inf
+    case = Case(w, 0, dy32=dy)
+    _, t = Q.qlora_fwd(case.lin, case.x_t)
+    dx, dA, dB = Q.qlora_bwd(case.lin, case.x_t, case.dy_t, t=t)
+    torch.cuda.synchronize()
+    odx, odA, odB = case.oracle_bwd()
+    for got, want, rt, what in ((dx, odx, RTOL[w.dtype], "dx"), (dA, odA, RTOL_F32, "dA"),
+                                (dB, odB, RTOL_F32, "dB")):
+        g = to_numpy(got).astype(np.float64)
+        fin = np.isfinite(want)
+        assert np.array_equal(np.isfinite(g), fin), f"{what}: non-finite pattern differs"
+        if fin.any():
+            elem, _ = rel_errors(g[fin], want[fin])
+            assert elem.max() <= rt, f"{what}: max rel err {elem.max():.3e} > {rt}"
 
 
 @pytest.mark.parametrize("spec", [
