@@ -151,8 +151,8 @@ SMALL = [
     (2, 130, 128, 144, 16),
     (2, 257, 512, 1040, 32),
     (2, 64, 3072, 128, 8),      # more dx column tiles than 64-n stages
-    (2, 1000, 64, 2048, 4),     # one 128-wide column tile, contraction split in 2
-    (2, 200, 320, 2240, 8),     # split contraction: 2 splits, ragged rows and k tile
+    (2, 1000, 64, 2048, 4),     # one 128-wide column tile, contraction split in 4
+    (2, 200, 320, 2240, 8),     # split contraction: 4 splits, ragged rows and k tile
     (2, 130, 208, 8320, 4),     # 8 splits of 17 stages, the last one of 11
     (3, 200, 3072, 400, 4),
     (1, 3, 4608, 32, 2),        # float32 rows past 4096 entries (two rows per block)
@@ -165,7 +165,7 @@ SMALL = [
     (2, 4100, 96, 48, 8),       # two rows per wave in the row pass, ragged last block
     (2, 8200, 96, 48, 8),       # four rows per wave in the row pass, ragged last block
     (2, 2100, 1040, 336, 8),    # 128 x 64 backward tiles: ragged rows, k tile and last stage
-    (2, 1, 256, 4096, 8),       # one row: input gradient split 4 ways
+    (2, 1, 256, 4096, 8),       # one row: input gradient split 8 ways
     (2, 1, 4112, 64, 4),        # one row: long-row pass, forward split 2 ways with a ragged k tail
     (2, 4100, 1552, 32, 16),    # two rows per wave at rank 16, three held chunks
     (1, 4100, 640, 32, 2),      # float32 rows, two per wave
@@ -173,7 +173,7 @@ SMALL = [
     (5, 1, 128, 16, 4),
     (5, 77, 256, 272, 8),
     (5, 130, 384, 144, 1),
-    (5, 77, 256, 4160, 8),      # 4-bit, contraction split in 4
+    (5, 77, 256, 4160, 8),      # 4-bit, contraction split in 8
     (5, 7, 8192, 64, 8),        # 4-bit: the adapter's down projection over long rows
     (5, 100, 256, 144, 32),     # 4-bit at rank 32: 128 x 128 backward tiles
     (2, 90, 512, 272, 16),      # rank 16: three column blocks of the split operands
@@ -234,7 +234,7 @@ def test_zero_B_is_plain_quantized_product(cid, M, K, N, r):
     (2, 1100, 2048, 96, 4),     # 128 x 64 backward tiles, ragged last row tile
     (2, 2100, 2048, 96, 8),     # 128 x 128 backward tiles, ragged last row tile
     (5, 2100, 2048, 256, 4),    # 4-bit 128 x 128 backward tiles
-    (2, 130, 2048, 4160, 4),    # input gradient split 4 ways
+    (2, 130, 2048, 4160, 4),    # input gradient split 8 ways
 ])
 def test_degenerate_rows_and_channels(spec):
     w = WL.small(*spec)
@@ -278,7 +278,7 @@ def test_degenerate_rows_and_channels(spec):
     (2, 1100, 2048, 96, 4),     # 128 x 64 backward tiles
     (2, 2100, 2048, 96, 8),     # 128 x 128 backward tiles
     (5, 2100, 2048, 256, 4),    # 4-bit 128 x 128 backward tiles
-    (2, 130, 2048, 4160, 4),    # input gradient split 4 ways
+    (2, 130, 2048, 4160, 4),    # input gradient split 8 ways
 ])
 def test_nonfinite_output_gradient(spec):
     """Infinite entries in dy: dx, dA and dB are non-finite exactly where the
