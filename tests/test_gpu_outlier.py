@@ -140,7 +140,7 @@ LAYER_CASES = [
     (70, 208, 2080, 4, 5),      # split contraction: 4 splits, ragged last stage
     (40, 128, 8192, 8, 6),      # 8 splits; the later ones start past 64 stages
     (9, 8208, 64, 8, 7),        # long rows: code sums over four waves; forward split 4 ways
-    (130, 4096, 80, 4, 8),      # forward split 2 ways over 2 x 2 ragged 128 x 64 tiles
+    (130, 4096, 80, 4, 8),      # forward split 4 ways over 2 x 2 ragged 128 x 64 tiles
 ]
 
 
