@@ -441,8 +441,8 @@ TRAFFIC = {
     "workload": 2,
     "weights": "w8",
     "sources": ["gemm_bwd.hip", "ring.hpp", "common.hpp"],
-    "sha256": "fa83d2a6b841ffa317fb1f5651d459ee0b154165af0faf86a54647bc25a62451",
-    "bytes_per_launch": 14785679,
+    "sha256": "587d370d4df651315135260072024a8ad54ed1d627196979edf5f1cb6a9eff23",
+    "bytes_per_launch": 14798984,
 }
 
 
