@@ -441,7 +441,7 @@ TRAFFIC = {
     "workload": 2,
     "weights": "w8",
     "sources": ["gemm_bwd.hip", "ring.hpp", "common.hpp"],
-    "sha256": "587d370d4df651315135260072024a8ad54ed1d627196979edf5f1cb6a9eff23",
+    "sha256": "0cc5ec7215c7463eaa7b5075f2ac045f1a34989fb63deb5a902953562410e936",
     "bytes_per_launch": 14798984,
 }
 

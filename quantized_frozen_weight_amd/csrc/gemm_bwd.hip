@@ -24,22 +24,24 @@
 //   * CB [BN k][64 n] = bf16(deq(W)[k, n]), the transposed dequantized
 //     weight, as swizzled 128-byte rows (4-bit: the nibbles unpacked and
 //     scaled by their group's fp16 scale, one 128-wide group per block);
-//   * BU [16 j][64 n] = bf16(B[j, n]).
+//   * BU [3 R j][64 n]: B[j, n] as three bf16 parts, hi | mid | lo
+//     (pk_bf16_split3 below), so that the rank-r products keep float32
+//     accuracy.
 // Then per 32 n, on v_mfma_f32_16x16x32_bf16:
 //   * dx += dy CB^T;
-//   * u  += dy BU^T, one MFMA per row block (the two column waves of a row
-//     split the row blocks);
+//   * u  += dy BU^T, one MFMA per row block and column block of BU (the two
+//     column waves of a row split the row blocks);
 //   * dB: the block whose column index equals the stage index modulo the
 //     column-tile count adds t^T dy over its rows for the stage's 64 n
-//     (dy^T through transposing LDS reads, t rounded to bf16), giving one
-//     partial per row block.
+//     (dy^T through transposing LDS reads, t as three bf16 parts), giving
+//     one partial per row block.
 // After the loop u goes to LDS and the dA partial x^T u over the block's
 // rows is taken from an x tile loaded into LDS: on the 64-row tiles a
 // float32 vector-ALU sum in row order (beside the consumers' epilogue), on
 // the 128-row tiles bf16 MFMAs with u split into hi, mid and lo parts like
-// B and t; the dx epilogue adds s u A^T on v_mfma_f32_16x16x4_f32. The partials of dA and dB
-// are added in row-block order by a small second launch. No atomics:
-// results are bitwise reproducible.
+// B and t; the dx epilogue adds s u A^T on v_mfma_f32_16x16x4_f32. The
+// partials of dA and dB are added in row-block order by a small second
+// launch. No atomics: results are bitwise reproducible.
 //
 // Outlier-compensated int8 weights (keras-llm-light README, "Simplified
 // Int8Variable quantization"; format in outlier.hpp) take the 64-row tiles:
