@@ -246,10 +246,9 @@ def test_degenerate_rows_and_channels(spec):
     W[:, 9] = 1e-45 if w.wfmt == "w8" else 0.0
     x = WL.activations(w, 0)
     x[2] = 0.0                   # zero row
-    if w.wfmt == "w8":
-        # non-finite row (NaN row scale); in the last, ragged row tile of
-        # the larger shapes
-        x[5 if M < 64 else M - 1, 11] = np.inf
+    # an infinite input (int8: a NaN row scale); in the last, ragged row tile
+    # of the larger shapes
+    x[5 if M < 64 else M - 1, 11] = np.inf
     case = Case(w, 0, W=W, x32=x)
     check_weights(case)
     if w.wfmt == "w8":
