@@ -84,8 +84,10 @@ FwdLayout fwd_layout(const qlora_linear* L, int M) {
   w.asum = off; off = align_up(off + (L->fmt == QLORA_W8O ? (size_t)M * 4 : 0));
   // split contraction of the int8 product (0 bytes when it does not split):
   // int32 partial sums, and the affine weights' partial corrections
+  // (4-bit weights: the float32 partial sums of the split 4-bit product)
   const bool w8 = L->fmt == QLORA_W8, w8o = L->fmt == QLORA_W8O;
-  const size_t nsplit = (w8 || w8o) ? fwd_split_ints(M, L->N, L->K, w8o) : 0;
+  const size_t nsplit = (w8 || w8o) ? fwd_split_ints(M, L->N, L->K, w8o)
+                                    : fwd_w4_split_floats(M, L->N, L->K);
   w.pacc = off; off = align_up(off + nsplit * 4);
   w.pcorr = off; off = align_up(off + (w8o ? nsplit * 4 : 0));
   // the row pass of long rows split over k (0 bytes for other widths)
@@ -323,7 +325,8 @@ int qlora_fwd_timed(const qlora_linear* L, int M, int dtype, const void* x,
       launch_gemm_fwd_w4(M, L->N, L->K, static_cast<const uint16_t*>(x),
                          static_cast<const uint8_t*>(L->codes),
                          static_cast<const _Float16*>(L->scales), t, L->B, head_width(L), L->r,
-                         lora_s(L), static_cast<uint16_t*>(y), s);
+                         lora_s(L), static_cast<uint16_t*>(y),
+                         reinterpret_cast<float*>(at(ws, w.pacc)), s);
     mark(ev_stop, s);
   }
   return launch_status();

@@ -59,7 +59,11 @@ void launch_gemm_fwd_w8o(int M, int N, int K, const int8_t* xq, const int8_t* co
 // groups per block in LDS (K <= 16384).
 constexpr int kW4MaxGroups = 128;
 
-// y = x deq4(W) + s * t B   (bf16 x and y)
+// y = x deq4(W) + s * t B   (bf16 x and y). Shapes with few 128-row tiles
+// and a long contraction split it when pacc is given
+// (fwd_w4_split_floats(M, N, K) floats, 0 when the shape does not split):
+// the float32 partial sums go there and a second launch adds them.
+size_t fwd_w4_split_floats(int M, int N, int K);
 // 4-bit weights with int8 activations: exact int8 x int4 sums per 128-wide
 // group, weighted by the group's fp16 scale, times sx[m], plus s t B (bf16 y)
 void launch_gemm_fwd_a8w4(int M, int N, int K, const int8_t* xq, const float* sx,
@@ -69,7 +73,7 @@ void launch_gemm_fwd_a8w4(int M, int N, int K, const int8_t* xq, const float* sx
 void launch_gemm_fwd_w4(int M, int N, int K, const uint16_t* x,
                         const uint8_t* packed, const _Float16* scales,
                         const float* t, const float* B, int hd, int r, float s,
-                        uint16_t* y, hipStream_t st);
+                        uint16_t* y, float* pacc, hipStream_t st);
 
 // u = dy B^T (float32 [M, r]); if dys != nullptr also dys = bf16(dy * sw[n]).
 void launch_bwd_rows(int dtype, const void* dy, int M, int N, const float* B, int hd,

@@ -174,13 +174,15 @@ SMALL = [
     (5, 77, 256, 272, 8),
     (5, 130, 384, 144, 1),
     (5, 77, 256, 4160, 8),      # 4-bit, contraction split in 8
-    (5, 7, 8192, 64, 8),        # 4-bit: the adapter's down projection over long rows
+    (5, 7, 8192, 64, 8),        # 4-bit: long rows; forward split 8 ways
     (5, 100, 256, 144, 32),     # 4-bit at rank 32: 128 x 128 backward tiles
     (2, 90, 512, 272, 16),      # rank 16: three column blocks of the split operands
     (2, 2100, 320, 4608, 8),    # 128 x 192 forward tiles: ragged rows and last k stage
     (2, 600, 256, 784, 6),      # 64-row backward with B and scales resident: ragged rows and last stage
-    (2, 2100, 2064, 208, 8),    # register-widening 128 x 128 backward: ragged rows, k tile and last stage
+    (2, 2100, 2064, 208, 8),    # 128 x 128 backward: ragged rows, k tile and last stage
     (2, 1100, 2048, 96, 3),     # the same at rank 3 of 4, two stages
+    (5, 160, 2048, 400, 4),     # 4-bit forward split 4 ways: ragged rows and columns
+    (5, 64, 4224, 256, 8),      # 4-bit forward split 8 ways, the last split of 3 stages
 ]
 
 
