@@ -159,7 +159,8 @@ def test_split_contraction_workspace(lib):
 def test_split_forward_workspace(lib):
     # 512 rows of a 16384 -> 2048 int8 layer: 4 x 16 output tiles of 128 x 128
     # over 128 stages of 128 k split 8 ways -> 8 int32 partial sums of
-    # [512, 2048]; the 4-bit layout of the same shape holds none
+    # [512, 2048]; the 4-bit product of the same shape (256 stages of 64 k)
+    # splits 8 ways too, into float32 partial sums of the same size
     st, w8 = _fwd_ws(lib, _lin(K=16384, N=2048, r=8), M=512)
     assert st == Q.QLORA_OK
     # codes, scales, t, and the row pass split over 2048-entry slices of k:
@@ -168,7 +169,12 @@ def test_split_forward_workspace(lib):
     assert w8 >= base + 8 * 512 * 2048 * 4
     assert w8 <= base + 8 * 512 * 2048 * 4 + 5 * 256
     st, w4 = _fwd_ws(lib, _lin(K=16384, N=2048, r=8, fmt=Q.QLORA_W4G128), M=512)
-    assert st == Q.QLORA_OK and w4 < base + 5 * 256
+    assert st == Q.QLORA_OK
+    assert base + 8 * 512 * 2048 * 4 <= w4 <= base + 8 * 512 * 2048 * 4 + 5 * 256
+    # 2048 rows (16 x 16 tiles) do not split: no partial sums
+    st, w4 = _fwd_ws(lib, _lin(K=16384, N=2048, r=8, fmt=Q.QLORA_W4G128), M=2048)
+    base4 = 2048 * 16384 + 2048 * 4 + 2048 * 8 * 4 + 2048 * 8 * 9 * 4
+    assert st == Q.QLORA_OK and base4 <= w4 < base4 + 5 * 256
     # outlier-compensated weights: 4 x 32 tiles of 128 x 64 split 4 ways ->
     # int32 partial sums and float partial corrections, 16 MiB each
     st, w8o = _fwd_ws(lib, _lin(K=16384, N=2048, r=8, fmt=Q.QLORA_W8O), M=512)
@@ -178,6 +184,21 @@ def test_split_forward_workspace(lib):
     # a short contraction does not split
     st, short = _fwd_ws(lib, _lin(K=1024, N=1024, r=8), M=1024)
     assert short < 1024 * 1024 + 1024 * 4 + 1024 * 8 * 4 + 4 * 256
+
+
+def _w4_split_bytes(M, N, K):
+    """Float32 partial sums of the split 4-bit forward, as documented: at
+    most 128 tiles of 128 x 128 split (up to 8 ways) while the grid stays
+    within 512 blocks and each split keeps at least 8 stages of 64 k."""
+    tiles = ((M + 127) // 128) * ((N + 127) // 128)
+    nk, sp = K // 64, 1
+    if tiles <= 128:
+        while sp < 8 and tiles * sp * 2 <= 512 and nk // (sp * 2) >= 8:
+            sp *= 2
+    if sp == 1:
+        return 0
+    nks = (nk + sp - 1) // sp
+    return ((nk + nks - 1) // nks) * tiles * 128 * 128 * 4
 
 
 @pytest.mark.parametrize("K,r,slices,R", [(4096, 8, 0, 0), (4224, 8, 3, 8), (8192, 3, 4, 4),
@@ -191,7 +212,7 @@ def test_row_split_workspace(lib, K, r, slices, R):
     extra = M * slices * (1 + R) * 4
     st, f = _fwd_ws(lib, _lin(K=K, N=256, r=r, fmt=Q.QLORA_W4G128), M=M)
     assert st == Q.QLORA_OK
-    base = M * K + M * 4 + M * r * 4
+    base = M * K + M * 4 + M * r * 4 + _w4_split_bytes(M, 256, K)
     assert base + extra <= f <= base + extra + 6 * 256
     b = _bwd_ws(lib, _lin(K=K, N=256, r=r), M, Q.QLORA_F32)
     b0 = 2 * M * r * 4 + ((M + 63) // 64) * r * (K + 256) * 4
