@@ -191,7 +191,11 @@ int qlora_quantize(const float* W, int K, int N, int fmt, void* codes,
 int qlora_quantize_heads(const float* W, int heads, int K, int N, int fmt,
                          void* codes, void* scales, void* stream);
 
-/* Workspace needed by qlora_fwd / qlora_fwd_acc for M rows. */
+/* Workspace needed by qlora_fwd / qlora_fwd_acc for M rows. Layers whose
+ * product has few 128 x 128 output tiles (at most 128) over a long
+ * contraction also keep there the per-split partial sums of the product, 4
+ * bytes per output per split (int32 for int8 weights, float32 for 4-bit
+ * ones; 32 MiB for 512 rows of a 16384 -> 2048 layer). */
 int qlora_fwd_workspace(const qlora_linear* L, int M, int dtype,
                         size_t* bytes);
 
