@@ -15,9 +15,11 @@ namespace {
 // 32 x 32 output tile per block (small layers still spread over many compute
 // units), contraction in slices of 128 n (small layers are latency-bound:
 // each slice is one round trip to memory), each thread a 2 x 2 register
-// tile. The next slice is fetched into registers while the current one is
-// used. dy * sw is formed once per element (one float32 rounding), then
-// multiplied by the exact integer code.
+// tile. The next slice is fetched into registers (16-byte loads from
+// clamped addresses, masked when used) while the current one is used, and
+// nothing consumes the fetched values before the slice's products are done.
+// dy * sw is formed once per element (one float32 rounding) as it goes to
+// LDS, then multiplied by the exact integer code.
 // ---------------------------------------------------------------------------
 constexpr int kT = 32, kS = 128;
 
@@ -35,35 +37,42 @@ __global__ __launch_bounds__(256) void gemm_dx_f32_kernel(
   // code rows (n) tid / 8 + 32 p, 4 k from 4 (tid % 8); p = 0..3
   const int lm = tid >> 5, ln = (tid & 31) * 4;
   const int wn = tid >> 3, wk = (tid & 7) * 4;
-  float dv[4][4];
+  // N and K are multiples of 16, so a thread's 4 consecutive n (or k) are
+  // all inside or all outside
+  f32x4 dv[4], swv;
   uint32_t wv[4];
+  bool okn = false, okw[4];
   auto fetch = [&](int n0) {
+    const int gn = n0 + ln;
+    okn = gn < N;
+    const int gnc = okn ? gn : 0;
+    swv = *reinterpret_cast<const f32x4*>(sw + gnc);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int gm = m0 + lm + 8 * p;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int gn = n0 + ln + i;
-        dv[p][i] = (gm < M && gn < N) ? dy[(long)gm * N + gn] * sw[gn] : 0.f;
-      }
+      dv[p] = *reinterpret_cast<const f32x4*>(dy + (long)(gm < M ? gm : M - 1) * N + gnc);
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const int gn = n0 + wn + 32 * p, gk = k0 + wk;
-      wv[p] = (gn < N && gk < K) ? *reinterpret_cast<const uint32_t*>(codes + (long)gn * K + gk) : 0u;
+      const int gw = n0 + wn + 32 * p, gk = k0 + wk;
+      okw[p] = gw < N && gk < K;
+      wv[p] = *reinterpret_cast<const uint32_t*>(codes + (long)(gw < N ? gw : 0) * K + (gk < K ? gk : 0));
     }
   };
   float acc[2][2] = {};
   fetch(0);
   for (int n0 = 0; n0 < N; n0 += kS) {
 #pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const bool ok = okn && m0 + lm + 8 * p < M;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Ds[ln + i][lm + 8 * p] = ok ? dv[p][i] * swv[i] : 0.f;
+    }
+#pragma unroll
     for (int p = 0; p < 4; ++p)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Ds[ln + i][lm + 8 * p] = dv[p][i];
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Ws[wn + 32 * p][wk + i] = (float)(((int)(wv[p] << (24 - 8 * i))) >> 24);
+      for (int i = 0; i < 4; ++i)
+        Ws[wn + 32 * p][wk + i] = okw[p] ? (float)(((int)(wv[p] << (24 - 8 * i))) >> 24) : 0.f;
     __syncthreads();
     if (n0 + kS < N) fetch(n0 + kS);
 #pragma unroll 8
