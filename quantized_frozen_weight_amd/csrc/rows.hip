@@ -819,6 +819,13 @@ void row_launch(const void* rows, int M, int L, const float* W, int hd, int r,
             row_multi_launch<T, R, MODE, 4>(nhc, mgrid, lds, p, M, L, W, r, out_r, xq, sx, asum, st);
         return;
       }
+      // one row per wave, rows of at most 2048 entries: the same pass with
+      // the held chunks sized to the row (row_kernel holds 8 per lane and
+      // loads them all)
+      if (nhc < kHoldChunks) {
+        row_multi_launch<T, R, MODE, 1>(nhc, grid, lds, p, M, L, W, r, out_r, xq, sx, asum, st);
+        return;
+      }
     }
   }
   if (L <= kHoldChunks * 512)
