@@ -183,6 +183,10 @@ SMALL = [
     (2, 1100, 2048, 96, 3),     # the same at rank 3 of 4, two stages
     (5, 160, 2048, 400, 4),     # 4-bit forward split 4 ways: ragged rows and columns
     (5, 64, 4224, 256, 8),      # 4-bit forward split 8 ways, the last split of 3 stages
+    (2, 1000, 1024, 1008, 8),   # MLP-sized layer with ragged rows and columns
+    (2, 77, 1008, 80, 3),       # rank 3 of 4; a last 64-wide k step three-quarters full
+    (2, 5, 48, 1024, 5),        # rows shorter than one 64-wide k step, rank 5 of 8
+    (2, 64, 784, 16, 8),        # one output tile, one 16-column block used
 ]
 
 
